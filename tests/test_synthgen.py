@@ -1,0 +1,87 @@
+"""Synthetic-input generator: known answers, determinism, slice regeneration, workload statistics."""
+import os
+
+import numpy as np
+import pytest
+
+import synthgen as sg
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def test_philox_known_answers():
+    with open(os.path.join(HERE, "golden", "philox4x32_10_kat.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 3
+    for row in rows:
+        v = [int(h, 16) for h in row]
+        assert sg.philox4x32_10(v[0:4], v[4:6]) == tuple(v[6:10])
+
+
+def test_deterministic_and_sliceable():
+    wl = sg.workload("c1")
+    a = sg.layer_host(wl, 0)
+    b = sg.layer_host(wl, 0)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+    # rows 100..109 of W_up regenerate alone, bit for bit
+    key = sg.key_seed(wl.index)
+    part = np.empty((10, wl.D), dtype=np.float16)
+    sg.fill_normal(part, key, sg.TAG_W_UP, 0, wl.sigma_w, start=100 * wl.D)
+    assert np.array_equal(part.view(np.uint16), a["W_up"][100:110].view(np.uint16))
+    # different layers / tags differ
+    c = sg.layer_host(wl, 1)
+    assert not np.array_equal(a["W_up"], c["W_up"])
+    assert not np.array_equal(a["W_up"], a["W_down"].T)
+
+
+def test_thread_count_does_not_change_bits(monkeypatch):
+    wl = sg.workload("c1")
+    key = sg.key_seed(wl.index)
+    a = np.empty(300_000, dtype=np.float16)
+    sg.fill_normal(a, key, sg.TAG_W_UP, 0, 0.02)
+    monkeypatch.setenv("SYNTH_THREADS", "1")
+    b = np.empty_like(a)
+    sg.fill_normal(b, key, sg.TAG_W_UP, 0, 0.02)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_normal_moments_and_range():
+    key = sg.key_seed(0)
+    a = np.empty(1 << 20, dtype=np.float32)
+    sg.fill_normal(a, key, sg.TAG_X_TEST, 0, 1.0)
+    assert abs(a.mean()) < 5e-3 and abs(a.std() - 1.0) < 5e-3
+    assert np.abs(a).max() <= 262140 / sg.IH8_STD + 1e-3   # Irwin-Hall support
+    q = np.empty(1 << 16, dtype=np.uint8)
+    sg.fill_q4(q, key, sg.TAG_Q_UP, 0)
+    assert q.max() == 15 and q.min() == 0 and abs(q.mean() - 7.5) < 0.1
+    s = np.empty(1 << 16, dtype=np.float16)
+    sg.fill_scales(s, key, sg.TAG_S_UP, 0)
+    sf = s.astype(np.float64)
+    assert sf.min() >= 0.001 - 1e-6 and sf.max() <= 0.01 + 1e-5 and abs(sf.mean() - 0.0055) < 1e-4
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_zipf_profile(name):
+    wl = sg.workload(name)
+    p = sg.zipf_probs(wl.F, wl.zipf_s, wl.density)
+    assert abs(p.mean() - wl.density) < 1e-9
+    assert p.max() <= sg.ZIPF_CAP and np.all(np.diff(p) <= 0) and p.min() > 0
+    ranks = sg.neuron_ranks(wl, 0)
+    assert sorted(ranks.tolist()) == list(range(1, wl.F + 1))
+
+
+def test_firing_rate_matches_profile():
+    wl = sg.workload("c1")
+    t = sg.layer_host(wl, 0)
+    X = np.stack([sg.inputs(wl, s, 1, tag=sg.TAG_X_TEST)[0] for s in range(4096)]).astype(np.float64)
+    pre = X @ t["W_up"].astype(np.float64).T + t["b_up"].astype(np.float64)[None, :]
+    rate = (pre > 0).mean(axis=0)
+    p = sg.neuron_probs(wl, 0)
+    assert abs(rate.mean() - wl.density) < 0.01
+    tol = 5 * np.sqrt(p * (1 - p) / 4096) + 0.01
+    assert np.mean(np.abs(rate - p) <= tol) > 0.995
+    # calibrated predictor marks about the target share; without c it marks about half
+    z = (X @ t["P1"].astype(np.float64).T) @ t["P2"].astype(np.float64).T
+    assert abs(((z + t["c"][None, :]) > 0).mean() - wl.density) < 0.01
+    assert abs((z > 0).mean() - 0.5) < 0.02
