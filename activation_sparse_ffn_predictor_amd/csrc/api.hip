@@ -1,0 +1,158 @@
+// C ABI of libsffn: argument checks (host only, before anything is enqueued) and dispatch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/sffn.h"
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SFFN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int MAX_B = 64, MAX_D = 16384, MAX_F = 1 << 22, MAX_R = 1024, MAX_BR = 32768, MAX_BD_VALU = 16384;
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool al(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_common(int B, int D, int F) {
+  if (B < 1 || B > MAX_B) return fail(SFFN_ERR_SHAPE, "B=%d outside [1, %d]", B, MAX_B);
+  if (D < 8 || D > MAX_D || D % 8) return fail(SFFN_ERR_SHAPE, "D=%d: need 8 <= D <= %d, D %% 8 == 0", D, MAX_D);
+  if (F < 1 || F > MAX_F) return fail(SFFN_ERR_SHAPE, "F=%d outside [1, %d]", F, MAX_F);
+  return SFFN_OK;
+}
+
+// Workspace layout: [activations a: F * B fp32][predictor h: B * r fp32], each part 256-byte aligned.
+// sffn_forward uses only the first part, sffn_predict only the second.
+size_t ws_forward_bytes(int B, int F) { return align256((size_t)F * B * sizeof(float)); }
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return fail(SFFN_ERR_NULL, "workspace is NULL");
+  if (!al(ws, 256)) return fail(SFFN_ERR_ALIGN, "workspace not 256-byte aligned");
+  if (ws_bytes < need) return fail(SFFN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  return SFFN_OK;
+}
+
+// batch sizes the decode-batch kernels are built for
+int check_forward_batch(int B, int D) {
+  if (!(B == 1 || B == 2 || B == 4 || B == 8) || (size_t)B * D > MAX_BD_VALU)
+    return fail(SFFN_ERR_SHAPE, "forward: B=%d with D=%d not supported (B in {1,2,4,8} and B*D <= %d)", B, D,
+                MAX_BD_VALU);
+  return SFFN_OK;
+}
+
+float* ws_abuf(void* ws) { return (float*)ws; }
+float* ws_hbuf(void* ws, int B, int F) { return (float*)((char*)ws + ws_forward_bytes(B, F)); }
+
+}  // namespace
+
+extern "C" {
+
+const char* sffn_status_string(int s) {
+  switch (s) {
+    case SFFN_OK: return "ok";
+    case SFFN_ERR_NULL: return "null pointer";
+    case SFFN_ERR_SHAPE: return "shape out of range";
+    case SFFN_ERR_ALIGN: return "misaligned pointer";
+    case SFFN_ERR_WORKSPACE: return "workspace too small";
+    case SFFN_ERR_ACT: return "bad activation or missing operand";
+    case SFFN_ERR_ARG: return "bad argument";
+    case SFFN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sffn_last_error(void) { return g_err; }
+
+size_t sffn_workspace_size(int B, int D, int F, int r) {
+  (void)D;
+  if (B < 1 || F < 1 || r < 1) return 0;
+  return ws_forward_bytes(B, F) + align256((size_t)B * r * sizeof(float));
+}
+
+int sffn_mask_words(int F) { return F < 1 ? 0 : (F + 63) / 64; }
+
+int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_rms, int B, int D, int F, int r,
+                 float t, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!P1 || !P2 || !x || !mask) return fail(SFFN_ERR_NULL, "predict: P1, P2, x and mask are required");
+  int s = check_common(B, D, F);
+  if (s) return s;
+  if (r < 8 || r > MAX_R || r % 8) return fail(SFFN_ERR_SHAPE, "r=%d: need 8 <= r <= %d, r %% 8 == 0", r, MAX_R);
+  if ((long)B * r > MAX_BR) return fail(SFFN_ERR_SHAPE, "B*r=%ld > %d", (long)B * r, MAX_BR);
+  if (!(t > 0.f && t < 1.f)) return fail(SFFN_ERR_ARG, "threshold t=%g outside (0, 1)", (double)t);
+  if (!al(P1, 16) || !al(P2, 16) || !al(x, 16) || !al(mask, 8) || (c && !al(c, 4)) || (logits && !al(logits, 4)))
+    return fail(SFFN_ERR_ALIGN, "predict: misaligned pointer");
+  s = check_ws(ws, ws_bytes, sffn_workspace_size(B, D, F, r));
+  if (s) return s;
+  const float tau = (float)log((double)t / (1.0 - (double)t));
+  hipError_t e = sffn_launch_predict(P1, P2, c, x, x_rms, B, D, F, r, tau, mask, logits, ws_hbuf(ws, B, F),
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? SFFN_OK : hip_fail(e, "predict launch");
+}
+
+int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W_up, const float* b_up,
+                 const void* W_downT, const float* x, int x_rms, int B, int D, int F, const uint64_t* mask,
+                 int32_t* active, int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU) return fail(SFFN_ERR_ACT, "unknown activation %d", act);
+  if (act == SFFN_ACT_REGLU && !W_gate) return fail(SFFN_ERR_ACT, "ReGLU needs W_gate");
+  if (!W_up || !W_downT || !x || !mask || !active || !n_active || !y)
+    return fail(SFFN_ERR_NULL, "forward: W_up, W_downT, x, mask, active, n_active and y are required");
+  int s = check_common(B, D, F);
+  if (s) return s;
+  s = check_forward_batch(B, D);
+  if (s) return s;
+  if ((act == SFFN_ACT_REGLU && !al(W_gate, 16)) || !al(W_up, 16) || !al(W_downT, 16) || !al(x, 16) ||
+      !al(mask, 8) || !al(active, 4) || !al(n_active, 4) || !al(y, 16) || (b_gate && !al(b_gate, 4)) ||
+      (b_up && !al(b_up, 4)))
+    return fail(SFFN_ERR_ALIGN, "forward: misaligned pointer");
+  s = check_ws(ws, ws_bytes, ws_forward_bytes(B, F));
+  if (s) return s;
+  hipError_t e = sffn_launch_forward(act, act == SFFN_ACT_REGLU ? W_gate : nullptr, act == SFFN_ACT_REGLU ? b_gate : nullptr,
+                                     W_up, act == SFFN_ACT_RELU ? b_up : nullptr, W_downT, x, x_rms, B, D, F, mask,
+                                     active, n_active, y, ws_abuf(ws), (hipStream_t)stream);
+  return e == hipSuccess ? SFFN_OK : hip_fail(e, "forward launch");
+}
+
+int sffn_forward_q4(int act, sffn_q4 W_gate, const float* b_gate, sffn_q4 W_up, const float* b_up, sffn_q4 W_downT,
+                    const float* x, int x_rms, int B, int D, int F, const uint64_t* mask, int32_t* active,
+                    int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU) return fail(SFFN_ERR_ACT, "unknown activation %d", act);
+  if (act == SFFN_ACT_REGLU && (!W_gate.q || !W_gate.s)) return fail(SFFN_ERR_ACT, "ReGLU needs W_gate");
+  if (!W_up.q || !W_up.s || !W_downT.q || !W_downT.s || !x || !mask || !active || !n_active || !y)
+    return fail(SFFN_ERR_NULL, "forward_q4: W_up, W_downT, x, mask, active, n_active and y are required");
+  int s = check_common(B, D, F);
+  if (s) return s;
+  if (D % 32) return fail(SFFN_ERR_SHAPE, "forward_q4: D=%d not a multiple of 32", D);
+  s = check_forward_batch(B, D);
+  if (s) return s;
+  if ((act == SFFN_ACT_REGLU && (!al(W_gate.q, 16) || !al(W_gate.s, 2))) || !al(W_up.q, 16) || !al(W_up.s, 2) ||
+      !al(W_downT.q, 16) || !al(W_downT.s, 2) || !al(x, 16) || !al(mask, 8) || !al(active, 4) ||
+      !al(n_active, 4) || !al(y, 16) || (b_gate && !al(b_gate, 4)) || (b_up && !al(b_up, 4)))
+    return fail(SFFN_ERR_ALIGN, "forward_q4: misaligned pointer");
+  s = check_ws(ws, ws_bytes, ws_forward_bytes(B, F));
+  if (s) return s;
+  const bool g = act == SFFN_ACT_REGLU;
+  hipError_t e = sffn_launch_forward_q4(act, g ? W_gate.q : nullptr, g ? W_gate.s : nullptr, g ? b_gate : nullptr,
+                                        W_up.q, W_up.s, g ? nullptr : b_up, W_downT.q, W_downT.s, x, x_rms, B, D, F,
+                                        mask, active, n_active, y, ws_abuf(ws), (hipStream_t)stream);
+  return e == hipSuccess ? SFFN_OK : hip_fail(e, "forward_q4 launch");
+}
+
+}  // extern "C"

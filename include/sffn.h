@@ -1,0 +1,131 @@
+/* sffn.h -- predictor-guided, neuron-aware sparse FFN for one MI355X (gfx950).
+ *
+ * C ABI of libsffn.so. Every entry point takes plain pointers and sizes; all
+ * tensor pointers are DEVICE pointers owned by the caller, and the library
+ * never allocates device memory. Calls enqueue work on `stream` (a
+ * hipStream_t, NULL = the null stream) and return at once; results are valid
+ * once the stream has reached them. No call synchronises the device, so a
+ * sequence of calls can be captured into a HIP graph.
+ *
+ * The operation follows the PowerInfer pages:
+ *   - "Online stage: neuron-aware inference engine" and "Adaptive sparsity
+ *     predictors" (Turkish article): a small per-layer predictor runs on every
+ *     token, marks the neurons that will be active, and the engine skips the
+ *     rest;
+ *   - "Neuron-aware operator" (same article): the sparse operators work on
+ *     individual rows and columns of the weight matrices, never a dense copy;
+ *   - "Neuron placement and management" (same article): neurons are stored in
+ *     a chosen order and a table maps each back to its original position;
+ *   - summary bullets and "Limitations/FAQ" (Indonesian digest): ReLU-family
+ *     FFNs (ReLU, ReGLU); "Quantization": INT4 Q4_0 weights.
+ *
+ * Notation. D = d_model, F = d_ffn (neurons), r = predictor rank, B = tokens
+ * of one call (1 for decode; B > 1 computes every token over the union of the
+ * per-token masks). "Stored order" is the caller's neuron order (a
+ * permutation of the original one); the library never sees the permutation:
+ * every per-neuron array (rows of P2, W_gate, W_up, W_down^T, b, c) must be
+ * given in the same stored order, and the caller maps ids back.
+ *
+ * Layouts (row-major, contiguous):
+ *   x        [B, D] fp32           token inputs
+ *   P1       [r, D] fp16           predictor first factor
+ *   P2       [F, r] fp16           predictor second factor (stored order)
+ *   c        [F]    fp32 or NULL   predictor bias
+ *   W_gate   [F, D] fp16           ReGLU gate rows (stored order), b_gate [F] fp32
+ *   W_up     [F, D] fp16           up rows, b_up [F] fp32 (ReLU)
+ *   W_downT  [F, D] fp16           W_down transposed: row k = column k of W_down
+ *   mask     [ceil(F/64)] uint64   bit (k % 64) of word k / 64 = stored neuron k active
+ *   y        [B, D] fp32
+ * Q4_0 matrices (sffn_q4): blocks of 32 consecutive weights along d_model in
+ * every neuron row, w = (q - 8) * s with q in 0..15:
+ *   q  [F, D/2] uint8: for block j of a row, bytes 16j..16j+15; byte i holds
+ *      element 32j+i in its low nibble and element 32j+16+i in its high nibble
+ *   s  [F, D/32] fp16 scale of each block.
+ *
+ * Alignment: every tensor pointer 16-byte aligned; the workspace 256-byte
+ * aligned. Limits: 1 <= B <= 64; 8 <= D <= 16384 with D % 8 == 0 (D % 32 == 0
+ * for Q4_0); 1 <= F <= 1<<22; 8 <= r <= 1024 with r % 8 == 0; B * r <= 32768.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; a
+ * failed check returns its status and leaves the stream untouched. A failed
+ * launch returns SFFN_ERR_HIP. sffn_last_error() gives the detail text of the
+ * calling thread's last failure. No exception crosses the ABI.
+ */
+#ifndef SFFN_H
+#define SFFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SFFN_OK = 0,
+  SFFN_ERR_NULL = 1,       /* a required pointer is NULL                      */
+  SFFN_ERR_SHAPE = 2,      /* B, D, F or r outside the limits above            */
+  SFFN_ERR_ALIGN = 3,      /* a pointer is not aligned as required             */
+  SFFN_ERR_WORKSPACE = 4,  /* workspace smaller than sffn_workspace_size()     */
+  SFFN_ERR_ACT = 5,        /* unknown activation, or operands it needs missing */
+  SFFN_ERR_ARG = 6,        /* other bad argument (threshold outside (0, 1))    */
+  SFFN_ERR_HIP = 7         /* the HIP runtime reported an error                */
+} sffn_status;
+
+typedef enum {
+  SFFN_ACT_RELU = 0,   /* a_k = max(0, W_up[k] x + b_up[k])                        */
+  SFFN_ACT_REGLU = 1   /* a_k = max(0, W_gate[k] x + b_gate[k]) * (W_up[k] x)      */
+} sffn_act;
+
+/* One Q4_0 matrix (device pointers, layout above). */
+typedef struct {
+  const uint8_t* q;
+  const void* s;
+} sffn_q4;
+
+/* Text of a status code (static storage). */
+const char* sffn_status_string(int status);
+
+/* Detail of the calling thread's last failure ("" if none). */
+const char* sffn_last_error(void);
+
+/* Bytes of workspace that sffn_predict / sffn_forward / sffn_forward_q4 need for these sizes. */
+size_t sffn_workspace_size(int B, int D, int F, int r);
+
+/* Number of 64-bit mask words for F neurons: ceil(F / 64). */
+int sffn_mask_words(int F);
+
+/* Activation predictor ("Adaptive sparsity predictors"; "Online stage").
+ *   h[b, :] = P1 xn[b, :]                     (fp32 accumulate; h is never rounded)
+ *   z[b, k] = P2[k, :] h[b, :] + c[k]         (c = NULL means 0)
+ *   neuron k active  <=>  sigmoid(z[b, k]) > t for some token b
+ *                    <=>  z[b, k] > ln(t / (1 - t))  (decided in logit space)
+ * xn = x, or, if x_rms != 0, xn[b, :] = x[b, :] / sqrt(mean(x[b, :]^2) + 1e-6)
+ * (the parameter-free normalisation between stacked layers).
+ * Outputs: mask (every word written, bits >= F zero); logits [B, F] fp32 if
+ * non-NULL. Uses the workspace. Two kernels. */
+int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_rms, int B, int D, int F,
+                 int r, float t, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/* Neuron-aware sparse FFN over the neurons set in `mask` ("Neuron-aware operator").
+ *   compaction: active[0 .. n) = ascending stored ids of the set bits, *n_active = n
+ *   a[b, j]  = act(row active[j] of W_gate / W_up, xn[b, :])   (only active rows are read)
+ *   y[b, :]  = sum_j a[b, j] * W_downT[active[j], :]          (only active rows are read)
+ * xn as in sffn_predict. W_gate / b_gate are used (and required) for REGLU only;
+ * b_up may be NULL (0). active [F] int32 and n_active [1] int32 are device
+ * outputs; y [B, D] is overwritten. Uses the workspace. Two kernels. */
+int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W_up, const float* b_up,
+                 const void* W_downT, const float* x, int x_rms, int B, int D, int F, const uint64_t* mask,
+                 int32_t* active, int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* sffn_forward with Q4_0 weights ("Quantization": INT4 Q4_0); weights are
+ * dequantised in registers, w = (q - 8) * s exactly in fp32. */
+int sffn_forward_q4(int act, sffn_q4 W_gate, const float* b_gate, sffn_q4 W_up, const float* b_up, sffn_q4 W_downT,
+                    const float* x, int x_rms, int B, int D, int F, const uint64_t* mask, int32_t* active,
+                    int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFFN_H */

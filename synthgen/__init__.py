@@ -134,6 +134,8 @@ def lib():
         h.synth_fill_q4.argtypes = [vp, i32, u64, u32, u32, u64, u64, vp]
         h.synth_fill_uniform_f16.argtypes = [vp, i32, u64, u32, u32, u64, u64, f32, f32, vp]
         h.synth_philox4x32_10.argtypes = [ctypes.POINTER(u32), ctypes.POINTER(u32), ctypes.POINTER(u32)]
+        h.synth_f32_to_f16.argtypes = [vp, vp, u64]
+        h.synth_f32_to_f16.restype = None
         for f in ("synth_fill_normal_f16", "synth_fill_normal_f32", "synth_fill_q4", "synth_fill_uniform_f16"):
             getattr(h, f).restype = i32
         h.synth_philox4x32_10.restype = None
@@ -147,6 +149,14 @@ def philox4x32_10(ctr: Sequence[int], key: Sequence[int]) -> Tuple[int, int, int
     o = (ctypes.c_uint32 * 4)()
     lib().synth_philox4x32_10(c, k, o)
     return tuple(int(v) for v in o)
+
+
+def f32_to_f16(a: np.ndarray) -> np.ndarray:
+    """The generator's own fp32 -> fp16 (round to nearest even) conversion, for tests."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.float16)
+    lib().synth_f32_to_f16(a.ctypes.data, out.ctypes.data, a.size)
+    return out
 
 
 def key_seed(wl_index: int, seed: int = MASTER_SEED) -> int:

@@ -10,8 +10,8 @@
 // (idx_lo, idx_hi, tag, layer), key = (seed_lo, seed_hi).
 //
 // Value transforms use only integer arithmetic plus a single correctly rounded
-// fp32 operation and an fp32->fp16 round-to-nearest-even conversion, so host
-// and device agree bit for bit:
+// fp32 operation and an integer-only fp32->fp16 round-to-nearest-even
+// conversion, so host and device agree bit for bit:
 //   normal  : Irwin-Hall sum of eight 16-bit uniforms, centred (an integer n
 //             with |n| <= 262140), then (float)n * scale, scale = sigma/std.
 //   q4      : low 4 bits of the first output word (uniform on 0..15).
@@ -66,11 +66,29 @@ __host__ __device__ inline int32_t ih8(const P4& o) {
   return s - 262140;
 }
 
+// fp32 -> fp16 bits, round to nearest, ties to even, written with integer operations only so that host and
+// device give the same bits without depending on a conversion instruction's rounding mode.
 __host__ __device__ inline uint16_t f32_to_f16_bits(float f) {
-  _Float16 h = (_Float16)f;
-  uint16_t b;
-  memcpy(&b, &h, 2);
-  return b;
+  uint32_t x;
+  memcpy(&x, &f, 4);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax > 0x7F800000u) return (uint16_t)(sign | 0x7E00u);           // NaN
+  if (ax >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u);          // >= 65520 rounds to infinity
+  if (ax < 0x38800000u) {                                            // below 2^-14: fp16 subnormal or zero
+    const int e = (int)(ax >> 23);
+    if (e < 102) return (uint16_t)sign;                              // < 2^-25: rounds to zero
+    const uint32_t m = (ax & 0x7FFFFFu) | 0x800000u;
+    const int sh = 126 - e;                                          // 14..24
+    uint32_t r = m >> sh;
+    const uint32_t rem = m & ((1u << sh) - 1u), half = 1u << (sh - 1);
+    if (rem > half || (rem == half && (r & 1u))) ++r;
+    return (uint16_t)(sign | r);
+  }
+  uint32_t r = (((ax >> 23) - 112u) << 10) | ((ax & 0x7FFFFFu) >> 13);
+  const uint32_t rem = ax & 0x1FFFu;
+  if (rem > 0x1000u || (rem == 0x1000u && (r & 1u))) ++r;           // a carry may step into the exponent
+  return (uint16_t)(sign | r);
 }
 
 enum Kind { K_NORMAL_F16 = 0, K_NORMAL_F32 = 1, K_Q4 = 2, K_UNIFORM_F16 = 3 };
@@ -140,6 +158,11 @@ int fill(int kind, void* out, int on_device, uint64_t seed, uint32_t tag, uint32
 }  // namespace
 
 extern "C" {
+
+// The fp32 -> fp16 conversion used by the fills (host), for tests.
+void synth_f32_to_f16(const float* in, uint16_t* out, uint64_t n) {
+  for (uint64_t i = 0; i < n; ++i) out[i] = f32_to_f16_bits(in[i]);
+}
 
 // Raw Philox4x32-10 block, for known-answer tests.
 void synth_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {

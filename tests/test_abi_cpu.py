@@ -1,0 +1,103 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry point, and rejects bad
+arguments on the host before anything is enqueued (fake, never-dereferenced pointers)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sffn.h")
+
+from activation_sparse_ffn_predictor_amd import _lib  # noqa: E402
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sffn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("sffn_predict", "sffn_forward", "sffn_forward_q4", "sffn_workspace_size", "sffn_status_string",
+              "sffn_last_error", "sffn_mask_words"):
+        assert n in names
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    h = _lib.lib()
+    for n in declared_functions():
+        assert hasattr(h, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings_and_sizes():
+    assert _lib.status_string(0) == "ok"
+    assert "workspace" in _lib.status_string(4)
+    assert _lib.mask_words(1) == 1 and _lib.mask_words(64) == 1 and _lib.mask_words(65) == 2
+    # [a: F*B fp32][h: B*r fp32], 256-byte parts
+    assert _lib.workspace_size(1, 4096, 11008, 256) == 44032 + 1024
+    assert _lib.workspace_size(8, 512, 100, 64) == 3328 + 2048
+
+
+A = 0x10000          # fake, 256-byte aligned, never dereferenced
+MIS = 0x10002        # fake, misaligned
+
+
+def _predict(**kw):
+    a = dict(P1=A, P2=A, c=None, x=A, x_rms=0, B=1, D=512, F=2048, r=64, t=0.5, mask=A, logits=None, ws=A,
+             ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return _lib.lib().sffn_predict(*a.values())
+
+
+def _forward(**kw):
+    a = dict(act=0, Wg=None, bg=None, Wu=A, bu=A, WdT=A, x=A, x_rms=0, B=1, D=512, F=2048, mask=A, active=A,
+             n_active=A, y=A, ws=A, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return _lib.lib().sffn_forward(*a.values())
+
+
+def _forward_q4(**kw):
+    Q = _lib._Q4(A, A)
+    a = dict(act=1, Wg=Q, bg=A, Wu=Q, bu=None, WdT=Q, x=A, x_rms=0, B=1, D=512, F=2048, mask=A, active=A, n_active=A,
+             y=A, ws=A, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return _lib.lib().sffn_forward_q4(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P1=None), 1), (dict(x=None), 1), (dict(mask=None), 1), (dict(ws=None), 1),
+    (dict(B=0), 2), (dict(B=65), 2), (dict(D=4), 2), (dict(D=100), 2), (dict(D=16392), 2), (dict(F=0), 2),
+    (dict(r=4), 2), (dict(r=100), 2), (dict(r=1032), 2), (dict(B=64, r=1024), 2),
+    (dict(t=0.0), 6), (dict(t=1.0), 6), (dict(t=float("nan")), 6),
+    (dict(P1=MIS), 3), (dict(x=MIS), 3), (dict(ws=A + 16), 3),
+    (dict(ws_bytes=100), 4),
+])
+def test_predict_rejects(kw, status):
+    assert _predict(**kw) == status
+    assert _lib.lib().sffn_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(act=7), 5), (dict(act=1, Wg=None), 5),
+    (dict(Wu=None), 1), (dict(WdT=None), 1), (dict(y=None), 1), (dict(active=None), 1), (dict(n_active=None), 1),
+    (dict(B=3), 2), (dict(B=8, D=4096), 2),
+    (dict(Wu=MIS), 3), (dict(y=A + 4), 3),
+    (dict(ws_bytes=16), 4),
+])
+def test_forward_rejects(kw, status):
+    assert _forward(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(act=1, Wg=_lib._Q4(None, None)), 5), (dict(Wu=_lib._Q4(A, None)), 1), (dict(D=520), 2),
+    (dict(WdT=_lib._Q4(MIS, A)), 3), (dict(ws_bytes=0), 4), (dict(B=16), 2),
+])
+def test_forward_q4_rejects(kw, status):
+    assert _forward_q4(**kw) == status

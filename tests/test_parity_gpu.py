@@ -1,0 +1,135 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on identical seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import synthgen as sg
+from parity_util import check, make_case, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _x(wl, B, step=0, tag=sg.TAG_X_TEST):
+    return sg.inputs(wl, step, B, tag=tag)
+
+
+def small(base, **kw):
+    return sg.custom(sg.workload(base), **kw)
+
+
+# reduced shapes: several 64-neuron tiles plus a ragged tail, ragged predictor rank
+SMALL = [
+    ("relu_f16", small("c1", D=256, F=1000, r=72, L=1)),
+    ("reglu_f16", small("c2", D=512, F=1250, r=64, L=1, density=0.2)),
+    ("reglu_q4", small("c5", D=512, F=700, r=40, L=1, density=0.3)),
+    ("relu_q4", sg.custom(small("c5", D=256, F=333, r=8, L=1), act="relu", density=0.25)),
+]
+
+
+@pytest.mark.parametrize("name,wl", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("B", [1, 2, 4, 8])
+def test_small_layers(gpu_ready, name, wl, B):
+    if B * wl.D > 16384:
+        pytest.skip("decode-batch kernels take B * D <= 16384")
+    case = make_case(wl, 0, gpu_ready)
+    for step in range(3):
+        x = _x(wl, B, step)
+        say(f"[{name}] B={B} step={step}")
+        res = run_gpu(case, torch.from_numpy(x).to(gpu_ready))
+        st = check(case, x, res)
+        say("   ", st)
+        assert st["logit_err"] < 1e-4
+
+
+@pytest.mark.parametrize("name,wl", SMALL[:3], ids=[s[0] for s in SMALL[:3]])
+def test_rms_input_and_no_predictor_bias(gpu_ready, name, wl):
+    case = make_case(wl, 0, gpu_ready, with_c=False)
+    x = 3.7 * _x(wl, 1, 5)                    # un-normalised input; the library normalises on load
+    res = run_gpu(case, torch.from_numpy(x).to(gpu_ready), x_rms=True)
+    st = check(case, x, res, x_rms=True)
+    say(name, st)
+    assert 0.3 < st["density"] < 0.7          # no bias: about half the neurons are marked
+
+
+@pytest.mark.parametrize("perm", ["identity", "random"])
+def test_permutation_invariance(gpu_ready, perm):
+    wl = SMALL[1][1]
+    x = _x(wl, 1, 2)
+    ys = []
+    for p in ("hot", perm):
+        case = make_case(wl, 0, gpu_ready, perm=p)
+        res = run_gpu(case, torch.from_numpy(x).to(gpu_ready))
+        check(case, x, res)
+        ys.append(res["y"])
+    assert np.max(np.abs(ys[0] - ys[1])) <= 1e-5 * np.max(np.abs(ys[0]))
+
+
+@pytest.mark.parametrize("t,expect", [(1e-30, "all"), (1.0 - 1e-7, "none")])
+def test_all_and_none_active(gpu_ready, t, expect):
+    wl = SMALL[0][1]
+    case = make_case(wl, 0, gpu_ready)
+    x = _x(wl, 1, 1)
+    res = run_gpu(case, torch.from_numpy(x).to(gpu_ready), t=t)
+    check(case, x, res, t=t)
+    if expect == "all":
+        assert res["n"] == wl.F
+    else:
+        assert res["n"] == 0 and np.all(res["y"] == 0.0)
+
+
+@pytest.mark.parametrize("F", [1, 63, 64, 65, 129])
+def test_tiny_neuron_counts(gpu_ready, F):
+    wl = small("c1", D=64, F=F, r=8, L=1, density=0.5)
+    case = make_case(wl, 0, gpu_ready)
+    for t in (1e-30, 0.5):
+        x = _x(wl, 1, 3)
+        res = run_gpu(case, torch.from_numpy(x).to(gpu_ready), t=t)
+        check(case, x, res, t=t)
+
+
+def test_minimum_d_q4(gpu_ready):
+    wl = small("c5", D=32, F=200, r=8, L=1, density=0.5)
+    case = make_case(wl, 0, gpu_ready)
+    x = _x(wl, 1, 0)
+    check(case, x, run_gpu(case, torch.from_numpy(x).to(gpu_ready)))
+
+
+def test_deterministic_reruns(gpu_ready):
+    wl = SMALL[1][1]
+    case = make_case(wl, 0, gpu_ready)
+    x = torch.from_numpy(_x(wl, 1, 4)).to(gpu_ready)
+    a, b = run_gpu(case, x), run_gpu(case, x)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["mask"], b["mask"])
+
+
+def test_device_generator_matches_host(gpu_ready):
+    for name in ("c1", "c5"):
+        wl = sg.workload(name)
+        wl = sg.custom(wl, F=min(wl.F, 4096))
+        host = sg.layer_host(wl, 3)
+        dev = sg.layer_device(wl, 3, gpu_ready)
+        for k, v in host.items():
+            d = dev[k].cpu().numpy()
+            assert np.array_equal(v.view(np.uint8), d.view(np.uint8)), (name, k)
+    xh = sg.inputs(sg.workload("c2"), 7, 4)
+    xd = torch.empty((4, 4096), dtype=torch.float32, device=gpu_ready)
+    sg.inputs(sg.workload("c2"), 7, 4, out=xd)
+    assert np.array_equal(xh, xd.cpu().numpy())
+
+
+# full-size single layers of every workload (decode batch 1), input from the generator
+FULL = ["c1", "c2", "c3", "c4", "c5"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_layer(gpu_ready, name):
+    wl = sg.workload(name)
+    layer = 0 if wl.L == 1 else 1
+    say(f"[full {name}] generating layer {layer}")
+    case = make_case(wl, layer, gpu_ready)
+    for step in range(2):
+        x = _x(wl, 1, step, tag=sg.TAG_X_DECODE)
+        res = run_gpu(case, torch.from_numpy(x).to(gpu_ready))
+        st = check(case, x, res)
+        say(f"[full {name}] step {step}: {st}")
+        assert abs(st["density"] - wl.density) < 0.05

@@ -85,3 +85,21 @@ def test_firing_rate_matches_profile():
     z = (X @ t["P1"].astype(np.float64).T) @ t["P2"].astype(np.float64).T
     assert abs(((z + t["c"][None, :]) > 0).mean() - wl.density) < 0.01
     assert abs((z > 0).mean() - 0.5) < 0.02
+
+
+def test_fp16_conversion_is_round_to_nearest_even():
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 2 ** 32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    # exact ties between fp16 neighbours, fp16 subnormal range, overflow edge
+    m = rng.integers(0, 1 << 10, size=20000).astype(np.uint32)
+    e = rng.integers(100, 143, size=20000).astype(np.uint32)
+    ties = ((e << 23) | (m << 13) | 0x1000).view(np.float32)
+    edge = np.array([65504, 65519.99, 65520, 65536, 2 ** -24, 2 ** -25, 1.5 * 2 ** -25, 2 ** -26, 0.0, -0.0,
+                     6.1e-5, 5.96e-8], dtype=np.float32)
+    for v in (vals, ties, -ties, edge, -edge):
+        ours = sg.f32_to_f16(v).view(np.uint16)
+        with np.errstate(over="ignore"):
+            ref = v.astype(np.float16).view(np.uint16)
+        assert np.array_equal(ours, ref)
