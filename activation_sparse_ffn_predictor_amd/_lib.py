@@ -16,7 +16,8 @@ ACT_RELU, ACT_REGLU = 0, 1
 ACTS = {"relu": ACT_RELU, "reglu": ACT_REGLU}
 
 EXPORTS = ("sffn_status_string", "sffn_last_error", "sffn_workspace_size", "sffn_mask_words", "sffn_predict",
-           "sffn_forward", "sffn_forward_q4")
+           "sffn_forward", "sffn_forward_q4", "sffn_profile_begin", "sffn_profile_end")
+K_PRED_H, K_PRED_Z, K_ROWS, K_COLS = 0, 1, 2, 3
 
 
 class SffnError(RuntimeError):
@@ -51,6 +52,8 @@ def lib() -> ctypes.CDLL:
         h.sffn_forward.restype = i32
         h.sffn_forward_q4.argtypes = [i32, _Q4, vp, _Q4, vp, _Q4, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         h.sffn_forward_q4.restype = i32
+        h.sffn_profile_begin.argtypes, h.sffn_profile_begin.restype = [i32, i32], i32
+        h.sffn_profile_end.argtypes, h.sffn_profile_end.restype = [ctypes.POINTER(ctypes.c_float), i32], i32
         _handle = h
     return _handle
 
@@ -88,35 +91,49 @@ def mask_words(F: int) -> int:
     return int(lib().sffn_mask_words(F))
 
 
-def predict(P1, P2, c, x, t: float, mask, ws, logits=None, x_rms: bool = False, stream=None):
+def predict(P1, P2, c, x, t: float, mask, ws, logits=None, x_norm: bool = False, stream=None):
     """sffn_predict. P1 [r, D] fp16, P2 [F, r] fp16, c [F] fp32 or None, x [B, D] fp32, mask [ceil(F/64)]
     int64 (bit pattern), ws uint8 workspace, logits [B, F] fp32 or None."""
     B, D = x.shape
     F, r = P2.shape
-    rc = lib().sffn_predict(_p(P1), _p(P2), _p(c), _p(x), int(bool(x_rms)), B, D, F, r, float(t), _p(mask), _p(logits),
+    rc = lib().sffn_predict(_p(P1), _p(P2), _p(c), _p(x), int(bool(x_norm)), B, D, F, r, float(t), _p(mask), _p(logits),
                             _p(ws), _nbytes(ws), _stream(stream, x))
     _check(rc, "sffn_predict")
 
 
-def forward(act, W_gate, b_gate, W_up, b_up, W_downT, x, mask, active, n_active, y, ws, x_rms: bool = False,
+def forward(act, W_gate, b_gate, W_up, b_up, W_downT, x, mask, active, n_active, y, ws, x_norm: bool = False,
             stream=None):
     """sffn_forward. W_gate/W_up/W_downT [F, D] fp16 in stored order, biases [F] fp32 or None,
     active [F] int32 and n_active [1] int32 outputs, y [B, D] fp32 output."""
     B, D = x.shape
     F = W_up.shape[0]
     rc = lib().sffn_forward(ACTS.get(act, act), _p(W_gate), _p(b_gate), _p(W_up), _p(b_up), _p(W_downT), _p(x),
-                            int(bool(x_rms)), B, D, F, _p(mask), _p(active), _p(n_active), _p(y), _p(ws), _nbytes(ws),
+                            int(bool(x_norm)), B, D, F, _p(mask), _p(active), _p(n_active), _p(y), _p(ws), _nbytes(ws),
                             _stream(stream, x))
     _check(rc, "sffn_forward")
 
 
-def forward_q4(act, W_gate, b_gate, W_up, b_up, W_downT, x, mask, active, n_active, y, ws, x_rms: bool = False,
+def forward_q4(act, W_gate, b_gate, W_up, b_up, W_downT, x, mask, active, n_active, y, ws, x_norm: bool = False,
                stream=None):
     """sffn_forward_q4. Each W is a pair (q [F, D/2] uint8, s [F, D/32] fp16) or None (W_gate for ReLU)."""
     B, D = x.shape
     F = W_up[0].shape[0]
     g = _Q4(*(map(_p, W_gate))) if W_gate is not None else _Q4(None, None)
     rc = lib().sffn_forward_q4(ACTS.get(act, act), g, _p(b_gate), _Q4(*map(_p, W_up)), _p(b_up),
-                               _Q4(*map(_p, W_downT)), _p(x), int(bool(x_rms)), B, D, F, _p(mask), _p(active),
+                               _Q4(*map(_p, W_downT)), _p(x), int(bool(x_norm)), B, D, F, _p(mask), _p(active),
                                _p(n_active), _p(y), _p(ws), _nbytes(ws), _stream(stream, x))
     _check(rc, "sffn_forward_q4")
+
+
+def profile_begin(kernel: int, max_launches: int):
+    """Bracket every launch of `kernel` (K_PRED_H, K_PRED_Z, K_ROWS, K_COLS) with HIP events."""
+    _check(lib().sffn_profile_begin(int(kernel), int(max_launches)), "sffn_profile_begin")
+
+
+def profile_end(max_launches: int):
+    """Per-launch elapsed milliseconds of the bracketed launches (list of floats)."""
+    buf = (ctypes.c_float * max(1, max_launches))()
+    n = lib().sffn_profile_end(buf, max_launches)
+    if n < 0:
+        _check(-n, "sffn_profile_end")
+    return [float(buf[i]) for i in range(min(n, max_launches))]

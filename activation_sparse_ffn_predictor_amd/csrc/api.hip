@@ -58,9 +58,74 @@ int check_forward_batch(int B, int D) {
 float* ws_abuf(void* ws) { return (float*)ws; }
 float* ws_hbuf(void* ws, int B, int F) { return (float*)((char*)ws + ws_forward_bytes(B, F)); }
 
+struct Prof {
+  int kernel = -1;
+  int max = 0;
+  int used = 0;
+  hipEvent_t* ev = nullptr;   // 2 * max events
+};
+thread_local Prof g_prof;
+
+void prof_free() {
+  if (g_prof.ev) {
+    for (int i = 0; i < 2 * g_prof.max; ++i) hipEventDestroy(g_prof.ev[i]);
+    delete[] g_prof.ev;
+  }
+  g_prof = Prof();
+}
+
 }  // namespace
 
+void sffn_prof_before(int kid, hipStream_t st) {
+  if (g_prof.kernel == kid && g_prof.used < g_prof.max) hipEventRecord(g_prof.ev[2 * g_prof.used], st);
+}
+
+void sffn_prof_after(int kid, hipStream_t st) {
+  if (g_prof.kernel == kid && g_prof.used < g_prof.max) {
+    hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st);
+    ++g_prof.used;
+  }
+}
+
 extern "C" {
+
+int sffn_profile_begin(int kernel, int max_launches) {
+  g_err[0] = 0;
+  if (kernel < SFFN_K_PRED_H || kernel > SFFN_K_COLS || max_launches < 1)
+    return fail(SFFN_ERR_ARG, "profile: bad kernel %d or count %d", kernel, max_launches);
+  prof_free();
+  g_prof.ev = new hipEvent_t[2 * (size_t)max_launches];
+  for (int i = 0; i < 2 * max_launches; ++i) {
+    hipError_t e = hipEventCreate(&g_prof.ev[i]);
+    if (e != hipSuccess) {
+      for (int k = 0; k < i; ++k) hipEventDestroy(g_prof.ev[k]);
+      delete[] g_prof.ev;
+      g_prof = Prof();
+      return hip_fail(e, "profile: hipEventCreate");
+    }
+  }
+  g_prof.kernel = kernel;
+  g_prof.max = max_launches;
+  return SFFN_OK;
+}
+
+int sffn_profile_end(float* ms, int max) {
+  g_err[0] = 0;
+  if (g_prof.kernel < 0) return -fail(SFFN_ERR_ARG, "profile: not started");
+  const int n = g_prof.used;
+  int rc = n;
+  if (n > 0) {
+    hipError_t e = hipEventSynchronize(g_prof.ev[2 * n - 1]);
+    if (e != hipSuccess) rc = -hip_fail(e, "profile: hipEventSynchronize");
+    for (int i = 0; rc >= 0 && i < n && i < max && ms; ++i) {
+      e = hipEventElapsedTime(&ms[i], g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+      if (e != hipSuccess) rc = -hip_fail(e, "profile: hipEventElapsedTime");
+    }
+  }
+  prof_free();
+  return rc;
+}
+
 
 const char* sffn_status_string(int s) {
   switch (s) {
@@ -86,7 +151,7 @@ size_t sffn_workspace_size(int B, int D, int F, int r) {
 
 int sffn_mask_words(int F) { return F < 1 ? 0 : (F + 63) / 64; }
 
-int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_rms, int B, int D, int F, int r,
+int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F, int r,
                  float t, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (!P1 || !P2 || !x || !mask) return fail(SFFN_ERR_NULL, "predict: P1, P2, x and mask are required");
@@ -100,13 +165,13 @@ int sffn_predict(const void* P1, const void* P2, const float* c, const float* x,
   s = check_ws(ws, ws_bytes, sffn_workspace_size(B, D, F, r));
   if (s) return s;
   const float tau = (float)log((double)t / (1.0 - (double)t));
-  hipError_t e = sffn_launch_predict(P1, P2, c, x, x_rms, B, D, F, r, tau, mask, logits, ws_hbuf(ws, B, F),
+  hipError_t e = sffn_launch_predict(P1, P2, c, x, x_norm, B, D, F, r, tau, mask, logits, ws_hbuf(ws, B, F),
                                      (hipStream_t)stream);
   return e == hipSuccess ? SFFN_OK : hip_fail(e, "predict launch");
 }
 
 int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W_up, const float* b_up,
-                 const void* W_downT, const float* x, int x_rms, int B, int D, int F, const uint64_t* mask,
+                 const void* W_downT, const float* x, int x_norm, int B, int D, int F, const uint64_t* mask,
                  int32_t* active, int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU) return fail(SFFN_ERR_ACT, "unknown activation %d", act);
@@ -124,13 +189,13 @@ int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W
   s = check_ws(ws, ws_bytes, ws_forward_bytes(B, F));
   if (s) return s;
   hipError_t e = sffn_launch_forward(act, act == SFFN_ACT_REGLU ? W_gate : nullptr, act == SFFN_ACT_REGLU ? b_gate : nullptr,
-                                     W_up, act == SFFN_ACT_RELU ? b_up : nullptr, W_downT, x, x_rms, B, D, F, mask,
+                                     W_up, act == SFFN_ACT_RELU ? b_up : nullptr, W_downT, x, x_norm, B, D, F, mask,
                                      active, n_active, y, ws_abuf(ws), (hipStream_t)stream);
   return e == hipSuccess ? SFFN_OK : hip_fail(e, "forward launch");
 }
 
 int sffn_forward_q4(int act, sffn_q4 W_gate, const float* b_gate, sffn_q4 W_up, const float* b_up, sffn_q4 W_downT,
-                    const float* x, int x_rms, int B, int D, int F, const uint64_t* mask, int32_t* active,
+                    const float* x, int x_norm, int B, int D, int F, const uint64_t* mask, int32_t* active,
                     int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU) return fail(SFFN_ERR_ACT, "unknown activation %d", act);
@@ -150,7 +215,7 @@ int sffn_forward_q4(int act, sffn_q4 W_gate, const float* b_gate, sffn_q4 W_up, 
   if (s) return s;
   const bool g = act == SFFN_ACT_REGLU;
   hipError_t e = sffn_launch_forward_q4(act, g ? W_gate.q : nullptr, g ? W_gate.s : nullptr, g ? b_gate : nullptr,
-                                        W_up.q, W_up.s, g ? nullptr : b_up, W_downT.q, W_downT.s, x, x_rms, B, D, F,
+                                        W_up.q, W_up.s, g ? nullptr : b_up, W_downT.q, W_downT.s, x, x_norm, B, D, F,
                                         mask, active, n_active, y, ws_abuf(ws), (hipStream_t)stream);
   return e == hipSuccess ? SFFN_OK : hip_fail(e, "forward_q4 launch");
 }

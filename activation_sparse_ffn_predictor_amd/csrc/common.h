@@ -7,12 +7,18 @@
 namespace sffn {
 
 constexpr int WAVE = 64;
-constexpr float RMS_EPS = 1e-6f;
+constexpr float NORM_EPS = 1e-6f;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float8v __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
   return v;
@@ -24,6 +30,59 @@ __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
   for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
   return v;
+}
+
+// Buffer loads (MUBUF, raw): one resource descriptor per tensor in scalar registers, a 32-bit byte offset per
+// lane. A lane whose offset is at or past the tensor's byte size reads zeros (hardware range check), so guarded
+// loads need neither branches nor selects and every load of a lane can be in flight at once. Tensors must be
+// smaller than 2 GiB; OOB is the offset used for lanes with nothing to load.
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
+constexpr uint32_t OOB = 0x80000000u;
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ Buf(const void* p, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000)) {}
+  __device__ __forceinline__ uint4 ld16(uint32_t off) const {
+    const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+  __device__ __forceinline__ float4 ldf4(uint32_t off) const {
+    const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+  }
+  __device__ __forceinline__ uint2 ld8(uint32_t off) const {
+    const v2u32 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return make_uint2(v.x, v.y);
+  }
+  __device__ __forceinline__ uint64_t ldu64(uint32_t off) const {
+    const v2u32 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return (uint64_t)v.x | ((uint64_t)v.y << 32);
+  }
+  __device__ __forceinline__ float ldf(uint32_t off) const {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+  }
+  __device__ __forceinline__ float ldh(uint32_t off) const {  // one fp16 value, widened
+    const unsigned short b = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    return (float)__builtin_bit_cast(_Float16, b);
+  }
+};
+__device__ __forceinline__ uint32_t boff(bool ok, uint32_t off) { return ok ? off : OOB; }
+
+// Branch-free guarded loads: the address is clamped to a valid element when `ok` is false and the value is
+// replaced afterwards, so the compiler emits straight-line loads that all stay in flight together.
+__device__ __forceinline__ uint4 ldg16(const uint4* __restrict__ p, size_t i, bool ok) {
+  const uint4 v = p[ok ? i : 0];
+  return ok ? v : make_uint4(0u, 0u, 0u, 0u);
+}
+__device__ __forceinline__ float4 ldgf4(const float4* __restrict__ p, size_t i, bool ok) {
+  const float4 v = p[ok ? i : 0];
+  return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+template <class T>
+__device__ __forceinline__ T ldg(const T* __restrict__ p, size_t i, bool ok, T dflt) {
+  const T v = p[ok ? i : 0];
+  return ok ? v : dflt;
 }
 
 __device__ __forceinline__ void f16x8_to_f32(const uint4& u, float* f) {
@@ -62,34 +121,215 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_tmp /* NT/64
   return lds_tmp[w] + inc - v;
 }
 
-// Stage xn[b, d] for b < nb, d < D into LDS (fp32, row stride D), normalising each token by its RMS if asked.
-// Every thread of the block takes part. red: >= (NT/64) * nb floats of LDS scratch. Deterministic: per-wave
+// Normalise one token held in registers across a wave: lane l holds chunks m (CW float4 each), chunk m valid
+// iff l + 64 m < nvalid (invalid chunks hold zeros and stay untouched). x' = (x - mean) / sqrt(var + eps) over
+// the D valid elements, mean first and then the centred variance (two wave reductions).
+template <int NCH, int CW>
+__device__ __forceinline__ void wave_norm_regs(float4 (&v)[NCH][CW], int nvalid, int D) {
+  const int lane = threadIdx.x & 63;
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < NCH; ++m)
+    if (lane + 64 * m < nvalid)
+#pragma unroll
+      for (int k = 0; k < CW; ++k) s += (v[m][k].x + v[m][k].y) + (v[m][k].z + v[m][k].w);
+  const float mu = wave_sum(s) / (float)D;
+  float q = 0.f;
+#pragma unroll
+  for (int m = 0; m < NCH; ++m)
+    if (lane + 64 * m < nvalid)
+#pragma unroll
+      for (int k = 0; k < CW; ++k) {
+        const float a = v[m][k].x - mu, b = v[m][k].y - mu, c = v[m][k].z - mu, d = v[m][k].w - mu;
+        q = fmaf(a, a, q); q = fmaf(b, b, q); q = fmaf(c, c, q); q = fmaf(d, d, q);
+      }
+  const float rs = 1.0f / sqrtf(wave_sum(q) / (float)D + NORM_EPS);
+#pragma unroll
+  for (int m = 0; m < NCH; ++m)
+    if (lane + 64 * m < nvalid)
+#pragma unroll
+      for (int k = 0; k < CW; ++k) {
+        v[m][k].x = (v[m][k].x - mu) * rs; v[m][k].y = (v[m][k].y - mu) * rs;
+        v[m][k].z = (v[m][k].z - mu) * rs; v[m][k].w = (v[m][k].w - mu) * rs;
+      }
+}
+
+// Stage xn[b, d] for b < nb, d < D into LDS (fp32, row stride D), normalising each token (centre, unit variance)
+// if asked. Every thread issues all of its global loads (at most XPT float4, nb * D <= 4 * NT * XPT) before its
+// first LDS write. red: >= 2 * (NT/64) * nb floats of LDS scratch. Deterministic: per-wave
 // partial sums are combined in wave order.
-template <int NT>
-__device__ __forceinline__ void stage_x(const float* __restrict__ x, int nb, int D, int x_rms, float* xs, float* red) {
-  const int n4 = D >> 2;  // D % 8 == 0
-  for (int b = 0; b < nb; ++b) {
-    const float4* src = reinterpret_cast<const float4*>(x + (size_t)b * D);
-    float4* dst = reinterpret_cast<float4*>(xs + (size_t)b * D);
-    for (int i = threadIdx.x; i < n4; i += NT) dst[i] = src[i];
+template <int NT, int XPT>
+__device__ __forceinline__ void stage_x(const float* __restrict__ x, int nb, int D, int x_norm, float* xs, float* red) {
+  // one straight-line round of loads: callers keep nb * D <= 4 * NT * XPT
+  const int n4 = (nb * D) >> 2;  // D % 8 == 0: rows are whole float4s
+  const Buf bx(x, (uint32_t)n4 * 16u);
+  float4* dst = reinterpret_cast<float4*>(xs);
+  float4 v[XPT];
+#pragma unroll
+  for (int k = 0; k < XPT; ++k) {
+    const int i = k * NT + threadIdx.x;
+    v[k] = bx.ldf4(boff(i < n4, (uint32_t)i * 16u));
+  }
+#pragma unroll
+  for (int k = 0; k < XPT; ++k) {
+    const int i = k * NT + threadIdx.x;
+    if (i < n4) dst[i] = v[k];
   }
   __syncthreads();
-  if (!x_rms) return;
+  if (!x_norm) return;
+  constexpr int NWB = NT / 64;
   const int w = threadIdx.x >> 6;
+  float* rs_ = red;               // [NWB][nb] sums
+  float* rq_ = red + NWB * nb;    // [NWB][nb] centred squares
   for (int b = 0; b < nb; ++b) {
     float s = 0.f;
-    for (int i = threadIdx.x; i < D; i += NT) { float v = xs[(size_t)b * D + i]; s = fmaf(v, v, s); }
+    for (int i = threadIdx.x; i < D; i += NT) s += xs[(size_t)b * D + i];
     s = wave_sum(s);
-    if ((threadIdx.x & 63) == 0) red[w * nb + b] = s;
+    if ((threadIdx.x & 63) == 0) rs_[w * nb + b] = s;
   }
   __syncthreads();
   for (int b = 0; b < nb; ++b) {
     float tot = 0.f;
-    for (int i = 0; i < NT / 64; ++i) tot += red[i * nb + b];
-    const float sc = 1.0f / sqrtf(tot / (float)D + RMS_EPS);
-    for (int i = threadIdx.x; i < D; i += NT) xs[(size_t)b * D + i] *= sc;
+    for (int i = 0; i < NWB; ++i) tot += rs_[i * nb + b];
+    const float mu = tot / (float)D;
+    float q = 0.f;
+    for (int i = threadIdx.x; i < D; i += NT) { const float d = xs[(size_t)b * D + i] - mu; q = fmaf(d, d, q); }
+    q = wave_sum(q);
+    if ((threadIdx.x & 63) == 0) rq_[w * nb + b] = q;
   }
   __syncthreads();
+  for (int b = 0; b < nb; ++b) {
+    float tot = 0.f, totq = 0.f;
+    for (int i = 0; i < NWB; ++i) { tot += rs_[i * nb + b]; totq += rq_[i * nb + b]; }
+    const float mu = tot / (float)D;
+    const float sc = 1.0f / sqrtf(totq / (float)D + NORM_EPS);
+    for (int i = threadIdx.x; i < D; i += NT) xs[(size_t)b * D + i] = (xs[(size_t)b * D + i] - mu) * sc;
+  }
+  __syncthreads();
+}
+
+// Split form of stage_x for kernels that overlap x with other loads: stage_load issues the (straight-line)
+// global loads into registers, stage_store writes them to LDS (caller syncs), stage_norm normalises in LDS.
+template <int NT, int XPT>
+__device__ __forceinline__ void stage_load(const float* __restrict__ x, int n4, float4 (&v)[XPT]) {
+  const Buf bx(x, (uint32_t)n4 * 16u);
+#pragma unroll
+  for (int k = 0; k < XPT; ++k) {
+    const int i = k * NT + threadIdx.x;
+    v[k] = bx.ldf4(boff(i < n4, (uint32_t)i * 16u));
+  }
+}
+template <int NT, int XPT>
+__device__ __forceinline__ void stage_store(float* xs, int n4, const float4 (&v)[XPT]) {
+  float4* dst = reinterpret_cast<float4*>(xs);
+#pragma unroll
+  for (int k = 0; k < XPT; ++k) {
+    const int i = k * NT + threadIdx.x;
+    if (i < n4) dst[i] = v[k];
+  }
+}
+// Normalise one token (B == 1) whose D values are spread over the block's registers before they are stored:
+// thread t holds float4 k*NT + t (k < XPT, valid iff < n4). Single pass with a shift (x - x0, x0 = x[0]) for
+// the sums, one block reduction (wave sums, then NT/64 partials in wave order). red: 2 * NT/64 floats.
+template <int NT, int XPT>
+__device__ __forceinline__ void block_norm_regs(float4 (&v)[XPT], int n4, float x0, float* red) {
+  constexpr int NWB = NT / 64;
+  float s = 0.f, q = 0.f;
+#pragma unroll
+  for (int k = 0; k < XPT; ++k) {
+    if (k * NT + (int)threadIdx.x < n4) {
+      const float a = v[k].x - x0, b = v[k].y - x0, c = v[k].z - x0, d = v[k].w - x0;
+      s += (a + b) + (c + d);
+      q = fmaf(a, a, q); q = fmaf(b, b, q); q = fmaf(c, c, q); q = fmaf(d, d, q);
+    }
+  }
+  s = wave_sum(s);
+  q = wave_sum(q);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[w] = s; red[NWB + w] = q; }
+  __syncthreads();
+  float ts = 0.f, tq = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWB; ++i) { ts += red[i]; tq += red[NWB + i]; }
+  const float n = (float)(n4 * 4);
+  const float m = ts / n;                         // mean of x - x0
+  const float var = fmaxf(tq / n - m * m, 0.f);
+  const float mu = x0 + m;
+  const float sc = 1.0f / sqrtf(var + NORM_EPS);
+#pragma unroll
+  for (int k = 0; k < XPT; ++k) {
+    v[k].x = (v[k].x - mu) * sc; v[k].y = (v[k].y - mu) * sc;
+    v[k].z = (v[k].z - mu) * sc; v[k].w = (v[k].w - mu) * sc;
+  }
+}
+
+// Normalise nb tokens of length D held in LDS (centre, unit variance); red: 2 * (NT/64) * nb floats. Starts and
+// ends with a block barrier.
+template <int NT>
+__device__ __forceinline__ void stage_norm(float* xs, int nb, int D, float* red) {
+  constexpr int NWB = NT / 64;
+  const int w = threadIdx.x >> 6;
+  float* rs_ = red;
+  float* rq_ = red + NWB * nb;
+  __syncthreads();
+  for (int b = 0; b < nb; ++b) {
+    float s = 0.f;
+    for (int i = threadIdx.x; i < D; i += NT) s += xs[(size_t)b * D + i];
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) rs_[w * nb + b] = s;
+  }
+  __syncthreads();
+  for (int b = 0; b < nb; ++b) {
+    float tot = 0.f;
+    for (int i = 0; i < NWB; ++i) tot += rs_[i * nb + b];
+    const float mu = tot / (float)D;
+    float q = 0.f;
+    for (int i = threadIdx.x; i < D; i += NT) { const float d = xs[(size_t)b * D + i] - mu; q = fmaf(d, d, q); }
+    q = wave_sum(q);
+    if ((threadIdx.x & 63) == 0) rq_[w * nb + b] = q;
+  }
+  __syncthreads();
+  for (int b = 0; b < nb; ++b) {
+    float tot = 0.f, totq = 0.f;
+    for (int i = 0; i < NWB; ++i) { tot += rs_[i * nb + b]; totq += rq_[i * nb + b]; }
+    const float mu = tot / (float)D;
+    const float sc = 1.0f / sqrtf(totq / (float)D + NORM_EPS);
+    for (int i = threadIdx.x; i < D; i += NT) xs[(size_t)b * D + i] = (xs[(size_t)b * D + i] - mu) * sc;
+  }
+  __syncthreads();
+}
+
+// Block-wide compaction of mask words [w0, w0 + nwr) into an LDS list of stored neuron ids (ascending).
+// Wave v handles words w0 + v*wpw .. + wpw (wpw <= 64); lane k < wpw loads word k of the wave's range (one
+// straight-line load, issued by the caller through `cw`). Returns the list length. cnt: NT/64 + 1 ints of LDS.
+template <int NT>
+__device__ __forceinline__ int compact_words(uint64_t cw, int w0, int nwr, int wpw, int nw, int F, int* list,
+                                             int* cnt) {
+  constexpr int NWB = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int first = w0 + w * wpw;                 // first word of this wave
+  const int nmine = max(0, min(wpw, w0 + nwr - first));
+  if (lane < nmine && first + lane == nw - 1 && (F & 63)) cw &= (1ull << (F & 63)) - 1ull;
+  if (lane >= nmine) cw = 0ull;
+  int tot = __popcll(cw);
+  tot = wave_sum_int(tot);
+  if (lane == 0) cnt[w] = tot;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < NWB; ++i) { const int c = cnt[i]; cnt[i] = run; run += c; }
+    cnt[NWB] = run;
+  }
+  __syncthreads();
+  int off = cnt[w];
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int k = 0; k < nmine; ++k) {
+    const uint64_t word = __shfl(cw, k, WAVE);
+    if ((word >> lane) & 1ull) list[off + __popcll(word & below)] = (first + k) * 64 + lane;
+    off += __popcll(word);
+  }
+  __syncthreads();
+  return cnt[NWB];
 }
 
 // Mask word t with the bits of neurons >= F cleared (callers may pass any bit pattern there).
@@ -99,10 +339,11 @@ __device__ __forceinline__ uint64_t mask_word(const uint64_t* __restrict__ mask,
   return w;
 }
 
-// Locate the i-th set bit (0-based, dense index i < total) of the mask. roff[T] = exclusive prefix of set bits
-// over thread ranges of WPT words each. Wave-uniform result: the stored neuron id.
-__device__ __forceinline__ int locate(const uint64_t* __restrict__ mask, const int* roff, int nranges, int wpt, int nw,
-                                      int F, int i) {
+// Locate the i-th set bit (0-based, dense index i < total) of the mask. words: the mask words, in LDS or
+// global memory (bits above F are ignored). roff[T] = exclusive prefix of set bits over thread ranges of wpt words
+// each. Wave-uniform result: the stored neuron id.
+__device__ __forceinline__ int locate(const uint64_t* words, const int* roff, int nranges, int wpt, int nw, int F,
+                                      int i) {
   int lo = 0, hi = nranges - 1;  // largest T with roff[T] <= i
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -112,7 +353,8 @@ __device__ __forceinline__ int locate(const uint64_t* __restrict__ mask, const i
   int t = lo * wpt;
   uint64_t word = 0;
   for (; t < nw; ++t) {
-    word = mask_word(mask, t, nw, F);
+    word = words[t];
+    if (t == nw - 1 && (F & 63)) word &= (1ull << (F & 63)) - 1ull;
     const int cnt = __popcll(word);
     if (rem < cnt) break;
     rem -= cnt;
@@ -125,13 +367,34 @@ __device__ __forceinline__ int locate(const uint64_t* __restrict__ mask, const i
   return t * 64 + (__ffsll((long long)sel) - 1);
 }
 
-// Per-block prefix over mask words: each thread owns WPT consecutive words; roff[t] = set bits before range t.
-template <int NT>
-__device__ __forceinline__ int mask_prefix(const uint64_t* __restrict__ mask, int nw, int F, int wpt, int* roff,
-                                           int* tmp) {
+// Per-block prefix over the mask: thread T owns words [T*wpt, T*wpt + wpt); roff[T] = set bits before its range.
+// When wl != nullptr (nw <= NT * WMAX) the words, cleared above F, are also copied to LDS (wl[0..nw)) for locate.
+// All of a thread's word loads are issued before the first use. Returns the total number of set bits.
+template <int NT, int WMAX>
+__device__ __forceinline__ int mask_prefix(const uint64_t* __restrict__ mask, int nw, int F, int wpt, uint64_t* wl,
+                                           int* roff, int* tmp) {
   const int t0 = threadIdx.x * wpt;
   int cnt = 0;
-  for (int t = t0; t < min(nw, t0 + wpt); ++t) cnt += __popcll(mask_word(mask, t, nw, F));
+  if (wpt <= WMAX) {
+    const Buf bm(mask, (uint32_t)nw * 8u);
+    uint64_t wr[WMAX];
+#pragma unroll
+    for (int k = 0; k < WMAX; ++k) {
+      const int t = t0 + k;
+      wr[k] = bm.ldu64(boff(k < wpt && t < nw, (uint32_t)t * 8u));
+    }
+#pragma unroll
+    for (int k = 0; k < WMAX; ++k) {
+      const int t = t0 + k;
+      if (k < wpt && t < nw) {
+        if (t == nw - 1 && (F & 63)) wr[k] &= (1ull << (F & 63)) - 1ull;
+        cnt += __popcll(wr[k]);
+        if (wl) wl[t] = wr[k];
+      }
+    }
+  } else {
+    for (int t = t0; t < min(nw, t0 + wpt); ++t) cnt += __popcll(mask_word(mask, t, nw, F));
+  }
   int total;
   const int ex = block_exclusive_scan<NT>(cnt, tmp, total);
   roff[threadIdx.x] = ex;
@@ -141,13 +404,28 @@ __device__ __forceinline__ int mask_prefix(const uint64_t* __restrict__ mask, in
 
 }  // namespace sffn
 
+// ---- host helper: allow a kernel all the LDS its static allocation leaves (160 KiB per workgroup on gfx950).
+// Returns the dynamic bytes available in *avail.
+inline hipError_t allow_dynamic_lds(const void* func, size_t* avail) {
+  hipFuncAttributes fa;
+  hipError_t e = hipFuncGetAttributes(&fa, func);
+  if (e != hipSuccess) return e;
+  const size_t total = 160 * 1024;
+  *avail = total > fa.sharedSizeBytes ? total - fa.sharedSizeBytes : 0;
+  return hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)*avail);
+}
+
+// ---- profiling hooks (api.hip): bracket a launch of kernel `kid` with events when profiling is on
+void sffn_prof_before(int kid, hipStream_t st);
+void sffn_prof_after(int kid, hipStream_t st);
+
 // ---- launchers (host side), defined in the kernel files; return hipError_t of the launch
-hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, const float* x, int x_rms, int B, int D,
+hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D,
                                int F, int r, float tau, uint64_t* mask, float* logits, float* hbuf, hipStream_t st);
 hipError_t sffn_launch_forward(int act, const void* Wg, const float* bg, const void* Wu, const float* bu,
-                               const void* WdT, const float* x, int x_rms, int B, int D, int F, const uint64_t* mask,
+                               const void* WdT, const float* x, int x_norm, int B, int D, int F, const uint64_t* mask,
                                int32_t* active, int32_t* n_active, float* y, float* abuf, hipStream_t st);
 hipError_t sffn_launch_forward_q4(int act, const uint8_t* qg, const void* sg, const float* bg, const uint8_t* qu,
                                   const void* su, const float* bu, const uint8_t* qd, const void* sd, const float* x,
-                                  int x_rms, int B, int D, int F, const uint64_t* mask, int32_t* active,
+                                  int x_norm, int B, int D, int F, const uint64_t* mask, int32_t* active,
                                   int32_t* n_active, float* y, float* abuf, hipStream_t st);

@@ -11,7 +11,8 @@
 // column gather). Every product is exact in fp32 before accumulation.
 //
 // Work split and compaction are those of the fp16 path: k_upgate_q4 (mask -> ids, row gather, fused
-// activation) and k_down_q4 (each block owns 256 output columns = 8 Q4 blocks of every W_downT row).
+// activation) and k_down_q4 (each block owns 128 output columns = 4 Q4 blocks of every W_downT row; a lane reads
+// half a block: 8 nibble bytes and the scale).
 #include "common.h"
 
 using namespace sffn;
@@ -19,75 +20,105 @@ using namespace sffn;
 namespace {
 
 constexpr int NT_UP = 256;
-constexpr int X_LDS_FLOATS = 16384;
+constexpr int WMAX = 2;            // mask words per thread in registers / LDS (F <= 32768; larger F reads them from memory)
 
-__device__ __forceinline__ float q4_block_dot(const uint4& nib, const float* __restrict__ xb /* 32 floats in LDS */) {
+// sum over a Q4 block of q_e * x_e: nib = 16 nibble bytes, xl/xh = x of the low-nibble (elements 0..15) and
+// high-nibble (elements 16..31) halves of the block, as four float4 each.
+__device__ __forceinline__ float q4_block_dot(const uint4& nib, const float4* xl, const float4* xh) {
   const uint32_t wds[4] = {nib.x, nib.y, nib.z, nib.w};
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t lo = wds[k] & 0x0F0F0F0Fu, hi = (wds[k] >> 4) & 0x0F0F0F0Fu;
-    const float4 xl = *reinterpret_cast<const float4*>(xb + 4 * k);
-    const float4 xh = *reinterpret_cast<const float4*>(xb + 16 + 4 * k);
-    s = fmaf((float)(lo & 0xFF), xl.x, s);
-    s = fmaf((float)((lo >> 8) & 0xFF), xl.y, s);
-    s = fmaf((float)((lo >> 16) & 0xFF), xl.z, s);
-    s = fmaf((float)(lo >> 24), xl.w, s);
-    s = fmaf((float)(hi & 0xFF), xh.x, s);
-    s = fmaf((float)((hi >> 8) & 0xFF), xh.y, s);
-    s = fmaf((float)((hi >> 16) & 0xFF), xh.z, s);
-    s = fmaf((float)(hi >> 24), xh.w, s);
+    s = fmaf((float)(lo & 0xFF), xl[k].x, s);
+    s = fmaf((float)((lo >> 8) & 0xFF), xl[k].y, s);
+    s = fmaf((float)((lo >> 16) & 0xFF), xl[k].z, s);
+    s = fmaf((float)(lo >> 24), xl[k].w, s);
+    s = fmaf((float)(hi & 0xFF), xh[k].x, s);
+    s = fmaf((float)((hi >> 8) & 0xFF), xh[k].y, s);
+    s = fmaf((float)((hi >> 16) & 0xFF), xh[k].z, s);
+    s = fmaf((float)(hi >> 24), xh[k].w, s);
   }
   return s;
 }
+
+__device__ __forceinline__ float sum4(const float4& v) { return (v.x + v.y) + (v.z + v.w); }
 
 template <int B, int ACT, int NQ>
 __global__ __launch_bounds__(NT_UP) void k_upgate_q4(const uint4* __restrict__ qg, const _Float16* __restrict__ sg,
                                                      const float* __restrict__ bg, const uint4* __restrict__ qu,
                                                      const _Float16* __restrict__ su, const float* __restrict__ bu,
-                                                     const float* __restrict__ x, int x_rms, int D, int F,
+                                                     const float* __restrict__ x, int x_norm, int D, int F,
                                                      const uint64_t* __restrict__ mask, int32_t* __restrict__ active,
                                                      int32_t* __restrict__ n_active, float* __restrict__ abuf) {
-  extern __shared__ float lds[];
+  extern __shared__ uint64_t lds64[];
   const int nblk = D >> 5;                                   // Q4 blocks per row
-  float* xs = lds;                                           // [B, D]
-  float* xsum = xs + (size_t)B * D;                          // [B, nblk]
-  float* red = xsum + (size_t)B * nblk;                      // [(NT/64) * B]
-  int* roff = reinterpret_cast<int*>(red + (NT_UP / 64) * B);  // [NT_UP]
-  int* tmp = roff + NT_UP;
   const int nw = (F + 63) >> 6;
   const int wpt = (nw + NT_UP - 1) / NT_UP;
-  const int n = mask_prefix<NT_UP>(mask, nw, F, wpt, roff, tmp);
+  const bool words_lds = wpt <= WMAX;
+  uint64_t* wl = lds64;
+  int* roff = reinterpret_cast<int*>(wl + (words_lds ? ((nw + 1) & ~1) : 0));
+  int* tmp = roff + NT_UP;
+  float* xs = reinterpret_cast<float*>(tmp + NT_UP / 64 + 4);  // [B, D], then xsum [B, nblk], then red
+  float* xsum = xs + (size_t)B * D;
+  float* red = xsum + (size_t)B * nblk;
+  const int lane = threadIdx.x & 63;
+  const int n4 = (B * D) >> 2;
+  constexpr int XPT = (B * NQ * 4 + 1) / 2;   // float4 of x per thread: B * D / (4 * NT_UP) <= B * NQ * 2
+
+  // round 1: x and the mask words, all loads issued before any use
+  float4 xv4[XPT];
+  stage_load<NT_UP, XPT>(x, n4, xv4);
+  const float x0 = x[0];
+  const int n = mask_prefix<NT_UP, WMAX>(mask, nw, F, wpt, words_lds ? wl : nullptr, roff, tmp);
   if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
   const int NW = gridDim.x * (NT_UP / 64);
   const int g0 = blockIdx.x * (NT_UP / 64);
   if (g0 >= n) return;
-  stage_x<NT_UP>(x, B, D, x_rms, xs, red);
+  if constexpr (B == 1) {
+    if (x_norm) block_norm_regs<NT_UP, XPT>(xv4, n4, x0, red);
+    stage_store<NT_UP, XPT>(xs, n4, xv4);
+    __syncthreads();
+  } else {
+    stage_store<NT_UP, XPT>(xs, n4, xv4);
+    if (x_norm) stage_norm<NT_UP>(xs, B, D, red);
+    else __syncthreads();
+  }
   for (int t = threadIdx.x; t < B * nblk; t += NT_UP) {
-    const float* p = xs + (size_t)(t / nblk) * D + 32 * (t % nblk);
-    float s = 0.f;
-    for (int e = 0; e < 32; ++e) s += p[e];
-    xsum[t] = s;
+    const float4* p = reinterpret_cast<const float4*>(xs + (size_t)(t / nblk) * D + 32 * (t % nblk));
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v += sum4(p[k]);
+    xsum[t] = v;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
+  const uint64_t* words = words_lds ? wl : mask;
+  const uint32_t qbytes = (uint32_t)F * (uint32_t)nblk * 16u, sbytes = (uint32_t)F * (uint32_t)nblk * 2u;
+  const Buf bqu(qu, qbytes), bsu(su, sbytes);
+  const Buf bqg(ACT == 1 ? (const void*)qg : (const void*)qu, ACT == 1 ? qbytes : 0u);
+  const Buf bsg(ACT == 1 ? (const void*)sg : (const void*)su, ACT == 1 ? sbytes : 0u);
+  const float* bp = ACT == 1 ? bg : bu;
+  const Buf bbias(bp ? (const void*)bp : (const void*)qu, bp ? (uint32_t)F * 4u : 0u);   // no bias: 0
+
   for (int i = g0 + (threadIdx.x >> 6); i < n; i += NW) {
-    const int id = locate(mask, roff, NT_UP, wpt, nw, F, i);
+    const int id = locate(words, roff, NT_UP, wpt, nw, F, i);
     if (lane == 0) active[i] = id;
+    // round 2: the neuron's nibbles, scales and bias
     uint4 nu[NQ], ng[NQ];
     float fu[NQ], fg[NQ];
 #pragma unroll
     for (int m = 0; m < NQ; ++m) {
       const int c = lane + 64 * m;
       const bool ok = c < nblk;
-      const size_t o = (size_t)id * nblk + c;
-      nu[m] = ok ? qu[o] : make_uint4(0u, 0u, 0u, 0u);
-      fu[m] = ok ? (float)su[o] : 0.f;
+      const uint32_t o = (uint32_t)id * nblk + c;
+      nu[m] = bqu.ld16(boff(ok, o * 16u));
+      fu[m] = bsu.ldh(boff(ok, o * 2u));
       if (ACT == 1) {
-        ng[m] = ok ? qg[o] : make_uint4(0u, 0u, 0u, 0u);
-        fg[m] = ok ? (float)sg[o] : 0.f;
+        ng[m] = bqg.ld16(boff(ok, o * 16u));
+        fg[m] = bsg.ldh(boff(ok, o * 2u));
       }
     }
+    const float bias = bbias.ldf((uint32_t)id * 4u);
     float au[B], ag[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) { au[b] = 0.f; ag[b] = 0.f; }
@@ -97,10 +128,10 @@ __global__ __launch_bounds__(NT_UP) void k_upgate_q4(const uint4* __restrict__ q
       if (c < nblk) {
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-          const float* xb = xs + (size_t)b * D + 32 * c;
+          const float4* xl = reinterpret_cast<const float4*>(xs + (size_t)b * D + 32 * c);
           const float xsb = xsum[b * nblk + c];
-          au[b] = fmaf(fu[m], q4_block_dot(nu[m], xb) - 8.f * xsb, au[b]);
-          if (ACT == 1) ag[b] = fmaf(fg[m], q4_block_dot(ng[m], xb) - 8.f * xsb, ag[b]);
+          au[b] = fmaf(fu[m], q4_block_dot(nu[m], xl, xl + 4) - 8.f * xsb, au[b]);
+          if (ACT == 1) ag[b] = fmaf(fg[m], q4_block_dot(ng[m], xl, xl + 4) - 8.f * xsb, ag[b]);
         }
       }
     }
@@ -109,10 +140,10 @@ __global__ __launch_bounds__(NT_UP) void k_upgate_q4(const uint4* __restrict__ q
       const float u = wave_sum(au[b]);
       float a;
       if (ACT == 1) {
-        const float g = wave_sum(ag[b]) + (bg ? bg[id] : 0.f);
+        const float g = wave_sum(ag[b]) + bias;
         a = fmaxf(g, 0.f) * u;
       } else {
-        a = fmaxf(u + (bu ? bu[id] : 0.f), 0.f);
+        a = fmaxf(u + bias, 0.f);
       }
       if (lane == 0) abuf[(size_t)i * B + b] = a;
     }
@@ -120,154 +151,147 @@ __global__ __launch_bounds__(NT_UP) void k_upgate_q4(const uint4* __restrict__ q
 }
 
 constexpr int NT_DN = 1024;
-constexpr int QSW = 256;               // output columns per block (8 Q4 blocks of each row)
+constexpr int NWV = NT_DN / 64;
+constexpr int LIST_WORDS = 512;        // mask words compacted per round (32768 neurons)
+constexpr int QSW = 128;               // output columns per block (4 Q4 blocks of each row)
+constexpr int QCPL = 16;               // columns per lane (half a Q4 block: 8 nibble bytes)
+constexpr int QLPR = QSW / QCPL;       // lanes per row slice (8)
+constexpr int QRPI = 64 / QLPR;        // rows per wave instruction (8)
 template <int B> struct QD {
-  static constexpr int CPL = B <= 2 ? 32 : 16;   // columns per lane
-  static constexpr int LPR = QSW / CPL;          // lanes per row slice
-  static constexpr int RPI = 64 / LPR;           // rows per wave instruction
-  static constexpr int CH = B == 1 ? 4096 : 8192 / B;
+  static constexpr int DU = 16;                   // row slices in flight per lane (3 loads each)
 };
-constexpr int QDU = 4;                 // row slices in flight per lane
 
 template <int B>
 __global__ __launch_bounds__(NT_DN) void k_down_q4(const uint8_t* __restrict__ qd, const _Float16* __restrict__ sd,
-                                                   const int32_t* __restrict__ active,
-                                                   const int32_t* __restrict__ n_active,
-                                                   const float* __restrict__ abuf, int D, float* __restrict__ y) {
-  constexpr int CPL = QD<B>::CPL, LPR = QD<B>::LPR, RPI = QD<B>::RPI, CH = QD<B>::CH;
-  constexpr int NWV = NT_DN / 64;
-  __shared__ int ids[CH];
-  __shared__ float as[CH * B];
-  __shared__ float red[NWV * B * 64];     // per wave: B x 64 columns per pass
+                                                   const uint64_t* __restrict__ mask, const float* __restrict__ abuf,
+                                                   int D, int F, float* __restrict__ y) {
+  constexpr int DU = QD<B>::DU;
+  extern __shared__ int list[];
+  __shared__ int cnt[NWV + 1];
+  __shared__ float red[NWV * B * QSW];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nblk = D >> 5;
-  const int rsub = lane / LPR, lsub = lane % LPR;
-  const int col0 = blockIdx.x * QSW + lsub * CPL;       // first column of this lane
-  const int qblk = col0 >> 5;                           // Q4 block of this lane
-  const int half = (CPL == 16) ? ((col0 >> 4) & 1) : 0; // which 8-byte half (16-column lanes)
+  const int rsub = lane / QLPR, lsub = lane % QLPR;
+  const int col0 = blockIdx.x * QSW + lsub * QCPL;
+  const int qblk = col0 >> 5;                 // Q4 block of this lane
+  const int half = (col0 >> 4) & 1;           // which 8-byte half of the block's nibbles
   const bool colok = col0 < D;
-  const int n = *n_active;
-  float acc[B][CPL];
+  const int nw = (F + 63) >> 6;
+  const Buf bm(mask, (uint32_t)nw * 8u);
+  const Buf bqd(qd, (uint32_t)F * (uint32_t)(D >> 1));
+  const Buf bsd(sd, (uint32_t)F * (uint32_t)nblk * 2u);
+  const Buf ba(abuf, (uint32_t)F * (uint32_t)B * 4u);
+  float acc[B][QCPL];
   float sas[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     sas[b] = 0.f;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) acc[b][e] = 0.f;
+    for (int e = 0; e < QCPL; ++e) acc[b][e] = 0.f;
   }
-  for (int r0 = 0; r0 < n; r0 += CH) {
-    const int nr = min(CH, n - r0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < nr; i += NT_DN) ids[i] = active[r0 + i];
-    for (int i = threadIdx.x; i < nr * B; i += NT_DN) as[i] = abuf[(size_t)r0 * B + i];
-    __syncthreads();
-    for (int base = w * RPI + rsub; base < nr; base += NWV * RPI * QDU) {
-      uint32_t nib[QDU][CPL / 8];
-      float sc[QDU];
+  int done = 0;
+  for (int w0 = 0; w0 < nw; w0 += LIST_WORDS) {
+    const int nwr = min(LIST_WORDS, nw - w0);
+    const int wpw = (nwr + NWV - 1) / NWV;
+    const int t = w0 + w * wpw + lane;
+    const uint64_t cw = bm.ldu64(boff(lane < wpw && t < w0 + nwr, (uint32_t)t * 8u));
+    if (w0 > 0) __syncthreads();
+    const int nr = compact_words<NT_DN>(cw, w0, nwr, wpw, nw, F, list, cnt);
+    for (int base = w * QRPI + rsub; base < nr; base += NWV * QRPI * DU) {
+      uint2 nib[DU];
+      float sc[DU];
+      float av[DU][B];
 #pragma unroll
-      for (int u = 0; u < QDU; ++u) {
-        const int i = base + u * NWV * RPI;
-        const bool ok = i < nr && colok;
-        const size_t row = ok ? (size_t)ids[i] : 0;
-        if (CPL == 32) {
-          const uint4 v = ok ? *reinterpret_cast<const uint4*>(qd + row * (D >> 1) + (size_t)qblk * 16)
-                             : make_uint4(0u, 0u, 0u, 0u);
-          nib[u][0] = v.x; nib[u][1] = v.y; nib[u][2] = v.z; nib[u][3] = v.w;
-        } else {
-          const uint2 v = ok ? *reinterpret_cast<const uint2*>(qd + row * (D >> 1) + (size_t)qblk * 16 + half * 8)
-                             : make_uint2(0u, 0u);
-          nib[u][0] = v.x; nib[u][1] = v.y;
-        }
-        sc[u] = ok ? (float)sd[row * nblk + qblk] : 0.f;
+      for (int u = 0; u < DU; ++u) {
+        const int i = base + u * NWV * QRPI;
+        const bool ok = i < nr;
+        const uint32_t row = ok ? (uint32_t)list[i] : 0u;
+        nib[u] = bqd.ld8(boff(ok && colok, row * (uint32_t)(D >> 1) + (uint32_t)qblk * 16u + (uint32_t)half * 8u));
+        sc[u] = bsd.ldh(boff(ok && colok, (row * nblk + qblk) * 2u));
+#pragma unroll
+        for (int b = 0; b < B; ++b) av[u][b] = ba.ldf(boff(ok, ((uint32_t)(done + i) * B + b) * 4u));
       }
 #pragma unroll
-      for (int u = 0; u < QDU; ++u) {
-        const int i = base + u * NWV * RPI;
-        if (i < nr) {
+      for (int u = 0; u < DU; ++u) {
 #pragma unroll
-          for (int b = 0; b < B; ++b) {
-            const float as_ = as[i * B + b] * sc[u];
-            sas[b] += as_;
+        for (int b = 0; b < B; ++b) {
+          const float as_ = av[u][b] * sc[u];
+          sas[b] += as_;
+          const uint32_t wds[2] = {nib[u].x, nib[u].y};
 #pragma unroll
-            for (int k = 0; k < CPL / 8; ++k) {
-              const uint32_t lo = nib[u][k] & 0x0F0F0F0Fu, hi = (nib[u][k] >> 4) & 0x0F0F0F0Fu;
-              // lane-local element order: [0, CPL/2) low nibbles, [CPL/2, CPL) high nibbles
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t lo = wds[k] & 0x0F0F0F0Fu, hi = (wds[k] >> 4) & 0x0F0F0F0Fu;
+            // lane-local element e: e < 8 low nibbles (block elements 8*half + e),
+            // e >= 8 high nibbles (block elements 16 + 8*half + e - 8)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                acc[b][4 * k + j] = fmaf(as_, (float)((lo >> (8 * j)) & 0xFF), acc[b][4 * k + j]);
-                acc[b][CPL / 2 + 4 * k + j] = fmaf(as_, (float)((hi >> (8 * j)) & 0xFF), acc[b][CPL / 2 + 4 * k + j]);
-              }
+            for (int j = 0; j < 4; ++j) {
+              acc[b][4 * k + j] = fmaf(as_, (float)((lo >> (8 * j)) & 0xFF), acc[b][4 * k + j]);
+              acc[b][8 + 4 * k + j] = fmaf(as_, (float)((hi >> (8 * j)) & 0xFF), acc[b][8 + 4 * k + j]);
             }
           }
         }
       }
     }
+    done += nr;
   }
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
+    for (int e = 0; e < QCPL; ++e) {
       float v = fmaf(-8.f, sas[b], acc[b][e]);
 #pragma unroll
-      for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o, WAVE);
+      for (int o = QLPR; o < 64; o <<= 1) v += __shfl_xor(v, o, WAVE);
       acc[b][e] = v;
     }
-  // lane-local element e -> column: low half e -> col0 + e (CPL=32) / col0 + e (CPL=16, e < 8);
-  // high half e -> the element 16 positions later in the Q4 block
-  auto col_of = [&](int e) -> int {
-    if (CPL == 32) return e < 16 ? col0 + e : col0 + 16 + (e - 16) - 16 + 16;  // col0 + e for both halves
-    return e < 8 ? (qblk * 32 + half * 8 + e) : (qblk * 32 + 16 + half * 8 + (e - 8));
-  };
-  float* red_w = red + (size_t)w * B * 64;
-  for (int pass = 0; pass < QSW / 64; ++pass) {
-    // columns [pass*64, pass*64+64) of the block's 256
-    __syncthreads();
-    if (lane < LPR) {
+  if (lane < QLPR) {
+    const int cb = qblk * 32 - blockIdx.x * QSW;   // first column of the lane's Q4 block, block-relative
 #pragma unroll
-      for (int b = 0; b < B; ++b)
+    for (int b = 0; b < B; ++b)
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          const int cc = col_of(e) - blockIdx.x * QSW - pass * 64;
-          if (cc >= 0 && cc < 64) red_w[b * 64 + cc] = acc[b][e];
-        }
-    }
-    __syncthreads();
-    for (int t = threadIdx.x; t < B * 64; t += NT_DN) {
-      const int b = t / 64, cc = t % 64;
-      float s = 0.f;
-      for (int ww = 0; ww < NWV; ++ww) s += red[(size_t)ww * B * 64 + b * 64 + cc];
-      const int d = blockIdx.x * QSW + pass * 64 + cc;
-      if (d < D) y[(size_t)b * D + d] = s;
-    }
+      for (int e = 0; e < QCPL; ++e) {
+        const int cc = e < 8 ? cb + 8 * half + e : cb + 16 + 8 * half + (e - 8);
+        red[(w * B + b) * QSW + cc] = acc[b][e];
+      }
+  }
+  __syncthreads();
+  for (int tt = threadIdx.x; tt < B * QSW; tt += NT_DN) {
+    const int b = tt / QSW, cc = tt % QSW;
+    float s = 0.f;
+    for (int ww = 0; ww < NWV; ++ww) s += red[(ww * B + b) * QSW + cc];
+    const int d = blockIdx.x * QSW + cc;
+    if (d < D) y[(size_t)b * D + d] = s;
   }
 }
 
 template <int B, int ACT, int NQ>
 hipError_t launch_up(const uint8_t* qg, const void* sg, const float* bg, const uint8_t* qu, const void* su,
-                     const float* bu, const float* x, int x_rms, int D, int F, const uint64_t* mask, int32_t* active,
+                     const float* bu, const float* x, int x_norm, int D, int F, const uint64_t* mask, int32_t* active,
                      int32_t* n_active, float* abuf, hipStream_t st) {
   const int nblk = D / 32;
-  const size_t lds = ((size_t)B * D + (size_t)B * nblk + (NT_UP / 64) * B) * sizeof(float) +
-                     (NT_UP + NT_UP / 64 + 1) * sizeof(int);
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_upgate_q4<B, ACT, NQ>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, X_LDS_FLOATS * 4 + 16384);
-    if (e != hipSuccess) return e;
-    attr = true;
+  const int nw = (F + 63) / 64;
+  const int wpt = (nw + NT_UP - 1) / NT_UP;
+  const size_t lds = (wpt <= WMAX ? (size_t)((nw + 1) & ~1) * 8 : 0) + (NT_UP + NT_UP / 64 + 4) * sizeof(int) +
+                     ((size_t)B * D + (size_t)B * nblk + 2 * (NT_UP / 64) * B) * sizeof(float);
+  static size_t avail = 0;
+  if (!avail) {
+    hipError_t ea = allow_dynamic_lds((const void*)k_upgate_q4<B, ACT, NQ>, &avail);
+    if (ea != hipSuccess) return ea;
   }
+  if (lds > avail) return hipErrorInvalidValue;
   const int grid = std::max(1, std::min((F + 3) / 4, 512));
+  sffn_prof_before(2, st);
   hipLaunchKernelGGL((k_upgate_q4<B, ACT, NQ>), dim3(grid), dim3(NT_UP), lds, st, (const uint4*)qg,
-                     (const _Float16*)sg, bg, (const uint4*)qu, (const _Float16*)su, bu, x, x_rms, D, F, mask, active,
+                     (const _Float16*)sg, bg, (const uint4*)qu, (const _Float16*)su, bu, x, x_norm, D, F, mask, active,
                      n_active, abuf);
+  sffn_prof_after(2, st);
   return hipGetLastError();
 }
 
 template <int B, int ACT>
 hipError_t dispatch_up(int nq, const uint8_t* qg, const void* sg, const float* bg, const uint8_t* qu, const void* su,
-                       const float* bu, const float* x, int x_rms, int D, int F, const uint64_t* mask, int32_t* active,
+                       const float* bu, const float* x, int x_norm, int D, int F, const uint64_t* mask, int32_t* active,
                        int32_t* n_active, float* abuf, hipStream_t st) {
-#define UPQ(N) return launch_up<B, ACT, N>(qg, sg, bg, qu, su, bu, x, x_rms, D, F, mask, active, n_active, abuf, st)
+#define UPQ(N) return launch_up<B, ACT, N>(qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st)
   if (nq <= 1) UPQ(1);
   if (nq <= 2) UPQ(2);
   if (nq <= 4) UPQ(4);
@@ -277,16 +301,25 @@ hipError_t dispatch_up(int nq, const uint8_t* qg, const void* sg, const float* b
 
 template <int B>
 hipError_t forward_b(int act, const uint8_t* qg, const void* sg, const float* bg, const uint8_t* qu, const void* su,
-                     const float* bu, const uint8_t* qd, const void* sd, const float* x, int x_rms, int D, int F,
+                     const float* bu, const uint8_t* qd, const void* sd, const float* x, int x_norm, int D, int F,
                      const uint64_t* mask, int32_t* active, int32_t* n_active, float* y, float* abuf, hipStream_t st) {
   const int nq = (D / 32 + 63) / 64;
   hipError_t e = act == 1
-                     ? dispatch_up<B, 1>(nq, qg, sg, bg, qu, su, bu, x, x_rms, D, F, mask, active, n_active, abuf, st)
-                     : dispatch_up<B, 0>(nq, qg, sg, bg, qu, su, bu, x, x_rms, D, F, mask, active, n_active, abuf, st);
+                     ? dispatch_up<B, 1>(nq, qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st)
+                     : dispatch_up<B, 0>(nq, qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st);
   if (e != hipSuccess) return e;
+  const int nw = (F + 63) / 64;
+  const size_t lds = (size_t)std::min(nw, LIST_WORDS) * 64 * sizeof(int);
+  static size_t avail = 0;
+  if (!avail) {
+    hipError_t ea = allow_dynamic_lds((const void*)k_down_q4<B>, &avail);
+    if (ea != hipSuccess) return ea;
+  }
+  if (lds > avail) return hipErrorInvalidValue;
   const int grid = (D + QSW - 1) / QSW;
-  hipLaunchKernelGGL(k_down_q4<B>, dim3(grid), dim3(NT_DN), 0, st, qd, (const _Float16*)sd, active, n_active, abuf, D,
-                     y);
+  sffn_prof_before(3, st);
+  hipLaunchKernelGGL(k_down_q4<B>, dim3(grid), dim3(NT_DN), lds, st, qd, (const _Float16*)sd, mask, abuf, D, F, y);
+  sffn_prof_after(3, st);
   return hipGetLastError();
 }
 
@@ -294,13 +327,13 @@ hipError_t forward_b(int act, const uint8_t* qg, const void* sg, const float* bg
 
 hipError_t sffn_launch_forward_q4(int act, const uint8_t* qg, const void* sg, const float* bg, const uint8_t* qu,
                                   const void* su, const float* bu, const uint8_t* qd, const void* sd, const float* x,
-                                  int x_rms, int B, int D, int F, const uint64_t* mask, int32_t* active,
+                                  int x_norm, int B, int D, int F, const uint64_t* mask, int32_t* active,
                                   int32_t* n_active, float* y, float* abuf, hipStream_t st) {
   switch (B) {
-    case 1: return forward_b<1>(act, qg, sg, bg, qu, su, bu, qd, sd, x, x_rms, D, F, mask, active, n_active, y, abuf, st);
-    case 2: return forward_b<2>(act, qg, sg, bg, qu, su, bu, qd, sd, x, x_rms, D, F, mask, active, n_active, y, abuf, st);
-    case 4: return forward_b<4>(act, qg, sg, bg, qu, su, bu, qd, sd, x, x_rms, D, F, mask, active, n_active, y, abuf, st);
-    case 8: return forward_b<8>(act, qg, sg, bg, qu, su, bu, qd, sd, x, x_rms, D, F, mask, active, n_active, y, abuf, st);
+    case 1: return forward_b<1>(act, qg, sg, bg, qu, su, bu, qd, sd, x, x_norm, D, F, mask, active, n_active, y, abuf, st);
+    case 2: return forward_b<2>(act, qg, sg, bg, qu, su, bu, qd, sd, x, x_norm, D, F, mask, active, n_active, y, abuf, st);
+    case 4: return forward_b<4>(act, qg, sg, bg, qu, su, bu, qd, sd, x, x_norm, D, F, mask, active, n_active, y, abuf, st);
+    case 8: return forward_b<8>(act, qg, sg, bg, qu, su, bu, qd, sd, x, x_norm, D, F, mask, active, n_active, y, abuf, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -4,56 +4,60 @@
 // predictor runs on every token and marks the neurons that will fire. Here it is the low-rank form
 // P2 (P1 x) + c with a sigmoid threshold t, decided in logit space (tau = ln(t / (1 - t))).
 //
-// Kernel 1 (k_pred_h): one wave per row of P1. Every lane issues all of its 16-byte loads of the row before
-// waiting, x is staged once per block in LDS (optionally RMS-normalised), the row dot products are reduced
-// across the wave. h stays fp32.
-// Kernel 2 (k_pred_z): one block per 64 neurons (one mask word). Groups of LPR lanes read one 2r-byte row of
-// P2 with 16-byte loads; h sits in LDS; the group reduces, compares with tau, and wave 0 turns the 64
-// decisions into the mask word with a wavefront ballot.
+// Both kernels cost one dependent memory round trip: every global load is issued branch-free (clamped address,
+// value selected afterwards) before the first use, so all of them are in flight together.
+// Kernel 1 (k_pred_h): one 64-thread block (one wave) per row of P1. Lane l owns the 16-byte chunks
+//   c = l + 64 i of its row and loads them with the matching 8 floats of x; the optional normalisation of x
+//   (mean, then centred variance) is two wave reductions over registers; the row dot product is reduced
+//   across the wave. h stays fp32.
+// Kernel 2 (k_pred_z): one block per 64 neurons (one mask word), 16 neurons per wave. Groups of LPR lanes read
+//   one 2r-byte row of P2 with 16-byte loads together with the matching slice of h and the bias; the group
+//   reduces, compares with tau, and wave 0 turns the 64 decisions into the mask word with a wavefront ballot.
 #include "common.h"
 
 using namespace sffn;
 
 namespace {
 
-constexpr int NT = 256;          // threads per block
-constexpr int X_LDS_FLOATS = 16384;  // x staging budget (64 KB)
+constexpr int NT = 256;
 
 template <int NCH>
-__global__ __launch_bounds__(NT) void k_pred_h(const uint4* __restrict__ P1, const float* __restrict__ x, int x_rms,
+__global__ __launch_bounds__(64) void k_pred_h(const uint4* __restrict__ P1, const float* __restrict__ x, int x_norm,
                                                int B, int D, int r, float* __restrict__ h) {
-  extern __shared__ float lds[];
-  const int TB = max(1, min(B, X_LDS_FLOATS / D));
-  float* xs = lds;                       // [TB, D]
-  float* red = lds + (size_t)TB * D;     // [(NT/64) * TB]
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int j = blockIdx.x * (NT / 64) + w;
+  const int lane = threadIdx.x;
+  const int j = blockIdx.x;
   const int nc = D >> 3;
+  const Buf bp(P1, (uint32_t)r * (uint32_t)D * 2u);
+  const Buf bx(x, (uint32_t)B * (uint32_t)D * 4u);
   uint4 wv[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + 64 * i;
-    wv[i] = (j < r && c < nc) ? P1[(size_t)j * nc + c] : make_uint4(0u, 0u, 0u, 0u);
+    wv[i] = bp.ld16(boff(c < nc, ((uint32_t)j * nc + c) * 16u));
   }
-  for (int tb = 0; tb < B; tb += TB) {
-    const int nb = min(TB, B - tb);
-    stage_x<NT>(x + (size_t)tb * D, nb, D, x_rms, xs, red);
-    for (int b = 0; b < nb; ++b) {
-      float acc = 0.f;
+  float4 xr[NCH][2];
+  auto load_x = [&](int b) {
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nc) {
-          const float4* xp = reinterpret_cast<const float4*>(xs + (size_t)b * D + 8 * c);
-          float4 x0 = xp[0], x1 = xp[1];
-          float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          acc += dot8(wv[i], xv);
-        }
-      }
-      acc = wave_sum(acc);
-      if (lane == 0 && j < r) h[(size_t)(tb + b) * r + j] = acc;
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      const uint32_t o = ((uint32_t)b * D + 8u * c) * 4u;
+      xr[i][0] = bx.ldf4(boff(c < nc, o));
+      xr[i][1] = bx.ldf4(boff(c < nc, o + 16u));
     }
-    __syncthreads();  // xs is overwritten by the next token group
+  };
+  load_x(0);  // before any loop: in flight together with the row of P1
+  for (int b = 0; b < B; ++b) {
+    if (b > 0) load_x(b);
+    if (x_norm) wave_norm_regs<NCH, 2>(xr, nc, D);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const float xv[8] = {xr[i][0].x, xr[i][0].y, xr[i][0].z, xr[i][0].w,
+                           xr[i][1].x, xr[i][1].y, xr[i][1].z, xr[i][1].w};
+      acc += dot8(wv[i], xv);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) h[(size_t)b * r + j] = acc;
   }
 }
 
@@ -65,14 +69,15 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
   constexpr int RPI = 64 / LPR;        // rows per load instruction
   constexpr int RPW = 16;              // rows per wave
   constexpr int NI = RPW / RPI;        // load instructions per chunk round
-  extern __shared__ float lds[];
-  float* hs = lds;                                     // [B, r]
-  int* flags = reinterpret_cast<int*>(lds + (size_t)B * r);  // [64]
+  __shared__ int flags[64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int rsub = lane / LPR, csub = lane % LPR;
   const int cpr = r >> 3;              // 16-byte chunks per row
   const int base = blockIdx.x * 64 + w * RPW;
 
+  const Buf bp(P2, (uint32_t)F * (uint32_t)r * 2u);
+  const Buf bc(c ? (const void*)c : (const void*)P2, c ? (uint32_t)F * 4u : 0u);   // no bias: every load is 0
+  const Buf bh(h, (uint32_t)B * (uint32_t)r * 4u);
   uint4 wv[ROUNDS][NI];
 #pragma unroll
   for (int q = 0; q < ROUNDS; ++q)
@@ -80,33 +85,41 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
     for (int i = 0; i < NI; ++i) {
       const int k = base + i * RPI + rsub;
       const int cc = q * LPR + csub;
-      wv[q][i] = (k < F && cc < cpr) ? P2[(size_t)k * cpr + cc] : make_uint4(0u, 0u, 0u, 0u);
+      wv[q][i] = bp.ld16(boff(k < F && cc < cpr, ((uint32_t)k * cpr + cc) * 16u));
     }
-  for (int i = threadIdx.x; i < B * r; i += NT) hs[i] = h[i];
-  __syncthreads();
-
+  float cb[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int k = base + i * RPI + rsub;
+    cb[i] = bc.ldf(boff(k < F, (uint32_t)k * 4u));
+  }
   bool pred[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) pred[i] = false;
+  float hv[ROUNDS][8];
+  auto load_h = [&](int b) {
+#pragma unroll
+    for (int q = 0; q < ROUNDS; ++q) {
+      const int cc = q * LPR + csub;
+      const bool ok = cc < cpr;
+      const float4 h0 = bh.ldf4(boff(ok, ((uint32_t)b * r + 8u * cc) * 4u));
+      const float4 h1 = bh.ldf4(boff(ok, ((uint32_t)b * r + 8u * cc + 4u) * 4u));
+      hv[q][0] = h0.x; hv[q][1] = h0.y; hv[q][2] = h0.z; hv[q][3] = h0.w;
+      hv[q][4] = h1.x; hv[q][5] = h1.y; hv[q][6] = h1.z; hv[q][7] = h1.w;
+    }
+  };
+  load_h(0);  // before any loop: in flight together with the P2 rows
   for (int b = 0; b < B; ++b) {
-    const float* hb = hs + (size_t)b * r;
+    if (b > 0) load_h(b);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float acc = 0.f;
 #pragma unroll
-      for (int q = 0; q < ROUNDS; ++q) {
-        const int cc = q * LPR + csub;
-        if (cc < cpr) {
-          const float4* hp = reinterpret_cast<const float4*>(hb + 8 * cc);
-          float4 h0 = hp[0], h1 = hp[1];
-          float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-          acc += dot8(wv[q][i], hv);
-        }
-      }
+      for (int q = 0; q < ROUNDS; ++q) acc += dot8(wv[q][i], hv[q]);
       acc = group_sum<LPR>(acc);
       const int k = base + i * RPI + rsub;
       if (csub == 0 && k < F) {
-        const float z = acc + (c ? c[k] : 0.f);
+        const float z = acc + cb[i];
         pred[i] = pred[i] || (z > tau);
         if (logits) logits[(size_t)b * F + k] = z;
       }
@@ -126,51 +139,37 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
 }
 
 template <int NCH>
-hipError_t launch_h(const void* P1, const float* x, int x_rms, int B, int D, int r, float* h, hipStream_t st) {
-  const int TB = std::max(1, std::min(B, X_LDS_FLOATS / D));
-  const size_t lds = ((size_t)TB * D + (NT / 64) * TB) * sizeof(float);
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_pred_h<NCH>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(X_LDS_FLOATS * 4 + 4096));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  const int grid = (r + NT / 64 - 1) / (NT / 64);
-  hipLaunchKernelGGL(k_pred_h<NCH>, dim3(grid), dim3(NT), lds, st, (const uint4*)P1, x, x_rms, B, D, r, h);
+hipError_t launch_h(const void* P1, const float* x, int x_norm, int B, int D, int r, float* h, hipStream_t st) {
+  sffn_prof_before(0, st);
+  hipLaunchKernelGGL(k_pred_h<NCH>, dim3(r), dim3(64), 0, st, (const uint4*)P1, x, x_norm, B, D, r, h);
+  sffn_prof_after(0, st);
   return hipGetLastError();
 }
 
 template <int LPR, int ROUNDS>
 hipError_t launch_z(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, uint64_t* mask,
                     float* logits, hipStream_t st) {
-  const size_t lds = (size_t)B * r * sizeof(float) + 64 * sizeof(int);
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_pred_z<LPR, ROUNDS>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * 4 + 256);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
   const int grid = (F + 63) / 64;
-  hipLaunchKernelGGL((k_pred_z<LPR, ROUNDS>), dim3(grid), dim3(NT), lds, st, (const uint4*)P2, c, h, B, F, r, tau,
+  sffn_prof_before(1, st);
+  hipLaunchKernelGGL((k_pred_z<LPR, ROUNDS>), dim3(grid), dim3(NT), 0, st, (const uint4*)P2, c, h, B, F, r, tau,
                      mask, logits);
+  sffn_prof_after(1, st);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, const float* x, int x_rms, int B, int D,
+hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D,
                                int F, int r, float tau, uint64_t* mask, float* logits, float* hbuf, hipStream_t st) {
   const int nch = (D / 8 + 63) / 64;
   hipError_t e;
-  if (nch <= 1) e = launch_h<1>(P1, x, x_rms, B, D, r, hbuf, st);
-  else if (nch <= 2) e = launch_h<2>(P1, x, x_rms, B, D, r, hbuf, st);
-  else if (nch <= 4) e = launch_h<4>(P1, x, x_rms, B, D, r, hbuf, st);
-  else if (nch <= 8) e = launch_h<8>(P1, x, x_rms, B, D, r, hbuf, st);
-  else if (nch <= 10) e = launch_h<10>(P1, x, x_rms, B, D, r, hbuf, st);
-  else if (nch <= 16) e = launch_h<16>(P1, x, x_rms, B, D, r, hbuf, st);
-  else e = launch_h<32>(P1, x, x_rms, B, D, r, hbuf, st);
+  if (nch <= 1) e = launch_h<1>(P1, x, x_norm, B, D, r, hbuf, st);
+  else if (nch <= 2) e = launch_h<2>(P1, x, x_norm, B, D, r, hbuf, st);
+  else if (nch <= 4) e = launch_h<4>(P1, x, x_norm, B, D, r, hbuf, st);
+  else if (nch <= 8) e = launch_h<8>(P1, x, x_norm, B, D, r, hbuf, st);
+  else if (nch <= 10) e = launch_h<10>(P1, x, x_norm, B, D, r, hbuf, st);
+  else if (nch <= 16) e = launch_h<16>(P1, x, x_norm, B, D, r, hbuf, st);
+  else e = launch_h<32>(P1, x, x_norm, B, D, r, hbuf, st);
   if (e != hipSuccess) return e;
   const int cpr = r / 8;
   int lpr = 8;

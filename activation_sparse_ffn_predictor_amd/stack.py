@@ -45,18 +45,18 @@ class SparseFFNStack:
         self.graphs = {}
 
     # ------------------------------------------------------------------ one layer
-    def layer_call(self, i: int, x: torch.Tensor, x_rms: bool, y: torch.Tensor, logits=None):
+    def layer_call(self, i: int, x: torch.Tensor, x_norm: bool, y: torch.Tensor, logits=None):
         """Predict + forward of stored layer i on input x [B, D]; writes self.mask[i], active[i], n_active[i], y."""
         t, wl = self.layers[i], self.wl
-        _lib.predict(t["P1"], t["P2"], t.get("c"), x, wl.t, self.mask[i], self.ws, logits=logits, x_rms=x_rms)
+        _lib.predict(t["P1"], t["P2"], t.get("c"), x, wl.t, self.mask[i], self.ws, logits=logits, x_norm=x_norm)
         if self.q4:
             g = (t["Q_gate"], t["S_gate"]) if wl.act == "reglu" else None
             _lib.forward_q4(wl.act, g, t.get("b_gate"), (t["Q_up"], t["S_up"]), t.get("b_up"),
                             (t["Q_downT"], t["S_downT"]), x, self.mask[i], self.active[i], self.n_active[i:i + 1], y,
-                            self.ws, x_rms=x_rms)
+                            self.ws, x_norm=x_norm)
         else:
             _lib.forward(wl.act, t.get("W_gate"), t.get("b_gate"), t["W_up"], t.get("b_up"), t["W_downT"], x,
-                         self.mask[i], self.active[i], self.n_active[i:i + 1], y, self.ws, x_rms=x_rms)
+                         self.mask[i], self.active[i], self.n_active[i:i + 1], y, self.ws, x_norm=x_norm)
 
     # ------------------------------------------------------------------ decode step
     def step(self, B: int = 1):

@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Sparse-FFN decode benchmark on one MI355X.
+
+One step = one decode token batch through every layer of the resident FFN stack: per layer the activation
+predictor (sffn_predict) and the neuron-aware sparse FFN (sffn_forward / sffn_forward_q4), layer l+1 reading
+layer l's output through the library's RMS-on-load option. Steps are replayed from a HIP graph; inputs
+x ~ N(0, 1) are fresh per step and already in HBM when the timed region starts.
+
+Printed: one JSON line with decode tokens/s (value), HBM GB/s on the active weight rows actually read, the
+roofline of the dominant kernel (per-launch HIP events around that kernel on its own stream), and the CPU
+oracle timed on this host's cores over a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "sparse-FFN decode tokens/s + achieved HBM GB/s on active weights (1 MI355X)"
+KERNEL_NAMES = {0: "predictor h = P1 x", 1: "predictor z = P2 h + c, threshold, mask",
+                2: "compaction + W_gate/W_up row gather + activation", 3: "W_downT column gather"}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", "--config", default="relullama_7b",
+                    help="toy_relu | relullama_7b | llama2_13b | falcon_40b | llama2_70b_q4 (or c1..c5)")
+    ap.add_argument("--batch", type=int, default=1, help="tokens per decode step (union mask when > 1)")
+    ap.add_argument("--profile-steps", type=int, default=8, help="eager steps per profiled kernel")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of replaying a graph")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle (plain fp64 NumPy dense FFN + predictor) timed on this host over a bounded sample of the same
+    workload: whole layers, one token at a time, extrapolated to the stack."""
+    import numpy as np
+    import oracle
+    import synthgen as sg
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    layers = [0, 1] if wl.L > 1 else [0]
+    ws = [oracle.logical_weights(sg.layer_host(wl, l)) for l in layers]
+    times, n = [], 0
+    t_start = time.perf_counter()
+    step = 0
+    while True:
+        for li, w in enumerate(ws):
+            x = sg.inputs(wl, step, 1)
+            t0 = time.perf_counter()
+            oracle.layer(wl.act, x, w, wl.t)
+            times.append(time.perf_counter() - t0)
+            n += 1
+        step += 1
+        if time.perf_counter() - t_start > budget_s or step >= 64:
+            break
+    per_layer = float(np.median(times))
+    tok_s = 1.0 / (per_layer * wl.L)
+    return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} layer-token evaluations of {wl.name} (layers {layers}, batch 1, fp64 NumPy dense FFN + "
+                      f"predictor), median {per_layer * 1e3:.1f} ms per layer, extrapolated to {wl.L} layers",
+            "seconds": round(time.perf_counter() - t_start, 2)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs the sparse-FFN stack on one GPU; --gpus must be 1"}),
+              flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthgen as sg
+    from activation_sparse_ffn_predictor_amd import _lib
+    from activation_sparse_ffn_predictor_amd.stack import SparseFFNStack
+
+    wl = sg.workload(args.workload)
+    B = args.batch
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    stack = SparseFFNStack(wl, dev, max_batch=B)
+    L = len(stack.layers)
+    setup_s = time.perf_counter() - t0
+    print(f"# setup: {wl.name}, {L} layers resident, {setup_s:.1f} s", file=sys.stderr, flush=True)
+
+    K, W = args.steps, args.warmup
+    X = torch.empty((W + K, B, wl.D), dtype=torch.float32, device=dev)
+    for s in range(W + K):
+        sg.inputs(wl, s, B, tag=sg.TAG_X_DECODE, out=X[s])
+    n_acc = torch.zeros(L, dtype=torch.int64, device=dev)
+
+    def body():
+        stack.step(B)
+        n_acc.add_(stack.n_active)
+
+    if args.no_graph:
+        run = body
+    else:
+        stack.x_in[:B].copy_(X[0])
+        body()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        run = g.replay
+
+    for s in range(W):
+        stack.x_in[:B].copy_(X[s])
+        run()
+    torch.cuda.synchronize()
+    n_acc.zero_()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for s in range(K):
+        stack.x_in[:B].copy_(X[W + s])
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / K
+    n_mean = n_acc.cpu().numpy().astype(np.float64) / K          # mean active rows per layer per step
+    row_bytes = stack.active_weight_bytes_per_row()
+    active_bytes_step = float(n_mean.sum()) * row_bytes
+    pred_bytes_step = L * stack.predictor_bytes()
+    tok_s = B * K / (ms_total * 1e-3)
+
+    # ---- per-kernel durations: eager steps with HIP events around every launch of one kernel
+    P = max(1, args.profile_steps)
+    prof = {}
+    nlog = []
+    for kid in (0, 1, 2, 3):
+        _lib.profile_begin(kid, P * L)
+        for s in range(P):
+            stack.x_in[:B].copy_(X[W + (s % K)])
+            stack.step(B)
+            if kid == 2:
+                nlog.append(stack.n_active.cpu().numpy().astype(np.float64))
+        ms = _lib.profile_end(P * L)
+        prof[kid] = np.asarray(ms, dtype=np.float64)
+    torch.cuda.synchronize()
+    mean_us = {k: float(v.mean() * 1e3) for k, v in prof.items()}
+    # algorithmic bytes per launch (active rows actually read by the profiled launches)
+    n_prof = np.concatenate(nlog) if nlog else np.zeros(1)
+    if stack.q4:
+        one_row = wl.D // 2 + 2 * (wl.D // 32)
+    else:
+        one_row = 2 * wl.D
+    rows_mats = wl.n_mats - 1
+    bytes_rows = n_prof * rows_mats * one_row                    # per launch of kernel 2
+    bytes_cols = n_prof * one_row                                # per launch of kernel 3
+    kb = {0: np.full(len(prof[0]), 2.0 * wl.r * wl.D), 1: np.full(len(prof[1]), 2.0 * wl.F * wl.r),
+          2: bytes_rows, 3: bytes_cols}
+    tot = {k: float(prof[k].sum()) for k in prof}
+    dom = max(tot, key=tot.get)
+    m = min(len(kb[dom]), len(prof[dom]))
+    achieved = float(kb[dom][:m].sum() / (prof[dom][:m].sum() * 1e-3) / 1e9)       # GB/s
+    fwd_us = mean_us[2] + mean_us[3]
+    fwd_gbs = (float(n_prof.mean()) * row_bytes) / (fwd_us * 1e-6) / 1e9
+
+    traffic = None
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if not stack.q4 else "q4_0",
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "d_model": wl.D, "d_ffn": wl.F, "rank": wl.r, "layers": L, "batch": B,
+                   "activation": wl.act, "weights": "fp16" if not stack.q4 else "q4_0", "density_target": wl.density,
+                   "graph": not args.no_graph},
+        "active_weight_gbs": round(active_bytes_step / (ms_step * 1e-3) / 1e9, 1),
+        "forward_active_gbs": round(fwd_gbs, 1),
+        "all_bytes_gbs": round((active_bytes_step + pred_bytes_step) / (ms_step * 1e-3) / 1e9, 1),
+        "active_rows_per_layer": round(float(n_mean.mean()), 1),
+        "density": round(float(n_mean.mean()) / wl.F, 4),
+        "kernel_us": {KERNEL_NAMES[k]: round(v, 3) for k, v in mean_us.items()},
+        "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "wall_s": round(wall, 3),
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

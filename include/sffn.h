@@ -100,11 +100,12 @@ int sffn_mask_words(int F);
  *   z[b, k] = P2[k, :] h[b, :] + c[k]         (c = NULL means 0)
  *   neuron k active  <=>  sigmoid(z[b, k]) > t for some token b
  *                    <=>  z[b, k] > ln(t / (1 - t))  (decided in logit space)
- * xn = x, or, if x_rms != 0, xn[b, :] = x[b, :] / sqrt(mean(x[b, :]^2) + 1e-6)
- * (the parameter-free normalisation between stacked layers).
+ * xn = x, or, if x_norm != 0, xn[b, :] = (x[b, :] - m) / sqrt(v + 1e-6) with m the mean and v the
+ * (population) variance of x[b, :] -- the parameter-free normalisation between stacked layers, applied as the
+ * input is loaded.
  * Outputs: mask (every word written, bits >= F zero); logits [B, F] fp32 if
  * non-NULL. Uses the workspace. Two kernels. */
-int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_rms, int B, int D, int F,
+int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F,
                  int r, float t, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream);
 
 /* Neuron-aware sparse FFN over the neurons set in `mask` ("Neuron-aware operator").
@@ -115,14 +116,26 @@ int sffn_predict(const void* P1, const void* P2, const float* c, const float* x,
  * b_up may be NULL (0). active [F] int32 and n_active [1] int32 are device
  * outputs; y [B, D] is overwritten. Uses the workspace. Two kernels. */
 int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W_up, const float* b_up,
-                 const void* W_downT, const float* x, int x_rms, int B, int D, int F, const uint64_t* mask,
+                 const void* W_downT, const float* x, int x_norm, int B, int D, int F, const uint64_t* mask,
                  int32_t* active, int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* sffn_forward with Q4_0 weights ("Quantization": INT4 Q4_0); weights are
  * dequantised in registers, w = (q - 8) * s exactly in fp32. */
 int sffn_forward_q4(int act, sffn_q4 W_gate, const float* b_gate, sffn_q4 W_up, const float* b_up, sffn_q4 W_downT,
-                    const float* x, int x_rms, int B, int D, int F, const uint64_t* mask, int32_t* active,
+                    const float* x, int x_norm, int B, int D, int F, const uint64_t* mask, int32_t* active,
                     int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Per-launch timing of one kernel (profiling aid; not needed for computing).
+ * kernel: SFFN_K_PRED_H (P1 x), SFFN_K_PRED_Z (P2 h + c, threshold, mask), SFFN_K_ROWS (compaction + W_gate /
+ * W_up row gather + activation), SFFN_K_COLS (W_downT column gather).
+ * Between sffn_profile_begin and sffn_profile_end, every launch of that kernel made by the calling thread is
+ * bracketed by two HIP events recorded on its launch stream, up to max_launches launches; the events are
+ * created by sffn_profile_begin (host call; not inside a graph capture). sffn_profile_end waits for the last
+ * event, writes the elapsed milliseconds of the bracketed launches to ms[0 .. min(count, max)) and returns
+ * the count (negative status on error). Returns SFFN_ERR_ARG for a bad kernel id or max_launches < 1. */
+enum { SFFN_K_PRED_H = 0, SFFN_K_PRED_Z = 1, SFFN_K_ROWS = 2, SFFN_K_COLS = 3 };
+int sffn_profile_begin(int kernel, int max_launches);
+int sffn_profile_end(float* ms, int max);
 
 #ifdef __cplusplus
 }

@@ -57,7 +57,7 @@ def make_case(wl, layer=0, device="cuda:0", with_c=True, perm="hot", from_device
     return LayerCase(wl, layer, host, w, dev, np.asarray(p))
 
 
-def run_gpu(case: LayerCase, x: torch.Tensor, x_rms=False, t=None, want_logits=True):
+def run_gpu(case: LayerCase, x: torch.Tensor, x_norm=False, t=None, want_logits=True):
     wl, d = case.wl, case.dev
     B, D = x.shape
     dev = x.device
@@ -68,14 +68,14 @@ def run_gpu(case: LayerCase, x: torch.Tensor, x_rms=False, t=None, want_logits=T
     logits = torch.full((B, wl.F), float("nan"), dtype=torch.float32, device=dev) if want_logits else None
     ws = torch.zeros(_lib.workspace_size(B, D, wl.F, wl.r), dtype=torch.uint8, device=dev)
     tt = wl.t if t is None else t
-    _lib.predict(d["P1"], d["P2"], d.get("c"), x, tt, mask, ws, logits=logits, x_rms=x_rms)
+    _lib.predict(d["P1"], d["P2"], d.get("c"), x, tt, mask, ws, logits=logits, x_norm=x_norm)
     if wl.wdtype == "q4":
         g = (d["Q_gate"], d["S_gate"]) if wl.act == "reglu" else None
         _lib.forward_q4(wl.act, g, d.get("b_gate"), (d["Q_up"], d["S_up"]), d.get("b_up"), (d["Q_downT"], d["S_downT"]),
-                        x, mask, active, n_active, y, ws, x_rms=x_rms)
+                        x, mask, active, n_active, y, ws, x_norm=x_norm)
     else:
         _lib.forward(wl.act, d.get("W_gate"), d.get("b_gate"), d["W_up"], d.get("b_up"), d["W_downT"], x, mask, active,
-                     n_active, y, ws, x_rms=x_rms)
+                     n_active, y, ws, x_norm=x_norm)
     torch.cuda.synchronize(dev)
     return dict(mask=mask.cpu().numpy().view(np.uint64), active=active.cpu().numpy(), n=int(n_active.item()),
                 y=y.cpu().numpy().astype(np.float64),
@@ -87,12 +87,12 @@ def mask_bits(words: np.ndarray, F: int) -> np.ndarray:
     return bits[:F].astype(bool)
 
 
-def check(case: LayerCase, x_host: np.ndarray, res: dict, x_rms=False, t=None, tol=Y_TOL):
+def check(case: LayerCase, x_host: np.ndarray, res: dict, x_norm=False, t=None, tol=Y_TOL):
     """Compare one GPU layer result with the oracle; raise AssertionError with details on mismatch.
     Returns a dict of statistics."""
     wl, F = case.wl, case.wl.F
     tt = wl.t if t is None else t
-    xo = oracle.rms_norm(x_host) if x_rms else np.atleast_2d(x_host).astype(np.float64)
+    xo = oracle.layer_norm(x_host) if x_norm else np.atleast_2d(x_host).astype(np.float64)
     z = oracle.predictor_logits(case.w["P1"], case.w["P2"], xo, case.w.get("c"))
     m_ref = oracle.union_mask(oracle.token_masks(z, tt))
     band = oracle.band_neurons(z, tt)

@@ -50,14 +50,14 @@ MIS = 0x10002        # fake, misaligned
 
 
 def _predict(**kw):
-    a = dict(P1=A, P2=A, c=None, x=A, x_rms=0, B=1, D=512, F=2048, r=64, t=0.5, mask=A, logits=None, ws=A,
+    a = dict(P1=A, P2=A, c=None, x=A, x_norm=0, B=1, D=512, F=2048, r=64, t=0.5, mask=A, logits=None, ws=A,
              ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return _lib.lib().sffn_predict(*a.values())
 
 
 def _forward(**kw):
-    a = dict(act=0, Wg=None, bg=None, Wu=A, bu=A, WdT=A, x=A, x_rms=0, B=1, D=512, F=2048, mask=A, active=A,
+    a = dict(act=0, Wg=None, bg=None, Wu=A, bu=A, WdT=A, x=A, x_norm=0, B=1, D=512, F=2048, mask=A, active=A,
              n_active=A, y=A, ws=A, ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return _lib.lib().sffn_forward(*a.values())
@@ -65,7 +65,7 @@ def _forward(**kw):
 
 def _forward_q4(**kw):
     Q = _lib._Q4(A, A)
-    a = dict(act=1, Wg=Q, bg=A, Wu=Q, bu=None, WdT=Q, x=A, x_rms=0, B=1, D=512, F=2048, mask=A, active=A, n_active=A,
+    a = dict(act=1, Wg=Q, bg=A, Wu=Q, bu=None, WdT=Q, x=A, x_norm=0, B=1, D=512, F=2048, mask=A, active=A, n_active=A,
              y=A, ws=A, ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return _lib.lib().sffn_forward_q4(*a.values())

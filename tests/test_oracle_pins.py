@@ -181,12 +181,15 @@ def test_closed_form_threshold_and_union():
     assert sf.union_mask(masks).tolist() == [True, False]
 
 
-def test_rms_norm_closed_form():
-    y = np.array([[3.0, -4.0], [0.0, 0.0]])
-    x = sf.rms_norm(y)
-    s = np.sqrt(12.5 + sf.RMS_EPS)
-    assert np.allclose(x[0], [3.0 / s, -4.0 / s], rtol=0, atol=1e-15)
-    assert x[1].tolist() == [0.0, 0.0]
+def test_layer_norm_closed_form():
+    # y = (3, -1): mean 1, centred (2, -2), variance 4 -> (2, -2) / sqrt(4 + eps)
+    y = np.array([[3.0, -1.0], [5.0, 5.0]])
+    x = sf.layer_norm(y)
+    s = np.sqrt(4.0 + sf.NORM_EPS)
+    assert np.allclose(x[0], [2.0 / s, -2.0 / s], rtol=0, atol=1e-15)
+    assert x[1].tolist() == [0.0, 0.0]                      # a constant token centres to zero
+    z = sf.layer_norm(np.random.default_rng(0).standard_normal((3, 1000)) * 7 + 40)
+    assert np.allclose(z.mean(axis=1), 0, atol=1e-12) and np.allclose((z * z).mean(axis=1), 1, atol=1e-6)
 
 
 # ----------------------------------------------------------------------------- library special cases
@@ -318,8 +321,14 @@ def test_band_rule():
 
 
 # ----------------------------------------------------------------------------- planted mistakes
+def check_layer_norm():
+    y = np.array([[3.0, -1.0]])
+    s = np.sqrt(4.0 + sf.NORM_EPS)
+    return np.allclose(sf.layer_norm(y)[0], [2.0 / s, -2.0 / s], rtol=0, atol=1e-15)
+
+
 def _all_pins():
-    return (all(check_brute_force(act, B, s) for act in ("relu", "reglu") for B in (1, 3) for s in (0, 1))
+    return check_layer_norm() and (all(check_brute_force(act, B, s) for act in ("relu", "reglu") for B in (1, 3) for s in (0, 1))
             and check_q4_exact() and check_true_mask_equals_dense("relu") and check_true_mask_equals_dense("reglu")
             and check_permutation_invariance())
 
@@ -371,6 +380,11 @@ def _mut_mask_ignored(act, x, w, mask):
     return sf.activations(act, x, w) @ w["W_down"].T
 
 
+def _mut_norm_uncentred(y, eps=sf.NORM_EPS):
+    y = np.atleast_2d(y)
+    return y / np.sqrt(np.mean(y * y, axis=1, keepdims=True) + eps)
+
+
 def _mut_mask_first_token(masks):
     return np.atleast_2d(masks)[0]
 
@@ -385,6 +399,7 @@ def _mut_mask_first_token(masks):
     ("dequant_q4_rows", _mut_q4_offset),
     ("ffn_masked", _mut_mask_ignored),
     ("union_mask", _mut_mask_first_token),
+    ("layer_norm", _mut_norm_uncentred),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, mutant):
     monkeypatch.setattr(sf, name, mutant)

@@ -42,11 +42,11 @@ def test_small_layers(gpu_ready, name, wl, B):
 
 
 @pytest.mark.parametrize("name,wl", SMALL[:3], ids=[s[0] for s in SMALL[:3]])
-def test_rms_input_and_no_predictor_bias(gpu_ready, name, wl):
+def test_normalised_input_and_no_predictor_bias(gpu_ready, name, wl):
     case = make_case(wl, 0, gpu_ready, with_c=False)
     x = 3.7 * _x(wl, 1, 5)                    # un-normalised input; the library normalises on load
-    res = run_gpu(case, torch.from_numpy(x).to(gpu_ready), x_rms=True)
-    st = check(case, x, res, x_rms=True)
+    res = run_gpu(case, torch.from_numpy(x).to(gpu_ready), x_norm=True)
+    st = check(case, x, res, x_norm=True)
     say(name, st)
     assert 0.3 < st["density"] < 0.7          # no bias: about half the neurons are marked
 
