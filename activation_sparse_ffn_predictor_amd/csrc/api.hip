@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/sffn.h"
 #include "common.h"
 
@@ -23,7 +25,11 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(SFFN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int MAX_B = 64, MAX_D = 16384, MAX_F = 1 << 22, MAX_R = 1024, MAX_BR = 32768, MAX_BD_VALU = 16384;
+constexpr int MAX_B = 64, MAX_D = 16384, MAX_F = 1 << 22, MAX_R = 1024, MAX_BR = 32768;
+constexpr int MAX_BD_VALU = 16384;   // decode-batch kernels: B in {1, 2, 4, 8} with B * D <= this
+constexpr int MAX_F_UNION = 32768;   // union kernels compact the whole mask in one block
+constexpr int KS_MAX = 8;            // row splits of the union down projection
+constexpr size_t MAX_TENSOR = (size_t)1 << 31;   // buffer loads address each tensor with 31-bit byte offsets
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -33,12 +39,30 @@ int check_common(int B, int D, int F) {
   if (B < 1 || B > MAX_B) return fail(SFFN_ERR_SHAPE, "B=%d outside [1, %d]", B, MAX_B);
   if (D < 8 || D > MAX_D || D % 8) return fail(SFFN_ERR_SHAPE, "D=%d: need 8 <= D <= %d, D %% 8 == 0", D, MAX_D);
   if (F < 1 || F > MAX_F) return fail(SFFN_ERR_SHAPE, "F=%d outside [1, %d]", F, MAX_F);
+  if ((size_t)F * D * 2 >= MAX_TENSOR || (size_t)F * B * 4 >= MAX_TENSOR)
+    return fail(SFFN_ERR_SHAPE, "F=%d, D=%d, B=%d: a tensor reaches 2 GiB", F, D, B);
   return SFFN_OK;
 }
 
-// Workspace layout: [activations a: F * B fp32][predictor h: B * r fp32], each part 256-byte aligned.
-// sffn_forward uses only the first part, sffn_predict only the second.
-size_t ws_forward_bytes(int B, int F) { return align256((size_t)F * B * sizeof(float)); }
+// Which kernels serve a call: B == 1, and B in {2, 4, 8} with B * D <= 16384, take the decode kernels (x staged
+// once per block in LDS); every other batch takes the union kernels on the matrix cores.
+bool decode_batch(int B, int D) {
+  return B == 1 || ((B == 2 || B == 4 || B == 8) && (size_t)B * D <= MAX_BD_VALU);
+}
+
+// Row splits of the union down projection: enough blocks of 128 columns x KS splits to cover the chip twice.
+int union_splits(int D) {
+  const int cb = (D + 127) / 128;
+  return std::min(KS_MAX, std::max(1, (512 + cb - 1) / cb));
+}
+
+// Workspace layout, each part 256-byte aligned:
+//   [activations a: F * B fp32][B > 1: normalised x: B * D fp32][B > 1: partial y: KS_MAX * B * D fp32]
+//   [predictor h: B * r fp32]
+size_t ws_a_bytes(int B, int F) { return align256((size_t)F * B * sizeof(float)); }
+size_t ws_xn_bytes(int B, int D) { return B > 1 ? align256((size_t)B * D * sizeof(float)) : 0; }
+size_t ws_part_bytes(int B, int D) { return B > 1 ? align256((size_t)KS_MAX * B * D * sizeof(float)) : 0; }
+size_t ws_forward_bytes(int B, int D, int F) { return ws_a_bytes(B, F) + ws_xn_bytes(B, D) + ws_part_bytes(B, D); }
 
 int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   if (!ws) return fail(SFFN_ERR_NULL, "workspace is NULL");
@@ -47,16 +71,17 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   return SFFN_OK;
 }
 
-// batch sizes the decode-batch kernels are built for
-int check_forward_batch(int B, int D) {
-  if (!(B == 1 || B == 2 || B == 4 || B == 8) || (size_t)B * D > MAX_BD_VALU)
-    return fail(SFFN_ERR_SHAPE, "forward: B=%d with D=%d not supported (B in {1,2,4,8} and B*D <= %d)", B, D,
-                MAX_BD_VALU);
+int check_union(int B, int D, int F) {
+  if (!decode_batch(B, D) && F > MAX_F_UNION)
+    return fail(SFFN_ERR_SHAPE, "forward: B=%d with D=%d takes the union kernels, which need F <= %d (F=%d)", B, D,
+                MAX_F_UNION, F);
   return SFFN_OK;
 }
 
 float* ws_abuf(void* ws) { return (float*)ws; }
-float* ws_hbuf(void* ws, int B, int F) { return (float*)((char*)ws + ws_forward_bytes(B, F)); }
+float* ws_xn(void* ws, int B, int F) { return (float*)((char*)ws + ws_a_bytes(B, F)); }
+float* ws_part(void* ws, int B, int D, int F) { return (float*)((char*)ws + ws_a_bytes(B, F) + ws_xn_bytes(B, D)); }
+float* ws_hbuf(void* ws, int B, int D, int F) { return (float*)((char*)ws + ws_forward_bytes(B, D, F)); }
 
 struct Prof {
   int kernel = -1;
@@ -86,6 +111,27 @@ void sffn_prof_after(int kid, hipStream_t st) {
     ++g_prof.used;
   }
 }
+
+namespace {
+
+// Union path (B > 1 outside the decode batches): optional token normalisation, row gather + activation, down
+// projection in row splits, sum of the splits.
+hipError_t run_union(int act, bool q4, const void* Wg, const void* Sg, const float* bg, const void* Wu, const void* Su,
+                     const float* bu, const void* Wd, const void* Sd, const float* x, int x_norm, int B, int D, int F,
+                     const uint64_t* mask, int32_t* active, int32_t* n_active, float* y, void* ws, hipStream_t st) {
+  const float* xin = x;
+  if (x_norm) {
+    hipError_t e = sffn_launch_norm_tokens(x, B, D, ws_xn(ws, B, F), st);
+    if (e != hipSuccess) return e;
+    xin = ws_xn(ws, B, F);
+  }
+  hipError_t e = sffn_launch_rows_mt(act, q4, Wg, Sg, bg, Wu, Su, bu, xin, B, D, F, mask, active, n_active,
+                                     ws_abuf(ws), st);
+  if (e != hipSuccess) return e;
+  return sffn_launch_down_mt(q4, Wd, Sd, mask, ws_abuf(ws), B, D, F, ws_part(ws, B, D, F), union_splits(D), y, st);
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -144,9 +190,8 @@ const char* sffn_status_string(int s) {
 const char* sffn_last_error(void) { return g_err; }
 
 size_t sffn_workspace_size(int B, int D, int F, int r) {
-  (void)D;
-  if (B < 1 || F < 1 || r < 1) return 0;
-  return ws_forward_bytes(B, F) + align256((size_t)B * r * sizeof(float));
+  if (B < 1 || D < 1 || F < 1 || r < 1) return 0;
+  return ws_forward_bytes(B, D, F) + align256((size_t)B * r * sizeof(float));
 }
 
 int sffn_mask_words(int F) { return F < 1 ? 0 : (F + 63) / 64; }
@@ -165,8 +210,20 @@ int sffn_predict(const void* P1, const void* P2, const float* c, const float* x,
   s = check_ws(ws, ws_bytes, sffn_workspace_size(B, D, F, r));
   if (s) return s;
   const float tau = (float)log((double)t / (1.0 - (double)t));
-  hipError_t e = sffn_launch_predict(P1, P2, c, x, x_norm, B, D, F, r, tau, mask, logits, ws_hbuf(ws, B, F),
-                                     (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  float* h = ws_hbuf(ws, B, D, F);
+  hipError_t e;
+  if (B == 1) {
+    e = sffn_launch_predict(P1, P2, c, x, x_norm, B, D, F, r, tau, mask, logits, h, st);
+  } else {
+    const float* xin = x;
+    e = hipSuccess;
+    if (x_norm) {
+      e = sffn_launch_norm_tokens(x, B, D, ws_xn(ws, B, F), st);
+      xin = ws_xn(ws, B, F);
+    }
+    if (e == hipSuccess) e = sffn_launch_predict_mt(P1, P2, c, xin, B, D, F, r, tau, mask, logits, h, st);
+  }
   return e == hipSuccess ? SFFN_OK : hip_fail(e, "predict launch");
 }
 
@@ -180,17 +237,24 @@ int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W
     return fail(SFFN_ERR_NULL, "forward: W_up, W_downT, x, mask, active, n_active and y are required");
   int s = check_common(B, D, F);
   if (s) return s;
-  s = check_forward_batch(B, D);
+  s = check_union(B, D, F);
   if (s) return s;
   if ((act == SFFN_ACT_REGLU && !al(W_gate, 16)) || !al(W_up, 16) || !al(W_downT, 16) || !al(x, 16) ||
       !al(mask, 8) || !al(active, 4) || !al(n_active, 4) || !al(y, 16) || (b_gate && !al(b_gate, 4)) ||
       (b_up && !al(b_up, 4)))
     return fail(SFFN_ERR_ALIGN, "forward: misaligned pointer");
-  s = check_ws(ws, ws_bytes, ws_forward_bytes(B, F));
+  s = check_ws(ws, ws_bytes, ws_forward_bytes(B, D, F));
   if (s) return s;
-  hipError_t e = sffn_launch_forward(act, act == SFFN_ACT_REGLU ? W_gate : nullptr, act == SFFN_ACT_REGLU ? b_gate : nullptr,
-                                     W_up, act == SFFN_ACT_RELU ? b_up : nullptr, W_downT, x, x_norm, B, D, F, mask,
-                                     active, n_active, y, ws_abuf(ws), (hipStream_t)stream);
+  const bool g = act == SFFN_ACT_REGLU;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (decode_batch(B, D)) {
+    e = sffn_launch_forward(act, g ? W_gate : nullptr, g ? b_gate : nullptr, W_up, g ? nullptr : b_up, W_downT, x,
+                            x_norm, B, D, F, mask, active, n_active, y, ws_abuf(ws), st);
+  } else {
+    e = run_union(act, false, g ? W_gate : nullptr, nullptr, g ? b_gate : nullptr, W_up, nullptr, g ? nullptr : b_up,
+                  W_downT, nullptr, x, x_norm, B, D, F, mask, active, n_active, y, ws, st);
+  }
   return e == hipSuccess ? SFFN_OK : hip_fail(e, "forward launch");
 }
 
@@ -205,18 +269,25 @@ int sffn_forward_q4(int act, sffn_q4 W_gate, const float* b_gate, sffn_q4 W_up, 
   int s = check_common(B, D, F);
   if (s) return s;
   if (D % 32) return fail(SFFN_ERR_SHAPE, "forward_q4: D=%d not a multiple of 32", D);
-  s = check_forward_batch(B, D);
+  s = check_union(B, D, F);
   if (s) return s;
   if ((act == SFFN_ACT_REGLU && (!al(W_gate.q, 16) || !al(W_gate.s, 2))) || !al(W_up.q, 16) || !al(W_up.s, 2) ||
       !al(W_downT.q, 16) || !al(W_downT.s, 2) || !al(x, 16) || !al(mask, 8) || !al(active, 4) ||
       !al(n_active, 4) || !al(y, 16) || (b_gate && !al(b_gate, 4)) || (b_up && !al(b_up, 4)))
     return fail(SFFN_ERR_ALIGN, "forward_q4: misaligned pointer");
-  s = check_ws(ws, ws_bytes, ws_forward_bytes(B, F));
+  s = check_ws(ws, ws_bytes, ws_forward_bytes(B, D, F));
   if (s) return s;
   const bool g = act == SFFN_ACT_REGLU;
-  hipError_t e = sffn_launch_forward_q4(act, g ? W_gate.q : nullptr, g ? W_gate.s : nullptr, g ? b_gate : nullptr,
-                                        W_up.q, W_up.s, g ? nullptr : b_up, W_downT.q, W_downT.s, x, x_norm, B, D, F,
-                                        mask, active, n_active, y, ws_abuf(ws), (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (decode_batch(B, D)) {
+    e = sffn_launch_forward_q4(act, g ? W_gate.q : nullptr, g ? W_gate.s : nullptr, g ? b_gate : nullptr, W_up.q,
+                               W_up.s, g ? nullptr : b_up, W_downT.q, W_downT.s, x, x_norm, B, D, F, mask, active,
+                               n_active, y, ws_abuf(ws), st);
+  } else {
+    e = run_union(act, true, g ? W_gate.q : nullptr, g ? W_gate.s : nullptr, g ? b_gate : nullptr, W_up.q, W_up.s,
+                  g ? nullptr : b_up, W_downT.q, W_downT.s, x, x_norm, B, D, F, mask, active, n_active, y, ws, st);
+  }
   return e == hipSuccess ? SFFN_OK : hip_fail(e, "forward_q4 launch");
 }
 

@@ -40,9 +40,10 @@ def test_status_strings_and_sizes():
     assert _lib.status_string(0) == "ok"
     assert "workspace" in _lib.status_string(4)
     assert _lib.mask_words(1) == 1 and _lib.mask_words(64) == 1 and _lib.mask_words(65) == 2
-    # [a: F*B fp32][h: B*r fp32], 256-byte parts
+    # [a: F*B fp32][B > 1: xn B*D fp32][B > 1: partial y 8*B*D fp32][h: B*r fp32], 256-byte parts
     assert _lib.workspace_size(1, 4096, 11008, 256) == 44032 + 1024
-    assert _lib.workspace_size(8, 512, 100, 64) == 3328 + 2048
+    assert _lib.workspace_size(8, 512, 100, 64) == 3328 + 16384 + 131072 + 2048
+    assert _lib.workspace_size(3, 40, 7, 8) == 256 + 512 + 3840 + 256
 
 
 A = 0x10000          # fake, 256-byte aligned, never dereferenced
@@ -87,7 +88,7 @@ def test_predict_rejects(kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(act=7), 5), (dict(act=1, Wg=None), 5),
     (dict(Wu=None), 1), (dict(WdT=None), 1), (dict(y=None), 1), (dict(active=None), 1), (dict(n_active=None), 1),
-    (dict(B=3), 2), (dict(B=8, D=4096), 2),
+    (dict(B=3, F=32769), 2), (dict(B=8, D=4096, F=40000), 2), (dict(F=1 << 21, D=1024), 2),
     (dict(Wu=MIS), 3), (dict(y=A + 4), 3),
     (dict(ws_bytes=16), 4),
 ])
@@ -97,7 +98,7 @@ def test_forward_rejects(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(act=1, Wg=_lib._Q4(None, None)), 5), (dict(Wu=_lib._Q4(A, None)), 1), (dict(D=520), 2),
-    (dict(WdT=_lib._Q4(MIS, A)), 3), (dict(ws_bytes=0), 4), (dict(B=16), 2),
+    (dict(WdT=_lib._Q4(MIS, A)), 3), (dict(ws_bytes=0), 4), (dict(B=16, F=32832), 2),
 ])
 def test_forward_q4_rejects(kw, status):
     assert _forward_q4(**kw) == status

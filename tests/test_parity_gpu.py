@@ -27,10 +27,8 @@ SMALL = [
 
 
 @pytest.mark.parametrize("name,wl", SMALL, ids=[s[0] for s in SMALL])
-@pytest.mark.parametrize("B", [1, 2, 4, 8])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 8, 16, 17, 64])
 def test_small_layers(gpu_ready, name, wl, B):
-    if B * wl.D > 16384:
-        pytest.skip("decode-batch kernels take B * D <= 16384")
     case = make_case(wl, 0, gpu_ready)
     for step in range(3):
         x = _x(wl, B, step)
@@ -49,6 +47,31 @@ def test_normalised_input_and_no_predictor_bias(gpu_ready, name, wl):
     st = check(case, x, res, x_norm=True)
     say(name, st)
     assert 0.3 < st["density"] < 0.7          # no bias: about half the neurons are marked
+
+
+@pytest.mark.parametrize("name,wl", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("B", [2, 5, 33])
+def test_union_normalised_input(gpu_ready, name, wl, B):
+    case = make_case(wl, 0, gpu_ready)
+    x = 2.5 * _x(wl, B, 6) + 0.75            # un-normalised tokens; normalised per token on load
+    say(f"[{name}] union B={B} x_norm")
+    res = run_gpu(case, torch.from_numpy(x).to(gpu_ready), x_norm=True)
+    st = check(case, x, res, x_norm=True)
+    say("   ", st)
+
+
+@pytest.mark.parametrize("B", [3, 16])
+@pytest.mark.parametrize("t,expect", [(1e-30, "all"), (1.0 - 1e-7, "none")])
+def test_union_all_and_none_active(gpu_ready, B, t, expect):
+    wl = SMALL[2][1]
+    case = make_case(wl, 0, gpu_ready)
+    x = _x(wl, B, 1)
+    res = run_gpu(case, torch.from_numpy(x).to(gpu_ready), t=t)
+    check(case, x, res, t=t)
+    if expect == "all":
+        assert res["n"] == wl.F
+    else:
+        assert res["n"] == 0 and np.all(res["y"] == 0.0)
 
 
 @pytest.mark.parametrize("perm", ["identity", "random"])
@@ -78,26 +101,38 @@ def test_all_and_none_active(gpu_ready, t, expect):
 
 
 @pytest.mark.parametrize("F", [1, 63, 64, 65, 129])
-def test_tiny_neuron_counts(gpu_ready, F):
+@pytest.mark.parametrize("B", [1, 3])
+def test_tiny_neuron_counts(gpu_ready, F, B):
     wl = small("c1", D=64, F=F, r=8, L=1, density=0.5)
     case = make_case(wl, 0, gpu_ready)
     for t in (1e-30, 0.5):
-        x = _x(wl, 1, 3)
+        x = _x(wl, B, 3)
         res = run_gpu(case, torch.from_numpy(x).to(gpu_ready), t=t)
         check(case, x, res, t=t)
 
 
-def test_minimum_d_q4(gpu_ready):
+@pytest.mark.parametrize("B", [1, 6])
+def test_minimum_d_q4(gpu_ready, B):
     wl = small("c5", D=32, F=200, r=8, L=1, density=0.5)
     case = make_case(wl, 0, gpu_ready)
-    x = _x(wl, 1, 0)
+    x = _x(wl, B, 0)
     check(case, x, run_gpu(case, torch.from_numpy(x).to(gpu_ready)))
 
 
-def test_deterministic_reruns(gpu_ready):
+def test_largest_union_f(gpu_ready):
+    # the union kernels take F up to 32768 (512 mask words), a ragged D and many k splits of few rows
+    wl = small("c1", D=200, F=32768, r=16, L=1, density=0.02)
+    case = make_case(wl, 0, gpu_ready)
+    x = _x(wl, 20, 0)
+    st = check(case, x, run_gpu(case, torch.from_numpy(x).to(gpu_ready)))
+    say("largest union F", st)
+
+
+@pytest.mark.parametrize("B", [1, 4, 24])
+def test_deterministic_reruns(gpu_ready, B):
     wl = SMALL[1][1]
     case = make_case(wl, 0, gpu_ready)
-    x = torch.from_numpy(_x(wl, 1, 4)).to(gpu_ready)
+    x = torch.from_numpy(_x(wl, B, 4)).to(gpu_ready)
     a, b = run_gpu(case, x), run_gpu(case, x)
     assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["mask"], b["mask"])
 
@@ -133,3 +168,21 @@ def test_full_size_layer(gpu_ready, name):
         st = check(case, x, res)
         say(f"[full {name}] step {step}: {st}")
         assert abs(st["density"] - wl.density) < 0.05
+
+
+# full-size union batches: the decode batches of the 13B shape that exceed the decode kernels, the Falcon shape at
+# B = 4, and the 70B Q4 prompt of 64 tokens
+UNION_FULL = [("c3", 4, sg.TAG_X_DECODE), ("c3", 8, sg.TAG_X_DECODE), ("c4", 4, sg.TAG_X_DECODE),
+              ("c5", 64, sg.TAG_X_PROMPT)]
+
+
+@pytest.mark.parametrize("name,B,tag", UNION_FULL, ids=[f"{n}-B{b}" for n, b, _ in UNION_FULL])
+def test_full_size_union(gpu_ready, name, B, tag):
+    wl = sg.workload(name)
+    layer = 0 if wl.L == 1 else 2
+    say(f"[full union {name} B={B}] generating layer {layer}")
+    case = make_case(wl, layer, gpu_ready)
+    x = _x(wl, B, 0, tag=tag)
+    res = run_gpu(case, torch.from_numpy(x).to(gpu_ready))
+    st = check(case, x, res)
+    say(f"[full union {name} B={B}]: {st}")
