@@ -126,14 +126,19 @@ def forward_q4(act, W_gate, b_gate, W_up, b_up, W_downT, x, mask, active, n_acti
 
 
 def profile_begin(kernel: int, max_launches: int):
-    """Bracket every launch of `kernel` (K_PRED_H, K_PRED_Z, K_ROWS, K_COLS) with HIP events."""
+    """Time every launch of `kernel` (K_PRED_H, K_PRED_Z, K_ROWS, K_COLS) with the kernel's own device timestamps
+    (eager launches only)."""
     _check(lib().sffn_profile_begin(int(kernel), int(max_launches)), "sffn_profile_begin")
 
 
-def profile_end(max_launches: int):
-    """Per-launch elapsed milliseconds of the bracketed launches (list of floats)."""
+def _profile_times(fn, name, max_launches):
     buf = (ctypes.c_float * max(1, max_launches))()
-    n = lib().sffn_profile_end(buf, max_launches)
+    n = fn(buf, max_launches)
     if n < 0:
-        _check(-n, "sffn_profile_end")
+        _check(-n, name)
     return [float(buf[i]) for i in range(min(n, max_launches))]
+
+
+def profile_end(max_launches: int):
+    """Per-launch elapsed milliseconds of the bracketed launches (list of floats); frees the events."""
+    return _profile_times(lib().sffn_profile_end, "sffn_profile_end", max_launches)

@@ -22,6 +22,7 @@ int fail(int status, const char* fmt, ...) {
 }
 
 int hip_fail(hipError_t e, const char* what) {
+  (void)hipGetLastError();   // reported here: do not leave it pending for the caller's next HIP call
   return fail(SFFN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
@@ -101,15 +102,12 @@ void prof_free() {
 
 }  // namespace
 
-void sffn_prof_before(int kid, hipStream_t st) {
-  if (g_prof.kernel == kid && g_prof.used < g_prof.max) hipEventRecord(g_prof.ev[2 * g_prof.used], st);
-}
-
-void sffn_prof_after(int kid, hipStream_t st) {
-  if (g_prof.kernel == kid && g_prof.used < g_prof.max) {
-    hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st);
-    ++g_prof.used;
-  }
+bool sffn_prof_events(int kid, hipEvent_t* start, hipEvent_t* stop) {
+  if (g_prof.kernel != kid || g_prof.used >= g_prof.max) return false;
+  *start = g_prof.ev[2 * g_prof.used];
+  *stop = g_prof.ev[2 * g_prof.used + 1];
+  ++g_prof.used;
+  return true;
 }
 
 namespace {

@@ -1,6 +1,7 @@
 // Shared device helpers and launch declarations of libsffn (gfx950, wave64).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -61,6 +62,9 @@ struct Buf {
   }
   __device__ __forceinline__ float ldf(uint32_t off) const {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+  }
+  __device__ __forceinline__ uint32_t ldu(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
   }
   __device__ __forceinline__ float ldh(uint32_t off) const {  // one fp16 value, widened
     const unsigned short b = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
@@ -415,9 +419,19 @@ inline hipError_t allow_dynamic_lds(const void* func, size_t* avail) {
   return hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)*avail);
 }
 
-// ---- profiling hooks (api.hip): bracket a launch of kernel `kid` with events when profiling is on
-void sffn_prof_before(int kid, hipStream_t st);
-void sffn_prof_after(int kid, hipStream_t st);
+// ---- profiling hook (api.hip): while kernel id `kid` is being profiled (sffn_profile_begin), hands out the next
+// pair of events. The launch then records the kernel's own start and end timestamps into them
+// (hipExtLaunchKernelGGL), the same clock a kernel trace reads; otherwise the plain launch is used.
+bool sffn_prof_events(int kid, hipEvent_t* start, hipEvent_t* stop);
+
+#define SFFN_LAUNCH(kid, kern, grid, block, shm, st, ...)                                   \
+  do {                                                                                       \
+    hipEvent_t sffn_e0_, sffn_e1_;                                                           \
+    if (sffn_prof_events(kid, &sffn_e0_, &sffn_e1_))                                         \
+      hipExtLaunchKernelGGL(kern, grid, block, shm, st, sffn_e0_, sffn_e1_, 0, __VA_ARGS__); \
+    else                                                                                     \
+      hipLaunchKernelGGL(kern, grid, block, shm, st, __VA_ARGS__);                           \
+  } while (0)
 
 // ---- launchers (host side), defined in the kernel files; return hipError_t of the launch
 hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D,

@@ -10,9 +10,10 @@
 // with the per-block sums of x precomputed in LDS for the row gather, and sum of a * s carried per lane for the
 // column gather). Every product is exact in fp32 before accumulation.
 //
-// Work split and compaction are those of the fp16 path: k_upgate_q4 (mask -> ids, row gather, fused
-// activation) and k_down_q4 (each block owns 128 output columns = 4 Q4 blocks of every W_downT row; a lane reads
-// half a block: 8 nibble bytes and the scale).
+// Work split and compaction are those of the fp16 path: k_upgate_q4 (mask -> ids, balanced dense-index
+// mapping, first rows in flight while x is staged, row gather, fused activation) and k_down_q4 (reads the ids
+// kernel 1 wrote to active[]; each block owns 128 output columns = 4 Q4 blocks of every W_downT row; a lane
+// reads half a block: 8 nibble bytes and the scale).
 #include "common.h"
 
 using namespace sffn;
@@ -72,9 +73,40 @@ __global__ __launch_bounds__(NT_UP) void k_upgate_q4(const uint4* __restrict__ q
   const float x0 = x[0];
   const int n = mask_prefix<NT_UP, WMAX>(mask, nw, F, wpt, words_lds ? wl : nullptr, roff, tmp);
   if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
-  const int NW = gridDim.x * (NT_UP / 64);
-  const int g0 = blockIdx.x * (NT_UP / 64);
-  if (g0 >= n) return;
+  const int G = gridDim.x;
+  if ((int)blockIdx.x >= n) return;  // block-uniform: no dense index maps to this block
+  const uint64_t* words = words_lds ? wl : mask;
+  const uint32_t qbytes = (uint32_t)F * (uint32_t)nblk * 16u, sbytes = (uint32_t)F * (uint32_t)nblk * 2u;
+  const Buf bqu(qu, qbytes), bsu(su, sbytes);
+  const Buf bqg(ACT == 1 ? (const void*)qg : (const void*)qu, ACT == 1 ? qbytes : 0u);
+  const Buf bsg(ACT == 1 ? (const void*)sg : (const void*)su, ACT == 1 ? sbytes : 0u);
+  const float* bp = ACT == 1 ? bg : bu;
+  const Buf bbias(bp ? (const void*)bp : (const void*)qu, bp ? (uint32_t)F * 4u : 0u);   // no bias: 0
+  const int NW = G * (NT_UP / 64);
+  int i = (int)blockIdx.x + G * (threadIdx.x >> 6);
+  uint4 nu[NQ], ng[NQ];
+  float fu[NQ], fg[NQ];
+  float bias = 0.f;
+  int id = 0;
+  auto issue = [&]() {  // round 2 for dense index i: the neuron's nibbles, scales and bias
+    id = locate(words, roff, NT_UP, wpt, nw, F, i);
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      const int c = lane + 64 * m;
+      const bool ok = c < nblk;
+      const uint32_t o = (uint32_t)id * nblk + c;
+      nu[m] = bqu.ld16(boff(ok, o * 16u));
+      fu[m] = bsu.ldh(boff(ok, o * 2u));
+      if (ACT == 1) {
+        ng[m] = bqg.ld16(boff(ok, o * 16u));
+        fg[m] = bsg.ldh(boff(ok, o * 2u));
+      }
+    }
+    bias = bbias.ldf((uint32_t)id * 4u);
+  };
+  const bool have = i < n;            // wave-uniform
+  if (have) issue();
+  // x: normalised, staged and summed per Q4 block while the first rows are in flight
   if constexpr (B == 1) {
     if (x_norm) block_norm_regs<NT_UP, XPT>(xv4, n4, x0, red);
     stage_store<NT_UP, XPT>(xs, n4, xv4);
@@ -92,33 +124,9 @@ __global__ __launch_bounds__(NT_UP) void k_upgate_q4(const uint4* __restrict__ q
     xsum[t] = v;
   }
   __syncthreads();
-  const uint64_t* words = words_lds ? wl : mask;
-  const uint32_t qbytes = (uint32_t)F * (uint32_t)nblk * 16u, sbytes = (uint32_t)F * (uint32_t)nblk * 2u;
-  const Buf bqu(qu, qbytes), bsu(su, sbytes);
-  const Buf bqg(ACT == 1 ? (const void*)qg : (const void*)qu, ACT == 1 ? qbytes : 0u);
-  const Buf bsg(ACT == 1 ? (const void*)sg : (const void*)su, ACT == 1 ? sbytes : 0u);
-  const float* bp = ACT == 1 ? bg : bu;
-  const Buf bbias(bp ? (const void*)bp : (const void*)qu, bp ? (uint32_t)F * 4u : 0u);   // no bias: 0
-
-  for (int i = g0 + (threadIdx.x >> 6); i < n; i += NW) {
-    const int id = locate(words, roff, NT_UP, wpt, nw, F, i);
+  if (!have) return;
+  for (;;) {
     if (lane == 0) active[i] = id;
-    // round 2: the neuron's nibbles, scales and bias
-    uint4 nu[NQ], ng[NQ];
-    float fu[NQ], fg[NQ];
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-      const int c = lane + 64 * m;
-      const bool ok = c < nblk;
-      const uint32_t o = (uint32_t)id * nblk + c;
-      nu[m] = bqu.ld16(boff(ok, o * 16u));
-      fu[m] = bsu.ldh(boff(ok, o * 2u));
-      if (ACT == 1) {
-        ng[m] = bqg.ld16(boff(ok, o * 16u));
-        fg[m] = bsg.ldh(boff(ok, o * 2u));
-      }
-    }
-    const float bias = bbias.ldf((uint32_t)id * 4u);
     float au[B], ag[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) { au[b] = 0.f; ag[b] = 0.f; }
@@ -147,27 +155,29 @@ __global__ __launch_bounds__(NT_UP) void k_upgate_q4(const uint4* __restrict__ q
       }
       if (lane == 0) abuf[(size_t)i * B + b] = a;
     }
+    i += NW;
+    if (i >= n) break;
+    issue();
   }
 }
 
-constexpr int NT_DN = 1024;
-constexpr int NWV = NT_DN / 64;
-constexpr int LIST_WORDS = 512;        // mask words compacted per round (32768 neurons)
 constexpr int QSW = 128;               // output columns per block (4 Q4 blocks of each row)
 constexpr int QCPL = 16;               // columns per lane (half a Q4 block: 8 nibble bytes)
 constexpr int QLPR = QSW / QCPL;       // lanes per row slice (8)
 constexpr int QRPI = 64 / QLPR;        // rows per wave instruction (8)
-template <int B> struct QD {
-  static constexpr int DU = 16;                   // row slices in flight per lane (3 loads each)
-};
+template <int B> struct QD;            // threads per block, row slices in flight per lane (3 loads each)
+template <> struct QD<1> { static constexpr int NT = 512, DU = 16; };
+template <> struct QD<2> { static constexpr int NT = 512, DU = 12; };
+template <> struct QD<4> { static constexpr int NT = 512, DU = 8; };
+template <> struct QD<8> { static constexpr int NT = 512, DU = 2; };
 
 template <int B>
-__global__ __launch_bounds__(NT_DN) void k_down_q4(const uint8_t* __restrict__ qd, const _Float16* __restrict__ sd,
-                                                   const uint64_t* __restrict__ mask, const float* __restrict__ abuf,
-                                                   int D, int F, float* __restrict__ y) {
-  constexpr int DU = QD<B>::DU;
-  extern __shared__ int list[];
-  __shared__ int cnt[NWV + 1];
+__global__ __launch_bounds__(QD<B>::NT) void k_down_q4(const uint8_t* __restrict__ qd, const _Float16* __restrict__ sd,
+                                                       const int32_t* __restrict__ active,
+                                                       const int32_t* __restrict__ n_active,
+                                                       const float* __restrict__ abuf, int D, int F,
+                                                       float* __restrict__ y) {
+  constexpr int NT = QD<B>::NT, DU = QD<B>::DU, NWV = NT / 64, STRIDE = NWV * QRPI * DU;
   __shared__ float red[NWV * B * QSW];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nblk = D >> 5;
@@ -176,11 +186,11 @@ __global__ __launch_bounds__(NT_DN) void k_down_q4(const uint8_t* __restrict__ q
   const int qblk = col0 >> 5;                 // Q4 block of this lane
   const int half = (col0 >> 4) & 1;           // which 8-byte half of the block's nibbles
   const bool colok = col0 < D;
-  const int nw = (F + 63) >> 6;
-  const Buf bm(mask, (uint32_t)nw * 8u);
   const Buf bqd(qd, (uint32_t)F * (uint32_t)(D >> 1));
   const Buf bsd(sd, (uint32_t)F * (uint32_t)nblk * 2u);
   const Buf ba(abuf, (uint32_t)F * (uint32_t)B * 4u);
+  const Buf bid(active, (uint32_t)F * 4u);
+  const Buf bn(n_active, 4u);
   float acc[B][QCPL];
   float sas[B];
 #pragma unroll
@@ -189,51 +199,53 @@ __global__ __launch_bounds__(NT_DN) void k_down_q4(const uint8_t* __restrict__ q
 #pragma unroll
     for (int e = 0; e < QCPL; ++e) acc[b][e] = 0.f;
   }
-  int done = 0;
-  for (int w0 = 0; w0 < nw; w0 += LIST_WORDS) {
-    const int nwr = min(LIST_WORDS, nw - w0);
-    const int wpw = (nwr + NWV - 1) / NWV;
-    const int t = w0 + w * wpw + lane;
-    const uint64_t cw = bm.ldu64(boff(lane < wpw && t < w0 + nwr, (uint32_t)t * 8u));
-    if (w0 > 0) __syncthreads();
-    const int nr = compact_words<NT_DN>(cw, w0, nwr, wpw, nw, F, list, cnt);
-    for (int base = w * QRPI + rsub; base < nr; base += NWV * QRPI * DU) {
-      uint2 nib[DU];
-      float sc[DU];
-      float av[DU][B];
+  // round 1: the count and the ids are loaded together (ids speculatively, bounded by F)
+  const int nraw = (int)bn.ldu(0u);
+  int k0 = 0;
+  do {
+    uint32_t ids[DU];
 #pragma unroll
-      for (int u = 0; u < DU; ++u) {
-        const int i = base + u * NWV * QRPI;
-        const bool ok = i < nr;
-        const uint32_t row = ok ? (uint32_t)list[i] : 0u;
-        nib[u] = bqd.ld8(boff(ok && colok, row * (uint32_t)(D >> 1) + (uint32_t)qblk * 16u + (uint32_t)half * 8u));
-        sc[u] = bsd.ldh(boff(ok && colok, (row * nblk + qblk) * 2u));
+    for (int u = 0; u < DU; ++u) {
+      const int i = k0 + w * QRPI + rsub + u * NWV * QRPI;
+      ids[u] = bid.ldu(boff(i < F, (uint32_t)i * 4u));
+    }
+    const int n = min(max(nraw, 0), F);
+    // round 2: nibbles, scales and activations of the row slices
+    uint2 nib[DU];
+    float sc[DU];
+    float av[DU][B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) av[u][b] = ba.ldf(boff(ok, ((uint32_t)(done + i) * B + b) * 4u));
-      }
+    for (int u = 0; u < DU; ++u) {
+      const int i = k0 + w * QRPI + rsub + u * NWV * QRPI;
+      const bool ok = i < n;
+      const uint32_t row = ids[u];
+      nib[u] = bqd.ld8(boff(ok && colok, row * (uint32_t)(D >> 1) + (uint32_t)qblk * 16u + (uint32_t)half * 8u));
+      sc[u] = bsd.ldh(boff(ok && colok, (row * nblk + qblk) * 2u));
 #pragma unroll
-      for (int u = 0; u < DU; ++u) {
+      for (int b = 0; b < B; ++b) av[u][b] = ba.ldf(boff(ok, ((uint32_t)i * B + b) * 4u));
+    }
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const float as_ = av[u][b] * sc[u];
-          sas[b] += as_;
-          const uint32_t wds[2] = {nib[u].x, nib[u].y};
+    for (int u = 0; u < DU; ++u) {
 #pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const uint32_t lo = wds[k] & 0x0F0F0F0Fu, hi = (wds[k] >> 4) & 0x0F0F0F0Fu;
-            // lane-local element e: e < 8 low nibbles (block elements 8*half + e),
-            // e >= 8 high nibbles (block elements 16 + 8*half + e - 8)
+      for (int b = 0; b < B; ++b) {
+        const float as_ = av[u][b] * sc[u];
+        sas[b] += as_;
+        const uint32_t wds[2] = {nib[u].x, nib[u].y};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              acc[b][4 * k + j] = fmaf(as_, (float)((lo >> (8 * j)) & 0xFF), acc[b][4 * k + j]);
-              acc[b][8 + 4 * k + j] = fmaf(as_, (float)((hi >> (8 * j)) & 0xFF), acc[b][8 + 4 * k + j]);
-            }
+        for (int k = 0; k < 2; ++k) {
+          const uint32_t lo = wds[k] & 0x0F0F0F0Fu, hi = (wds[k] >> 4) & 0x0F0F0F0Fu;
+          // lane-local element e: e < 8 low nibbles (block elements 8*half + e),
+          // e >= 8 high nibbles (block elements 16 + 8*half + e - 8)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[b][4 * k + j] = fmaf(as_, (float)((lo >> (8 * j)) & 0xFF), acc[b][4 * k + j]);
+            acc[b][8 + 4 * k + j] = fmaf(as_, (float)((hi >> (8 * j)) & 0xFF), acc[b][8 + 4 * k + j]);
           }
         }
       }
     }
-    done += nr;
-  }
+    k0 += STRIDE;
+  } while (k0 < min(max(nraw, 0), F));
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
@@ -254,7 +266,7 @@ __global__ __launch_bounds__(NT_DN) void k_down_q4(const uint8_t* __restrict__ q
       }
   }
   __syncthreads();
-  for (int tt = threadIdx.x; tt < B * QSW; tt += NT_DN) {
+  for (int tt = threadIdx.x; tt < B * QSW; tt += NT) {
     const int b = tt / QSW, cc = tt % QSW;
     float s = 0.f;
     for (int ww = 0; ww < NWV; ++ww) s += red[(ww * B + b) * QSW + cc];
@@ -279,11 +291,9 @@ hipError_t launch_up(const uint8_t* qg, const void* sg, const float* bg, const u
   }
   if (lds > avail) return hipErrorInvalidValue;
   const int grid = std::max(1, std::min((F + 3) / 4, 512));
-  sffn_prof_before(2, st);
-  hipLaunchKernelGGL((k_upgate_q4<B, ACT, NQ>), dim3(grid), dim3(NT_UP), lds, st, (const uint4*)qg,
+  SFFN_LAUNCH(2, (k_upgate_q4<B, ACT, NQ>), dim3(grid), dim3(NT_UP), lds, st, (const uint4*)qg,
                      (const _Float16*)sg, bg, (const uint4*)qu, (const _Float16*)su, bu, x, x_norm, D, F, mask, active,
                      n_active, abuf);
-  sffn_prof_after(2, st);
   return hipGetLastError();
 }
 
@@ -308,18 +318,9 @@ hipError_t forward_b(int act, const uint8_t* qg, const void* sg, const float* bg
                      ? dispatch_up<B, 1>(nq, qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st)
                      : dispatch_up<B, 0>(nq, qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st);
   if (e != hipSuccess) return e;
-  const int nw = (F + 63) / 64;
-  const size_t lds = (size_t)std::min(nw, LIST_WORDS) * 64 * sizeof(int);
-  static size_t avail = 0;
-  if (!avail) {
-    hipError_t ea = allow_dynamic_lds((const void*)k_down_q4<B>, &avail);
-    if (ea != hipSuccess) return ea;
-  }
-  if (lds > avail) return hipErrorInvalidValue;
   const int grid = (D + QSW - 1) / QSW;
-  sffn_prof_before(3, st);
-  hipLaunchKernelGGL(k_down_q4<B>, dim3(grid), dim3(NT_DN), lds, st, qd, (const _Float16*)sd, mask, abuf, D, F, y);
-  sffn_prof_after(3, st);
+  SFFN_LAUNCH(3, k_down_q4<B>, dim3(grid), dim3(QD<B>::NT), 0, st, qd, (const _Float16*)sd, active, n_active, abuf, D,
+              F, y);
   return hipGetLastError();
 }
 

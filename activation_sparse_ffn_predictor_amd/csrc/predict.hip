@@ -4,15 +4,17 @@
 // predictor runs on every token and marks the neurons that will fire. Here it is the low-rank form
 // P2 (P1 x) + c with a sigmoid threshold t, decided in logit space (tau = ln(t / (1 - t))).
 //
-// Both kernels cost one dependent memory round trip: every global load is issued branch-free (clamped address,
-// value selected afterwards) before the first use, so all of them are in flight together.
-// Kernel 1 (k_pred_h): one 64-thread block (one wave) per row of P1. Lane l owns the 16-byte chunks
-//   c = l + 64 i of its row and loads them with the matching 8 floats of x; the optional normalisation of x
-//   (mean, then centred variance) is two wave reductions over registers; the row dot product is reduced
-//   across the wave. h stays fp32.
-// Kernel 2 (k_pred_z): one block per 64 neurons (one mask word), 16 neurons per wave. Groups of LPR lanes read
-//   one 2r-byte row of P2 with 16-byte loads together with the matching slice of h and the bias; the group
-//   reduces, compares with tau, and wave 0 turns the 64 decisions into the mask word with a wavefront ballot.
+// Both kernels cost one dependent memory round trip: every global load is issued branch-free (buffer loads whose
+// out-of-range offsets read 0) before the first use, so all of them are in flight together.
+// Kernel 1 (k_pred_h): one 256-thread block per row of P1. Thread t owns the 16-byte chunks c = t + 256 m of the
+//   row and loads them with the matching 8 floats of x. One block reduction of four sums gives the row dot
+//   product and, for the optional normalisation of x, the statistics: with x' = x - x[0] (a shift that keeps the
+//   single-pass variance well conditioned), mu' = mean(x'), var = mean(x'^2) - mu'^2 and
+//   P1[j] . (x - mean) / sqrt(var + eps) = (sum P1[j] x' - mu' sum P1[j]) / sqrt(var + eps). h stays fp32.
+// Kernel 2 (k_pred_z): one wave per 16 neurons, four waves per block (one mask word per block), no block
+//   barrier. Groups of LPR lanes read one 2r-byte row of P2 with 16-byte loads together with the matching slice
+//   of h and the bias; the group reduces and compares with tau, a wavefront ballot gathers the wave's 16
+//   decisions, and the wave stores them as its 16-bit quarter of the mask word.
 #include "common.h"
 
 using namespace sffn;
@@ -21,10 +23,13 @@ namespace {
 
 constexpr int NT = 256;
 
+constexpr int NTH = 256;
+
 template <int NCH>
-__global__ __launch_bounds__(64) void k_pred_h(const uint4* __restrict__ P1, const float* __restrict__ x, int x_norm,
-                                               int B, int D, int r, float* __restrict__ h) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(NTH) void k_pred_h(const uint4* __restrict__ P1, const float* __restrict__ x, int x_norm,
+                                                int B, int D, int r, float* __restrict__ h) {
+  __shared__ float red[4][NTH / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int j = blockIdx.x;
   const int nc = D >> 3;
   const Buf bp(P1, (uint32_t)r * (uint32_t)D * 2u);
@@ -32,32 +37,62 @@ __global__ __launch_bounds__(64) void k_pred_h(const uint4* __restrict__ P1, con
   uint4 wv[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = lane + 64 * i;
+    const int c = threadIdx.x + NTH * i;
     wv[i] = bp.ld16(boff(c < nc, ((uint32_t)j * nc + c) * 16u));
   }
   float4 xr[NCH][2];
+  float x0 = 0.f;
   auto load_x = [&](int b) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
+      const int c = threadIdx.x + NTH * i;
       const uint32_t o = ((uint32_t)b * D + 8u * c) * 4u;
       xr[i][0] = bx.ldf4(boff(c < nc, o));
       xr[i][1] = bx.ldf4(boff(c < nc, o + 16u));
     }
+    x0 = x_norm ? bx.ldf((uint32_t)b * D * 4u) : 0.f;
   };
   load_x(0);  // before any loop: in flight together with the row of P1
   for (int b = 0; b < B; ++b) {
     if (b > 0) load_x(b);
-    if (x_norm) wave_norm_regs<NCH, 2>(xr, nc, D);
-    float acc = 0.f;
+    float spx = 0.f, sp = 0.f, sx = 0.f, sxx = 0.f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const float xv[8] = {xr[i][0].x, xr[i][0].y, xr[i][0].z, xr[i][0].w,
-                           xr[i][1].x, xr[i][1].y, xr[i][1].z, xr[i][1].w};
-      acc += dot8(wv[i], xv);
+      const int c = threadIdx.x + NTH * i;
+      if (c < nc) {
+        float pf[8];
+        f16x8_to_f32(wv[i], pf);
+        const float xv[8] = {xr[i][0].x, xr[i][0].y, xr[i][0].z, xr[i][0].w,
+                             xr[i][1].x, xr[i][1].y, xr[i][1].z, xr[i][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = xv[e] - x0;
+          spx = fmaf(pf[e], d, spx);
+          sp += pf[e];
+          sx += d;
+          sxx = fmaf(d, d, sxx);
+        }
+      }
     }
-    acc = wave_sum(acc);
-    if (lane == 0) h[(size_t)b * r + j] = acc;
+    spx = wave_sum(spx);
+    if (x_norm) { sp = wave_sum(sp); sx = wave_sum(sx); sxx = wave_sum(sxx); }
+    if (lane == 0) { red[0][w] = spx; red[1][w] = sp; red[2][w] = sx; red[3][w] = sxx; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int ww = 0; ww < NTH / 64; ++ww) t[k] += red[k][ww];
+      float hv = t[0];
+      if (x_norm) {
+        const float mu = t[2] / (float)D;
+        const float var = fmaxf(t[3] / (float)D - mu * mu, 0.f);
+        hv = (t[0] - mu * t[1]) / sqrtf(var + NORM_EPS);
+      }
+      h[(size_t)b * r + j] = hv;
+    }
+    __syncthreads();   // red is reused by the next token
   }
 }
 
@@ -67,9 +102,8 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
                                                const float* __restrict__ h, int B, int F, int r, float tau,
                                                uint64_t* __restrict__ mask, float* __restrict__ logits) {
   constexpr int RPI = 64 / LPR;        // rows per load instruction
-  constexpr int RPW = 16;              // rows per wave
+  constexpr int RPW = 16;              // rows per wave = one 16-bit quarter of a mask word
   constexpr int NI = RPW / RPI;        // load instructions per chunk round
-  __shared__ int flags[64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int rsub = lane / LPR, csub = lane % LPR;
   const int cpr = r >> 3;              // 16-byte chunks per row
@@ -125,24 +159,21 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
       }
     }
   }
-  if (csub == 0) {
+  // gather the 16 decisions: instruction i, row group q sits at lane q * LPR
+  uint32_t bits = 0;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) flags[w * RPW + i * RPI + rsub] = pred[i] ? 1 : 0;
+  for (int i = 0; i < NI; ++i) {
+    const unsigned long long bal = __ballot(csub == 0 && pred[i]);
+#pragma unroll
+    for (int q = 0; q < RPI; ++q)
+      if ((bal >> (q * LPR)) & 1ull) bits |= 1u << (i * RPI + q);
   }
-  __syncthreads();
-  if (w == 0) {
-    const int k = blockIdx.x * 64 + lane;
-    const bool bit = (k < F) && flags[lane] != 0;
-    const unsigned long long word = __ballot(bit);
-    if (lane == 0) mask[blockIdx.x] = (uint64_t)word;
-  }
+  if (lane == 0) reinterpret_cast<uint16_t*>(mask)[(size_t)blockIdx.x * 4 + w] = (uint16_t)bits;
 }
 
 template <int NCH>
 hipError_t launch_h(const void* P1, const float* x, int x_norm, int B, int D, int r, float* h, hipStream_t st) {
-  sffn_prof_before(0, st);
-  hipLaunchKernelGGL(k_pred_h<NCH>, dim3(r), dim3(64), 0, st, (const uint4*)P1, x, x_norm, B, D, r, h);
-  sffn_prof_after(0, st);
+  SFFN_LAUNCH(0, k_pred_h<NCH>, dim3(r), dim3(NTH), 0, st, (const uint4*)P1, x, x_norm, B, D, r, h);
   return hipGetLastError();
 }
 
@@ -150,10 +181,8 @@ template <int LPR, int ROUNDS>
 hipError_t launch_z(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, uint64_t* mask,
                     float* logits, hipStream_t st) {
   const int grid = (F + 63) / 64;
-  sffn_prof_before(1, st);
-  hipLaunchKernelGGL((k_pred_z<LPR, ROUNDS>), dim3(grid), dim3(NT), 0, st, (const uint4*)P2, c, h, B, F, r, tau,
+  SFFN_LAUNCH(1, (k_pred_z<LPR, ROUNDS>), dim3(grid), dim3(NT), 0, st, (const uint4*)P2, c, h, B, F, r, tau,
                      mask, logits);
-  sffn_prof_after(1, st);
   return hipGetLastError();
 }
 
@@ -161,15 +190,14 @@ hipError_t launch_z(const void* P2, const float* c, const float* h, int B, int F
 
 hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D,
                                int F, int r, float tau, uint64_t* mask, float* logits, float* hbuf, hipStream_t st) {
-  const int nch = (D / 8 + 63) / 64;
+  const int nch = (D / 8 + NTH - 1) / NTH;   // 16-byte chunks per thread (D <= 16384: at most 8)
   hipError_t e;
   if (nch <= 1) e = launch_h<1>(P1, x, x_norm, B, D, r, hbuf, st);
   else if (nch <= 2) e = launch_h<2>(P1, x, x_norm, B, D, r, hbuf, st);
+  else if (nch <= 3) e = launch_h<3>(P1, x, x_norm, B, D, r, hbuf, st);
   else if (nch <= 4) e = launch_h<4>(P1, x, x_norm, B, D, r, hbuf, st);
-  else if (nch <= 8) e = launch_h<8>(P1, x, x_norm, B, D, r, hbuf, st);
-  else if (nch <= 10) e = launch_h<10>(P1, x, x_norm, B, D, r, hbuf, st);
-  else if (nch <= 16) e = launch_h<16>(P1, x, x_norm, B, D, r, hbuf, st);
-  else e = launch_h<32>(P1, x, x_norm, B, D, r, hbuf, st);
+  else if (nch <= 6) e = launch_h<6>(P1, x, x_norm, B, D, r, hbuf, st);
+  else e = launch_h<8>(P1, x, x_norm, B, D, r, hbuf, st);
   if (e != hipSuccess) return e;
   const int cpr = r / 8;
   int lpr = 8;

@@ -468,15 +468,11 @@ __global__ void k_sum_parts(const float* __restrict__ part, int KS, int n, float
 template <int NTT>
 hipError_t predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F, int r,
                       float tau, uint64_t* mask, float* logits, float* hbuf, hipStream_t st) {
-  sffn_prof_before(0, st);
-  hipLaunchKernelGGL(k_mt_h<NTT>, dim3((r + 15) / 16), dim3(NTK), 0, st, (const uint4*)P1, x, B, D, r, hbuf);
-  sffn_prof_after(0, st);
+  SFFN_LAUNCH(0, k_mt_h<NTT>, dim3((r + 15) / 16), dim3(NTK), 0, st, (const uint4*)P1, x, B, D, r, hbuf);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  sffn_prof_before(1, st);
-  hipLaunchKernelGGL(k_mt_z<NTT>, dim3((F + 63) / 64), dim3(256), 0, st, (const uint4*)P2, c, hbuf, B, F, r, tau, mask,
+  SFFN_LAUNCH(1, k_mt_z<NTT>, dim3((F + 63) / 64), dim3(256), 0, st, (const uint4*)P2, c, hbuf, B, F, r, tau, mask,
                      logits);
-  sffn_prof_after(1, st);
   return hipGetLastError();
 }
 
@@ -493,10 +489,8 @@ hipError_t rows_mt(const void* Wg, const void* Sg, const float* bg, const void* 
     if (ea != hipSuccess) return ea;
   }
   if (lds > avail) return hipErrorInvalidValue;
-  sffn_prof_before(2, st);
-  hipLaunchKernelGGL((k_mt_rows<NTT, ACT, Q4>), dim3((F + 15) / 16), dim3(NTK), lds, st, Wg, Sg, bg, Wu, Su, bu, x, B,
+  SFFN_LAUNCH(2, (k_mt_rows<NTT, ACT, Q4>), dim3((F + 15) / 16), dim3(NTK), lds, st, Wg, Sg, bg, Wu, Su, bu, x, B,
                      D, F, mask, active, n_active, abuf);
-  sffn_prof_after(2, st);
   return hipGetLastError();
 }
 
@@ -511,10 +505,8 @@ hipError_t down_mt(const void* Wd, const void* Sd, const uint64_t* mask, const f
     if (ea != hipSuccess) return ea;
   }
   if (lds > avail) return hipErrorInvalidValue;
-  sffn_prof_before(3, st);
-  hipLaunchKernelGGL((k_mt_down<NTT, Q4>), dim3((D + DS_COLS - 1) / DS_COLS, KS), dim3(DN_T), lds, st, Wd, Sd, mask,
+  SFFN_LAUNCH(3, (k_mt_down<NTT, Q4>), dim3((D + DS_COLS - 1) / DS_COLS, KS), dim3(DN_T), lds, st, Wd, Sd, mask,
                      abuf, B, D, F, part);
-  sffn_prof_after(3, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = B * D;

@@ -1,6 +1,6 @@
 """A resident sparse-FFN stack on one GPU: every layer's predictor and weights in HBM, one decode step =
 sffn_predict + sffn_forward (or sffn_forward_q4) per layer, layer l+1 reading layer l's output through the
-library's RMS-on-load option. A step can be captured once into a HIP graph and replayed.
+library's normalise-on-load option (a parameter-free LayerNorm). A step can be captured once into a HIP graph and replayed.
 
 The pages' decode touches the whole model for every token (Turkish article, motivation section); the stack
 is the FFN part of that, with the neuron order of every layer chosen hot-first (pack.hot_first_perm).

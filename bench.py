@@ -3,12 +3,15 @@
 
 One step = one decode token batch through every layer of the resident FFN stack: per layer the activation
 predictor (sffn_predict) and the neuron-aware sparse FFN (sffn_forward / sffn_forward_q4), layer l+1 reading
-layer l's output through the library's RMS-on-load option. Steps are replayed from a HIP graph; inputs
-x ~ N(0, 1) are fresh per step and already in HBM when the timed region starts.
+layer l's output through the library's normalise-on-load option. Steps are replayed from a HIP graph; inputs
+x ~ N(0, 1) are fresh per step and already in HBM when the timed region starts. A workload with a prompt (the
+70B Q4_0 stack) also times the prompt as one union-mask batch through the stack, reported beside the decode
+figure.
 
 Printed: one JSON line with decode tokens/s (value), HBM GB/s on the active weight rows actually read, the
-roofline of the dominant kernel (per-launch HIP events around that kernel on its own stream), and the CPU
-oracle timed on this host's cores over a bounded sample.
+roofline of the dominant kernel, and the CPU oracle timed on this host's cores over a bounded sample. Kernel
+durations come from eager steps of the same stack on the timed inputs: each launch of the profiled kernel
+writes its own device start and end timestamps into a HIP event pair on its stream (hipExtLaunchKernelGGL).
 """
 from __future__ import annotations
 
@@ -37,14 +40,16 @@ def parse():
     ap.add_argument("--batch", type=int, default=1, help="tokens per decode step (union mask when > 1)")
     ap.add_argument("--profile-steps", type=int, default=8, help="eager steps per profiled kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--prompt", type=int, default=None,
+                    help="prompt tokens timed as one union batch (default: the workload's own, 64 for the 70B)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of replaying a graph")
     return ap.parse_args()
 
 
-def cpu_baseline(wl, budget_s: float):
+def cpu_baseline(wl, B: int, budget_s: float):
     """The oracle (plain fp64 NumPy dense FFN + predictor) timed on this host over a bounded sample of the same
-    workload: whole layers, one token at a time, extrapolated to the stack."""
+    workload: whole layers, B tokens per evaluation, until the time budget is spent; extrapolated to the stack."""
     import numpy as np
     import oracle
     import synthgen as sg
@@ -58,21 +63,19 @@ def cpu_baseline(wl, budget_s: float):
     times, n = [], 0
     t_start = time.perf_counter()
     step = 0
-    while True:
-        for li, w in enumerate(ws):
-            x = sg.inputs(wl, step, 1)
+    while time.perf_counter() - t_start < budget_s:
+        for w in ws:
+            x = sg.inputs(wl, step, B)
             t0 = time.perf_counter()
             oracle.layer(wl.act, x, w, wl.t)
             times.append(time.perf_counter() - t0)
             n += 1
         step += 1
-        if time.perf_counter() - t_start > budget_s or step >= 64:
-            break
     per_layer = float(np.median(times))
-    tok_s = 1.0 / (per_layer * wl.L)
+    tok_s = B / (per_layer * wl.L)
     return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} layer-token evaluations of {wl.name} (layers {layers}, batch 1, fp64 NumPy dense FFN + "
-                      f"predictor), median {per_layer * 1e3:.1f} ms per layer, extrapolated to {wl.L} layers",
+            "sample": f"{n} layer evaluations of {wl.name} (layers {layers}, {B} token(s) each, fp64 NumPy dense FFN "
+                      f"+ predictor), median {per_layer * 1e3:.1f} ms per layer, extrapolated to {wl.L} layers",
             "seconds": round(time.perf_counter() - t_start, 2)}
 
 
@@ -93,9 +96,10 @@ def main():
 
     wl = sg.workload(args.workload)
     B = args.batch
+    PB = wl.prompt if args.prompt is None else args.prompt
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
-    stack = SparseFFNStack(wl, dev, max_batch=B)
+    stack = SparseFFNStack(wl, dev, max_batch=max(B, PB))
     L = len(stack.layers)
     setup_s = time.perf_counter() - t0
     print(f"# setup: {wl.name}, {L} layers resident, {setup_s:.1f} s", file=sys.stderr, flush=True)
@@ -106,37 +110,67 @@ def main():
         sg.inputs(wl, s, B, tag=sg.TAG_X_DECODE, out=X[s])
     n_acc = torch.zeros(L, dtype=torch.int64, device=dev)
 
-    def body():
-        stack.step(B)
-        n_acc.add_(stack.n_active)
-
-    if args.no_graph:
-        run = body
-    else:
-        stack.x_in[:B].copy_(X[0])
+    def make_run(nb, acc):
+        def body():
+            stack.step(nb)
+            if acc is not None:
+                acc.add_(stack.n_active)
+        if args.no_graph:
+            return body
         body()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             body()
-        run = g.replay
+        return g.replay
 
+    # ---- optional prompt: PB tokens through the stack as one union-mask batch, timed on its own
+    prompt = None
+    if PB > 0:
+        XP = torch.empty((PB, wl.D), dtype=torch.float32, device=dev)
+        sg.inputs(wl, 0, PB, tag=sg.TAG_X_PROMPT, out=XP)
+        stack.x_in[:PB].copy_(XP)
+        run_p = make_run(PB, None)
+        reps = 5
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        for _ in range(2):
+            stack.x_in[:PB].copy_(XP)
+            run_p()
+        torch.cuda.synchronize()
+        for i in range(reps):
+            stack.x_in[:PB].copy_(XP)
+            ev[i].record()
+            run_p()
+        ev[reps].record()
+        torch.cuda.synchronize()
+        p_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+        n_p = float(stack.n_active.double().mean().item())
+        prompt = {"tokens": PB, "ms_median": round(p_ms[reps // 2], 4), "tokens_s": round(PB / (p_ms[reps // 2] * 1e-3), 1),
+                  "union_rows_per_layer": round(n_p, 1), "union_density": round(n_p / wl.F, 4),
+                  "active_weight_gbs": round(n_p * stack.active_weight_bytes_per_row() * L / (p_ms[reps // 2] * 1e-3)
+                                             / 1e9, 1)}
+        print(f"# prompt: {prompt}", file=sys.stderr, flush=True)
+
+    # ---- decode steps: W warm-up replays, then K timed replays with an event between consecutive steps
+    stack.x_in[:B].copy_(X[0])
+    run = make_run(B, n_acc)
     for s in range(W):
         stack.x_in[:B].copy_(X[s])
         run()
     torch.cuda.synchronize()
     n_acc.zero_()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    e0.record()
     for s in range(K):
+        ev[s].record()
         stack.x_in[:B].copy_(X[W + s])
         run()
-    e1.record()
+    ev[K].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms_total = e0.elapsed_time(e1)
+    ms_total = ev[0].elapsed_time(ev[K])
+    per_step = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(K)])
     ms_step = ms_total / K
     n_mean = n_acc.cpu().numpy().astype(np.float64) / K          # mean active rows per layer per step
     row_bytes = stack.active_weight_bytes_per_row()
@@ -144,10 +178,11 @@ def main():
     pred_bytes_step = L * stack.predictor_bytes()
     tok_s = B * K / (ms_total * 1e-3)
 
-    # ---- per-kernel durations: eager steps with HIP events around every launch of one kernel
+    # ---- per-kernel durations: P eager steps of the same stack on the timed inputs; every launch of the
+    # profiled kernel records its own device start and end timestamps into a HIP event pair on its stream
     P = max(1, args.profile_steps)
-    prof = {}
-    nlog = []
+    prof, nlog = {}, []
+    timing = "eager steps, device timestamps of each launch"
     for kid in (0, 1, 2, 3):
         _lib.profile_begin(kid, P * L)
         for s in range(P):
@@ -155,8 +190,7 @@ def main():
             stack.step(B)
             if kid == 2:
                 nlog.append(stack.n_active.cpu().numpy().astype(np.float64))
-        ms = _lib.profile_end(P * L)
-        prof[kid] = np.asarray(ms, dtype=np.float64)
+        prof[kid] = np.asarray(_lib.profile_end(P * L), dtype=np.float64)
     torch.cuda.synchronize()
     mean_us = {k: float(v.mean() * 1e3) for k, v in prof.items()}
     # algorithmic bytes per launch (active rows actually read by the profiled launches)
@@ -186,6 +220,7 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -201,6 +236,8 @@ def main():
         "active_rows_per_layer": round(float(n_mean.mean()), 1),
         "density": round(float(n_mean.mean()) / wl.F, 4),
         "kernel_us": {KERNEL_NAMES[k]: round(v, 3) for k, v in mean_us.items()},
+        "kernel_timing": timing,
+        "prompt": prompt,
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
@@ -208,7 +245,7 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, B, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

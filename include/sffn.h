@@ -44,7 +44,23 @@
  *
  * Alignment: every tensor pointer 16-byte aligned; the workspace 256-byte
  * aligned. Limits: 1 <= B <= 64; 8 <= D <= 16384 with D % 8 == 0 (D % 32 == 0
- * for Q4_0); 1 <= F <= 1<<22; 8 <= r <= 1024 with r % 8 == 0; B * r <= 32768.
+ * for Q4_0); 1 <= F <= 1<<22; 8 <= r <= 1024 with r % 8 == 0; B * r <= 32768;
+ * every weight matrix and the B x F activations below 2 GiB.
+ *
+ * Batches. B == 1 (decode) and B in {2, 4, 8} with B * D <= 16384 run the
+ * decode kernels (vector ALU, x staged once per block). Every other B > 1 runs
+ * the union kernels on the matrix cores ("Neuron-aware operator": each active
+ * row is read once for the whole batch); these compact the whole mask inside
+ * one workgroup and take F <= 32768 in sffn_forward / sffn_forward_q4. fp32
+ * inputs enter the matrix cores as two fp16 halves (x = hi + lo), so the
+ * batch results match the decode kernels' to within fp32 rounding.
+ *
+ * Workspace (sffn_workspace_size bytes, 256-byte parts, caller-owned, no
+ * state kept between calls): activations a [F, B] fp32; for B > 1 also the
+ * normalised inputs [B, D] and 8 row-split partial sums [8, B, D] fp32; the
+ * predictor's h [B, r] fp32 last. One workspace may serve the predict and
+ * forward calls of a layer in turn on one stream; calls that overlap in time
+ * need separate workspaces.
  *
  * Errors: arguments are checked on the host before anything is enqueued; a
  * failed check returns its status and leaves the stream untouched. A failed
@@ -104,7 +120,7 @@ int sffn_mask_words(int F);
  * (population) variance of x[b, :] -- the parameter-free normalisation between stacked layers, applied as the
  * input is loaded.
  * Outputs: mask (every word written, bits >= F zero); logits [B, F] fp32 if
- * non-NULL. Uses the workspace. Two kernels. */
+ * non-NULL. Uses the workspace. Two kernels (three for B > 1 with x_norm: the tokens are normalised first). */
 int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F,
                  int r, float t, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream);
 
@@ -114,7 +130,7 @@ int sffn_predict(const void* P1, const void* P2, const float* c, const float* x,
  *   y[b, :]  = sum_j a[b, j] * W_downT[active[j], :]          (only active rows are read)
  * xn as in sffn_predict. W_gate / b_gate are used (and required) for REGLU only;
  * b_up may be NULL (0). active [F] int32 and n_active [1] int32 are device
- * outputs; y [B, D] is overwritten. Uses the workspace. Two kernels. */
+ * outputs; y [B, D] is overwritten. Uses the workspace. Two kernels; the union kernels add a sum of the row-split partials (and a normalisation pass for x_norm). */
 int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W_up, const float* b_up,
                  const void* W_downT, const float* x, int x_norm, int B, int D, int F, const uint64_t* mask,
                  int32_t* active, int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream);
@@ -127,12 +143,15 @@ int sffn_forward_q4(int act, sffn_q4 W_gate, const float* b_gate, sffn_q4 W_up, 
 
 /* Per-launch timing of one kernel (profiling aid; not needed for computing).
  * kernel: SFFN_K_PRED_H (P1 x), SFFN_K_PRED_Z (P2 h + c, threshold, mask), SFFN_K_ROWS (compaction + W_gate /
- * W_up row gather + activation), SFFN_K_COLS (W_downT column gather).
- * Between sffn_profile_begin and sffn_profile_end, every launch of that kernel made by the calling thread is
- * bracketed by two HIP events recorded on its launch stream, up to max_launches launches; the events are
- * created by sffn_profile_begin (host call; not inside a graph capture). sffn_profile_end waits for the last
- * event, writes the elapsed milliseconds of the bracketed launches to ms[0 .. min(count, max)) and returns
- * the count (negative status on error). Returns SFFN_ERR_ARG for a bad kernel id or max_launches < 1. */
+ * W_up row gather + activation), SFFN_K_COLS (W_downT column gather; in the union path the row-split down
+ * projection, not the sum of its partials).
+ * Between sffn_profile_begin and sffn_profile_end, every launch of that kernel made by the calling thread, up
+ * to max_launches of them, is issued with a pair of HIP events that take the kernel's own start and end
+ * timestamps (hipExtLaunchKernelGGL): the kernel's time on the device, without host-side queueing. The events
+ * are created by sffn_profile_begin (host call; launches under graph capture are not timed: profile eager
+ * calls). sffn_profile_end waits for the last event, writes the elapsed milliseconds of the launches to
+ * ms[0 .. min(count, max)) and returns the count (negative status on error). Returns SFFN_ERR_ARG for a bad
+ * kernel id or max_launches < 1. */
 enum { SFFN_K_PRED_H = 0, SFFN_K_PRED_Z = 1, SFFN_K_ROWS = 2, SFFN_K_COLS = 3 };
 int sffn_profile_begin(int kernel, int max_launches);
 int sffn_profile_end(float* ms, int max);

@@ -57,6 +57,14 @@ def make_case(wl, layer=0, device="cuda:0", with_c=True, perm="hot", from_device
     return LayerCase(wl, layer, host, w, dev, np.asarray(p))
 
 
+def host_case(wl, layer=0, perm=None):
+    """Oracle-side case of a layer whose device tensors live elsewhere (a resident stack): logical host tensors,
+    fp64 weights and the stored order (hot-first by default, as the stack packs it)."""
+    host = sg.layer_host(wl, layer)
+    p = hot_first_perm(sg.neuron_probs(wl, layer)) if perm is None else perm
+    return LayerCase(wl, layer, host, oracle.logical_weights(host), {}, np.asarray(p))
+
+
 def run_gpu(case: LayerCase, x: torch.Tensor, x_norm=False, t=None, want_logits=True):
     wl, d = case.wl, case.dev
     B, D = x.shape

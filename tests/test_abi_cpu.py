@@ -102,3 +102,17 @@ def test_forward_rejects(kw, status):
 ])
 def test_forward_q4_rejects(kw, status):
     assert _forward_q4(**kw) == status
+
+
+def test_profile_calls_reject_bad_arguments():
+    h = _lib.lib()
+    assert h.sffn_profile_begin(9, 4) == 6
+    assert h.sffn_profile_begin(0, 0) == 6
+    assert h.sffn_profile_end(None, 0) < 0         # nothing started
+
+
+def test_union_batches_are_routed_not_rejected():
+    # B = 3 and B = 16 take the union kernels: shape accepted, the fake workspace size is what fails
+    assert _forward(B=3, ws_bytes=16) == 4
+    assert _forward_q4(B=16, ws_bytes=16) == 4
+    assert _predict(B=5, ws_bytes=16) == 4

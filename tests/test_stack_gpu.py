@@ -1,0 +1,58 @@
+"""The resident stack in the launch configuration the benchmark times: a step captured once into a HIP graph
+and replayed, every layer checked against the oracle with its input taken from the GPU's previous layer
+(teacher-forced), at the full layer sizes of each workload (a few of its layers), for decode and union batches."""
+import numpy as np
+import pytest
+import torch
+
+import synthgen as sg
+from activation_sparse_ffn_predictor_amd.stack import SparseFFNStack
+from parity_util import check, host_case, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer_results(stack, i, B):
+    return dict(mask=stack.mask[i].cpu().numpy().view(np.uint64), active=stack.active[i].cpu().numpy(),
+                n=int(stack.n_active[i].item()), y=stack.y[i, :B].cpu().numpy().astype(np.float64), logits=None)
+
+
+def _check_stack(stack, cases, x0, B):
+    stats = []
+    for i, case in enumerate(cases):
+        res = _layer_results(stack, i, B)
+        xin = x0 if i == 0 else stack.y[i - 1, :B].cpu().numpy()
+        stats.append(check(case, xin, res, x_norm=i > 0))
+    return stats
+
+
+CASES = [("c2", 1, 3, 0), ("c3", 1, 3, 0), ("c3", 4, 3, 0), ("c4", 1, 2, 0), ("c5", 1, 2, 0), ("c5", 64, 2, 1)]
+
+
+@pytest.mark.parametrize("name,B,nl,prompt", CASES, ids=[f"{c[0]}-B{c[1]}" for c in CASES])
+def test_graph_replay_matches_oracle(gpu_ready, name, B, nl, prompt):
+    wl = sg.workload(name)
+    layers = list(range(nl))
+    say(f"[stack {name} B={B}] building {nl} layers")
+    stack = SparseFFNStack(wl, gpu_ready, layers=layers, max_batch=B)
+    cases = [host_case(wl, l) for l in layers]
+    tag = sg.TAG_X_PROMPT if prompt else sg.TAG_X_DECODE
+    xs = [sg.inputs(wl, s, B, tag=tag) for s in range(3)]
+    stack.x_in[:B].copy_(torch.from_numpy(xs[0]))
+    g = stack.capture(B)
+    for rep, x in enumerate(xs):
+        stack.x_in[:B].copy_(torch.from_numpy(x))
+        stack.replay(B)
+        torch.cuda.synchronize()
+        st = _check_stack(stack, cases, x, B)
+        say(f"[stack {name} B={B}] replay {rep}: " + "; ".join(
+            f"L{i} n={s['n']} flips={s['flips']} rel={s['rel_err']:.1e}" for i, s in enumerate(st)))
+        # eager work on the same buffers between replays
+        stack.x_in[:B].copy_(torch.from_numpy(xs[(rep + 1) % 3]))
+        stack.step(B)
+        torch.cuda.synchronize()
+        ye = stack.y[:, :B].clone()
+        stack.replay(B)
+        torch.cuda.synchronize()
+        assert torch.equal(ye, stack.y[:, :B]), "graph replay differs from the eager step on the same input"
+    del g
