@@ -44,7 +44,54 @@ def parse():
                     help="prompt tokens timed as one union batch (default: the workload's own, 64 for the 70B)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of replaying a graph")
+    ap.add_argument("--copy-only", type=float, default=None, metavar="MIB",
+                    help="only copy MIB mebibytes device to device 8 times and exit (the reference transfer that "
+                         "scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("common.h", "predict.hip", "forward.hip", "forward_q4.hip", "union.hip")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources: counter results taken on other sources are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "activation_sparse_ffn_predictor_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_for(workload: str, batch: int, kernel: str, launches: float):
+    """(HBM bytes per launch, detail) of `kernel` measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each
+    scaled by the same counter on a plain copy of known size), if such a measurement exists for these kernel
+    sources; None otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    e = t.get("runs", {}).get(f"{workload}/B{batch}", {}).get(kernel)
+    if not e:
+        return None
+    return e["fetch_bytes"] + e["write_bytes"], {
+        "fetch_bytes": e["fetch_bytes"], "write_bytes": e["write_bytes"],
+        "algorithmic_bytes_per_launch": round(launches, 1), "source": "profiles/traffic.json"}
+
+
+def copy_only(mib: float):
+    import torch
+    n = int(mib * 1024 * 1024) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(8):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 4 * n, "launches": 8}), flush=True)
 
 
 def cpu_baseline(wl, B: int, budget_s: float):
@@ -86,6 +133,10 @@ def main():
         print(json.dumps({"error": "this benchmark runs the sparse-FFN stack on one GPU; --gpus must be 1"}),
               flush=True)
         sys.exit(2)
+
+    if args.copy_only is not None:
+        copy_only(args.copy_only)
+        return
 
     import numpy as np
     import torch
@@ -211,7 +262,8 @@ def main():
     fwd_us = mean_us[2] + mean_us[3]
     fwd_gbs = (float(n_prof.mean()) * row_bytes) / (fwd_us * 1e-6) / 1e9
 
-    traffic = None
+    tr = traffic_for(wl.name, B, KERNEL_NAMES[dom], float(kb[dom][:m].mean()))
+    traffic, traffic_detail = tr if tr else (None, None)
     out = {
         "metric": METRIC,
         "value": round(tok_s, 2),
@@ -240,7 +292,7 @@ def main():
         "prompt": prompt,
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic, "traffic_detail": traffic_detail},
         "wall_s": round(wall, 3),
         "setup_s": round(setup_s, 1),
     }
