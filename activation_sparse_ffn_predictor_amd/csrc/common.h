@@ -336,6 +336,14 @@ __device__ __forceinline__ int compact_words(uint64_t cw, int w0, int nwr, int w
   return cnt[NWB];
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on XCD i % 8) and every XCD has its own
+// L2. For a grid of G = 8 * per workgroups, xcd_slice maps workgroup i to slice (i % 8) * per + i / 8, so
+// neighbouring slices -- which share cache lines when a slice is narrower than a line -- run on one XCD and
+// share its L2 instead of fetching the same lines once per XCD.
+__device__ __forceinline__ int xcd_slice(int i, int G) {
+  return (i & 7) * (G >> 3) + (i >> 3);
+}
+
 // Mask word t with the bits of neurons >= F cleared (callers may pass any bit pattern there).
 __device__ __forceinline__ uint64_t mask_word(const uint64_t* __restrict__ mask, int t, int nw, int F) {
   uint64_t w = mask[t];

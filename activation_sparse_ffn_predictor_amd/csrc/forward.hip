@@ -26,7 +26,16 @@ using namespace sffn;
 
 namespace {
 
-constexpr int NT_UP = 256;
+#ifndef SFFN_UP_NT
+#define SFFN_UP_NT 256           // threads per block of the row gather
+#endif
+#ifndef SFFN_UP_GRID
+#define SFFN_UP_GRID 512         // blocks of the row gather (dense index i -> block i % grid)
+#endif
+constexpr int NT_UP = SFFN_UP_NT;
+#ifndef SFFN_DOWN_XCD
+#define SFFN_DOWN_XCD 1          // XCD-aware order of the column slices of the column gather
+#endif
 constexpr int WMAX = 2;           // mask words per thread kept in registers / LDS (F <= 32768; larger F reads them from memory)
 
 template <int B, int ACT, int NCH>
@@ -47,7 +56,7 @@ __global__ __launch_bounds__(NT_UP) void k_upgate(const uint4* __restrict__ Wg, 
   const int lane = threadIdx.x & 63;
   const int nc = D >> 3;
   const int n4 = (B * D) >> 2;
-  constexpr int XPT = (B * NCH + 1) / 2;   // float4 of x per thread: B * D / (4 * NT_UP) <= B * NCH / 2
+  constexpr int XPT = (128 * B * NCH + NT_UP - 1) / NT_UP;   // float4 of x per thread: B * D / 4 <= 128 * B * NCH
 
   // round 1: x and the mask words, all loads issued before any use
   float4 xv4[XPT];
@@ -132,10 +141,38 @@ __global__ __launch_bounds__(NT_UP) void k_upgate(const uint4* __restrict__ Wg, 
 // Column gather: B tokens, SW columns per block, NT threads, DU row slices in flight per lane.
 template <int B>
 struct DownCfg;
-template <> struct DownCfg<1> { static constexpr int NT = 1024, DU = 16; };
+template <> struct DownCfg<1> { static constexpr int NT = 512, DU = 16; };
 template <> struct DownCfg<2> { static constexpr int NT = 512, DU = 16; };
 template <> struct DownCfg<4> { static constexpr int NT = 512, DU = 12; };
 template <> struct DownCfg<8> { static constexpr int NT = 512, DU = 8; };
+
+// One pass of the column gather over rows k0 + w * RPI + rsub + u * NWV * RPI (u < DU): every row-slice and
+// activation load is issued before the first multiply-add (the scheduling barrier keeps the compiler from
+// interleaving them, which would leave only a few loads in flight per lane).
+template <int B, int LPR, int RPI, int NWV, int DU>
+__device__ __forceinline__ void down_pass(const Buf& bwd, const Buf& ba, const uint32_t (&ids)[DU], int k0, int n,
+                                          int w, int rsub, bool colok, int nc, int cchunk, float (&acc)[B][8]) {
+  uint4 wv[DU];
+  float av[DU][B];
+#pragma unroll
+  for (int u = 0; u < DU; ++u) {
+    const int i = k0 + w * RPI + rsub + u * NWV * RPI;
+    const bool ok = i < n;
+    wv[u] = bwd.ld16(boff(ok && colok, (ids[u] * nc + cchunk) * 16u));
+#pragma unroll
+    for (int b = 0; b < B; ++b) av[u][b] = ba.ldf(boff(ok, ((uint32_t)i * B + b) * 4u));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < DU; ++u) {
+    float wf[8];
+    f16x8_to_f32(wv[u], wf);
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[b][e] = fmaf(av[u][b], wf[e], acc[b][e]);
+  }
+}
 
 template <int B, int SW>
 __global__ __launch_bounds__(DownCfg<B>::NT) void k_down(const uint4* __restrict__ WdT,
@@ -151,7 +188,9 @@ __global__ __launch_bounds__(DownCfg<B>::NT) void k_down(const uint4* __restrict
   __shared__ float red[NWV * B * SW];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nc = D >> 3;
-  const int cchunk = blockIdx.x * LPR + (lane % LPR);  // 16-byte chunk of this lane's 8 columns
+  const int slice = SFFN_DOWN_XCD ? xcd_slice(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  if (slice * SW >= D) return;                          // block-uniform: padding of the grid to 8 * per
+  const int cchunk = slice * LPR + (lane % LPR);        // 16-byte chunk of this lane's 8 columns
   const bool colok = cchunk < nc;
   const int rsub = lane / LPR;
   const Buf bwd(WdT, (uint32_t)F * (uint32_t)D * 2u);
@@ -164,39 +203,23 @@ __global__ __launch_bounds__(DownCfg<B>::NT) void k_down(const uint4* __restrict
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
 
-  // round 1: the count and the ids are loaded together (ids speculatively, bounded by F)
-  const int nraw = (int)bn.ldu(0u);
-  int k0 = 0;
-  do {
-    uint32_t ids[DU];
+  auto load_ids = [&](int k0, uint32_t (&ids)[DU]) {  // speculative, bounded by F
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
       const int i = k0 + w * RPI + rsub + u * NWV * RPI;
       ids[u] = bid.ldu(boff(i < F, (uint32_t)i * 4u));
     }
-    const int n = min(max(nraw, 0), F);
-    // round 2: row slices and activations
-    uint4 wv[DU];
-    float av[DU][B];
-#pragma unroll
-    for (int u = 0; u < DU; ++u) {
-      const int i = k0 + w * RPI + rsub + u * NWV * RPI;
-      const bool ok = i < n;
-      wv[u] = bwd.ld16(boff(ok && colok, (ids[u] * nc + cchunk) * 16u));
-#pragma unroll
-      for (int b = 0; b < B; ++b) av[u][b] = ba.ldf(boff(ok, ((uint32_t)i * B + b) * 4u));
-    }
-#pragma unroll
-    for (int u = 0; u < DU; ++u) {
-      float wf[8];
-      f16x8_to_f32(wv[u], wf);
-#pragma unroll
-      for (int b = 0; b < B; ++b)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[b][e] = fmaf(av[u][b], wf[e], acc[b][e]);
-    }
-    k0 += STRIDE;
-  } while (k0 < min(max(nraw, 0), F));
+  };
+  // round 1: the count and the first pass's ids together; round 2: that pass's rows and activations
+  const int nraw = (int)bn.ldu(0u);
+  uint32_t ids[DU];
+  load_ids(0, ids);
+  const int n = min(max(nraw, 0), F);
+  down_pass<B, LPR, RPI, NWV, DU>(bwd, ba, ids, 0, n, w, rsub, colok, nc, cchunk, acc);
+  for (int k0 = STRIDE; k0 < n; k0 += STRIDE) {       // more rows than one pass holds
+    load_ids(k0, ids);
+    down_pass<B, LPR, RPI, NWV, DU>(bwd, ba, ids, k0, n, w, rsub, colok, nc, cchunk, acc);
+  }
   // reduce over the row groups of the wave (lanes with equal lane % LPR), then across waves
 #pragma unroll
   for (int b = 0; b < B; ++b)
@@ -218,7 +241,7 @@ __global__ __launch_bounds__(DownCfg<B>::NT) void k_down(const uint4* __restrict
     const int b = tt / SW, col = tt % SW;
     float s = 0.f;
     for (int ww = 0; ww < NWV; ++ww) s += red[(ww * B + b) * SW + col];
-    const int d = blockIdx.x * SW + col;
+    const int d = slice * SW + col;
     if (d < D) y[(size_t)b * D + d] = s;
   }
 }
@@ -228,17 +251,17 @@ hipError_t launch_up(const void* Wg, const float* bg, const void* Wu, const floa
                      int F, const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf, hipStream_t st) {
   const int nw = (F + 63) / 64;
   const int wpt = (nw + NT_UP - 1) / NT_UP;
-  const size_t lds = (wpt <= WMAX ? (size_t)((nw + 1) & ~1) * 8 : 0) + (NT_UP + NT_UP / 64 + 4) * sizeof(int) +
-                     ((size_t)B * D + 2 * (NT_UP / 64) * B) * sizeof(float);
+  const size_t lds_scan = (wpt <= WMAX ? (size_t)((nw + 1) & ~1) * 8 : 0) + (NT_UP + NT_UP / 64 + 4) * sizeof(int);
+  const int grid = std::max(1, std::min((F + 3) / 4, SFFN_UP_GRID));
+  const size_t lds = lds_scan + ((size_t)B * D + 2 * (NT_UP / 64) * B) * sizeof(float);
   static size_t avail = 0;
   if (!avail) {
     hipError_t ea = allow_dynamic_lds((const void*)k_upgate<B, ACT, NCH>, &avail);
     if (ea != hipSuccess) return ea;
   }
   if (lds > avail) return hipErrorInvalidValue;
-  const int grid = std::max(1, std::min((F + 3) / 4, 512));
   SFFN_LAUNCH(2, (k_upgate<B, ACT, NCH>), dim3(grid), dim3(NT_UP), lds, st, (const uint4*)Wg, bg,
-                     (const uint4*)Wu, bu, x, x_norm, D, F, mask, active, n_active, abuf);
+              (const uint4*)Wu, bu, x, x_norm, D, F, mask, active, n_active, abuf);
   return hipGetLastError();
 }
 
@@ -257,12 +280,17 @@ hipError_t dispatch_up(int nch, const void* Wg, const float* bg, const void* Wu,
 #undef UP
 }
 
-constexpr int DOWN_SW = 64;   // 128 bytes of every active W_downT row per block
+// Output columns per block of the column gather; with the XCD-aware slice order neighbouring slices share L2.
+#ifndef SFFN_DOWN_SW
+#define SFFN_DOWN_SW 32
+#endif
+constexpr int DOWN_SW = SFFN_DOWN_SW;
 
 template <int B>
 hipError_t launch_down(const void* WdT, const int32_t* active, const int32_t* n_active, const float* abuf, int D,
                        int F, float* y, hipStream_t st) {
-  const int grid = (D + DOWN_SW - 1) / DOWN_SW;
+  const int slices = (D + DOWN_SW - 1) / DOWN_SW;
+  const int grid = SFFN_DOWN_XCD ? (slices + 7) / 8 * 8 : slices;
   SFFN_LAUNCH(3, (k_down<B, DOWN_SW>), dim3(grid), dim3(DownCfg<B>::NT), 0, st, (const uint4*)WdT, active, n_active,
               abuf, D, F, y);
   return hipGetLastError();

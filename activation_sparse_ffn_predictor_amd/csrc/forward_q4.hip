@@ -20,7 +20,13 @@ using namespace sffn;
 
 namespace {
 
-constexpr int NT_UP = 256;
+#ifndef SFFN_UP_NT
+#define SFFN_UP_NT 256           // threads per block of the row gather
+#endif
+#ifndef SFFN_UP_GRID
+#define SFFN_UP_GRID 512         // blocks of the row gather (dense index i -> block i % grid)
+#endif
+constexpr int NT_UP = SFFN_UP_NT;
 constexpr int WMAX = 2;            // mask words per thread in registers / LDS (F <= 32768; larger F reads them from memory)
 
 // sum over a Q4 block of q_e * x_e: nib = 16 nibble bytes, xl/xh = x of the low-nibble (elements 0..15) and
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(NT_UP) void k_upgate_q4(const uint4* __restrict__ q
   float* red = xsum + (size_t)B * nblk;
   const int lane = threadIdx.x & 63;
   const int n4 = (B * D) >> 2;
-  constexpr int XPT = (B * NQ * 4 + 1) / 2;   // float4 of x per thread: B * D / (4 * NT_UP) <= B * NQ * 2
+  constexpr int XPT = (512 * B * NQ + NT_UP - 1) / NT_UP;   // float4 of x per thread: B * D / 4 <= 512 * B * NQ
 
   // round 1: x and the mask words, all loads issued before any use
   float4 xv4[XPT];
@@ -161,7 +167,13 @@ __global__ __launch_bounds__(NT_UP) void k_upgate_q4(const uint4* __restrict__ q
   }
 }
 
-constexpr int QSW = 128;               // output columns per block (4 Q4 blocks of each row)
+#ifndef SFFN_DOWN_XCD
+#define SFFN_DOWN_XCD 1                // XCD-aware order of the column slices of the column gather
+#endif
+#ifndef SFFN_Q4_DOWN_SW
+#define SFFN_Q4_DOWN_SW 64
+#endif
+constexpr int QSW = SFFN_Q4_DOWN_SW;   // output columns per block (QSW / 32 Q4 blocks of each row)
 constexpr int QCPL = 16;               // columns per lane (half a Q4 block: 8 nibble bytes)
 constexpr int QLPR = QSW / QCPL;       // lanes per row slice (8)
 constexpr int QRPI = 64 / QLPR;        // rows per wave instruction (8)
@@ -182,7 +194,9 @@ __global__ __launch_bounds__(QD<B>::NT) void k_down_q4(const uint8_t* __restrict
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nblk = D >> 5;
   const int rsub = lane / QLPR, lsub = lane % QLPR;
-  const int col0 = blockIdx.x * QSW + lsub * QCPL;
+  const int slice = SFFN_DOWN_XCD ? xcd_slice(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  if (slice * QSW >= D) return;               // block-uniform: padding of the grid to 8 * per
+  const int col0 = slice * QSW + lsub * QCPL;
   const int qblk = col0 >> 5;                 // Q4 block of this lane
   const int half = (col0 >> 4) & 1;           // which 8-byte half of the block's nibbles
   const bool colok = col0 < D;
@@ -199,18 +213,16 @@ __global__ __launch_bounds__(QD<B>::NT) void k_down_q4(const uint8_t* __restrict
 #pragma unroll
     for (int e = 0; e < QCPL; ++e) acc[b][e] = 0.f;
   }
-  // round 1: the count and the ids are loaded together (ids speculatively, bounded by F)
-  const int nraw = (int)bn.ldu(0u);
-  int k0 = 0;
-  do {
-    uint32_t ids[DU];
+  auto load_ids = [&](int k0, uint32_t (&ids)[DU]) {  // speculative, bounded by F
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
       const int i = k0 + w * QRPI + rsub + u * NWV * QRPI;
       ids[u] = bid.ldu(boff(i < F, (uint32_t)i * 4u));
     }
-    const int n = min(max(nraw, 0), F);
-    // round 2: nibbles, scales and activations of the row slices
+  };
+  // one pass: every nibble, scale and activation load is issued before the first multiply-add (the scheduling
+  // barrier keeps the compiler from interleaving them, which would leave few loads in flight per lane)
+  auto pass = [&](int k0, int n, const uint32_t (&ids)[DU]) {
     uint2 nib[DU];
     float sc[DU];
     float av[DU][B];
@@ -224,6 +236,7 @@ __global__ __launch_bounds__(QD<B>::NT) void k_down_q4(const uint8_t* __restrict
 #pragma unroll
       for (int b = 0; b < B; ++b) av[u][b] = ba.ldf(boff(ok, ((uint32_t)i * B + b) * 4u));
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
 #pragma unroll
@@ -244,8 +257,17 @@ __global__ __launch_bounds__(QD<B>::NT) void k_down_q4(const uint8_t* __restrict
         }
       }
     }
-    k0 += STRIDE;
-  } while (k0 < min(max(nraw, 0), F));
+  };
+  // round 1: the count and the first pass's ids together; round 2: that pass's nibbles, scales, activations
+  const int nraw = (int)bn.ldu(0u);
+  uint32_t ids[DU];
+  load_ids(0, ids);
+  const int n = min(max(nraw, 0), F);
+  pass(0, n, ids);
+  for (int k0 = STRIDE; k0 < n; k0 += STRIDE) {       // more rows than one pass holds
+    load_ids(k0, ids);
+    pass(k0, n, ids);
+  }
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
@@ -256,7 +278,7 @@ __global__ __launch_bounds__(QD<B>::NT) void k_down_q4(const uint8_t* __restrict
       acc[b][e] = v;
     }
   if (lane < QLPR) {
-    const int cb = qblk * 32 - blockIdx.x * QSW;   // first column of the lane's Q4 block, block-relative
+    const int cb = qblk * 32 - slice * QSW;        // first column of the lane's Q4 block, block-relative
 #pragma unroll
     for (int b = 0; b < B; ++b)
 #pragma unroll
@@ -270,7 +292,7 @@ __global__ __launch_bounds__(QD<B>::NT) void k_down_q4(const uint8_t* __restrict
     const int b = tt / QSW, cc = tt % QSW;
     float s = 0.f;
     for (int ww = 0; ww < NWV; ++ww) s += red[(ww * B + b) * QSW + cc];
-    const int d = blockIdx.x * QSW + cc;
+    const int d = slice * QSW + cc;
     if (d < D) y[(size_t)b * D + d] = s;
   }
 }
@@ -290,7 +312,7 @@ hipError_t launch_up(const uint8_t* qg, const void* sg, const float* bg, const u
     if (ea != hipSuccess) return ea;
   }
   if (lds > avail) return hipErrorInvalidValue;
-  const int grid = std::max(1, std::min((F + 3) / 4, 512));
+  const int grid = std::max(1, std::min((F + 3) / 4, SFFN_UP_GRID));
   SFFN_LAUNCH(2, (k_upgate_q4<B, ACT, NQ>), dim3(grid), dim3(NT_UP), lds, st, (const uint4*)qg,
                      (const _Float16*)sg, bg, (const uint4*)qu, (const _Float16*)su, bu, x, x_norm, D, F, mask, active,
                      n_active, abuf);
@@ -318,7 +340,8 @@ hipError_t forward_b(int act, const uint8_t* qg, const void* sg, const float* bg
                      ? dispatch_up<B, 1>(nq, qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st)
                      : dispatch_up<B, 0>(nq, qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st);
   if (e != hipSuccess) return e;
-  const int grid = (D + QSW - 1) / QSW;
+  const int slices = (D + QSW - 1) / QSW;
+  const int grid = SFFN_DOWN_XCD ? (slices + 7) / 8 * 8 : slices;
   SFFN_LAUNCH(3, k_down_q4<B>, dim3(grid), dim3(QD<B>::NT), 0, st, qd, (const _Float16*)sd, active, n_active, abuf, D,
               F, y);
   return hipGetLastError();
