@@ -126,7 +126,8 @@ hipError_t run_union(int act, bool q4, const void* Wg, const void* Sg, const flo
   hipError_t e = sffn_launch_rows_mt(act, q4, Wg, Sg, bg, Wu, Su, bu, xin, B, D, F, mask, active, n_active,
                                      ws_abuf(ws), st);
   if (e != hipSuccess) return e;
-  return sffn_launch_down_mt(q4, Wd, Sd, mask, ws_abuf(ws), B, D, F, ws_part(ws, B, D, F), union_splits(D), y, st);
+  return sffn_launch_down_mt(q4, Wd, Sd, active, n_active, ws_abuf(ws), B, D, F, ws_part(ws, B, D, F),
+                             union_splits(D), y, st);
 }
 
 }  // namespace
@@ -220,7 +221,11 @@ int sffn_predict(const void* P1, const void* P2, const float* c, const float* x,
       e = sffn_launch_norm_tokens(x, B, D, ws_xn(ws, B, F), st);
       xin = ws_xn(ws, B, F);
     }
-    if (e == hipSuccess) e = sffn_launch_predict_mt(P1, P2, c, xin, B, D, F, r, tau, mask, logits, h, st);
+    // shares of d for the union predictor's first stage; their partial sums use the partials region
+    // (KS_MAX * B * D floats >= ksh * B * r)
+    const int ksh = std::max(1, std::min({KS_MAX, D / 32 > 0 ? D / 32 : 1, (KS_MAX * D) / r}));
+    if (e == hipSuccess)
+      e = sffn_launch_predict_mt(P1, P2, c, xin, B, D, F, r, tau, mask, logits, h, ws_part(ws, B, D, F), ksh, st);
   }
   return e == hipSuccess ? SFFN_OK : hip_fail(e, "predict launch");
 }

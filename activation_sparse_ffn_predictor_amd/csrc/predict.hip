@@ -27,79 +27,73 @@ constexpr int NTH = 256;
 
 template <int NCH>
 __global__ __launch_bounds__(NTH) void k_pred_h(const uint4* __restrict__ P1, const float* __restrict__ x, int x_norm,
-                                                int B, int D, int r, float* __restrict__ h) {
+                                                int D, int r, float* __restrict__ h) {
   __shared__ float red[4][NTH / 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int j = blockIdx.x;
   const int nc = D >> 3;
   const Buf bp(P1, (uint32_t)r * (uint32_t)D * 2u);
-  const Buf bx(x, (uint32_t)B * (uint32_t)D * 4u);
+  const Buf bx(x, (uint32_t)D * 4u);
+  // one round trip: x, its first element (the shift) and the row of P1, all issued before the first use
+  float4 xr[NCH][2];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + NTH * i;
+    xr[i][0] = bx.ldf4(boff(c < nc, 32u * c));
+    xr[i][1] = bx.ldf4(boff(c < nc, 32u * c + 16u));
+  }
+  const float x0 = bx.ldf(boff(x_norm != 0, 0u));
   uint4 wv[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + NTH * i;
     wv[i] = bp.ld16(boff(c < nc, ((uint32_t)j * nc + c) * 16u));
   }
-  float4 xr[NCH][2];
-  float x0 = 0.f;
-  auto load_x = [&](int b) {
+  __builtin_amdgcn_sched_barrier(0);
+  float spx = 0.f, sp = 0.f, sx = 0.f, sxx = 0.f;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = threadIdx.x + NTH * i;
-      const uint32_t o = ((uint32_t)b * D + 8u * c) * 4u;
-      xr[i][0] = bx.ldf4(boff(c < nc, o));
-      xr[i][1] = bx.ldf4(boff(c < nc, o + 16u));
-    }
-    x0 = x_norm ? bx.ldf((uint32_t)b * D * 4u) : 0.f;
-  };
-  load_x(0);  // before any loop: in flight together with the row of P1
-  for (int b = 0; b < B; ++b) {
-    if (b > 0) load_x(b);
-    float spx = 0.f, sp = 0.f, sx = 0.f, sxx = 0.f;
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + NTH * i;
+    if (c < nc) {
+      float pf[8];
+      f16x8_to_f32(wv[i], pf);
+      const float xv[8] = {xr[i][0].x, xr[i][0].y, xr[i][0].z, xr[i][0].w,
+                           xr[i][1].x, xr[i][1].y, xr[i][1].z, xr[i][1].w};
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = threadIdx.x + NTH * i;
-      if (c < nc) {
-        float pf[8];
-        f16x8_to_f32(wv[i], pf);
-        const float xv[8] = {xr[i][0].x, xr[i][0].y, xr[i][0].z, xr[i][0].w,
-                             xr[i][1].x, xr[i][1].y, xr[i][1].z, xr[i][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float d = xv[e] - x0;
-          spx = fmaf(pf[e], d, spx);
-          sp += pf[e];
-          sx += d;
-          sxx = fmaf(d, d, sxx);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float d = xv[e] - x0;
+        spx = fmaf(pf[e], d, spx);
+        sp += pf[e];
+        sx += d;
+        sxx = fmaf(d, d, sxx);
       }
     }
-    spx = wave_sum(spx);
-    if (x_norm) { sp = wave_sum(sp); sx = wave_sum(sx); sxx = wave_sum(sxx); }
-    if (lane == 0) { red[0][w] = spx; red[1][w] = sp; red[2][w] = sx; red[3][w] = sxx; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float t[4] = {0.f, 0.f, 0.f, 0.f};
+  }
+  spx = wave_sum(spx);
+  if (x_norm) { sp = wave_sum(sp); sx = wave_sum(sx); sxx = wave_sum(sxx); }
+  if (lane == 0) { red[0][w] = spx; red[1][w] = sp; red[2][w] = sx; red[3][w] = sxx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < 4; ++k)
 #pragma unroll
-        for (int ww = 0; ww < NTH / 64; ++ww) t[k] += red[k][ww];
-      float hv = t[0];
-      if (x_norm) {
-        const float mu = t[2] / (float)D;
-        const float var = fmaxf(t[3] / (float)D - mu * mu, 0.f);
-        hv = (t[0] - mu * t[1]) / sqrtf(var + NORM_EPS);
-      }
-      h[(size_t)b * r + j] = hv;
+      for (int ww = 0; ww < NTH / 64; ++ww) t[k] += red[k][ww];
+    float hv = t[0];
+    if (x_norm) {
+      const float mu = t[2] / (float)D;
+      const float var = fmaxf(t[3] / (float)D - mu * mu, 0.f);
+      hv = (t[0] - mu * t[1]) / sqrtf(var + NORM_EPS);
     }
-    __syncthreads();   // red is reused by the next token
+    h[j] = hv;
   }
 }
 
-// LPR lanes per P2 row (power of two, 8..64), ROUNDS chunk rounds per row (1 or 2).
+// LPR lanes per P2 row (power of two, 8..64), ROUNDS chunk rounds per row (1 or 2). One token (larger batches
+// take the matrix-core kernels).
 template <int LPR, int ROUNDS>
 __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, const float* __restrict__ c,
-                                               const float* __restrict__ h, int B, int F, int r, float tau,
+                                               const float* __restrict__ h, int F, int r, float tau,
                                                uint64_t* __restrict__ mask, float* __restrict__ logits) {
   constexpr int RPI = 64 / LPR;        // rows per load instruction
   constexpr int RPW = 16;              // rows per wave = one 16-bit quarter of a mask word
@@ -111,7 +105,9 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
 
   const Buf bp(P2, (uint32_t)F * (uint32_t)r * 2u);
   const Buf bc(c ? (const void*)c : (const void*)P2, c ? (uint32_t)F * 4u : 0u);   // no bias: every load is 0
-  const Buf bh(h, (uint32_t)B * (uint32_t)r * 4u);
+  const Buf bh(h, (uint32_t)r * 4u);
+  // one round trip: P2 rows, h slice and biases are all issued before the first use (P2 first: its addresses
+  // need no loaded value)
   uint4 wv[ROUNDS][NI];
 #pragma unroll
   for (int q = 0; q < ROUNDS; ++q)
@@ -121,49 +117,36 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
       const int cc = q * LPR + csub;
       wv[q][i] = bp.ld16(boff(k < F && cc < cpr, ((uint32_t)k * cpr + cc) * 16u));
     }
+  float hv[ROUNDS][8];
+#pragma unroll
+  for (int q = 0; q < ROUNDS; ++q) {
+    const int cc = q * LPR + csub;
+    const bool ok = cc < cpr;
+    const float4 h0 = bh.ldf4(boff(ok, 32u * cc));
+    const float4 h1 = bh.ldf4(boff(ok, 32u * cc + 16u));
+    hv[q][0] = h0.x; hv[q][1] = h0.y; hv[q][2] = h0.z; hv[q][3] = h0.w;
+    hv[q][4] = h1.x; hv[q][5] = h1.y; hv[q][6] = h1.z; hv[q][7] = h1.w;
+  }
   float cb[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int k = base + i * RPI + rsub;
     cb[i] = bc.ldf(boff(k < F, (uint32_t)k * 4u));
   }
-  bool pred[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) pred[i] = false;
-  float hv[ROUNDS][8];
-  auto load_h = [&](int b) {
-#pragma unroll
-    for (int q = 0; q < ROUNDS; ++q) {
-      const int cc = q * LPR + csub;
-      const bool ok = cc < cpr;
-      const float4 h0 = bh.ldf4(boff(ok, ((uint32_t)b * r + 8u * cc) * 4u));
-      const float4 h1 = bh.ldf4(boff(ok, ((uint32_t)b * r + 8u * cc + 4u) * 4u));
-      hv[q][0] = h0.x; hv[q][1] = h0.y; hv[q][2] = h0.z; hv[q][3] = h0.w;
-      hv[q][4] = h1.x; hv[q][5] = h1.y; hv[q][6] = h1.z; hv[q][7] = h1.w;
-    }
-  };
-  load_h(0);  // before any loop: in flight together with the P2 rows
-  for (int b = 0; b < B; ++b) {
-    if (b > 0) load_h(b);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float acc = 0.f;
-#pragma unroll
-      for (int q = 0; q < ROUNDS; ++q) acc += dot8(wv[q][i], hv[q]);
-      acc = group_sum<LPR>(acc);
-      const int k = base + i * RPI + rsub;
-      if (csub == 0 && k < F) {
-        const float z = acc + cb[i];
-        pred[i] = pred[i] || (z > tau);
-        if (logits) logits[(size_t)b * F + k] = z;
-      }
-    }
-  }
-  // gather the 16 decisions: instruction i, row group q sits at lane q * LPR
+  __builtin_amdgcn_sched_barrier(0);
+  // decisions: instruction i, row group q sits at lane q * LPR
   uint32_t bits = 0;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const unsigned long long bal = __ballot(csub == 0 && pred[i]);
+    float acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < ROUNDS; ++q) acc += dot8(wv[q][i], hv[q]);
+    acc = group_sum<LPR>(acc);
+    const int k = base + i * RPI + rsub;
+    const float z = acc + cb[i];
+    const bool on = csub == 0 && k < F && z > tau;
+    if (logits && csub == 0 && k < F) logits[k] = z;
+    const unsigned long long bal = __ballot(on);
 #pragma unroll
     for (int q = 0; q < RPI; ++q)
       if ((bal >> (q * LPR)) & 1ull) bits |= 1u << (i * RPI + q);
@@ -173,7 +156,7 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
 
 template <int NCH>
 hipError_t launch_h(const void* P1, const float* x, int x_norm, int B, int D, int r, float* h, hipStream_t st) {
-  SFFN_LAUNCH(0, k_pred_h<NCH>, dim3(r), dim3(NTH), 0, st, (const uint4*)P1, x, x_norm, B, D, r, h);
+  SFFN_LAUNCH(0, k_pred_h<NCH>, dim3(r), dim3(NTH), 0, st, (const uint4*)P1, x, x_norm, D, r, h);
   return hipGetLastError();
 }
 
@@ -181,8 +164,8 @@ template <int LPR, int ROUNDS>
 hipError_t launch_z(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, uint64_t* mask,
                     float* logits, hipStream_t st) {
   const int grid = (F + 63) / 64;
-  SFFN_LAUNCH(1, (k_pred_z<LPR, ROUNDS>), dim3(grid), dim3(NT), 0, st, (const uint4*)P2, c, h, B, F, r, tau,
-                     mask, logits);
+  SFFN_LAUNCH(1, (k_pred_z<LPR, ROUNDS>), dim3(grid), dim3(NT), 0, st, (const uint4*)P2, c, h, F, r, tau, mask,
+              logits);
   return hipGetLastError();
 }
 
@@ -190,6 +173,7 @@ hipError_t launch_z(const void* P2, const float* c, const float* h, int B, int F
 
 hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D,
                                int F, int r, float tau, uint64_t* mask, float* logits, float* hbuf, hipStream_t st) {
+  if (B != 1) return hipErrorInvalidValue;   // batches of several tokens take the matrix-core kernels
   const int nch = (D / 8 + NTH - 1) / NTH;   // 16-byte chunks per thread (D <= 16384: at most 8)
   hipError_t e;
   if (nch <= 1) e = launch_h<1>(P1, x, x_norm, B, D, r, hbuf, st);

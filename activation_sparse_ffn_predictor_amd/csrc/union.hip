@@ -13,13 +13,14 @@
 //
 // Kernels:
 //   k_norm_tokens : per-token normalisation of x into the workspace (when the layer input is normalised)
-//   k_mt_h        : h = P1 x, 16 rows of P1 per block, k split over 8 waves, LDS reduction
+//   k_mt_h        : partial h = P1 x over a share of d, 16 rows of P1 per block, shares over blocks (grid y),
+//                   split again over 8 waves with an LDS reduction; k_sum_parts adds the shares in fixed order
 //   k_mt_z        : z = P2 h + c, 64 neurons per block (one mask word), OR over tokens by ballot
 //   k_mt_rows     : compaction + W_gate / W_up row gather over 16 active neurons per block, k split over 8
 //                   waves, fused activation, dense activations a[i, b]
-//   k_mt_down     : y partial sums over a slice of 128 columns and a share of the active rows; W_downT tiles
-//                   are staged in LDS and read transposed as the B operand; activations (times the Q4 block
-//                   scale) are the A operand
+//   k_mt_down     : y partial sums over a slice of 128 columns and every KS-th step of 64 active rows (ids from
+//                   the row kernel's active[]); W_downT tiles are staged in LDS and read transposed as the B
+//                   operand; activations (times the Q4 block scale) are the A operand; next step loaded ahead
 //   k_sum_parts   : y = sum of the partial sums
 #include "common.h"
 
@@ -97,33 +98,69 @@ __device__ __forceinline__ void load_xtile(const Buf& bx, int B, int K, int t, i
   split8(v, hi, lo);
 }
 
+// raw fp32 B-operand values of token tile t at k block kb (split into fp16 halves at use)
+struct XRaw { float4 a, b; };
+__device__ __forceinline__ XRaw load_xraw(const Buf& bx, int B, int K, int t, int kb) {
+  const int lane = threadIdx.x & 63;
+  const int tok = t * 16 + (lane & 15);
+  const int k = kb * 32 + (lane >> 4) * 8;
+  const bool ok = tok < B && k < K;
+  const uint32_t o = ((uint32_t)tok * K + k) * 4u;
+  return XRaw{bx.ldf4(boff(ok, o)), bx.ldf4(boff(ok, o + 16u))};
+}
+__device__ __forceinline__ void split_xraw(const XRaw& r, half8& hi, half8& lo) {
+  const float v[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+  split8(v, hi, lo);
+}
+
+// k blocks whose loads are issued together (one memory round trip per chunk), by token tiles
+template <int NTT> struct KChunk { static constexpr int CH = NTT == 1 ? 8 : (NTT == 2 ? 4 : 2); };
+
 constexpr int NTK = 512;            // 8 waves split the k dimension
 constexpr int KW = NTK / 64;
 
-// h[b, j] = sum_d P1[j, d] x[b, d]; block = 16 rows of P1
+// Partial h over one of gridDim.y shares of d: hp[ks][b][j] = sum_{d in share ks} P1[j, d] x[b, d]; block = 16
+// rows of P1 and one share of the k range, split again over the 8 waves.
 template <int NTT>
 __global__ __launch_bounds__(NTK) void k_mt_h(const uint4* __restrict__ P1, const float* __restrict__ x, int B, int D,
-                                              int r, float* __restrict__ h) {
+                                              int r, float* __restrict__ hp) {
   __shared__ f32x4 part[KW][NTT][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int j0 = blockIdx.x * 16;
   const int KB = (D + 31) / 32;
-  const int kpw = (KB + KW - 1) / KW;
-  const int kb0 = w * kpw, kb1 = min(KB, kb0 + kpw);
+  const int KSH = gridDim.y, ks = blockIdx.y;
+  const int kps = (KB + KSH - 1) / KSH;                  // k blocks of this share
+  const int ks0 = ks * kps, ks1 = min(KB, ks0 + kps);
+  const int kpw = (kps + KW - 1) / KW;
+  const int kb0 = ks0 + w * kpw, kb1 = min(ks1, kb0 + kpw);
   const Buf bp(P1, (uint32_t)r * D * 2u), bx(x, (uint32_t)B * D * 4u);
   const int row = j0 + (lane & 15);
   f32x4 acc[NTT];
 #pragma unroll
   for (int t = 0; t < NTT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int k = kb * 32 + (lane >> 4) * 8;
-    const uint4 av = bp.ld16(boff(row < r && k < D, ((uint32_t)row * D + k) * 2u));
-    half8 xh[NTT], xl[NTT];
+  constexpr int CH = KChunk<NTT>::CH;
+  for (int c0 = kb0; c0 < kb1; c0 += CH) {
+    uint4 av[CH];
+    XRaw xr[CH][NTT];
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) load_xtile(bx, B, D, t, kb, xh[t], xl[t]);
-    const half8 a = __builtin_bit_cast(half8, av);
+    for (int q = 0; q < CH; ++q) {
+      const int kb = c0 + q;
+      const int k = kb * 32 + (lane >> 4) * 8;
+      av[q] = bp.ld16(boff(kb < kb1 && row < r && k < D, ((uint32_t)row * D + k) * 2u));
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) acc[t] = mfma16(a, xl[t], mfma16(a, xh[t], acc[t]));
+      for (int t = 0; t < NTT; ++t) xr[q][t] = load_xraw(bx, B, kb < kb1 ? D : 0, t, kb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const half8 a = __builtin_bit_cast(half8, av[q]);
+#pragma unroll
+      for (int t = 0; t < NTT; ++t) {
+        half8 xh, xl;
+        split_xraw(xr[q][t], xh, xl);
+        acc[t] = mfma16(a, xl, mfma16(a, xh, acc[t]));
+      }
+    }
   }
 #pragma unroll
   for (int t = 0; t < NTT; ++t) part[w][t][lane] = acc[t];
@@ -137,7 +174,7 @@ __global__ __launch_bounds__(NTK) void k_mt_h(const uint4* __restrict__ P1, cons
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + (lane >> 4) * 4 + i;
-        if (tok < B && j < r) h[(size_t)tok * r + j] = s[i];
+        if (tok < B && j < r) hp[((size_t)ks * B + tok) * r + j] = s[i];
       }
     }
   }
@@ -158,15 +195,29 @@ __global__ __launch_bounds__(256) void k_mt_z(const uint4* __restrict__ P2, cons
   f32x4 acc[NTT];
 #pragma unroll
   for (int t = 0; t < NTT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < KB; ++kb) {
-    const int k = kb * 32 + (lane >> 4) * 8;
-    const uint4 av = bp.ld16(boff(row < F && k < r, ((uint32_t)row * r + k) * 2u));
-    half8 hh[NTT], hl[NTT];
+  constexpr int CH = KChunk<NTT>::CH;
+  for (int c0 = 0; c0 < KB; c0 += CH) {
+    uint4 av[CH];
+    XRaw hr[CH][NTT];
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) load_xtile(bh, B, r, t, kb, hh[t], hl[t]);
-    const half8 a = __builtin_bit_cast(half8, av);
+    for (int q = 0; q < CH; ++q) {
+      const int kb = c0 + q;
+      const int k = kb * 32 + (lane >> 4) * 8;
+      av[q] = bp.ld16(boff(kb < KB && row < F && k < r, ((uint32_t)row * r + k) * 2u));
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) acc[t] = mfma16(a, hl[t], mfma16(a, hh[t], acc[t]));
+      for (int t = 0; t < NTT; ++t) hr[q][t] = load_xraw(bh, B, kb < KB ? r : 0, t, kb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const half8 a = __builtin_bit_cast(half8, av[q]);
+#pragma unroll
+      for (int t = 0; t < NTT; ++t) {
+        half8 hh, hl;
+        split_xraw(hr[q][t], hh, hl);
+        acc[t] = mfma16(a, hl, mfma16(a, hh, acc[t]));
+      }
+    }
   }
   // lane l holds rows 4*(l/16)+i of token l%16 (per token tile)
   float cb[4];
@@ -284,45 +335,66 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
   f32x4 au[NTT], ag[NTT];
 #pragma unroll
   for (int t = 0; t < NTT; ++t) { au[t] = f32x4{0.f, 0.f, 0.f, 0.f}; ag[t] = au[t]; }
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int k = kb * 32 + (lane >> 4) * 8;
-    const bool ok = idl >= 0 && k < D;
-    half8 a_u, a_g;
-    float su4[4], sg4[4];
-    if constexpr (Q4) {
-      const uint32_t o = (uint32_t)(ok ? idl : 0) * (uint32_t)(D >> 1) + (uint32_t)kb * 16u + ((lane >> 4) & 1) * 8u;
-      a_u = q4_to_half8(bwu.ld8(boff(ok, o)), lane >> 4);
-      if (ACT) a_g = q4_to_half8(bwg.ld8(boff(ok, o)), lane >> 4);
+  constexpr int CH = KChunk<NTT>::CH;
+  for (int c0 = kb0; c0 < kb1; c0 += CH) {
+    // one round trip per chunk: weight rows (or nibbles and scales) and x tiles of CH k blocks
+    uint4 wu_[CH], wg_[CH];
+    uint2 qu_[CH], qg_[CH];
+    float su4[CH][4], sg4[CH][4];
+    XRaw xr[CH][NTT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool okr = idr[i] >= 0;
-        const uint32_t so = ((uint32_t)(okr ? idr[i] : 0) * nblk + kb) * 2u;
-        su4[i] = bsu.ldh(boff(okr, so));
-        if (ACT) sg4[i] = bsg.ldh(boff(okr, so));
-      }
-    } else {
-      const uint32_t o = ((uint32_t)(ok ? idl : 0) * D + k) * 2u;
-      a_u = __builtin_bit_cast(half8, bwu.ld16(boff(ok, o)));
-      if (ACT) a_g = __builtin_bit_cast(half8, bwg.ld16(boff(ok, o)));
-    }
-    half8 xh[NTT], xl[NTT];
-#pragma unroll
-    for (int t = 0; t < NTT; ++t) load_xtile(bx, B, D, t, kb, xh[t], xl[t]);
-#pragma unroll
-    for (int t = 0; t < NTT; ++t) {
+    for (int q = 0; q < CH; ++q) {
+      const int kb = c0 + q;
+      const int k = kb * 32 + (lane >> 4) * 8;
+      const bool ok = kb < kb1 && idl >= 0 && k < D;
       if constexpr (Q4) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 pu = mfma16(a_u, xl[t], mfma16(a_u, xh[t], z));
+        const uint32_t o = (uint32_t)(ok ? idl : 0) * (uint32_t)(D >> 1) + (uint32_t)kb * 16u + ((lane >> 4) & 1) * 8u;
+        qu_[q] = bwu.ld8(boff(ok, o));
+        if (ACT) qg_[q] = bwg.ld8(boff(ok, o));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) au[t][i] = fmaf(su4[i], pu[i], au[t][i]);
-        if (ACT) {
-          const f32x4 pg = mfma16(a_g, xl[t], mfma16(a_g, xh[t], z));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ag[t][i] = fmaf(sg4[i], pg[i], ag[t][i]);
+        for (int i = 0; i < 4; ++i) {
+          const bool okr = kb < kb1 && idr[i] >= 0;
+          const uint32_t so = ((uint32_t)(okr ? idr[i] : 0) * nblk + kb) * 2u;
+          su4[q][i] = bsu.ldh(boff(okr, so));
+          if (ACT) sg4[q][i] = bsg.ldh(boff(okr, so));
         }
       } else {
-        au[t] = mfma16(a_u, xl[t], mfma16(a_u, xh[t], au[t]));
-        if (ACT) ag[t] = mfma16(a_g, xl[t], mfma16(a_g, xh[t], ag[t]));
+        const uint32_t o = ((uint32_t)(ok ? idl : 0) * D + k) * 2u;
+        wu_[q] = bwu.ld16(boff(ok, o));
+        if (ACT) wg_[q] = bwg.ld16(boff(ok, o));
+      }
+#pragma unroll
+      for (int t = 0; t < NTT; ++t) xr[q][t] = load_xraw(bx, B, kb < kb1 ? D : 0, t, kb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      half8 a_u, a_g;
+      if constexpr (Q4) {
+        a_u = q4_to_half8(qu_[q], lane >> 4);
+        if (ACT) a_g = q4_to_half8(qg_[q], lane >> 4);
+      } else {
+        a_u = __builtin_bit_cast(half8, wu_[q]);
+        if (ACT) a_g = __builtin_bit_cast(half8, wg_[q]);
+      }
+#pragma unroll
+      for (int t = 0; t < NTT; ++t) {
+        half8 xh, xl;
+        split_xraw(xr[q][t], xh, xl);
+        if constexpr (Q4) {
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          const f32x4 pu = mfma16(a_u, xl, mfma16(a_u, xh, z));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) au[t][i] = fmaf(su4[q][i], pu[i], au[t][i]);
+          if (ACT) {
+            const f32x4 pg = mfma16(a_g, xl, mfma16(a_g, xh, z));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ag[t][i] = fmaf(sg4[q][i], pg[i], ag[t][i]);
+          }
+        } else {
+          au[t] = mfma16(a_u, xl, mfma16(a_u, xh, au[t]));
+          if (ACT) ag[t] = mfma16(a_g, xl, mfma16(a_g, xh, ag[t]));
+        }
       }
     }
   }
@@ -360,91 +432,137 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
 
 constexpr int DN_T = 512;            // 8 waves
 constexpr int DS_COLS = 128;         // output columns per block (8 waves x 16)
-constexpr int DS_K = 32;             // active rows per step
+constexpr int DS_K = 64;             // active rows per step (two 32-row MFMA k steps)
 
-// Partial y over a slice of 128 columns and a share of the active rows; part_out: [KS][B][D].
-// The whole mask is compacted once per block (nw <= 512 words: one word per lane and wave).
+// Partial y over a slice of 128 columns; part_out: [KS][B][D]. Row split ks takes the steps s = ks, ks + KS, ...
+// of DS_K consecutive dense indices, reading the ids the row kernel wrote to active[]. All of the block's ids are
+// staged in LDS first (one round trip, speculatively up to F); then every step's weight tile, scales and
+// activations are loaded into registers one step ahead, so each step's round trip overlaps the previous step's
+// matrix-core work.
 template <int NTT, bool Q4>
 __global__ __launch_bounds__(DN_T) void k_mt_down(const void* __restrict__ Wd, const void* __restrict__ Sd,
-                                                  const uint64_t* __restrict__ mask, const float* __restrict__ abuf,
-                                                  int B, int D, int F, float* __restrict__ part_out) {
-  extern __shared__ int list[];                        // [nw * 64] compacted ids
-  __shared__ int cnt[DN_T / 64 + 1];
+                                                  const int32_t* __restrict__ active,
+                                                  const int32_t* __restrict__ n_active,
+                                                  const float* __restrict__ abuf, int B, int D, int F,
+                                                  float* __restrict__ part_out) {
+  extern __shared__ int ids_lds[];                     // [M * DS_K] ids of this block's steps
   __shared__ _Float16 wt[DS_K][DS_COLS + 8];           // fp16 weights or exact (q - 8), padded rows
   __shared__ float at[DS_K][65];                       // activations [row][token]
   __shared__ float st[DS_K][DS_COLS / 32];             // Q4: scales of the slice's 32-column blocks
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int nw = (F + 63) >> 6;
   const int KS = gridDim.y, ks = blockIdx.y;
   const int c0 = blockIdx.x * DS_COLS;
   const int nblk = D >> 5;
-  const Buf bm(mask, (uint32_t)nw * 8u);
+  const int M = (F + DS_K * KS - 1) / (DS_K * KS);     // steps of this block at most
   const Buf bw(Wd, Q4 ? (uint32_t)F * (uint32_t)(D >> 1) : (uint32_t)F * D * 2u);
   const Buf bs(Q4 ? Sd : Wd, Q4 ? (uint32_t)F * nblk * 2u : 0u);
   const Buf ba(abuf, (uint32_t)F * B * 4u);
-  const int wpw = (nw + DN_T / 64 - 1) / (DN_T / 64);  // <= 64 (host keeps nw <= 512)
-  const int tw = w * wpw + lane;
-  const uint64_t cw = bm.ldu64(boff(lane < wpw && tw < nw, (uint32_t)tw * 8u));
-  const int total = compact_words<DN_T>(cw, 0, nw, wpw, nw, F, list, cnt);
-  const int per_ks = (total + KS - 1) / KS;
-  const int j0 = ks * per_ks, j1 = min(total, j0 + per_ks);
+  const Buf bid(active, (uint32_t)F * 4u);
+  const Buf bn(n_active, 4u);
+  // round 1: the count and all of this block's ids (speculatively, bounded by F)
+  const int nraw = (int)bn.ldu(0u);
+  for (int e = threadIdx.x; e < M * DS_K; e += DN_T) {
+    const int i = (ks + KS * (e / DS_K)) * DS_K + (e % DS_K);
+    ids_lds[e] = (int)bid.ldu(boff(i < F, (uint32_t)i * 4u));
+  }
+  const int n = min(max(nraw, 0), F);
+  __syncthreads();
+  // staging roles: fp16 tiles as 2 x (32 rows x 16 parts of 8 columns); Q4 as 64 rows x 8 half-blocks, scales
+  // as 64 rows x 4 blocks; activations 8 per thread
+  struct Regs { uint4 w16[2]; uint2 nib; float sc; float av[8]; };
+  auto load_step = [&](int m, Regs& R) {
+    const int base = (ks + KS * m) * DS_K;           // dense index of the step's first row
+    if constexpr (Q4) {
+      const int row = threadIdx.x >> 3, part = threadIdx.x & 7;
+      const int i = base + row;
+      const bool ok = i < n;
+      const uint32_t id = ok ? (uint32_t)ids_lds[m * DS_K + row] : 0u;
+      const int q = part >> 1, hh = part & 1;
+      const int blk = (c0 >> 5) + q;
+      R.nib = bw.ld8(boff(ok && blk < nblk, id * (uint32_t)(D >> 1) + (uint32_t)blk * 16u + hh * 8u));
+      const int srow = threadIdx.x >> 2, sq = threadIdx.x & 3;
+      const int si = base + srow;
+      const bool sok = threadIdx.x < DS_K * 4 && si < n && (c0 >> 5) + sq < nblk;
+      const uint32_t sid = sok ? (uint32_t)ids_lds[m * DS_K + srow] : 0u;
+      R.sc = bs.ldh(boff(sok, (sid * nblk + (c0 >> 5) + sq) * 2u));
+    } else {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int row = (threadIdx.x >> 4) + 32 * p, part = threadIdx.x & 15;
+        const int i = base + row;
+        const int cc = c0 + part * 8;
+        const bool ok = i < n && cc < D;
+        const uint32_t id = i < n ? (uint32_t)ids_lds[m * DS_K + row] : 0u;
+        R.w16[p] = bw.ld16(boff(ok, (id * D + cc) * 2u));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int e = threadIdx.x + DN_T * k;            // DS_K * 64 = 8 * DN_T entries
+      const int kr = e >> 6, tok = e & 63;
+      const int i = base + kr;
+      R.av[k] = ba.ldf(boff(i < n && tok < B, ((uint32_t)i * B + tok) * 4u));
+    }
+  };
+  auto store_step = [&](const Regs& R) {
+    if constexpr (Q4) {
+      const int row = threadIdx.x >> 3, part = threadIdx.x & 7;
+      const int q = part >> 1, hh = part & 1;
+      // 8 nibble bytes = half of a 32-column block: elements 8h..8h+7 (low) and 16+8h..16+8h+7 (high)
+      const half8 lo8 = q4_to_half8(R.nib, hh), hi8 = q4_to_half8(R.nib, 2 + hh);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        wt[row][q * 32 + hh * 8 + e] = lo8[e];
+        wt[row][q * 32 + 16 + hh * 8 + e] = hi8[e];
+      }
+      if (threadIdx.x < DS_K * 4) st[threadIdx.x >> 2][threadIdx.x & 3] = R.sc;
+    } else {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int row = (threadIdx.x >> 4) + 32 * p, part = threadIdx.x & 15;
+        *reinterpret_cast<uint4*>(&wt[row][part * 8]) = R.w16[p];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int e = threadIdx.x + DN_T * k;
+      at[e >> 6][e & 63] = R.av[k];
+    }
+  };
   f32x4 acc[NTT];
 #pragma unroll
   for (int t = 0; t < NTT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int srow = threadIdx.x >> 4, spart = threadIdx.x & 15;   // staging: 32 rows x 16 parts
-  for (int jb = j0; jb < j1; jb += DS_K) {
-    {
-      const int j = jb + srow;
-      const bool ok = j < j1;
-      const uint32_t id = ok ? (uint32_t)list[j] : 0u;
-      if constexpr (Q4) {
-        if (spart < 8) {
-          // 8 nibble bytes = half of a 32-column block: elements 8h..8h+7 (low) and 16+8h..16+8h+7 (high)
-          const int q = spart >> 1, hh = spart & 1;
-          const int blk = (c0 >> 5) + q;
-          const uint2 pbytes = bw.ld8(boff(ok && blk < nblk, id * (uint32_t)(D >> 1) + (uint32_t)blk * 16u + hh * 8u));
-          const half8 lo8 = q4_to_half8(pbytes, hh), hi8 = q4_to_half8(pbytes, 2 + hh);
+  Regs R;
+  int m = 0;
+  if ((ks + KS * m) * DS_K < n) load_step(m, R);
+  while ((ks + KS * m) * DS_K < n) {                   // block-uniform
+    store_step(R);
+    __syncthreads();
+    const bool more = (ks + KS * (m + 1)) * DS_K < n;
+    if (more) load_step(m + 1, R);                     // in flight during this step's matrix-core work
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            wt[srow][q * 32 + hh * 8 + e] = lo8[e];
-            wt[srow][q * 32 + 16 + hh * 8 + e] = hi8[e];
-          }
-        } else if (spart < 8 + DS_COLS / 32) {
-          const int q = spart - 8;
-          const int blk = (c0 >> 5) + q;
-          st[srow][q] = bs.ldh(boff(ok && blk < nblk, (id * nblk + blk) * 2u));
+    for (int kc = 0; kc < DS_K / 32; ++kc) {
+      // B operand: rows k = 8*(l/16)+i of column 16w + l%16 (read transposed from LDS)
+      half8 bop;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bop[i] = wt[kc * 32 + (lane >> 4) * 8 + i][w * 16 + (lane & 15)];
+#pragma unroll
+      for (int t = 0; t < NTT; ++t) {
+        float av[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int kr = kc * 32 + (lane >> 4) * 8 + i;
+          float a = at[kr][t * 16 + (lane & 15)];
+          if constexpr (Q4) a *= st[kr][w >> 1];         // this wave's 16 columns lie in block w / 2
+          av[i] = a;
         }
-      } else {
-        const int cc = c0 + spart * 8;
-        const uint4 v = bw.ld16(boff(ok && cc < D, (id * D + cc) * 2u));
-        *reinterpret_cast<uint4*>(&wt[srow][spart * 8]) = v;
-      }
-      for (int e = threadIdx.x; e < DS_K * 64; e += DN_T) {
-        const int kr = e >> 6, tok = e & 63;
-        const int jj = jb + kr;
-        at[kr][tok] = ba.ldf(boff(jj < j1 && tok < B, ((uint32_t)jj * B + tok) * 4u));
+        half8 ah, al;
+        split8(av, ah, al);
+        acc[t] = mfma16(al, bop, mfma16(ah, bop, acc[t]));
       }
     }
     __syncthreads();
-    // B operand: rows k = 8*(l/16)+i of column 16w + l%16 (read transposed from LDS)
-    half8 bop;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) bop[i] = wt[(lane >> 4) * 8 + i][w * 16 + (lane & 15)];
-#pragma unroll
-    for (int t = 0; t < NTT; ++t) {
-      float av[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kr = (lane >> 4) * 8 + i;
-        float a = at[kr][t * 16 + (lane & 15)];
-        if constexpr (Q4) a *= st[kr][w >> 1];           // this wave's 16 columns lie in block w / 2
-        av[i] = a;
-      }
-      half8 ah, al;
-      split8(av, ah, al);
-      acc[t] = mfma16(al, bop, mfma16(ah, bop, acc[t]));
-    }
-    __syncthreads();
+    ++m;
   }
   // D layout: lane l holds tokens 16t + 4(l/16) + i of column 16w + l%16
   const int col = c0 + w * 16 + (lane & 15);
@@ -467,12 +585,16 @@ __global__ void k_sum_parts(const float* __restrict__ part, int KS, int n, float
 
 template <int NTT>
 hipError_t predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F, int r,
-                      float tau, uint64_t* mask, float* logits, float* hbuf, hipStream_t st) {
-  SFFN_LAUNCH(0, k_mt_h<NTT>, dim3((r + 15) / 16), dim3(NTK), 0, st, (const uint4*)P1, x, B, D, r, hbuf);
+                      float tau, uint64_t* mask, float* logits, float* hbuf, float* hpart, int KSH, hipStream_t st) {
+  SFFN_LAUNCH(0, k_mt_h<NTT>, dim3((r + 15) / 16, KSH), dim3(NTK), 0, st, (const uint4*)P1, x, B, D, r, hpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int nh = B * r;
+  hipLaunchKernelGGL(k_sum_parts, dim3((nh + 255) / 256), dim3(256), 0, st, hpart, KSH, nh, hbuf);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   SFFN_LAUNCH(1, k_mt_z<NTT>, dim3((F + 63) / 64), dim3(256), 0, st, (const uint4*)P2, c, hbuf, B, F, r, tau, mask,
-                     logits);
+              logits);
   return hipGetLastError();
 }
 
@@ -495,18 +617,18 @@ hipError_t rows_mt(const void* Wg, const void* Sg, const float* bg, const void* 
 }
 
 template <int NTT, bool Q4>
-hipError_t down_mt(const void* Wd, const void* Sd, const uint64_t* mask, const float* abuf, int B, int D, int F,
-                   float* part, int KS, float* y, hipStream_t st) {
-  const int nw = (F + 63) / 64;
-  const size_t lds = (size_t)nw * 64 * sizeof(int);
+hipError_t down_mt(const void* Wd, const void* Sd, const int32_t* active, const int32_t* n_active, const float* abuf,
+                   int B, int D, int F, float* part, int KS, float* y, hipStream_t st) {
+  const int M = (F + DS_K * KS - 1) / (DS_K * KS);
+  const size_t lds = (size_t)M * DS_K * sizeof(int);
   static size_t avail = 0;
   if (!avail) {
     hipError_t ea = allow_dynamic_lds((const void*)k_mt_down<NTT, Q4>, &avail);
     if (ea != hipSuccess) return ea;
   }
   if (lds > avail) return hipErrorInvalidValue;
-  SFFN_LAUNCH(3, (k_mt_down<NTT, Q4>), dim3((D + DS_COLS - 1) / DS_COLS, KS), dim3(DN_T), lds, st, Wd, Sd, mask,
-                     abuf, B, D, F, part);
+  SFFN_LAUNCH(3, (k_mt_down<NTT, Q4>), dim3((D + DS_COLS - 1) / DS_COLS, KS), dim3(DN_T), lds, st, Wd, Sd, active,
+              n_active, abuf, B, D, F, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = B * D;
@@ -523,13 +645,14 @@ hipError_t sffn_launch_norm_tokens(const float* x, int B, int D, float* xn, hipS
 }
 
 hipError_t sffn_launch_predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F,
-                                  int r, float tau, uint64_t* mask, float* logits, float* hbuf, hipStream_t st) {
+                                  int r, float tau, uint64_t* mask, float* logits, float* hbuf, float* hpart, int KSH,
+                                  hipStream_t st) {
   const int ntt = (B + 15) / 16;
   switch (ntt) {
-    case 1: return predict_mt<1>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, st);
-    case 2: return predict_mt<2>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, st);
-    case 3: return predict_mt<3>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, st);
-    case 4: return predict_mt<4>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, st);
+    case 1: return predict_mt<1>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, hpart, KSH, st);
+    case 2: return predict_mt<2>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, hpart, KSH, st);
+    case 3: return predict_mt<3>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, hpart, KSH, st);
+    case 4: return predict_mt<4>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, hpart, KSH, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -553,11 +676,12 @@ hipError_t sffn_launch_rows_mt(int act, bool q4, const void* Wg, const void* Sg,
 #undef RMT
 }
 
-hipError_t sffn_launch_down_mt(bool q4, const void* Wd, const void* Sd, const uint64_t* mask, const float* abuf, int B,
-                               int D, int F, float* part, int KS, float* y, hipStream_t st) {
+hipError_t sffn_launch_down_mt(bool q4, const void* Wd, const void* Sd, const int32_t* active,
+                               const int32_t* n_active, const float* abuf, int B, int D, int F, float* part, int KS,
+                               float* y, hipStream_t st) {
   const int ntt = (B + 15) / 16;
-#define DMT(N) return q4 ? down_mt<N, true>(Wd, Sd, mask, abuf, B, D, F, part, KS, y, st) \
-                         : down_mt<N, false>(Wd, Sd, mask, abuf, B, D, F, part, KS, y, st)
+#define DMT(N) return q4 ? down_mt<N, true>(Wd, Sd, active, n_active, abuf, B, D, F, part, KS, y, st) \
+                         : down_mt<N, false>(Wd, Sd, active, n_active, abuf, B, D, F, part, KS, y, st)
   switch (ntt) {
     case 1: DMT(1);
     case 2: DMT(2);
