@@ -16,7 +16,7 @@ ACT_RELU, ACT_REGLU = 0, 1
 ACTS = {"relu": ACT_RELU, "reglu": ACT_REGLU}
 
 EXPORTS = ("sffn_status_string", "sffn_last_error", "sffn_workspace_size", "sffn_mask_words", "sffn_predict",
-           "sffn_forward", "sffn_forward_q4", "sffn_profile_begin", "sffn_profile_end")
+           "sffn_forward", "sffn_forward_q4", "sffn_profile_begin", "sffn_profile_end", "sffn_forward_path")
 K_PRED_H, K_PRED_Z, K_ROWS, K_COLS = 0, 1, 2, 3
 
 
@@ -53,6 +53,7 @@ def lib() -> ctypes.CDLL:
         h.sffn_forward_q4.argtypes = [i32, _Q4, vp, _Q4, vp, _Q4, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         h.sffn_forward_q4.restype = i32
         h.sffn_profile_begin.argtypes, h.sffn_profile_begin.restype = [i32, i32], i32
+        h.sffn_forward_path.argtypes, h.sffn_forward_path.restype = [i32, i32, i32, i32, i32], i32
         h.sffn_profile_end.argtypes, h.sffn_profile_end.restype = [ctypes.POINTER(ctypes.c_float), i32], i32
         _handle = h
     return _handle
@@ -123,6 +124,14 @@ def forward_q4(act, W_gate, b_gate, W_up, b_up, W_downT, x, mask, active, n_acti
                                _Q4(*map(_p, W_downT)), _p(x), int(bool(x_norm)), B, D, F, _p(mask), _p(active),
                                _p(n_active), _p(y), _p(ws), _nbytes(ws), _stream(stream, x))
     _check(rc, "sffn_forward_q4")
+
+
+PATH_DECODE, PATH_FUSED, PATH_UNION = 0, 1, 2
+
+
+def forward_path(act, q4: bool, B: int, D: int, F: int) -> int:
+    """Which kernels a forward call of these sizes runs (PATH_DECODE, PATH_FUSED or PATH_UNION)."""
+    return int(lib().sffn_forward_path(ACTS.get(act, act), int(bool(q4)), B, D, F))
 
 
 def profile_begin(kernel: int, max_launches: int):

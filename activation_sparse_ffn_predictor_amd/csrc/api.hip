@@ -30,6 +30,7 @@ constexpr int MAX_B = 64, MAX_D = 16384, MAX_F = 1 << 22, MAX_R = 1024, MAX_BR =
 constexpr int MAX_BD_VALU = 16384;   // decode-batch kernels: B in {1, 2, 4, 8} with B * D <= this
 constexpr int MAX_F_UNION = 32768;   // union kernels compact the whole mask in one block
 constexpr int KS_MAX = 8;            // row splits of the union down projection
+constexpr int G_FUSED = 256;         // blocks (= partial sums of y) of the fused single-token forward
 constexpr size_t MAX_TENSOR = (size_t)1 << 31;   // buffer loads address each tensor with 31-bit byte offsets
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -58,11 +59,13 @@ int union_splits(int D) {
 }
 
 // Workspace layout, each part 256-byte aligned:
-//   [activations a: F * B fp32][B > 1: normalised x: B * D fp32][B > 1: partial y: KS_MAX * B * D fp32]
-//   [predictor h: B * r fp32]
+//   [activations a: F * B fp32][B > 1: normalised x: B * D fp32]
+//   [partial y: KS_MAX * B * D fp32 for B > 1, G_FUSED * D fp32 for B == 1][predictor h: B * r fp32]
 size_t ws_a_bytes(int B, int F) { return align256((size_t)F * B * sizeof(float)); }
 size_t ws_xn_bytes(int B, int D) { return B > 1 ? align256((size_t)B * D * sizeof(float)) : 0; }
-size_t ws_part_bytes(int B, int D) { return B > 1 ? align256((size_t)KS_MAX * B * D * sizeof(float)) : 0; }
+size_t ws_part_bytes(int B, int D) {
+  return align256((size_t)(B > 1 ? KS_MAX * B : G_FUSED) * D * sizeof(float));
+}
 size_t ws_forward_bytes(int B, int D, int F) { return ws_a_bytes(B, F) + ws_xn_bytes(B, D) + ws_part_bytes(B, D); }
 
 int check_ws(const void* ws, size_t ws_bytes, size_t need) {
@@ -195,6 +198,12 @@ size_t sffn_workspace_size(int B, int D, int F, int r) {
 
 int sffn_mask_words(int F) { return F < 1 ? 0 : (F + 63) / 64; }
 
+int sffn_forward_path(int act, int q4, int B, int D, int F) {
+  if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU) return -1;
+  if (sffn_fused_ok(B, D, F, act, q4 != 0)) return SFFN_PATH_FUSED;
+  return decode_batch(B, D) ? SFFN_PATH_DECODE : SFFN_PATH_UNION;
+}
+
 int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F, int r,
                  float t, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
@@ -251,7 +260,10 @@ int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W
   const bool g = act == SFFN_ACT_REGLU;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (decode_batch(B, D)) {
+  if (sffn_fused_ok(B, D, F, act, false)) {
+    e = sffn_launch_fused(act, g ? W_gate : nullptr, g ? b_gate : nullptr, W_up, g ? nullptr : b_up, W_downT, x,
+                          x_norm, D, F, mask, active, n_active, ws_part(ws, B, D, F), G_FUSED, y, st);
+  } else if (decode_batch(B, D)) {
     e = sffn_launch_forward(act, g ? W_gate : nullptr, g ? b_gate : nullptr, W_up, g ? nullptr : b_up, W_downT, x,
                             x_norm, B, D, F, mask, active, n_active, y, ws_abuf(ws), st);
   } else {
@@ -283,7 +295,11 @@ int sffn_forward_q4(int act, sffn_q4 W_gate, const float* b_gate, sffn_q4 W_up, 
   const bool g = act == SFFN_ACT_REGLU;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (decode_batch(B, D)) {
+  if (sffn_fused_ok(B, D, F, act, true)) {
+    e = sffn_launch_fused_q4(act, g ? W_gate.q : nullptr, g ? W_gate.s : nullptr, g ? b_gate : nullptr, W_up.q, W_up.s,
+                             g ? nullptr : b_up, W_downT.q, W_downT.s, x, x_norm, D, F, mask, active, n_active,
+                             ws_part(ws, B, D, F), G_FUSED, y, st);
+  } else if (decode_batch(B, D)) {
     e = sffn_launch_forward_q4(act, g ? W_gate.q : nullptr, g ? W_gate.s : nullptr, g ? b_gate : nullptr, W_up.q,
                                W_up.s, g ? nullptr : b_up, W_downT.q, W_downT.s, x, x_norm, B, D, F, mask, active,
                                n_active, y, ws_abuf(ws), st);

@@ -451,6 +451,16 @@ hipError_t sffn_launch_forward_q4(int act, const uint8_t* qg, const void* sg, co
                                   const void* su, const float* bu, const uint8_t* qd, const void* sd, const float* x,
                                   int x_norm, int B, int D, int F, const uint64_t* mask, int32_t* active,
                                   int32_t* n_active, float* y, float* abuf, hipStream_t st);
+// single-token fused row + column gather (fused.hip): usable when sffn_fused_ok(B, D, F)
+bool sffn_fused_ok(int B, int D, int F, int act, bool q4);
+hipError_t sffn_launch_fused(int act, const void* Wg, const float* bg, const void* Wu, const float* bu,
+                             const void* WdT, const float* x, int x_norm, int D, int F, const uint64_t* mask,
+                             int32_t* active, int32_t* n_active, float* part, int G, float* y, hipStream_t st);
+hipError_t sffn_launch_fused_q4(int act, const uint8_t* qg, const void* sg, const float* bg, const uint8_t* qu,
+                                const void* su, const float* bu, const uint8_t* qd, const void* sd, const float* x,
+                                int x_norm, int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active,
+                                float* part, int G, float* y, hipStream_t st);
+
 // multi-token (union-mask) path, matrix cores (union.hip)
 hipError_t sffn_launch_norm_tokens(const float* x, int B, int D, float* xn, hipStream_t st);
 hipError_t sffn_launch_predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F,

@@ -1,0 +1,466 @@
+// Single-token sparse FFN in one pass over the active rows: row gather, activation and column gather fused.
+//
+// PowerInfer pages, Turkish article, "Neuron-aware operator": only the rows of W_gate / W_up and of W_downT that
+// belong to predicted-active neurons are read. Here each neuron's three rows are read in the same memory round
+// trip, and the down projection is accumulated where the activation is computed, so the activations never go
+// through memory and the column gather needs no launch of its own.
+//
+// k_fused1 (G blocks of 8 waves): round 1 loads x and the mask words; a block scan gives prefix offsets and
+// dense index i goes to block i % G, wave (i / G) % 8 (every block gets rows). Per pass, each wave locates its
+// neuron (binary search over the offsets, then a ballot over lane ranks) and issues its gate/up row loads; the
+// block's neuron ids go through LDS and every thread issues the loads of its 16-byte chunks of the 8 rows of
+// W_downT, all before x is normalised and staged. Each wave reduces its row dot products to the activation
+// a_i; the 8 activations go through LDS and every thread adds a_i * W_downT[id_i, its chunks] in wave order.
+// The block's partial sum of y over its rows is written to part[block][D]. Every sum has a fixed order, so the
+// result does not depend on timing.
+// k_sum_rows: y[d] = sum over blocks b < min(G, n) of part[b][d] in a fixed order (16 groups of blocks per
+// column, each summed in block order, then the groups in order); all of a thread's loads are issued together.
+#include "common.h"
+
+using namespace sffn;
+
+namespace {
+
+constexpr int NT_F = 512;            // 8 waves: rows per block pass
+constexpr int FW = NT_F / 64;
+constexpr int WMAX_F = 1;            // mask words per thread kept in LDS (nw <= 512)
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS accesses, not for its outstanding global loads
+// (those stay in flight across the barrier). The empty asm keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maximum (no wait)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int ACT, int NCH, int DCH>
+__global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, const float* __restrict__ bg,
+                                                 const uint4* __restrict__ Wu, const float* __restrict__ bu,
+                                                 const uint4* __restrict__ WdT, const float* __restrict__ x,
+                                                 int x_norm, int D, int F, const uint64_t* __restrict__ mask,
+                                                 int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                                                 float* __restrict__ part) {
+  extern __shared__ uint64_t lds64[];
+  const int nw = (F + 63) >> 6;
+  uint64_t* wl = lds64;                                                  // [nw] mask words
+  int* roff = reinterpret_cast<int*>(wl + ((nw + 1) & ~1));              // [NT_F] range offsets
+  int* tmp = roff + NT_F;                                                // [NT_F/64 + 1] scan scratch
+  int* ids = tmp + NT_F / 64 + 4;                                        // [FW] ids of the pass (-1: none)
+  float* av = reinterpret_cast<float*>(ids + FW);                        // [FW] activations of the pass
+  float* red = av + FW;                                                  // [2 * FW] normalisation scratch
+  float* xs = red + 2 * FW + 4;                                          // [D] x (16-byte aligned)
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nc = D >> 3;
+  const int n4 = D >> 2;
+  constexpr int XPT = (128 * NCH + NT_F - 1) / NT_F;   // float4 of x per thread: D / 4 <= 128 * NCH
+
+  // round 1: x and the mask words, all loads issued before any use
+  float4 xv4[XPT];
+  stage_load<NT_F, XPT>(x, n4, xv4);
+  const float x0 = x[0];                               // shift for the single-pass statistics
+  const int n = mask_prefix<NT_F, WMAX_F>(mask, nw, F, 1, wl, roff, tmp);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
+  const int G = gridDim.x;
+  if ((int)blockIdx.x >= n) return;                    // block-uniform: no row here; its partial is never read
+  const uint32_t wbytes = (uint32_t)F * (uint32_t)D * 2u;
+  const Buf bwu(Wu, wbytes), bwd(WdT, wbytes);
+  const Buf bwg(ACT == 1 ? (const void*)Wg : (const void*)Wu, ACT == 1 ? wbytes : 0u);
+  const float* bp = ACT == 1 ? bg : bu;
+  const Buf bbias(bp ? (const void*)bp : (const void*)Wu, bp ? (uint32_t)F * 4u : 0u);   // no bias: 0
+
+  float acc[DCH][8];
+#pragma unroll
+  for (int q = 0; q < DCH; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
+
+  bool first = true;
+  for (int k0 = blockIdx.x; k0 < n; k0 += G * FW) {    // passes (block-uniform)
+    const int i = k0 + G * w;
+    const bool have = i < n;                           // wave-uniform
+    // round 2: this wave's neuron, its gate/up rows and bias; then the block's W_downT rows
+    int id = -1;
+    uint4 wu[NCH], wg[NCH];
+    float bias = 0.f;
+    if (have) {
+      id = locate(wl, roff, NT_F, 1, nw, F, i);
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        const int c = lane + 64 * m;
+        const uint32_t o = boff(c < nc, ((uint32_t)id * nc + c) * 16u);
+        wu[m] = bwu.ld16(o);
+        if (ACT == 1) wg[m] = bwg.ld16(o);
+      }
+      bias = bbias.ldf((uint32_t)id * 4u);
+    }
+    if (lane == 0) ids[w] = id;
+    lds_barrier();
+    uint4 wd[FW][DCH];
+#pragma unroll
+    for (int j = 0; j < FW; ++j) {
+      const int idj = ids[j];
+#pragma unroll
+      for (int q = 0; q < DCH; ++q) {
+        const int c = threadIdx.x + NT_F * q;
+        wd[j][q] = bwd.ld16(boff(idj >= 0 && c < nc, ((uint32_t)(idj >= 0 ? idj : 0) * nc + c) * 16u));
+      }
+    }
+    if (first) {                                       // x: normalised and staged while the rows are in flight
+      if (x_norm) block_norm_regs<NT_F, XPT>(xv4, n4, x0, red);
+      stage_store<NT_F, XPT>(xs, n4, xv4);
+      lds_barrier();
+      first = false;
+    }
+    if (have) {
+      float au = 0.f, ag = 0.f;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        const int c = lane + 64 * m;
+        if (c < nc) {
+          const float4* xp = reinterpret_cast<const float4*>(xs + 8 * c);
+          const float4 xa = xp[0], xb = xp[1];
+          const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+          au += dot8(wu[m], xv);
+          if (ACT == 1) ag += dot8(wg[m], xv);
+        }
+      }
+      const float u = wave_sum(au);
+      float a;
+      if (ACT == 1) {
+        const float g = wave_sum(ag) + bias;
+        a = fmaxf(g, 0.f) * u;
+      } else {
+        a = fmaxf(u + bias, 0.f);
+      }
+      if (lane == 0) { av[w] = a; active[i] = id; }
+    } else if (lane == 0) {
+      av[w] = 0.f;
+    }
+    lds_barrier();
+    // column gather of the pass, rows in wave order
+#pragma unroll
+    for (int j = 0; j < FW; ++j) {
+      const float aj = av[j];
+#pragma unroll
+      for (int q = 0; q < DCH; ++q) {
+        float wf[8];
+        f16x8_to_f32(wd[j][q], wf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(aj, wf[e], acc[q][e]);
+      }
+    }
+    lds_barrier();                                     // ids / av are rewritten by the next pass
+  }
+  float* pb = part + (size_t)blockIdx.x * D;
+#pragma unroll
+  for (int q = 0; q < DCH; ++q) {
+    const int c = threadIdx.x + NT_F * q;
+    if (c < nc) {
+      float4* o = reinterpret_cast<float4*>(pb + 8 * c);
+      o[0] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+      o[1] = make_float4(acc[q][4], acc[q][5], acc[q][6], acc[q][7]);
+    }
+  }
+}
+
+// sum over a Q4 block of q_e * x_e: nib = 16 nibble bytes, xl / xh = x of the low-nibble (elements 0..15) and
+// high-nibble (16..31) halves of the block, as four float4 each
+__device__ __forceinline__ float q4_dot(const uint4& nib, const float4* xl, const float4* xh) {
+  const uint32_t wds[4] = {nib.x, nib.y, nib.z, nib.w};
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = wds[k] & 0x0F0F0F0Fu, hi = (wds[k] >> 4) & 0x0F0F0F0Fu;
+    s = fmaf((float)(lo & 0xFF), xl[k].x, s);
+    s = fmaf((float)((lo >> 8) & 0xFF), xl[k].y, s);
+    s = fmaf((float)((lo >> 16) & 0xFF), xl[k].z, s);
+    s = fmaf((float)(lo >> 24), xl[k].w, s);
+    s = fmaf((float)(hi & 0xFF), xh[k].x, s);
+    s = fmaf((float)((hi >> 8) & 0xFF), xh[k].y, s);
+    s = fmaf((float)((hi >> 16) & 0xFF), xh[k].z, s);
+    s = fmaf((float)(hi >> 24), xh[k].w, s);
+  }
+  return s;
+}
+
+// Q4_0 form: gate/up rows as nibbles + block scales (the "- 8" folded out with per-block sums of x); thread t owns
+// half-block t of every W_downT row (8 nibble bytes = 16 columns, and the block scale) and carries sum(a * s) for
+// the "- 8" of its columns. NQ: Q4 blocks per lane of a row; D <= 32 * NT_F (one half-block per thread).
+template <int ACT, int NQ>
+__global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg, const _Float16* __restrict__ sg,
+                                                    const float* __restrict__ bg, const uint4* __restrict__ qu,
+                                                    const _Float16* __restrict__ su, const float* __restrict__ bu,
+                                                    const uint8_t* __restrict__ qd, const _Float16* __restrict__ sd,
+                                                    const float* __restrict__ x, int x_norm, int D, int F,
+                                                    const uint64_t* __restrict__ mask, int32_t* __restrict__ active,
+                                                    int32_t* __restrict__ n_active, float* __restrict__ part) {
+  extern __shared__ uint64_t lds64[];
+  const int nw = (F + 63) >> 6;
+  const int nblk = D >> 5;
+  uint64_t* wl = lds64;                                                  // [nw] mask words
+  int* roff = reinterpret_cast<int*>(wl + ((nw + 1) & ~1));              // [NT_F] range offsets
+  int* tmp = roff + NT_F;                                                // [NT_F/64 + 1] scan scratch
+  int* ids = tmp + NT_F / 64 + 4;                                        // [FW] ids of the pass (-1: none)
+  float* av = reinterpret_cast<float*>(ids + FW);                        // [FW] activations of the pass
+  float* red = av + FW;                                                  // [2 * FW] normalisation scratch
+  float* xs = red + 2 * FW + 4;                                          // [D] x (16-byte aligned)
+  float* xsum = xs + D;                                                  // [D / 32] per-block sums of x
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n4 = D >> 2;
+  constexpr int XPT = (512 * NQ + NT_F - 1) / NT_F;    // float4 of x per thread: D / 4 <= 512 * NQ
+
+  float4 xv4[XPT];
+  stage_load<NT_F, XPT>(x, n4, xv4);
+  const float x0 = x[0];
+  const int n = mask_prefix<NT_F, WMAX_F>(mask, nw, F, 1, wl, roff, tmp);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
+  const int G = gridDim.x;
+  if ((int)blockIdx.x >= n) return;                    // block-uniform: no row here; its partial is never read
+  const uint32_t qbytes = (uint32_t)F * (uint32_t)nblk * 16u, sbytes = (uint32_t)F * (uint32_t)nblk * 2u;
+  const Buf bqu(qu, qbytes), bsu(su, sbytes), bqd(qd, qbytes), bsd(sd, sbytes);
+  const Buf bqg(ACT == 1 ? (const void*)qg : (const void*)qu, ACT == 1 ? qbytes : 0u);
+  const Buf bsg(ACT == 1 ? (const void*)sg : (const void*)su, ACT == 1 ? sbytes : 0u);
+  const float* bp = ACT == 1 ? bg : bu;
+  const Buf bbias(bp ? (const void*)bp : (const void*)qu, bp ? (uint32_t)F * 4u : 0u);   // no bias: 0
+  // this thread's half-block of W_downT rows
+  const int hb = threadIdx.x;                          // half-block index: Q4 block hb / 2, half hb % 2
+  const bool hok = hb < 2 * nblk;
+  const uint32_t hoff = (uint32_t)(hb >> 1) * 16u + (uint32_t)(hb & 1) * 8u;
+
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  float sas = 0.f;
+
+  bool first = true;
+  for (int k0 = blockIdx.x; k0 < n; k0 += G * FW) {    // passes (block-uniform)
+    const int i = k0 + G * w;
+    const bool have = i < n;                           // wave-uniform
+    int id = -1;
+    uint4 nu[NQ], ng[NQ];
+    float fu[NQ], fg[NQ];
+    float bias = 0.f;
+    if (have) {
+      id = locate(wl, roff, NT_F, 1, nw, F, i);
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) {
+        const int c = lane + 64 * m;
+        const bool ok = c < nblk;
+        const uint32_t o = (uint32_t)id * nblk + c;
+        nu[m] = bqu.ld16(boff(ok, o * 16u));
+        fu[m] = bsu.ldh(boff(ok, o * 2u));
+        if (ACT == 1) {
+          ng[m] = bqg.ld16(boff(ok, o * 16u));
+          fg[m] = bsg.ldh(boff(ok, o * 2u));
+        }
+      }
+      bias = bbias.ldf((uint32_t)id * 4u);
+    }
+    if (lane == 0) ids[w] = id;
+    lds_barrier();
+    uint2 dn[FW];
+    float ds[FW];
+#pragma unroll
+    for (int j = 0; j < FW; ++j) {
+      const int idj = ids[j];
+      const bool ok = idj >= 0 && hok;
+      const uint32_t row = (uint32_t)(idj >= 0 ? idj : 0);
+      dn[j] = bqd.ld8(boff(ok, row * (uint32_t)nblk * 16u + hoff));
+      ds[j] = bsd.ldh(boff(ok, (row * nblk + (hb >> 1)) * 2u));
+    }
+    if (first) {                                       // x: normalised, staged and summed per Q4 block
+      if (x_norm) block_norm_regs<NT_F, XPT>(xv4, n4, x0, red);
+      stage_store<NT_F, XPT>(xs, n4, xv4);
+      lds_barrier();
+      for (int t = threadIdx.x; t < nblk; t += NT_F) {
+        const float4* p = reinterpret_cast<const float4*>(xs + 32 * t);
+        float v = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v += (p[k].x + p[k].y) + (p[k].z + p[k].w);
+        xsum[t] = v;
+      }
+      lds_barrier();
+      first = false;
+    }
+    if (have) {
+      float au = 0.f, ag = 0.f;
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) {
+        const int c = lane + 64 * m;
+        if (c < nblk) {
+          const float4* xl = reinterpret_cast<const float4*>(xs + 32 * c);
+          const float xsb = xsum[c];
+          au = fmaf(fu[m], q4_dot(nu[m], xl, xl + 4) - 8.f * xsb, au);
+          if (ACT == 1) ag = fmaf(fg[m], q4_dot(ng[m], xl, xl + 4) - 8.f * xsb, ag);
+        }
+      }
+      const float u = wave_sum(au);
+      float a;
+      if (ACT == 1) {
+        const float g = wave_sum(ag) + bias;
+        a = fmaxf(g, 0.f) * u;
+      } else {
+        a = fmaxf(u + bias, 0.f);
+      }
+      if (lane == 0) { av[w] = a; active[i] = id; }
+    } else if (lane == 0) {
+      av[w] = 0.f;
+    }
+    lds_barrier();
+    // column gather of the pass, rows in wave order: element e < 8 is low nibble e of the half (block element
+    // 8 * half + e), e >= 8 the high nibble (block element 16 + 8 * half + e - 8)
+#pragma unroll
+    for (int j = 0; j < FW; ++j) {
+      const float as_ = av[j] * ds[j];
+      sas += as_;
+      const uint32_t wds[2] = {dn[j].x, dn[j].y};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t lo = wds[k] & 0x0F0F0F0Fu, hi = (wds[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          acc[4 * k + b] = fmaf(as_, (float)((lo >> (8 * b)) & 0xFF), acc[4 * k + b]);
+          acc[8 + 4 * k + b] = fmaf(as_, (float)((hi >> (8 * b)) & 0xFF), acc[8 + 4 * k + b]);
+        }
+      }
+    }
+    lds_barrier();                                     // ids / av are rewritten by the next pass
+  }
+  if (hok) {
+    float* pb = part + (size_t)blockIdx.x * D + 32 * (hb >> 1) + 8 * (hb & 1);
+    float4* lo = reinterpret_cast<float4*>(pb);
+    float4* hi = reinterpret_cast<float4*>(pb + 16);
+    const float c8 = -8.f * sas;
+    lo[0] = make_float4(acc[0] + c8, acc[1] + c8, acc[2] + c8, acc[3] + c8);
+    lo[1] = make_float4(acc[4] + c8, acc[5] + c8, acc[6] + c8, acc[7] + c8);
+    hi[0] = make_float4(acc[8] + c8, acc[9] + c8, acc[10] + c8, acc[11] + c8);
+    hi[1] = make_float4(acc[12] + c8, acc[13] + c8, acc[14] + c8, acc[15] + c8);
+  }
+}
+
+constexpr int NT_S = 512;            // 32 columns x 16 groups of blocks
+constexpr int SC = 32;
+constexpr int SG = NT_S / SC;
+constexpr int SPG = 16;              // partials per group: G <= SG * SPG = 256
+
+__global__ __launch_bounds__(NT_S) void k_sum_rows(const float* __restrict__ part, const int32_t* __restrict__ n_active,
+                                                   int G, int D, float* __restrict__ y) {
+  __shared__ float red[SG][SC];
+  const int c = threadIdx.x % SC, g = threadIdx.x / SC;
+  const int col = blockIdx.x * SC + c;
+  const int nb = min(G, max(*n_active, 0));            // blocks that wrote a partial
+  const Buf bp(part, (uint32_t)G * (uint32_t)D * 4u);
+  // every load of the thread is issued before the first add (group g takes blocks g, g + SG, ...)
+  float v[SPG];
+#pragma unroll
+  for (int k = 0; k < SPG; ++k) {
+    const int b = g + SG * k;
+    v[k] = bp.ldf(boff(b < nb && col < D, ((uint32_t)b * D + col) * 4u));
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < SPG; ++k) s += v[k];
+  red[g][c] = s;
+  __syncthreads();
+  if (g == 0 && col < D) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < SG; ++k) t += red[k][c];
+    y[col] = t;
+  }
+}
+
+template <int ACT, int NCH, int DCH>
+hipError_t launch_fused(const void* Wg, const float* bg, const void* Wu, const float* bu, const void* WdT,
+                        const float* x, int x_norm, int D, int F, const uint64_t* mask, int32_t* active,
+                        int32_t* n_active, float* part, int G, float* y, hipStream_t st) {
+  const int nw = (F + 63) / 64;
+  const size_t lds = (size_t)((nw + 1) & ~1) * 8 + (NT_F + NT_F / 64 + 4 + FW) * sizeof(int) +
+                     (FW + 2 * FW + 4 + (size_t)D) * sizeof(float) + 16;
+  static size_t avail = 0;
+  if (!avail) {
+    hipError_t ea = allow_dynamic_lds((const void*)k_fused1<ACT, NCH, DCH>, &avail);
+    if (ea != hipSuccess) return ea;
+  }
+  if (lds > avail) return hipErrorInvalidValue;
+  SFFN_LAUNCH(2, (k_fused1<ACT, NCH, DCH>), dim3(G), dim3(NT_F), lds, st, (const uint4*)Wg, bg, (const uint4*)Wu, bu,
+              (const uint4*)WdT, x, x_norm, D, F, mask, active, n_active, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (G > SG * SPG) return hipErrorInvalidValue;
+  SFFN_LAUNCH(3, k_sum_rows, dim3((D + SC - 1) / SC), dim3(NT_S), 0, st, part, n_active, G, D, y);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t dispatch_fused(const void* Wg, const float* bg, const void* Wu, const float* bu, const void* WdT,
+                          const float* x, int x_norm, int D, int F, const uint64_t* mask, int32_t* active,
+                          int32_t* n_active, float* part, int G, float* y, hipStream_t st) {
+  const int nch = (D / 8 + 63) / 64;
+#define FU(N, Q) return launch_fused<ACT, N, Q>(Wg, bg, Wu, bu, WdT, x, x_norm, D, F, mask, active, n_active, part, G, y, st)
+  if (nch <= 2) FU(2, 1);          // D <= 1024
+  if (nch <= 4) FU(4, 1);          // D <= 2048
+  if (nch <= 8) FU(8, 1);          // D <= 4096
+  if (nch <= 10) FU(10, 2);        // D <= 5120
+  if constexpr (ACT == 0) FU(16, 2);  // D <= 8192 (ReLU: one matrix; ReGLU rows this wide keep two kernels)
+  return hipErrorInvalidValue;
+#undef FU
+}
+
+template <int ACT, int NQ>
+hipError_t launch_fused_q4(const uint8_t* qg, const void* sg, const float* bg, const uint8_t* qu, const void* su,
+                           const float* bu, const uint8_t* qd, const void* sd, const float* x, int x_norm, int D, int F,
+                           const uint64_t* mask, int32_t* active, int32_t* n_active, float* part, int G, float* y,
+                           hipStream_t st) {
+  const int nw = (F + 63) / 64;
+  const size_t lds = (size_t)((nw + 1) & ~1) * 8 + (NT_F + NT_F / 64 + 4 + FW) * sizeof(int) +
+                     (FW + 2 * FW + 4 + (size_t)D + (size_t)D / 32) * sizeof(float) + 16;
+  static size_t avail = 0;
+  if (!avail) {
+    hipError_t ea = allow_dynamic_lds((const void*)k_fused1_q4<ACT, NQ>, &avail);
+    if (ea != hipSuccess) return ea;
+  }
+  if (lds > avail || G > SG * SPG) return hipErrorInvalidValue;
+  SFFN_LAUNCH(2, (k_fused1_q4<ACT, NQ>), dim3(G), dim3(NT_F), lds, st, (const uint4*)qg, (const _Float16*)sg, bg,
+              (const uint4*)qu, (const _Float16*)su, bu, qd, (const _Float16*)sd, x, x_norm, D, F, mask, active,
+              n_active, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SFFN_LAUNCH(3, k_sum_rows, dim3((D + SC - 1) / SC), dim3(NT_S), 0, st, part, n_active, G, D, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t sffn_launch_fused_q4(int act, const uint8_t* qg, const void* sg, const float* bg, const uint8_t* qu,
+                                const void* su, const float* bu, const uint8_t* qd, const void* sd, const float* x,
+                                int x_norm, int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active,
+                                float* part, int G, float* y, hipStream_t st) {
+  const int nq = (D / 32 + 63) / 64;   // Q4 blocks per lane of a row
+#define FQ(A, N) return launch_fused_q4<A, N>(qg, sg, bg, qu, su, bu, qd, sd, x, x_norm, D, F, mask, active, n_active, part, G, y, st)
+  if (act == 1) {
+    if (nq <= 1) FQ(1, 1);
+    if (nq <= 2) FQ(1, 2);
+    FQ(1, 4);
+  }
+  if (nq <= 1) FQ(0, 1);
+  if (nq <= 2) FQ(0, 2);
+  FQ(0, 4);
+#undef FQ
+}
+
+// Fused single-token forward: F <= 32768 (mask words fit one per thread); fp16: D <= 5120 (ReGLU: gate, up and
+// down chunks in registers) or D <= 8192 (ReLU); Q4_0: D <= 8192 (one half-block of every W_downT row per thread).
+bool sffn_fused_ok(int B, int D, int F, int act, bool q4) {
+  if (B != 1 || F > 32768) return false;
+  if (q4) return D <= 8192;
+  return D <= 5120 || (act == 0 && D <= 8192);
+}
+
+hipError_t sffn_launch_fused(int act, const void* Wg, const float* bg, const void* Wu, const float* bu,
+                             const void* WdT, const float* x, int x_norm, int D, int F, const uint64_t* mask,
+                             int32_t* active, int32_t* n_active, float* part, int G, float* y, hipStream_t st) {
+  return act == 1 ? dispatch_fused<1>(Wg, bg, Wu, bu, WdT, x, x_norm, D, F, mask, active, n_active, part, G, y, st)
+                  : dispatch_fused<0>(Wg, bg, Wu, bu, WdT, x, x_norm, D, F, mask, active, n_active, part, G, y, st);
+}

@@ -28,6 +28,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "sparse-FFN decode tokens/s + achieved HBM GB/s on active weights (1 MI355X)"
 KERNEL_NAMES = {0: "predictor h = P1 x", 1: "predictor z = P2 h + c, threshold, mask",
                 2: "compaction + W_gate/W_up row gather + activation", 3: "W_downT column gather"}
+FUSED_NAMES = {2: "compaction + W_gate/W_up/W_downT row gather + activation (fused)",
+               3: "sum of the per-block partials of y"}
 
 
 def parse():
@@ -251,18 +253,25 @@ def main():
     else:
         one_row = 2 * wl.D
     rows_mats = wl.n_mats - 1
-    bytes_rows = n_prof * rows_mats * one_row                    # per launch of kernel 2
-    bytes_cols = n_prof * one_row                                # per launch of kernel 3
+    path = _lib.forward_path(wl.act, stack.q4, B, wl.D, wl.F)
+    if path == _lib.PATH_FUSED:
+        # kernel 2 gathers gate/up and W_downT rows; kernel 3 adds the per-block partial sums of y
+        bytes_rows = n_prof * wl.n_mats * one_row
+        bytes_cols = (np.minimum(n_prof, 256) * wl.D + B * wl.D) * 4.0
+    else:
+        bytes_rows = n_prof * rows_mats * one_row                # per launch of kernel 2
+        bytes_cols = n_prof * one_row                            # per launch of kernel 3
     kb = {0: np.full(len(prof[0]), 2.0 * wl.r * wl.D), 1: np.full(len(prof[1]), 2.0 * wl.F * wl.r),
           2: bytes_rows, 3: bytes_cols}
     tot = {k: float(prof[k].sum()) for k in prof}
     dom = max(tot, key=tot.get)
     m = min(len(kb[dom]), len(prof[dom]))
     achieved = float(kb[dom][:m].sum() / (prof[dom][:m].sum() * 1e-3) / 1e9)       # GB/s
+    names = {**KERNEL_NAMES, **(FUSED_NAMES if path == _lib.PATH_FUSED else {})}
     fwd_us = mean_us[2] + mean_us[3]
     fwd_gbs = (float(n_prof.mean()) * row_bytes) / (fwd_us * 1e-6) / 1e9
 
-    tr = traffic_for(wl.name, B, KERNEL_NAMES[dom], float(kb[dom][:m].mean()))
+    tr = traffic_for(wl.name, B, names[dom], float(kb[dom][:m].mean()))
     traffic, traffic_detail = tr if tr else (None, None)
     out = {
         "metric": METRIC,
@@ -287,10 +296,10 @@ def main():
         "all_bytes_gbs": round((active_bytes_step + pred_bytes_step) / (ms_step * 1e-3) / 1e9, 1),
         "active_rows_per_layer": round(float(n_mean.mean()), 1),
         "density": round(float(n_mean.mean()) / wl.F, 4),
-        "kernel_us": {KERNEL_NAMES[k]: round(v, 3) for k, v in mean_us.items()},
+        "kernel_us": {names[k]: round(v, 3) for k, v in mean_us.items()},
         "kernel_timing": timing,
         "prompt": prompt,
-        "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "traffic_detail": traffic_detail},
         "wall_s": round(wall, 3),

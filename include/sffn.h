@@ -111,6 +111,18 @@ size_t sffn_workspace_size(int B, int D, int F, int r);
 /* Number of 64-bit mask words for F neurons: ceil(F / 64). */
 int sffn_mask_words(int F);
 
+/* Which kernels sffn_forward (q4 = 0) or sffn_forward_q4 (q4 = 1) runs for these sizes:
+ *   SFFN_PATH_FUSED (B == 1, F <= 32768, and D <= 5120 for fp16 ReGLU, D <= 8192 for fp16 ReLU and for Q4_0):
+ *     one kernel gathers the gate/up rows, applies the activation and accumulates the W_downT rows into
+ *     per-block partial sums of y; a second kernel adds the partials in fixed order (timing ids SFFN_K_ROWS and
+ *     SFFN_K_COLS);
+ *   SFFN_PATH_DECODE (other B == 1, and B in {2, 4, 8} with B * D <= 16384): row gather + activation, then the
+ *     column gather;
+ *   SFFN_PATH_UNION (every other B): matrix-core kernels over the union mask.
+ * Returns -1 for an unknown activation. */
+enum { SFFN_PATH_DECODE = 0, SFFN_PATH_FUSED = 1, SFFN_PATH_UNION = 2 };
+int sffn_forward_path(int act, int q4, int B, int D, int F);
+
 /* Activation predictor ("Adaptive sparsity predictors"; "Online stage").
  *   h[b, :] = P1 xn[b, :]                     (fp32 accumulate; h is never rounded)
  *   z[b, k] = P2[k, :] h[b, :] + c[k]         (c = NULL means 0)

@@ -40,8 +40,8 @@ def test_status_strings_and_sizes():
     assert _lib.status_string(0) == "ok"
     assert "workspace" in _lib.status_string(4)
     assert _lib.mask_words(1) == 1 and _lib.mask_words(64) == 1 and _lib.mask_words(65) == 2
-    # [a: F*B fp32][B > 1: xn B*D fp32][B > 1: partial y 8*B*D fp32][h: B*r fp32], 256-byte parts
-    assert _lib.workspace_size(1, 4096, 11008, 256) == 44032 + 1024
+    # [a: F*B fp32][B > 1: xn B*D fp32][partial y: 8*B*D fp32 (B > 1) or 256*D fp32 (B = 1)][h: B*r fp32]
+    assert _lib.workspace_size(1, 4096, 11008, 256) == 44032 + 256 * 4096 * 4 + 1024
     assert _lib.workspace_size(8, 512, 100, 64) == 3328 + 16384 + 131072 + 2048
     assert _lib.workspace_size(3, 40, 7, 8) == 256 + 512 + 3840 + 256
 
@@ -116,3 +116,16 @@ def test_union_batches_are_routed_not_rejected():
     assert _forward(B=3, ws_bytes=16) == 4
     assert _forward_q4(B=16, ws_bytes=16) == 4
     assert _predict(B=5, ws_bytes=16) == 4
+
+
+def test_forward_path_routing():
+    assert _lib.forward_path("reglu", False, 1, 5120, 13824) == _lib.PATH_FUSED
+    assert _lib.forward_path("relu", False, 1, 8192, 32768) == _lib.PATH_FUSED
+    assert _lib.forward_path("reglu", False, 1, 8192, 1000) == _lib.PATH_DECODE   # ReGLU wider than 5120
+    assert _lib.forward_path("relu", False, 1, 64, 33000) == _lib.PATH_DECODE     # more than 32768 neurons
+    assert _lib.forward_path("reglu", True, 1, 8192, 28672) == _lib.PATH_FUSED
+    assert _lib.forward_path("reglu", True, 1, 16384, 2048) == _lib.PATH_DECODE   # Q4_0 rows wider than 8192
+    assert _lib.forward_path("reglu", False, 4, 4096, 11008) == _lib.PATH_DECODE
+    assert _lib.forward_path("reglu", False, 4, 5120, 13824) == _lib.PATH_UNION
+    assert _lib.forward_path("relu", True, 64, 8192, 28672) == _lib.PATH_UNION
+    assert _lib.lib().sffn_forward_path(5, 0, 1, 64, 64) == -1

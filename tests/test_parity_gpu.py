@@ -119,6 +119,21 @@ def test_minimum_d_q4(gpu_ready, B):
     check(case, x, run_gpu(case, torch.from_numpy(x).to(gpu_ready)))
 
 
+@pytest.mark.parametrize("name,wl", [
+    ("reglu_wide_d", small("c2", D=5632, F=900, r=16, L=1, density=0.1)),        # ReGLU wider than the fused kernel
+    ("relu_wide_d", small("c1", D=8704, F=700, r=16, L=1, density=0.1)),         # ReLU wider than the fused kernel
+    ("relu_many_neurons", small("c1", D=64, F=33000, r=8, L=1, density=0.01)),   # more mask words than threads
+    ("relu_fused_widest", small("c1", D=8192, F=600, r=16, L=1, density=0.2)),
+])
+def test_single_token_path_boundaries(gpu_ready, name, wl):
+    case = make_case(wl, 0, gpu_ready)
+    for step in range(2):
+        x = _x(wl, 1, step)
+        say(f"[{name}] step {step}")
+        st = check(case, x, run_gpu(case, torch.from_numpy(x).to(gpu_ready)))
+        say("   ", st)
+
+
 def test_largest_union_f(gpu_ready):
     # the union kernels take F up to 32768 (512 mask words), a ragged D and many k splits of few rows
     wl = small("c1", D=200, F=32768, r=16, L=1, density=0.02)
