@@ -56,9 +56,11 @@
  * batch results match the decode kernels' to within fp32 rounding.
  *
  * Workspace (sffn_workspace_size bytes, 256-byte parts, caller-owned, no
- * state kept between calls): activations a [F, B] fp32; for B > 1 also the
- * normalised inputs [B, D] and 8 row-split partial sums [8, B, D] fp32; the
- * predictor's h [B, r] fp32 last. One workspace may serve the predict and
+ * state kept between calls): activations a [F, B] fp32; for B > 1 the
+ * normalised inputs [B, D]; partial sums of y, [256, D] fp32 for B == 1 (one
+ * per block of the fused kernel) or [8, B, D] for B > 1 (row splits; the
+ * union predictor also keeps its partial h there); the predictor's h [B, r]
+ * fp32 last. One workspace may serve the predict and
  * forward calls of a layer in turn on one stream; calls that overlap in time
  * need separate workspaces.
  *
