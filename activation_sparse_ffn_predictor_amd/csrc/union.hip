@@ -335,13 +335,16 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
   f32x4 au[NTT], ag[NTT];
 #pragma unroll
   for (int t = 0; t < NTT; ++t) { au[t] = f32x4{0.f, 0.f, 0.f, 0.f}; ag[t] = au[t]; }
-  constexpr int CH = KChunk<NTT>::CH;
-  for (int c0 = kb0; c0 < kb1; c0 += CH) {
-    // one round trip per chunk: weight rows (or nibbles and scales) and x tiles of CH k blocks
-    uint4 wu_[CH], wg_[CH];
-    uint2 qu_[CH], qg_[CH];
-    float su4[CH][4], sg4[CH][4];
+  // Double-buffered chunks of CH k blocks: the next chunk's weight rows (or nibbles and scales) and x tiles are
+  // issued before the current chunk's matrix-core work, so consecutive round trips overlap.
+  constexpr int CH = KChunk<NTT>::CH / 2 > 0 ? KChunk<NTT>::CH / 2 : 1;
+  struct Chunk {
+    uint4 wu[CH], wg[CH];
+    uint2 qu[CH], qg[CH];
+    float su[CH][4], sg[CH][4];
     XRaw xr[CH][NTT];
+  };
+  auto load_chunk = [&](int c0, Chunk& C) {
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       const int kb = c0 + q;
@@ -349,47 +352,48 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
       const bool ok = kb < kb1 && idl >= 0 && k < D;
       if constexpr (Q4) {
         const uint32_t o = (uint32_t)(ok ? idl : 0) * (uint32_t)(D >> 1) + (uint32_t)kb * 16u + ((lane >> 4) & 1) * 8u;
-        qu_[q] = bwu.ld8(boff(ok, o));
-        if (ACT) qg_[q] = bwg.ld8(boff(ok, o));
+        C.qu[q] = bwu.ld8(boff(ok, o));
+        if (ACT) C.qg[q] = bwg.ld8(boff(ok, o));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool okr = kb < kb1 && idr[i] >= 0;
           const uint32_t so = ((uint32_t)(okr ? idr[i] : 0) * nblk + kb) * 2u;
-          su4[q][i] = bsu.ldh(boff(okr, so));
-          if (ACT) sg4[q][i] = bsg.ldh(boff(okr, so));
+          C.su[q][i] = bsu.ldh(boff(okr, so));
+          if (ACT) C.sg[q][i] = bsg.ldh(boff(okr, so));
         }
       } else {
         const uint32_t o = ((uint32_t)(ok ? idl : 0) * D + k) * 2u;
-        wu_[q] = bwu.ld16(boff(ok, o));
-        if (ACT) wg_[q] = bwg.ld16(boff(ok, o));
+        C.wu[q] = bwu.ld16(boff(ok, o));
+        if (ACT) C.wg[q] = bwg.ld16(boff(ok, o));
       }
 #pragma unroll
-      for (int t = 0; t < NTT; ++t) xr[q][t] = load_xraw(bx, B, kb < kb1 ? D : 0, t, kb);
+      for (int t = 0; t < NTT; ++t) C.xr[q][t] = load_xraw(bx, B, kb < kb1 ? D : 0, t, kb);
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute_chunk = [&](const Chunk& C) {
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       half8 a_u, a_g;
       if constexpr (Q4) {
-        a_u = q4_to_half8(qu_[q], lane >> 4);
-        if (ACT) a_g = q4_to_half8(qg_[q], lane >> 4);
+        a_u = q4_to_half8(C.qu[q], lane >> 4);
+        if (ACT) a_g = q4_to_half8(C.qg[q], lane >> 4);
       } else {
-        a_u = __builtin_bit_cast(half8, wu_[q]);
-        if (ACT) a_g = __builtin_bit_cast(half8, wg_[q]);
+        a_u = __builtin_bit_cast(half8, C.wu[q]);
+        if (ACT) a_g = __builtin_bit_cast(half8, C.wg[q]);
       }
 #pragma unroll
       for (int t = 0; t < NTT; ++t) {
         half8 xh, xl;
-        split_xraw(xr[q][t], xh, xl);
+        split_xraw(C.xr[q][t], xh, xl);
         if constexpr (Q4) {
           const f32x4 z = {0.f, 0.f, 0.f, 0.f};
           const f32x4 pu = mfma16(a_u, xl, mfma16(a_u, xh, z));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) au[t][i] = fmaf(su4[q][i], pu[i], au[t][i]);
+          for (int i = 0; i < 4; ++i) au[t][i] = fmaf(C.su[q][i], pu[i], au[t][i]);
           if (ACT) {
             const f32x4 pg = mfma16(a_g, xl, mfma16(a_g, xh, z));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ag[t][i] = fmaf(sg4[q][i], pg[i], ag[t][i]);
+            for (int i = 0; i < 4; ++i) ag[t][i] = fmaf(C.sg[q][i], pg[i], ag[t][i]);
           }
         } else {
           au[t] = mfma16(a_u, xl, mfma16(a_u, xh, au[t]));
@@ -397,6 +401,17 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
         }
       }
     }
+  };
+  Chunk cA, cB;
+  if (kb0 < kb1) load_chunk(kb0, cA);
+  for (int c0 = kb0; c0 < kb1; c0 += 2 * CH) {
+    if (c0 + CH < kb1) load_chunk(c0 + CH, cB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_chunk(cA);
+    if (c0 + CH >= kb1) break;
+    if (c0 + 2 * CH < kb1) load_chunk(c0 + 2 * CH, cA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_chunk(cB);
   }
 #pragma unroll
   for (int t = 0; t < NTT; ++t) {
