@@ -22,6 +22,9 @@ using namespace sffn;
 namespace {
 
 constexpr int NT = 256;
+#ifndef SFFN_Z_LPR_MAX
+#define SFFN_Z_LPR_MAX 8         // lanes per P2 row in the stage-2 kernel (fewer lanes: more chunk rounds per lane)
+#endif
 
 constexpr int NTH = 256;
 
@@ -185,17 +188,24 @@ hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, c
   if (e != hipSuccess) return e;
   const int cpr = r / 8;
   int lpr = 8;
-  while (lpr * 2 <= cpr && lpr < 64) lpr *= 2;
-  const int rounds = (cpr + lpr - 1) / lpr;  // 1 or 2 for r <= 1024
-  switch (lpr * 10 + rounds) {
-    case 81: return launch_z<8, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 82: return launch_z<8, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 161: return launch_z<16, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 162: return launch_z<16, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 321: return launch_z<32, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 322: return launch_z<32, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 641: return launch_z<64, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 642: return launch_z<64, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+  while (lpr * 2 <= cpr && lpr < SFFN_Z_LPR_MAX) lpr *= 2;
+  int rounds = 1;
+  while (rounds * lpr < cpr) rounds *= 2;   // cpr <= 128: at most 16 rounds of 8 lanes
+  switch (lpr * 100 + rounds) {
+    case 801: return launch_z<8, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 802: return launch_z<8, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 804: return launch_z<8, 4>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 808: return launch_z<8, 8>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 816: return launch_z<8, 16>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 1601: return launch_z<16, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 1602: return launch_z<16, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 1604: return launch_z<16, 4>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 1608: return launch_z<16, 8>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 3201: return launch_z<32, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 3202: return launch_z<32, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 3204: return launch_z<32, 4>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 6401: return launch_z<64, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 6402: return launch_z<64, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
     default: return hipErrorInvalidValue;
   }
 }
