@@ -19,12 +19,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
-}
-
 // sum over aligned groups of G lanes (G a power of two <= 64); every lane of the group gets the sum
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
@@ -73,22 +67,6 @@ struct Buf {
 };
 __device__ __forceinline__ uint32_t boff(bool ok, uint32_t off) { return ok ? off : OOB; }
 
-// Branch-free guarded loads: the address is clamped to a valid element when `ok` is false and the value is
-// replaced afterwards, so the compiler emits straight-line loads that all stay in flight together.
-__device__ __forceinline__ uint4 ldg16(const uint4* __restrict__ p, size_t i, bool ok) {
-  const uint4 v = p[ok ? i : 0];
-  return ok ? v : make_uint4(0u, 0u, 0u, 0u);
-}
-__device__ __forceinline__ float4 ldgf4(const float4* __restrict__ p, size_t i, bool ok) {
-  const float4 v = p[ok ? i : 0];
-  return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
-}
-template <class T>
-__device__ __forceinline__ T ldg(const T* __restrict__ p, size_t i, bool ok, T dflt) {
-  const T v = p[ok ? i : 0];
-  return ok ? v : dflt;
-}
-
 __device__ __forceinline__ void f16x8_to_f32(const uint4& u, float* f) {
   half8 h = __builtin_bit_cast(half8, u);
 #pragma unroll
@@ -125,95 +103,9 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_tmp /* NT/64
   return lds_tmp[w] + inc - v;
 }
 
-// Normalise one token held in registers across a wave: lane l holds chunks m (CW float4 each), chunk m valid
-// iff l + 64 m < nvalid (invalid chunks hold zeros and stay untouched). x' = (x - mean) / sqrt(var + eps) over
-// the D valid elements, mean first and then the centred variance (two wave reductions).
-template <int NCH, int CW>
-__device__ __forceinline__ void wave_norm_regs(float4 (&v)[NCH][CW], int nvalid, int D) {
-  const int lane = threadIdx.x & 63;
-  float s = 0.f;
-#pragma unroll
-  for (int m = 0; m < NCH; ++m)
-    if (lane + 64 * m < nvalid)
-#pragma unroll
-      for (int k = 0; k < CW; ++k) s += (v[m][k].x + v[m][k].y) + (v[m][k].z + v[m][k].w);
-  const float mu = wave_sum(s) / (float)D;
-  float q = 0.f;
-#pragma unroll
-  for (int m = 0; m < NCH; ++m)
-    if (lane + 64 * m < nvalid)
-#pragma unroll
-      for (int k = 0; k < CW; ++k) {
-        const float a = v[m][k].x - mu, b = v[m][k].y - mu, c = v[m][k].z - mu, d = v[m][k].w - mu;
-        q = fmaf(a, a, q); q = fmaf(b, b, q); q = fmaf(c, c, q); q = fmaf(d, d, q);
-      }
-  const float rs = 1.0f / sqrtf(wave_sum(q) / (float)D + NORM_EPS);
-#pragma unroll
-  for (int m = 0; m < NCH; ++m)
-    if (lane + 64 * m < nvalid)
-#pragma unroll
-      for (int k = 0; k < CW; ++k) {
-        v[m][k].x = (v[m][k].x - mu) * rs; v[m][k].y = (v[m][k].y - mu) * rs;
-        v[m][k].z = (v[m][k].z - mu) * rs; v[m][k].w = (v[m][k].w - mu) * rs;
-      }
-}
-
-// Stage xn[b, d] for b < nb, d < D into LDS (fp32, row stride D), normalising each token (centre, unit variance)
-// if asked. Every thread issues all of its global loads (at most XPT float4, nb * D <= 4 * NT * XPT) before its
-// first LDS write. red: >= 2 * (NT/64) * nb floats of LDS scratch. Deterministic: per-wave
-// partial sums are combined in wave order.
-template <int NT, int XPT>
-__device__ __forceinline__ void stage_x(const float* __restrict__ x, int nb, int D, int x_norm, float* xs, float* red) {
-  // one straight-line round of loads: callers keep nb * D <= 4 * NT * XPT
-  const int n4 = (nb * D) >> 2;  // D % 8 == 0: rows are whole float4s
-  const Buf bx(x, (uint32_t)n4 * 16u);
-  float4* dst = reinterpret_cast<float4*>(xs);
-  float4 v[XPT];
-#pragma unroll
-  for (int k = 0; k < XPT; ++k) {
-    const int i = k * NT + threadIdx.x;
-    v[k] = bx.ldf4(boff(i < n4, (uint32_t)i * 16u));
-  }
-#pragma unroll
-  for (int k = 0; k < XPT; ++k) {
-    const int i = k * NT + threadIdx.x;
-    if (i < n4) dst[i] = v[k];
-  }
-  __syncthreads();
-  if (!x_norm) return;
-  constexpr int NWB = NT / 64;
-  const int w = threadIdx.x >> 6;
-  float* rs_ = red;               // [NWB][nb] sums
-  float* rq_ = red + NWB * nb;    // [NWB][nb] centred squares
-  for (int b = 0; b < nb; ++b) {
-    float s = 0.f;
-    for (int i = threadIdx.x; i < D; i += NT) s += xs[(size_t)b * D + i];
-    s = wave_sum(s);
-    if ((threadIdx.x & 63) == 0) rs_[w * nb + b] = s;
-  }
-  __syncthreads();
-  for (int b = 0; b < nb; ++b) {
-    float tot = 0.f;
-    for (int i = 0; i < NWB; ++i) tot += rs_[i * nb + b];
-    const float mu = tot / (float)D;
-    float q = 0.f;
-    for (int i = threadIdx.x; i < D; i += NT) { const float d = xs[(size_t)b * D + i] - mu; q = fmaf(d, d, q); }
-    q = wave_sum(q);
-    if ((threadIdx.x & 63) == 0) rq_[w * nb + b] = q;
-  }
-  __syncthreads();
-  for (int b = 0; b < nb; ++b) {
-    float tot = 0.f, totq = 0.f;
-    for (int i = 0; i < NWB; ++i) { tot += rs_[i * nb + b]; totq += rq_[i * nb + b]; }
-    const float mu = tot / (float)D;
-    const float sc = 1.0f / sqrtf(totq / (float)D + NORM_EPS);
-    for (int i = threadIdx.x; i < D; i += NT) xs[(size_t)b * D + i] = (xs[(size_t)b * D + i] - mu) * sc;
-  }
-  __syncthreads();
-}
-
-// Split form of stage_x for kernels that overlap x with other loads: stage_load issues the (straight-line)
-// global loads into registers, stage_store writes them to LDS (caller syncs), stage_norm normalises in LDS.
+// Staging of x into LDS (fp32, token stride D) for kernels that overlap it with other loads: stage_load issues
+// the straight-line global loads into registers (every load before the first use; thread t holds float4
+// k * NT + t, k < XPT), stage_store writes them to LDS (the caller synchronises), stage_norm normalises in LDS.
 template <int NT, int XPT>
 __device__ __forceinline__ void stage_load(const float* __restrict__ x, int n4, float4 (&v)[XPT]) {
   const Buf bx(x, (uint32_t)n4 * 16u);
@@ -301,39 +193,6 @@ __device__ __forceinline__ void stage_norm(float* xs, int nb, int D, float* red)
     for (int i = threadIdx.x; i < D; i += NT) xs[(size_t)b * D + i] = (xs[(size_t)b * D + i] - mu) * sc;
   }
   __syncthreads();
-}
-
-// Block-wide compaction of mask words [w0, w0 + nwr) into an LDS list of stored neuron ids (ascending).
-// Wave v handles words w0 + v*wpw .. + wpw (wpw <= 64); lane k < wpw loads word k of the wave's range (one
-// straight-line load, issued by the caller through `cw`). Returns the list length. cnt: NT/64 + 1 ints of LDS.
-template <int NT>
-__device__ __forceinline__ int compact_words(uint64_t cw, int w0, int nwr, int wpw, int nw, int F, int* list,
-                                             int* cnt) {
-  constexpr int NWB = NT / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int first = w0 + w * wpw;                 // first word of this wave
-  const int nmine = max(0, min(wpw, w0 + nwr - first));
-  if (lane < nmine && first + lane == nw - 1 && (F & 63)) cw &= (1ull << (F & 63)) - 1ull;
-  if (lane >= nmine) cw = 0ull;
-  int tot = __popcll(cw);
-  tot = wave_sum_int(tot);
-  if (lane == 0) cnt[w] = tot;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < NWB; ++i) { const int c = cnt[i]; cnt[i] = run; run += c; }
-    cnt[NWB] = run;
-  }
-  __syncthreads();
-  int off = cnt[w];
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int k = 0; k < nmine; ++k) {
-    const uint64_t word = __shfl(cw, k, WAVE);
-    if ((word >> lane) & 1ull) list[off + __popcll(word & below)] = (first + k) * 64 + lane;
-    off += __popcll(word);
-  }
-  __syncthreads();
-  return cnt[NWB];
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on XCD i % 8) and every XCD has its own
