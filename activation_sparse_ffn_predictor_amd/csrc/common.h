@@ -60,6 +60,9 @@ struct Buf {
   __device__ __forceinline__ uint32_t ldu(uint32_t off) const {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
   }
+  __device__ __forceinline__ _Float16 ldh16(uint32_t off) const {  // one fp16 value
+    return __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+  }
   __device__ __forceinline__ float ldh(uint32_t off) const {  // one fp16 value, widened
     const unsigned short b = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
     return (float)__builtin_bit_cast(_Float16, b);
@@ -208,6 +211,33 @@ __device__ __forceinline__ uint64_t mask_word(const uint64_t* __restrict__ mask,
   uint64_t w = mask[t];
   if (t == nw - 1 && (F & 63)) w &= (1ull << (F & 63)) - 1ull;
   return w;
+}
+
+// Position of the k-th set bit (0-based, k < popcount) of a 64-bit word, by halving.
+__device__ __forceinline__ int select_bit(uint64_t w, int k) {
+  int pos = 0;
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) {
+    const uint64_t lowmask = (h == 64) ? ~0ull : ((1ull << h) - 1ull);
+    const int c = __popcll(w & lowmask);
+    if (k >= c) { k -= c; w >>= h; pos += h; }
+  }
+  return pos;
+}
+
+// The ids of the rows a block owns when dense index i goes to block i % G (G >= 64): bids[k] = the neuron with
+// dense index blk + G * k. Thread t owns mask word t (one word per thread: nw <= blockDim.x) and roff[t] = set
+// bits before it; owned indices are G >= 64 apart, so a word holds at most one, found by a rank select. The
+// caller synchronises before reading bids.
+__device__ __forceinline__ void block_row_ids(const uint64_t* wl, const int* roff, int nw, int blk, int G, int* bids) {
+  const int t = threadIdx.x;
+  if (t < nw) {
+    const uint64_t word = wl[t];
+    const int base = roff[t];
+    int k = (blk - base) % G;                          // rank in the word of the first owned index >= base
+    if (k < 0) k += G;
+    if (k < __popcll(word)) bids[(base + k - blk) / G] = 64 * t + select_bit(word, k);
+  }
 }
 
 // Locate the i-th set bit (0-based, dense index i < total) of the mask. words: the mask words, in LDS or

@@ -5,16 +5,20 @@
 // trip, and the down projection is accumulated where the activation is computed, so the activations never go
 // through memory and the column gather needs no launch of its own.
 //
-// k_fused1 (G blocks of 8 waves): round 1 loads x and the mask words; a block scan gives prefix offsets and
-// dense index i goes to block i % G, wave (i / G) % 8 (every block gets rows). Per pass, each wave locates its
-// neuron (binary search over the offsets, then a ballot over lane ranks) and issues its gate/up row loads; the
-// block's neuron ids go through LDS and every thread issues the loads of its 16-byte chunks of the 8 rows of
-// W_downT, all before x is normalised and staged. Each wave reduces its row dot products to the activation
-// a_i; the 8 activations go through LDS and every thread adds a_i * W_downT[id_i, its chunks] in wave order.
-// The block's partial sum of y over its rows is written to part[block][D]. Every sum has a fixed order, so the
-// result does not depend on timing.
+// k_fused1 (G >= 64 blocks of 8 waves): round 1 loads x and the mask words; a block scan gives each thread the
+// set bits before its mask word. Dense index i goes to block i % G, so every block gets a near-equal share. A
+// block's rows are G apart in dense order, so a mask word holds at most one of them: each thread finds its word's
+// one by a rank select, and the block has the ids of all its rows in LDS at once. Per pass of 8 rows, each wave
+// issues the loads of its row of W_gate / W_up and every thread the loads of its 16-byte chunks of the pass's 8
+// rows of W_downT, all together and before x is normalised and staged. Each wave reduces its row dot products to
+// the activation a_i; the 8 activations go through LDS and every thread adds a_i * W_downT[id_i, its chunks] in
+// row order. The block's partial sum of y over its rows is written to part[block][D].
+// k_fused1_q4: the same for Q4_0 rows (nibbles and fp16 block scales). x sits in LDS transposed, so the lane of a
+// Q4 block reads its 32 values of x without bank conflicts; the pass's W_downT nibble rows are loaded straight
+// into LDS (buffer loads with the LDS destination) instead of registers.
 // k_sum_rows: y[d] = sum over blocks b < min(G, n) of part[b][d] in a fixed order (16 groups of blocks per
 // column, each summed in block order, then the groups in order); all of a thread's loads are issued together.
+// Every sum has a fixed order, so the results do not depend on timing.
 #include "common.h"
 
 using namespace sffn;
@@ -24,6 +28,9 @@ namespace {
 constexpr int NT_F = 512;            // 8 waves: rows per block pass
 constexpr int FW = NT_F / 64;
 constexpr int WMAX_F = 1;            // mask words per thread kept in LDS (nw <= 512)
+#ifndef SFFN_Q4_FUSED_RPW
+#define SFFN_Q4_FUSED_RPW 1          // Q4_0 rows per wave per pass (measured best at the 70B shape: 1, over 2 and 3)
+#endif
 
 // Workgroup barrier for LDS data only: waits for this wave's LDS accesses, not for its outstanding global loads
 // (those stay in flight across the barrier). The empty asm keeps the compiler from moving memory accesses across.
@@ -46,10 +53,10 @@ __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, c
   uint64_t* wl = lds64;                                                  // [nw] mask words
   int* roff = reinterpret_cast<int*>(wl + ((nw + 1) & ~1));              // [NT_F] range offsets
   int* tmp = roff + NT_F;                                                // [NT_F/64 + 1] scan scratch
-  int* ids = tmp + NT_F / 64 + 4;                                        // [FW] ids of the pass (-1: none)
-  float* av = reinterpret_cast<float*>(ids + FW);                        // [FW] activations of the pass
+  float* av = reinterpret_cast<float*>(tmp + NT_F / 64 + 4);             // [FW] activations of the pass
   float* red = av + FW;                                                  // [2 * FW] normalisation scratch
   float* xs = red + 2 * FW + 4;                                          // [D] x (16-byte aligned)
+  int* bids = reinterpret_cast<int*>(xs + D);                            // [ceil(F / G)] the block's row ids
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nc = D >> 3;
   const int n4 = D >> 2;
@@ -75,16 +82,23 @@ __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, c
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
 
+  // the block's rows: dense indices blk + G * k, k < nrow, their ids in LDS (one rank select per mask word)
+  const int blk = blockIdx.x;
+  const int nrow = (n - blk + G - 1) / G;
+  block_row_ids(wl, roff, nw, blk, G, bids);
+  lds_barrier();
+  const bool wq_last = (int)__builtin_amdgcn_readfirstlane(threadIdx.x) + NT_F * (DCH - 1) < nc;   // wave-uniform
+
   bool first = true;
-  for (int k0 = blockIdx.x; k0 < n; k0 += G * FW) {    // passes (block-uniform)
-    const int i = k0 + G * w;
-    const bool have = i < n;                           // wave-uniform
-    // round 2: this wave's neuron, its gate/up rows and bias; then the block's W_downT rows
+  for (int k0 = 0; k0 < nrow; k0 += FW) {              // passes (block-uniform); row k0 + w on wave w
+    const int k = k0 + w;
+    const bool have = k < nrow;                        // wave-uniform
+    // round 2: this wave's neuron, its gate/up rows and bias; then the block's W_downT rows, all issued together
     int id = -1;
     uint4 wu[NCH], wg[NCH];
     float bias = 0.f;
     if (have) {
-      id = locate(wl, roff, NT_F, 1, nw, F, i);
+      id = bids[k];
 #pragma unroll
       for (int m = 0; m < NCH; ++m) {
         const int c = lane + 64 * m;
@@ -94,15 +108,17 @@ __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, c
       }
       bias = bbias.ldf((uint32_t)id * 4u);
     }
-    if (lane == 0) ids[w] = id;
-    lds_barrier();
     uint4 wd[FW][DCH];
 #pragma unroll
     for (int j = 0; j < FW; ++j) {
-      const int idj = ids[j];
+      const int idj = k0 + j < nrow ? bids[k0 + j] : -1;
 #pragma unroll
       for (int q = 0; q < DCH; ++q) {
         const int c = threadIdx.x + NT_F * q;
+        if (q == DCH - 1 && !wq_last) {                // chunks past the row end on this whole wave: no load
+          wd[j][q] = make_uint4(0u, 0u, 0u, 0u);
+          continue;
+        }
         wd[j][q] = bwd.ld16(boff(idj >= 0 && c < nc, ((uint32_t)(idj >= 0 ? idj : 0) * nc + c) * 16u));
       }
     }
@@ -133,7 +149,7 @@ __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, c
       } else {
         a = fmaxf(u + bias, 0.f);
       }
-      if (lane == 0) { av[w] = a; active[i] = id; }
+      if (lane == 0) { av[w] = a; active[blk + G * k] = id; }
     } else if (lane == 0) {
       av[w] = 0.f;
     }
@@ -164,22 +180,17 @@ __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, c
   }
 }
 
-// sum over a Q4 block of q_e * x_e: nib = 16 nibble bytes, xl / xh = x of the low-nibble (elements 0..15) and
-// high-nibble (16..31) halves of the block, as four float4 each
-__device__ __forceinline__ float q4_dot(const uint4& nib, const float4* xl, const float4* xh) {
+// sum over half a Q4 block of q_e * x_e: nib = the block's 16 nibble bytes (byte k: low nibble = element k, high
+// nibble = element 16 + k); H = 0: elements 0..15 (low nibbles), H = 1: elements 16..31; xh = those 16 values of x
+template <int H>
+__device__ __forceinline__ float q4_dot_half(const uint4& nib, const float (&xh)[16]) {
   const uint32_t wds[4] = {nib.x, nib.y, nib.z, nib.w};
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t lo = wds[k] & 0x0F0F0F0Fu, hi = (wds[k] >> 4) & 0x0F0F0F0Fu;
-    s = fmaf((float)(lo & 0xFF), xl[k].x, s);
-    s = fmaf((float)((lo >> 8) & 0xFF), xl[k].y, s);
-    s = fmaf((float)((lo >> 16) & 0xFF), xl[k].z, s);
-    s = fmaf((float)(lo >> 24), xl[k].w, s);
-    s = fmaf((float)(hi & 0xFF), xh[k].x, s);
-    s = fmaf((float)((hi >> 8) & 0xFF), xh[k].y, s);
-    s = fmaf((float)((hi >> 16) & 0xFF), xh[k].z, s);
-    s = fmaf((float)(hi >> 24), xh[k].w, s);
+    const uint32_t q = (wds[k] >> (4 * H)) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) s = fmaf((float)((q >> (8 * b)) & 0xFF), xh[4 * k + b], s);
   }
   return s;
 }
@@ -187,7 +198,7 @@ __device__ __forceinline__ float q4_dot(const uint4& nib, const float4* xl, cons
 // Q4_0 form: gate/up rows as nibbles + block scales (the "- 8" folded out with per-block sums of x); thread t owns
 // half-block t of every W_downT row (8 nibble bytes = 16 columns, and the block scale) and carries sum(a * s) for
 // the "- 8" of its columns. NQ: Q4 blocks per lane of a row; D <= 32 * NT_F (one half-block per thread).
-template <int ACT, int NQ>
+template <int ACT, int NQ, int RPW>
 __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg, const _Float16* __restrict__ sg,
                                                     const float* __restrict__ bg, const uint4* __restrict__ qu,
                                                     const _Float16* __restrict__ su, const float* __restrict__ bu,
@@ -201,11 +212,17 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
   uint64_t* wl = lds64;                                                  // [nw] mask words
   int* roff = reinterpret_cast<int*>(wl + ((nw + 1) & ~1));              // [NT_F] range offsets
   int* tmp = roff + NT_F;                                                // [NT_F/64 + 1] scan scratch
-  int* ids = tmp + NT_F / 64 + 4;                                        // [FW] ids of the pass (-1: none)
-  float* av = reinterpret_cast<float*>(ids + FW);                        // [FW] activations of the pass
-  float* red = av + FW;                                                  // [2 * FW] normalisation scratch
+  constexpr int NS = FW * RPW;                                           // rows (slots) per pass
+  float* av = reinterpret_cast<float*>(tmp + NT_F / 64 + 4);             // [NS] activations of the pass
+  float* red = av + NS;                                                  // [2 * FW] normalisation scratch
   float* xs = red + 2 * FW + 4;                                          // [D] x (16-byte aligned)
   float* xsum = xs + D;                                                  // [D / 32] per-block sums of x
+  const int nch_row = (nblk + 63) >> 6;                // 1 kB pieces (64 lanes x 16 bytes) of a nibble row
+  const uint32_t rstride = (uint32_t)nch_row * 1024u;
+  int* bids = reinterpret_cast<int*>(xsum + nblk);                      // [ceil(F / G)] the block's row ids
+  uint8_t* sdn = reinterpret_cast<uint8_t*>(lds64) +   // [NS][rstride] the pass's W_downT nibble rows
+                 ((reinterpret_cast<uintptr_t>(bids + (F + gridDim.x - 1) / gridDim.x) -
+                   reinterpret_cast<uintptr_t>(lds64) + 15) & ~(uintptr_t)15);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n4 = D >> 2;
   constexpr int XPT = (512 * NQ + NT_F - 1) / NT_F;    // float4 of x per thread: D / 4 <= 512 * NQ
@@ -233,88 +250,144 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   float sas = 0.f;
 
-  bool first = true;
-  for (int k0 = blockIdx.x; k0 < n; k0 += G * FW) {    // passes (block-uniform)
-    const int i = k0 + G * w;
-    const bool have = i < n;                           // wave-uniform
-    int id = -1;
-    uint4 nu[NQ], ng[NQ];
-    float fu[NQ], fg[NQ];
-    float bias = 0.f;
-    if (have) {
-      id = locate(wl, roff, NT_F, 1, nw, F, i);
+  // x: normalised, staged in LDS and summed per Q4 block during the first pass, while its rows are in flight
+  constexpr bool EARLY_X = false;
+  // x is stored transposed, xs[e * nblk + c] = x[32 c + e]: the lane that owns Q4 block c reads its 32 values as
+  // words c, c + nblk, ..., so a wave reads 64 consecutive words per step (no LDS bank conflicts)
+  auto stage_x = [&]() {
+    if (x_norm) block_norm_regs<NT_F, XPT>(xv4, n4, x0, red);
+#pragma unroll
+    for (int k = 0; k < XPT; ++k) {
+      const int i = k * NT_F + (int)threadIdx.x;       // float4 i: elements 4 i .. 4 i + 3 of block i / 8
+      if (i < n4) {
+        float* d = xs + (4 * i & 31) * nblk + (i >> 3);
+        d[0] = xv4[k].x; d[nblk] = xv4[k].y; d[2 * nblk] = xv4[k].z; d[3 * nblk] = xv4[k].w;
+      }
+    }
+    lds_barrier();
+    for (int t = threadIdx.x; t < nblk; t += NT_F) {
+      float v = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; e += 4)
+        v += (xs[e * nblk + t] + xs[(e + 1) * nblk + t]) + (xs[(e + 2) * nblk + t] + xs[(e + 3) * nblk + t]);
+      xsum[t] = v;
+    }
+    lds_barrier();
+  };
+  if (EARLY_X) stage_x();
+  // A pass takes NS = 8 * RPW rows: slot s (dense index k0 + G * s) runs on wave s % 8 as its row s / 8, so a
+  // block with up to NS rows reads them all in one round trip. The wave of a slot also issues the loads of the
+  // slot's W_downT nibble row straight into LDS (no registers), in the same round trip as its gate/up rows.
+  const int wv = __builtin_amdgcn_readfirstlane(w);   // wave index, in a scalar register (LDS load bases)
+  // the block's rows: dense indices blk + G * k, k < nrow, their ids in LDS (one rank select per mask word)
+  const int blk = blockIdx.x;
+  const int nrow = (n - blk + G - 1) / G;
+  block_row_ids(wl, roff, nw, blk, G, bids);
+  lds_barrier();
+  bool first = !EARLY_X;
+  for (int k0 = 0; k0 < nrow; k0 += NS) {              // passes (block-uniform); row k0 + s in slot s
+    int idr[RPW];
+    uint4 nu[RPW][NQ], ng[RPW][NQ];
+    _Float16 fu[RPW][NQ], fg[RPW][NQ];                 // (fp16 kept as loaded: two per register)
+    float bias[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int kr = k0 + w + FW * r;
+      const bool have = kr < nrow;                     // wave-uniform
+      idr[r] = have ? bids[kr] : -1;
+      const uint32_t row = (uint32_t)(have ? idr[r] : 0);
 #pragma unroll
       for (int m = 0; m < NQ; ++m) {
         const int c = lane + 64 * m;
-        const bool ok = c < nblk;
-        const uint32_t o = (uint32_t)id * nblk + c;
-        nu[m] = bqu.ld16(boff(ok, o * 16u));
-        fu[m] = bsu.ldh(boff(ok, o * 2u));
+        const bool ok = have && c < nblk;
+        const uint32_t o = row * nblk + c;
+        nu[r][m] = bqu.ld16(boff(ok, o * 16u));
+        fu[r][m] = bsu.ldh16(boff(ok, o * 2u));
         if (ACT == 1) {
-          ng[m] = bqg.ld16(boff(ok, o * 16u));
-          fg[m] = bsg.ldh(boff(ok, o * 2u));
+          ng[r][m] = bqg.ld16(boff(ok, o * 16u));
+          fg[r][m] = bsg.ldh16(boff(ok, o * 2u));
         }
       }
-      bias = bbias.ldf((uint32_t)id * 4u);
+      bias[r] = bbias.ldf(boff(have, row * 4u));
+      uint8_t* dst = sdn + (uint32_t)(wv + FW * r) * rstride;
+      for (int c = 0; c < nch_row; ++c) {              // the slot's nibble row, 1 kB per load
+        const uint32_t o = (uint32_t)c * 1024u + (uint32_t)lane * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            bqd.r, (__attribute__((address_space(3))) void*)(dst + c * 1024), 16,
+            boff(have && o < (uint32_t)nblk * 16u, row * (uint32_t)nblk * 16u + o), 0, 0, 0);
+      }
     }
-    if (lane == 0) ids[w] = id;
-    lds_barrier();
-    uint2 dn[FW];
-    float ds[FW];
+    _Float16 ds[NS];                                   // this thread's block scale of every W_downT row
 #pragma unroll
-    for (int j = 0; j < FW; ++j) {
-      const int idj = ids[j];
+    for (int j = 0; j < NS; ++j) {
+      const int idj = k0 + j < nrow ? bids[k0 + j] : -1;
       const bool ok = idj >= 0 && hok;
       const uint32_t row = (uint32_t)(idj >= 0 ? idj : 0);
-      dn[j] = bqd.ld8(boff(ok, row * (uint32_t)nblk * 16u + hoff));
-      ds[j] = bsd.ldh(boff(ok, (row * nblk + (hb >> 1)) * 2u));
+      ds[j] = bsd.ldh16(boff(ok, (row * nblk + (hb >> 1)) * 2u));
     }
-    if (first) {                                       // x: normalised, staged and summed per Q4 block
-      if (x_norm) block_norm_regs<NT_F, XPT>(xv4, n4, x0, red);
-      stage_store<NT_F, XPT>(xs, n4, xv4);
-      lds_barrier();
-      for (int t = threadIdx.x; t < nblk; t += NT_F) {
-        const float4* p = reinterpret_cast<const float4*>(xs + 32 * t);
-        float v = 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v += (p[k].x + p[k].y) + (p[k].z + p[k].w);
-        xsum[t] = v;
-      }
-      lds_barrier();
+    if (first) {
+      stage_x();
       first = false;
     }
-    if (have) {
-      float au = 0.f, ag = 0.f;
+    // dot products of the wave's rows: Q4 block m of the lane outer (its 32 values of x read once from LDS for all
+    // of the wave's rows), rows inner
+    float au[RPW], ag[RPW];
 #pragma unroll
-      for (int m = 0; m < NQ; ++m) {
-        const int c = lane + 64 * m;
-        if (c < nblk) {
-          const float4* xl = reinterpret_cast<const float4*>(xs + 32 * c);
-          const float xsb = xsum[c];
-          au = fmaf(fu[m], q4_dot(nu[m], xl, xl + 4) - 8.f * xsb, au);
-          if (ACT == 1) ag = fmaf(fg[m], q4_dot(ng[m], xl, xl + 4) - 8.f * xsb, ag);
+    for (int r = 0; r < RPW; ++r) au[r] = ag[r] = 0.f;
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      const int c = lane + 64 * m;
+      if (c < nblk) {
+        float du[RPW], dg[RPW];                        // sum q_e x_e over the block, by row
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) du[r] = dg[r] = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {                  // the block's two halves, 16 values of x at a time
+          float xh[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) xh[e] = xs[(16 * h + e) * nblk + c];
+#pragma unroll
+          for (int r = 0; r < RPW; ++r) {
+            if (idr[r] >= 0) {                         // wave-uniform
+              du[r] += h ? q4_dot_half<1>(nu[r][m], xh) : q4_dot_half<0>(nu[r][m], xh);
+              if (ACT == 1) dg[r] += h ? q4_dot_half<1>(ng[r][m], xh) : q4_dot_half<0>(ng[r][m], xh);
+            }
+          }
+        }
+        const float xsb = xsum[c];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          au[r] = fmaf((float)fu[r][m], du[r] - 8.f * xsb, au[r]);
+          if (ACT == 1) ag[r] = fmaf((float)fg[r][m], dg[r] - 8.f * xsb, ag[r]);
         }
       }
-      const float u = wave_sum(au);
-      float a;
-      if (ACT == 1) {
-        const float g = wave_sum(ag) + bias;
-        a = fmaxf(g, 0.f) * u;
-      } else {
-        a = fmaxf(u + bias, 0.f);
-      }
-      if (lane == 0) { av[w] = a; active[i] = id; }
-    } else if (lane == 0) {
-      av[w] = 0.f;
     }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      if (idr[r] >= 0) {                               // wave-uniform
+        const float u = wave_sum(au[r]);
+        float a;
+        if (ACT == 1) {
+          const float g = wave_sum(ag[r]) + bias[r];
+          a = fmaxf(g, 0.f) * u;
+        } else {
+          a = fmaxf(u + bias[r], 0.f);
+        }
+        if (lane == 0) { av[w + FW * r] = a; active[blk + G * (k0 + w + FW * r)] = idr[r]; }
+      } else if (lane == 0) {
+        av[w + FW * r] = 0.f;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);                     // this wave's nibble rows have landed in LDS
     lds_barrier();
-    // column gather of the pass, rows in wave order: element e < 8 is low nibble e of the half (block element
+    // column gather of the pass, rows in slot order: element e < 8 is low nibble e of the half (block element
     // 8 * half + e), e >= 8 the high nibble (block element 16 + 8 * half + e - 8)
 #pragma unroll
-    for (int j = 0; j < FW; ++j) {
-      const float as_ = av[j] * ds[j];
+    for (int j = 0; j < NS; ++j) {
+      const float as_ = av[j] * (float)ds[j];
       sas += as_;
-      const uint32_t wds[2] = {dn[j].x, dn[j].y};
+      const uint2 dj = hok ? *reinterpret_cast<const uint2*>(sdn + (uint32_t)j * rstride + hoff) : make_uint2(0u, 0u);
+      const uint32_t wds[2] = {dj.x, dj.y};
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const uint32_t lo = wds[k] & 0x0F0F0F0Fu, hi = (wds[k] >> 4) & 0x0F0F0F0Fu;
@@ -349,18 +422,20 @@ __global__ __launch_bounds__(NT_S) void k_sum_rows(const float* __restrict__ par
   __shared__ float red[SG][SC];
   const int c = threadIdx.x % SC, g = threadIdx.x / SC;
   const int col = blockIdx.x * SC + c;
-  const int nb = min(G, max(*n_active, 0));            // blocks that wrote a partial
   const Buf bp(part, (uint32_t)G * (uint32_t)D * 4u);
-  // every load of the thread is issued before the first add (group g takes blocks g, g + SG, ...)
+  // every load of the thread, n_active included, is issued before the first use (group g takes blocks g,
+  // g + SG, ...); partials of blocks that wrote none are loaded too and dropped by a select afterwards, so the
+  // partial loads need not wait for n_active
   float v[SPG];
 #pragma unroll
   for (int k = 0; k < SPG; ++k) {
     const int b = g + SG * k;
-    v[k] = bp.ldf(boff(b < nb && col < D, ((uint32_t)b * D + col) * 4u));
+    v[k] = bp.ldf(boff(b < G && col < D, ((uint32_t)b * D + col) * 4u));
   }
+  const int nb = min(G, max(*n_active, 0));            // blocks that wrote a partial
   float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < SPG; ++k) s += v[k];
+  for (int k = 0; k < SPG; ++k) s += (g + SG * k < nb) ? v[k] : 0.f;
   red[g][c] = s;
   __syncthreads();
   if (g == 0 && col < D) {
@@ -376,8 +451,9 @@ hipError_t launch_fused(const void* Wg, const float* bg, const void* Wu, const f
                         const float* x, int x_norm, int D, int F, const uint64_t* mask, int32_t* active,
                         int32_t* n_active, float* part, int G, float* y, hipStream_t st) {
   const int nw = (F + 63) / 64;
-  const size_t lds = (size_t)((nw + 1) & ~1) * 8 + (NT_F + NT_F / 64 + 4 + FW) * sizeof(int) +
-                     (FW + 2 * FW + 4 + (size_t)D) * sizeof(float) + 16;
+  if (G < 64) return hipErrorInvalidValue;            // one owned row per mask word at most
+  const size_t lds = (size_t)((nw + 1) & ~1) * 8 + (NT_F + NT_F / 64 + 4) * sizeof(int) +
+                     (FW + 2 * FW + 4 + (size_t)D) * sizeof(float) + ((size_t)(F + G - 1) / G) * sizeof(int) + 16;
   static size_t avail = 0;
   if (!avail) {
     hipError_t ea = allow_dynamic_lds((const void*)k_fused1<ACT, NCH, DCH>, &avail);
@@ -408,21 +484,25 @@ hipError_t dispatch_fused(const void* Wg, const float* bg, const void* Wu, const
 #undef FU
 }
 
-template <int ACT, int NQ>
+template <int ACT, int NQ, int RPW>
 hipError_t launch_fused_q4(const uint8_t* qg, const void* sg, const float* bg, const uint8_t* qu, const void* su,
                            const float* bu, const uint8_t* qd, const void* sd, const float* x, int x_norm, int D, int F,
                            const uint64_t* mask, int32_t* active, int32_t* n_active, float* part, int G, float* y,
                            hipStream_t st) {
   const int nw = (F + 63) / 64;
-  const size_t lds = (size_t)((nw + 1) & ~1) * 8 + (NT_F + NT_F / 64 + 4 + FW) * sizeof(int) +
-                     (FW + 2 * FW + 4 + (size_t)D + (size_t)D / 32) * sizeof(float) + 16;
+  constexpr int NS = FW * RPW;
+  if (G < 64) return hipErrorInvalidValue;            // one owned row per mask word at most
+  const size_t nblk = (size_t)D / 32;
+  const size_t lds = (size_t)((nw + 1) & ~1) * 8 + (NT_F + NT_F / 64 + 4) * sizeof(int) +
+                     (NS + 2 * FW + 4 + (size_t)D + nblk) * sizeof(float) + ((size_t)(F + G - 1) / G) * sizeof(int) +
+                     16 + (size_t)NS * ((nblk + 63) / 64) * 1024 + 16;   // + the pass's nibble rows
   static size_t avail = 0;
   if (!avail) {
-    hipError_t ea = allow_dynamic_lds((const void*)k_fused1_q4<ACT, NQ>, &avail);
+    hipError_t ea = allow_dynamic_lds((const void*)k_fused1_q4<ACT, NQ, RPW>, &avail);
     if (ea != hipSuccess) return ea;
   }
   if (lds > avail || G > SG * SPG) return hipErrorInvalidValue;
-  SFFN_LAUNCH(2, (k_fused1_q4<ACT, NQ>), dim3(G), dim3(NT_F), lds, st, (const uint4*)qg, (const _Float16*)sg, bg,
+  SFFN_LAUNCH(2, (k_fused1_q4<ACT, NQ, RPW>), dim3(G), dim3(NT_F), lds, st, (const uint4*)qg, (const _Float16*)sg, bg,
               (const uint4*)qu, (const _Float16*)su, bu, qd, (const _Float16*)sd, x, x_norm, D, F, mask, active,
               n_active, part);
   hipError_t e = hipGetLastError();
@@ -438,7 +518,7 @@ hipError_t sffn_launch_fused_q4(int act, const uint8_t* qg, const void* sg, cons
                                 int x_norm, int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active,
                                 float* part, int G, float* y, hipStream_t st) {
   const int nq = (D / 32 + 63) / 64;   // Q4 blocks per lane of a row
-#define FQ(A, N) return launch_fused_q4<A, N>(qg, sg, bg, qu, su, bu, qd, sd, x, x_norm, D, F, mask, active, n_active, part, G, y, st)
+#define FQ(A, N) return launch_fused_q4<A, N, SFFN_Q4_FUSED_RPW>(qg, sg, bg, qu, su, bu, qd, sd, x, x_norm, D, F, mask, active, n_active, part, G, y, st)
   if (act == 1) {
     if (nq <= 1) FQ(1, 1);
     if (nq <= 2) FQ(1, 2);
