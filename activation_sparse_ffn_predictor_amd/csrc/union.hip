@@ -59,31 +59,25 @@ __device__ __forceinline__ half8 q4_to_half8(const uint2& p, int j) {
   return h;
 }
 
-constexpr int NTN = 256;
+constexpr int NTN = 512;
 
-// per-token normalisation (centre, unit variance): one block per token
+// per-token normalisation (centre, unit variance): one block per token; every load of the token is issued at
+// once, the statistics are single-pass about x[0] (block_norm_regs) and the result is written from registers
+template <int XPT>
 __global__ __launch_bounds__(NTN) void k_norm_tokens(const float* __restrict__ x, int D, float* __restrict__ xn) {
   __shared__ float red[2 * (NTN / 64)];
+  const int n4 = D >> 2;
   const float* xb = x + (size_t)blockIdx.x * D;
-  float* ob = xn + (size_t)blockIdx.x * D;
-  const int w = threadIdx.x >> 6;
-  float s = 0.f;
-  for (int i = threadIdx.x; i < D; i += NTN) s += xb[i];
-  s = wave_sum(s);
-  if ((threadIdx.x & 63) == 0) red[w] = s;
-  __syncthreads();
-  float t = 0.f;
-  for (int i = 0; i < NTN / 64; ++i) t += red[i];
-  const float mu = t / (float)D;
-  float q = 0.f;
-  for (int i = threadIdx.x; i < D; i += NTN) { const float d = xb[i] - mu; q = fmaf(d, d, q); }
-  q = wave_sum(q);
-  if ((threadIdx.x & 63) == 0) red[NTN / 64 + w] = q;
-  __syncthreads();
-  float tq = 0.f;
-  for (int i = 0; i < NTN / 64; ++i) tq += red[NTN / 64 + i];
-  const float sc = 1.0f / sqrtf(tq / (float)D + NORM_EPS);
-  for (int i = threadIdx.x; i < D; i += NTN) ob[i] = (xb[i] - mu) * sc;
+  float4 v[XPT];
+  stage_load<NTN, XPT>(xb, n4, v);
+  const float x0 = xb[0];
+  block_norm_regs<NTN, XPT>(v, n4, x0, red);
+  float4* ob = reinterpret_cast<float4*>(xn + (size_t)blockIdx.x * D);
+#pragma unroll
+  for (int k = 0; k < XPT; ++k) {
+    const int i = k * NTN + (int)threadIdx.x;
+    if (i < n4) ob[i] = v[k];
+  }
 }
 
 // B operand for token tile t at k block kb: lane l reads x[t*16 + l%16][32 kb + 8 (l/16) .. +8] (fp32) and splits it
@@ -251,19 +245,6 @@ __global__ __launch_bounds__(256) void k_mt_z(const uint4* __restrict__ P2, cons
                        ((uint64_t)bits16[3] << 48);
     mask[blockIdx.x] = m;
   }
-}
-
-// the i-th set bit of a 64-bit word (i < popcount), by halving
-__device__ __forceinline__ int select_bit(uint64_t w, int i) {
-  int pos = 0;
-#pragma unroll
-  for (int half = 32; half >= 1; half >>= 1) {
-    const uint64_t lowmask = (half == 64) ? ~0ull : ((1ull << half) - 1ull);
-    const int c = __popcll(w & lowmask);
-    if (i >= c) { i -= c; w >>= half; pos += half; }
-    else w &= lowmask;
-  }
-  return pos;
 }
 
 // per-lane version of locate: stored id of dense index i (i < total)
@@ -655,7 +636,12 @@ hipError_t down_mt(const void* Wd, const void* Sd, const int32_t* active, const 
 
 // ---- entry points used by the C ABI for B > 1
 hipError_t sffn_launch_norm_tokens(const float* x, int B, int D, float* xn, hipStream_t st) {
-  hipLaunchKernelGGL(k_norm_tokens, dim3(B), dim3(NTN), 0, st, x, D, xn);
+  const int xpt = (D / 4 + NTN - 1) / NTN;
+  if (xpt <= 1) hipLaunchKernelGGL(k_norm_tokens<1>, dim3(B), dim3(NTN), 0, st, x, D, xn);
+  else if (xpt <= 2) hipLaunchKernelGGL(k_norm_tokens<2>, dim3(B), dim3(NTN), 0, st, x, D, xn);
+  else if (xpt <= 4) hipLaunchKernelGGL(k_norm_tokens<4>, dim3(B), dim3(NTN), 0, st, x, D, xn);
+  else if (xpt <= 8) hipLaunchKernelGGL(k_norm_tokens<8>, dim3(B), dim3(NTN), 0, st, x, D, xn);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
