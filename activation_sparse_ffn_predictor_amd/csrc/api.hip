@@ -223,6 +223,10 @@ int sffn_predict(const void* P1, const void* P2, const float* c, const float* x,
   hipError_t e;
   if (B == 1) {
     e = sffn_launch_predict(P1, P2, c, x, x_norm, B, D, F, r, tau, mask, logits, h, st);
+  } else if (B <= 8) {
+    // a few tokens: h in one kernel (each P1 row read once with every token, normalisation folded in), then z
+    e = sffn_launch_predict_hb(P1, x, x_norm, B, D, r, h, st);
+    if (e == hipSuccess) e = sffn_launch_predict_mt(P1, P2, c, x, B, D, F, r, tau, mask, logits, h, nullptr, 0, st);
   } else {
     const float* xin = x;
     e = hipSuccess;

@@ -13,17 +13,41 @@ constexpr float NORM_EPS = 1e-6f;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float8v __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+// v from another lane of the same 16-lane row, by a DPP control (VALU latency, no LDS crossbar): 0xB1 swaps lane
+// pairs, 0x4E swaps pairs of pairs, 0x141 mirrors each half row (lane i <- 7 - i), 0x140 mirrors the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// sum over each aligned 16-lane row; every lane of the row gets it
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
   return v;
+}
+
+// sum over the wave; every lane gets it (row sums by DPP, then the four rows read as scalars)
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // sum over aligned groups of G lanes (G a power of two <= 64); every lane of the group gets the sum
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  if (G >= 2) v += dpp_f<0xB1>(v);
+  if (G >= 4) v += dpp_f<0x4E>(v);
+  if (G >= 8) v += dpp_f<0x141>(v);
+  if (G >= 16) v += dpp_f<0x140>(v);
+  if (G >= 32) v += __shfl_xor(v, 16, WAVE);
+  if (G >= 64) v += __shfl_xor(v, 32, WAVE);
   return v;
 }
 
@@ -333,6 +357,8 @@ bool sffn_prof_events(int kid, hipEvent_t* start, hipEvent_t* stop);
 // ---- launchers (host side), defined in the kernel files; return hipError_t of the launch
 hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D,
                                int F, int r, float tau, uint64_t* mask, float* logits, float* hbuf, hipStream_t st);
+hipError_t sffn_launch_predict_hb(const void* P1, const float* x, int x_norm, int B, int D, int r, float* hbuf,
+                                  hipStream_t st);
 hipError_t sffn_launch_forward(int act, const void* Wg, const float* bg, const void* Wu, const float* bu,
                                const void* WdT, const float* x, int x_norm, int B, int D, int F, const uint64_t* mask,
                                int32_t* active, int32_t* n_active, float* y, float* abuf, hipStream_t st);

@@ -92,6 +92,97 @@ __global__ __launch_bounds__(NTH) void k_pred_h(const uint4* __restrict__ P1, co
   }
 }
 
+// Kernel 1 for a few tokens (k_pred_hb, 2 <= B <= 8): one 512-thread block per row of P1; the row is read once
+// and every token's x with it. Tokens are taken TB at a time (TB = 8 when D <= 8192: one round trip); per token
+// the same four sums as k_pred_h, reduced together. h[b][j] is complete: no partial sums, no separate
+// normalisation of x.
+constexpr int NTB = 512;
+
+template <int NCH, int TB>
+__global__ __launch_bounds__(NTB) void k_pred_hb(const uint4* __restrict__ P1, const float* __restrict__ x,
+                                                 int x_norm, int B, int D, int r, float* __restrict__ h) {
+  constexpr int NV = 3 * TB + 1;                       // per token: sum p x', sum x', sum x'^2; then sum p
+  __shared__ float red[NV][NTB / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = blockIdx.x;
+  const int nc = D >> 3;
+  const Buf bp(P1, (uint32_t)r * (uint32_t)D * 2u);
+  const Buf bx(x, (uint32_t)B * (uint32_t)D * 4u);
+  uint4 wv[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + NTB * i;
+    wv[i] = bp.ld16(boff(c < nc, ((uint32_t)j * nc + c) * 16u));
+  }
+  for (int b0 = 0; b0 < B; b0 += TB) {                 // token groups (block-uniform)
+    // x of the group's tokens and their first elements (the shifts), all issued before the first use
+    float4 xr[TB][NCH][2];
+    float x0[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const bool okt = b0 + t < B;
+      const uint32_t tb = (uint32_t)(b0 + t) * (uint32_t)D * 4u;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = threadIdx.x + NTB * i;
+        xr[t][i][0] = bx.ldf4(boff(okt && c < nc, tb + 32u * c));
+        xr[t][i][1] = bx.ldf4(boff(okt && c < nc, tb + 32u * c + 16u));
+      }
+      x0[t] = bx.ldf(boff(okt && x_norm != 0, tb));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = threadIdx.x + NTB * i;
+      if (c < nc) {
+        float pf[8];
+        f16x8_to_f32(wv[i], pf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[3 * TB] += pf[e];
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          const float xv[8] = {xr[t][i][0].x, xr[t][i][0].y, xr[t][i][0].z, xr[t][i][0].w,
+                               xr[t][i][1].x, xr[t][i][1].y, xr[t][i][1].z, xr[t][i][1].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float d = xv[e] - x0[t];
+            v[3 * t] = fmaf(pf[e], d, v[3 * t]);
+            v[3 * t + 1] += d;
+            v[3 * t + 2] = fmaf(d, d, v[3 * t + 2]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (k % 3 != 0 && !x_norm) continue;             // the statistics and sum p only when x is normalised
+      v[k] = wave_sum(v[k]);
+      if (lane == 0) red[k][w] = v[k];
+    }
+    __syncthreads();
+    if (threadIdx.x < TB && b0 + (int)threadIdx.x < B) {
+      const int t = threadIdx.x;
+      float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ww = 0; ww < NTB / 64; ++ww) {
+        s[0] += red[3 * t][ww];
+        if (x_norm) { s[1] += red[3 * t + 1][ww]; s[2] += red[3 * t + 2][ww]; s[3] += red[3 * TB][ww]; }
+      }
+      float hv = s[0];
+      if (x_norm) {
+        const float mu = s[1] / (float)D;
+        const float var = fmaxf(s[2] / (float)D - mu * mu, 0.f);
+        hv = (s[0] - mu * s[3]) / sqrtf(var + NORM_EPS);
+      }
+      h[(size_t)(b0 + t) * r + j] = hv;
+    }
+    __syncthreads();                                   // red is reused by the next token group
+  }
+}
+
 // LPR lanes per P2 row (power of two, 8..64), ROUNDS chunk rounds per row (1 or 2). One token (larger batches
 // take the matrix-core kernels).
 template <int LPR, int ROUNDS>
@@ -163,6 +254,12 @@ hipError_t launch_h(const void* P1, const float* x, int x_norm, int B, int D, in
   return hipGetLastError();
 }
 
+template <int NCH, int TB>
+hipError_t launch_hb(const void* P1, const float* x, int x_norm, int B, int D, int r, float* h, hipStream_t st) {
+  SFFN_LAUNCH(0, (k_pred_hb<NCH, TB>), dim3(r), dim3(NTB), 0, st, (const uint4*)P1, x, x_norm, B, D, r, h);
+  return hipGetLastError();
+}
+
 template <int LPR, int ROUNDS>
 hipError_t launch_z(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, uint64_t* mask,
                     float* logits, hipStream_t st) {
@@ -208,4 +305,14 @@ hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, c
     case 6402: return launch_z<64, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Stage 1 for 2 <= B <= 8 tokens: h[b][j] (fp32, [B][r]) with the optional per-token normalisation folded in.
+hipError_t sffn_launch_predict_hb(const void* P1, const float* x, int x_norm, int B, int D, int r, float* hbuf,
+                                  hipStream_t st) {
+  if (B < 2 || B > 8) return hipErrorInvalidValue;
+  const int nch = (D / 8 + NTB - 1) / NTB;   // 16-byte chunks per thread (D <= 16384: at most 4)
+  if (nch <= 1) return launch_hb<1, 8>(P1, x, x_norm, B, D, r, hbuf, st);
+  if (nch <= 2) return launch_hb<2, 8>(P1, x, x_norm, B, D, r, hbuf, st);
+  return launch_hb<4, 4>(P1, x, x_norm, B, D, r, hbuf, st);
 }

@@ -582,13 +582,16 @@ __global__ void k_sum_parts(const float* __restrict__ part, int KS, int n, float
 template <int NTT>
 hipError_t predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F, int r,
                       float tau, uint64_t* mask, float* logits, float* hbuf, float* hpart, int KSH, hipStream_t st) {
-  SFFN_LAUNCH(0, k_mt_h<NTT>, dim3((r + 15) / 16, KSH), dim3(NTK), 0, st, (const uint4*)P1, x, B, D, r, hpart);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nh = B * r;
-  hipLaunchKernelGGL(k_sum_parts, dim3((nh + 255) / 256), dim3(256), 0, st, hpart, KSH, nh, hbuf);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (KSH > 0) {                                       // else hbuf holds h already
+    SFFN_LAUNCH(0, k_mt_h<NTT>, dim3((r + 15) / 16, KSH), dim3(NTK), 0, st, (const uint4*)P1, x, B, D, r, hpart);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nh = B * r;
+    hipLaunchKernelGGL(k_sum_parts, dim3((nh + 255) / 256), dim3(256), 0, st, hpart, KSH, nh, hbuf);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   SFFN_LAUNCH(1, k_mt_z<NTT>, dim3((F + 63) / 64), dim3(256), 0, st, (const uint4*)P2, c, hbuf, B, F, r, tau, mask,
               logits);
   return hipGetLastError();
