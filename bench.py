@@ -53,7 +53,7 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("common.h", "predict.hip", "forward.hip", "forward_q4.hip", "union.hip")
+KERNEL_SOURCES = ("common.h", "api.hip", "predict.hip", "forward.hip", "forward_q4.hip", "union.hip", "fused.hip")
 
 
 def kernel_source_hash() -> str:
