@@ -27,7 +27,10 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int MAX_B = 64, MAX_D = 16384, MAX_F = 1 << 22, MAX_R = 1024, MAX_BR = 32768;
-constexpr int MAX_BD_VALU = 16384;   // decode-batch kernels: B in {1, 2, 4, 8} with B * D <= this
+#ifndef SFFN_MAX_BD_VALU
+#define SFFN_MAX_BD_VALU 16384
+#endif
+constexpr int MAX_BD_VALU = SFFN_MAX_BD_VALU;   // decode-batch kernels (B in {2, 4, 8}): B * D <= this
 constexpr int MAX_F_UNION = 32768;   // union kernels compact the whole mask in one block
 constexpr int KS_MAX = 8;            // row splits of the union down projection
 constexpr int G_FUSED = 256;         // blocks (= partial sums of y) of the fused single-token forward
@@ -46,10 +49,14 @@ int check_common(int B, int D, int F) {
   return SFFN_OK;
 }
 
-// Which kernels serve a call: B == 1, and B in {2, 4, 8} with B * D <= 16384, take the decode kernels (x staged
-// once per block in LDS); every other batch takes the union kernels on the matrix cores.
-bool decode_batch(int B, int D) {
-  return B == 1 || ((B == 2 || B == 4 || B == 8) && (size_t)B * D <= MAX_BD_VALU);
+// Which kernels serve a call: B == 1 and B == 2 (with B * D <= 16384) take the decode kernels (x staged once per
+// block in LDS); so do B in {4, 8} with B * D <= 16384 when F is too large for the union kernels' one-workgroup
+// compaction. Every other batch takes the union kernels on the matrix cores, which measured faster from B = 4 on
+// (7B shape: 2667 against 2218 tokens/s at B = 4) and slower at B = 2 (1465 against 1624).
+bool decode_batch(int B, int D, int F) {
+  if (B == 1) return true;
+  if ((size_t)B * D > MAX_BD_VALU) return false;
+  return B == 2 || ((B == 4 || B == 8) && F > MAX_F_UNION);
 }
 
 // Row splits of the union down projection: enough blocks of 128 columns x KS splits to cover the chip twice.
@@ -76,7 +83,7 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 }
 
 int check_union(int B, int D, int F) {
-  if (!decode_batch(B, D) && F > MAX_F_UNION)
+  if (!decode_batch(B, D, F) && F > MAX_F_UNION)
     return fail(SFFN_ERR_SHAPE, "forward: B=%d with D=%d takes the union kernels, which need F <= %d (F=%d)", B, D,
                 MAX_F_UNION, F);
   return SFFN_OK;
@@ -201,7 +208,7 @@ int sffn_mask_words(int F) { return F < 1 ? 0 : (F + 63) / 64; }
 int sffn_forward_path(int act, int q4, int B, int D, int F) {
   if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU) return -1;
   if (sffn_fused_ok(B, D, F, act, q4 != 0)) return SFFN_PATH_FUSED;
-  return decode_batch(B, D) ? SFFN_PATH_DECODE : SFFN_PATH_UNION;
+  return decode_batch(B, D, F) ? SFFN_PATH_DECODE : SFFN_PATH_UNION;
 }
 
 int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F, int r,
@@ -267,7 +274,7 @@ int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W
   if (sffn_fused_ok(B, D, F, act, false)) {
     e = sffn_launch_fused(act, g ? W_gate : nullptr, g ? b_gate : nullptr, W_up, g ? nullptr : b_up, W_downT, x,
                           x_norm, D, F, mask, active, n_active, ws_part(ws, B, D, F), G_FUSED, y, st);
-  } else if (decode_batch(B, D)) {
+  } else if (decode_batch(B, D, F)) {
     e = sffn_launch_forward(act, g ? W_gate : nullptr, g ? b_gate : nullptr, W_up, g ? nullptr : b_up, W_downT, x,
                             x_norm, B, D, F, mask, active, n_active, y, ws_abuf(ws), st);
   } else {
@@ -303,7 +310,7 @@ int sffn_forward_q4(int act, sffn_q4 W_gate, const float* b_gate, sffn_q4 W_up, 
     e = sffn_launch_fused_q4(act, g ? W_gate.q : nullptr, g ? W_gate.s : nullptr, g ? b_gate : nullptr, W_up.q, W_up.s,
                              g ? nullptr : b_up, W_downT.q, W_downT.s, x, x_norm, D, F, mask, active, n_active,
                              ws_part(ws, B, D, F), G_FUSED, y, st);
-  } else if (decode_batch(B, D)) {
+  } else if (decode_batch(B, D, F)) {
     e = sffn_launch_forward_q4(act, g ? W_gate.q : nullptr, g ? W_gate.s : nullptr, g ? b_gate : nullptr, W_up.q,
                                W_up.s, g ? nullptr : b_up, W_downT.q, W_downT.s, x, x_norm, B, D, F, mask, active,
                                n_active, y, ws_abuf(ws), st);

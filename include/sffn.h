@@ -47,11 +47,12 @@
  * for Q4_0); 1 <= F <= 1<<22; 8 <= r <= 1024 with r % 8 == 0; B * r <= 32768;
  * every weight matrix and the B x F activations below 2 GiB.
  *
- * Batches. B == 1 (decode) and B in {2, 4, 8} with B * D <= 16384 run the
- * decode kernels (vector ALU, x staged once per block). Every other B > 1 runs
- * the union kernels on the matrix cores ("Neuron-aware operator": each active
- * row is read once for the whole batch); these compact the whole mask inside
- * one workgroup and take F <= 32768 in sffn_forward / sffn_forward_q4. fp32
+ * Batches. B == 1 (decode) and B == 2 with 2 * D <= 16384 run the decode
+ * kernels (vector ALU, x staged once per block); so do B in {4, 8} with
+ * B * D <= 16384 when F > 32768. Every other B > 1 runs the union kernels on
+ * the matrix cores ("Neuron-aware operator": each active row is read once for
+ * the whole batch); these compact the whole mask inside one workgroup and
+ * take F <= 32768 in sffn_forward / sffn_forward_q4. fp32
  * inputs enter the matrix cores as two fp16 halves (x = hi + lo), so the
  * batch results match the decode kernels' to within fp32 rounding.
  *
@@ -118,8 +119,8 @@ int sffn_mask_words(int F);
  *     one kernel gathers the gate/up rows, applies the activation and accumulates the W_downT rows into
  *     per-block partial sums of y; a second kernel adds the partials in fixed order (timing ids SFFN_K_ROWS and
  *     SFFN_K_COLS);
- *   SFFN_PATH_DECODE (other B == 1, and B in {2, 4, 8} with B * D <= 16384): row gather + activation, then the
- *     column gather;
+ *   SFFN_PATH_DECODE (other B == 1; B == 2 with 2 * D <= 16384; B in {4, 8} with B * D <= 16384 and
+ *     F > 32768): row gather + activation, then the column gather;
  *   SFFN_PATH_UNION (every other B): matrix-core kernels over the union mask.
  * Returns -1 for an unknown activation. */
 enum { SFFN_PATH_DECODE = 0, SFFN_PATH_FUSED = 1, SFFN_PATH_UNION = 2 };

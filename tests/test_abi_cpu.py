@@ -125,7 +125,11 @@ def test_forward_path_routing():
     assert _lib.forward_path("relu", False, 1, 64, 33000) == _lib.PATH_DECODE     # more than 32768 neurons
     assert _lib.forward_path("reglu", True, 1, 8192, 28672) == _lib.PATH_FUSED
     assert _lib.forward_path("reglu", True, 1, 16384, 2048) == _lib.PATH_DECODE   # Q4_0 rows wider than 8192
-    assert _lib.forward_path("reglu", False, 4, 4096, 11008) == _lib.PATH_DECODE
+    assert _lib.forward_path("reglu", False, 2, 4096, 11008) == _lib.PATH_DECODE
+    assert _lib.forward_path("reglu", False, 2, 16384, 1024) == _lib.PATH_UNION    # 2 D above 16384
+    assert _lib.forward_path("reglu", False, 4, 4096, 11008) == _lib.PATH_UNION
+    assert _lib.forward_path("reglu", False, 4, 4096, 40000) == _lib.PATH_DECODE   # F too large for the union
+    assert _lib.forward_path("relu", False, 8, 2048, 40000) == _lib.PATH_DECODE
     assert _lib.forward_path("reglu", False, 4, 5120, 13824) == _lib.PATH_UNION
     assert _lib.forward_path("relu", True, 64, 8192, 28672) == _lib.PATH_UNION
     assert _lib.lib().sffn_forward_path(5, 0, 1, 64, 64) == -1
