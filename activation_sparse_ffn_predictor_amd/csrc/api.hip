@@ -233,7 +233,10 @@ int sffn_predict(const void* P1, const void* P2, const float* c, const float* x,
   } else if (B <= 8) {
     // a few tokens: h in one kernel (each P1 row read once with every token, normalisation folded in), then z
     e = sffn_launch_predict_hb(P1, x, x_norm, B, D, r, h, st);
-    if (e == hipSuccess) e = sffn_launch_predict_mt(P1, P2, c, x, B, D, F, r, tau, mask, logits, h, nullptr, 0, st);
+    // z: vector-ALU kernel for up to 4 tokens, matrix-core kernel beyond (measured: equal at 4, faster at 8)
+    if (e == hipSuccess)
+      e = B <= 4 ? sffn_launch_predict_zb(P2, c, h, B, F, r, tau, mask, logits, st)
+                 : sffn_launch_predict_mt(P1, P2, c, x, B, D, F, r, tau, mask, logits, h, nullptr, 0, st);
   } else {
     const float* xin = x;
     e = hipSuccess;

@@ -359,6 +359,8 @@ hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, c
                                int F, int r, float tau, uint64_t* mask, float* logits, float* hbuf, hipStream_t st);
 hipError_t sffn_launch_predict_hb(const void* P1, const float* x, int x_norm, int B, int D, int r, float* hbuf,
                                   hipStream_t st);
+hipError_t sffn_launch_predict_zb(const void* P2, const float* c, const float* hbuf, int B, int F, int r, float tau,
+                                  uint64_t* mask, float* logits, hipStream_t st);
 hipError_t sffn_launch_forward(int act, const void* Wg, const float* bg, const void* Wu, const float* bu,
                                const void* WdT, const float* x, int x_norm, int B, int D, int F, const uint64_t* mask,
                                int32_t* active, int32_t* n_active, float* y, float* abuf, hipStream_t st);

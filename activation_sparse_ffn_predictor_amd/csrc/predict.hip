@@ -93,8 +93,9 @@ __global__ __launch_bounds__(NTH) void k_pred_h(const uint4* __restrict__ P1, co
 }
 
 // Kernel 1 for a few tokens (k_pred_hb, 2 <= B <= 8): one 512-thread block per row of P1; the row is read once
-// and every token's x with it. Tokens are taken TB at a time (TB = 8 when D <= 8192: one round trip); per token
-// the same four sums as k_pred_h, reduced together. h[b][j] is complete: no partial sums, no separate
+// and every token's x with it. Tokens are taken TB at a time (TB = the batch rounded up to 2, 4 or 8, at most 4
+// when D > 8192; a batch within one group costs one round trip); per token the same four sums as k_pred_h,
+// reduced together. h[b][j] is complete: no partial sums, no separate
 // normalisation of x.
 constexpr int NTB = 512;
 
@@ -248,6 +249,94 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
   if (lane == 0) reinterpret_cast<uint16_t*>(mask)[(size_t)blockIdx.x * 4 + w] = (uint16_t)bits;
 }
 
+// Kernel 2 for a few tokens (k_pred_zb, 2 <= B <= 4): the k_pred_z layout, with the tokens' h staged in LDS so that
+// each row of P2 is read once for all of them. Every token's logit is computed and stored; the mask bit is the OR
+// of the tokens' decisions (the union mask of the batch). P2 rows, h and the biases are issued together: one round
+// trip, then one block barrier for the LDS copy of h.
+template <int LPR, int ROUNDS, int TB>
+__global__ __launch_bounds__(NT) void k_pred_zb(const uint4* __restrict__ P2, const float* __restrict__ c,
+                                                const float* __restrict__ h, int B, int F, int r, float tau,
+                                                uint64_t* __restrict__ mask, float* __restrict__ logits) {
+  constexpr int RPI = 64 / LPR;
+  constexpr int RPW = 16;
+  constexpr int NI = RPW / RPI;
+  constexpr int RMAX = 8 * LPR * ROUNDS;               // h elements per token held in LDS (r <= RMAX)
+  constexpr int NHL = (TB * RMAX / 4 + NT - 1) / NT;   // float4 loads per thread for the LDS copy
+  __shared__ float4 hs4[TB * RMAX / 4];
+  const float* hs = reinterpret_cast<const float*>(hs4);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rsub = lane / LPR, csub = lane % LPR;
+  const int cpr = r >> 3;
+  const int base = blockIdx.x * 64 + w * RPW;
+
+  const Buf bp(P2, (uint32_t)F * (uint32_t)r * 2u);
+  const Buf bc(c ? (const void*)c : (const void*)P2, c ? (uint32_t)F * 4u : 0u);
+  const Buf bh(h, (uint32_t)B * (uint32_t)r * 4u);
+  uint4 wv[ROUNDS][NI];
+#pragma unroll
+  for (int q = 0; q < ROUNDS; ++q)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int k = base + i * RPI + rsub;
+      const int cc = q * LPR + csub;
+      wv[q][i] = bp.ld16(boff(k < F && cc < cpr, ((uint32_t)k * cpr + cc) * 16u));
+    }
+  float4 hl[NHL];
+#pragma unroll
+  for (int l = 0; l < NHL; ++l) {
+    const int e = (threadIdx.x + NT * l) * 4;          // LDS element: token e / RMAX, h index e % RMAX
+    const int t = e / RMAX, j = e % RMAX;
+    hl[l] = bh.ldf4(boff(t < B && j < r, ((uint32_t)t * r + j) * 4u));   // r % 8 == 0: j < r means j + 4 <= r
+  }
+  float cb[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int k = base + i * RPI + rsub;
+    cb[i] = bc.ldf(boff(k < F, (uint32_t)k * 4u));
+  }
+#pragma unroll
+  for (int l = 0; l < NHL; ++l)
+    if (threadIdx.x + NT * l < TB * RMAX / 4) hs4[threadIdx.x + NT * l] = hl[l];
+  __syncthreads();
+  bool any[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) any[i] = false;
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    if (t >= B) break;                                 // block-uniform
+    float acc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int q = 0; q < ROUNDS; ++q) {
+      const int cc = q * LPR + csub;                   // cc >= cpr: the P2 chunk read 0 and the LDS slot holds 0
+      const float4 h0 = *reinterpret_cast<const float4*>(hs + t * RMAX + 8 * cc);
+      const float4 h1 = *reinterpret_cast<const float4*>(hs + t * RMAX + 8 * cc + 4);
+      const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+      for (int i = 0; i < NI; ++i) acc[i] += dot8(wv[q][i], hv);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float s = group_sum<LPR>(acc[i]);
+      const int k = base + i * RPI + rsub;
+      const float z = s + cb[i];
+      if (logits && csub == 0 && k < F) logits[(size_t)t * F + k] = z;
+      any[i] = any[i] || z > tau;
+    }
+  }
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int k = base + i * RPI + rsub;
+    const unsigned long long bal = __ballot(csub == 0 && k < F && any[i]);
+#pragma unroll
+    for (int q = 0; q < RPI; ++q)
+      if ((bal >> (q * LPR)) & 1ull) bits |= 1u << (i * RPI + q);
+  }
+  if (lane == 0) reinterpret_cast<uint16_t*>(mask)[(size_t)blockIdx.x * 4 + w] = (uint16_t)bits;
+}
+
 template <int NCH>
 hipError_t launch_h(const void* P1, const float* x, int x_norm, int B, int D, int r, float* h, hipStream_t st) {
   SFFN_LAUNCH(0, k_pred_h<NCH>, dim3(r), dim3(NTH), 0, st, (const uint4*)P1, x, x_norm, D, r, h);
@@ -269,6 +358,48 @@ hipError_t launch_z(const void* P2, const float* c, const float* h, int B, int F
   return hipGetLastError();
 }
 
+template <int LPR, int ROUNDS, int TB>
+hipError_t launch_zb(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, uint64_t* mask,
+                     float* logits, hipStream_t st) {
+  SFFN_LAUNCH(1, (k_pred_zb<LPR, ROUNDS, TB>), dim3((F + 63) / 64), dim3(NT), 0, st, (const uint4*)P2, c, h, B, F, r,
+              tau, mask, logits);
+  return hipGetLastError();
+}
+
+// stage-2 shape for rank r: lanes per P2 row (8 .. SFFN_Z_LPR_MAX) and chunk rounds per lane, as 100 lpr + rounds
+int z_shape(int r) {
+  const int cpr = r / 8;
+  int lpr = 8;
+  while (lpr * 2 <= cpr && lpr < SFFN_Z_LPR_MAX) lpr *= 2;
+  int rounds = 1;
+  while (rounds * lpr < cpr) rounds *= 2;   // cpr <= 128: at most 16 rounds of 8 lanes
+  return lpr * 100 + rounds;
+}
+
+template <int TB>
+hipError_t dispatch_zb(const void* P2, const float* c, const float* h, int B, int F, int r, float tau,
+                       uint64_t* mask, float* logits, hipStream_t st) {
+#define ZB(L, R) return launch_zb<L, R, TB>(P2, c, h, B, F, r, tau, mask, logits, st)
+  switch (z_shape(r)) {
+    case 801: ZB(8, 1);
+    case 802: ZB(8, 2);
+    case 804: ZB(8, 4);
+    case 808: ZB(8, 8);
+    case 816: ZB(8, 16);
+    case 1601: ZB(16, 1);
+    case 1602: ZB(16, 2);
+    case 1604: ZB(16, 4);
+    case 1608: ZB(16, 8);
+    case 3201: ZB(32, 1);
+    case 3202: ZB(32, 2);
+    case 3204: ZB(32, 4);
+    case 6401: ZB(64, 1);
+    case 6402: ZB(64, 2);
+    default: return hipErrorInvalidValue;
+  }
+#undef ZB
+}
+
 }  // namespace
 
 hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D,
@@ -283,12 +414,7 @@ hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, c
   else if (nch <= 6) e = launch_h<6>(P1, x, x_norm, B, D, r, hbuf, st);
   else e = launch_h<8>(P1, x, x_norm, B, D, r, hbuf, st);
   if (e != hipSuccess) return e;
-  const int cpr = r / 8;
-  int lpr = 8;
-  while (lpr * 2 <= cpr && lpr < SFFN_Z_LPR_MAX) lpr *= 2;
-  int rounds = 1;
-  while (rounds * lpr < cpr) rounds *= 2;   // cpr <= 128: at most 16 rounds of 8 lanes
-  switch (lpr * 100 + rounds) {
+  switch (z_shape(r)) {
     case 801: return launch_z<8, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
     case 802: return launch_z<8, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
     case 804: return launch_z<8, 4>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
@@ -312,7 +438,25 @@ hipError_t sffn_launch_predict_hb(const void* P1, const float* x, int x_norm, in
                                   hipStream_t st) {
   if (B < 2 || B > 8) return hipErrorInvalidValue;
   const int nch = (D / 8 + NTB - 1) / NTB;   // 16-byte chunks per thread (D <= 16384: at most 4)
-  if (nch <= 1) return launch_hb<1, 8>(P1, x, x_norm, B, D, r, hbuf, st);
-  if (nch <= 2) return launch_hb<2, 8>(P1, x, x_norm, B, D, r, hbuf, st);
+  if (nch <= 1) {
+    if (B <= 2) return launch_hb<1, 2>(P1, x, x_norm, B, D, r, hbuf, st);
+    if (B <= 4) return launch_hb<1, 4>(P1, x, x_norm, B, D, r, hbuf, st);
+    return launch_hb<1, 8>(P1, x, x_norm, B, D, r, hbuf, st);
+  }
+  if (nch <= 2) {
+    if (B <= 2) return launch_hb<2, 2>(P1, x, x_norm, B, D, r, hbuf, st);
+    if (B <= 4) return launch_hb<2, 4>(P1, x, x_norm, B, D, r, hbuf, st);
+    return launch_hb<2, 8>(P1, x, x_norm, B, D, r, hbuf, st);
+  }
+  if (B <= 2) return launch_hb<4, 2>(P1, x, x_norm, B, D, r, hbuf, st);
   return launch_hb<4, 4>(P1, x, x_norm, B, D, r, hbuf, st);
+}
+
+// Stage 2 for 2 <= B <= 4 tokens: logits [B][F] (optional) and the union mask from h [B][r]. (At 8 tokens the
+// matrix-core kernel is the faster one.)
+hipError_t sffn_launch_predict_zb(const void* P2, const float* c, const float* hbuf, int B, int F, int r, float tau,
+                                  uint64_t* mask, float* logits, hipStream_t st) {
+  if (B < 2 || B > 4) return hipErrorInvalidValue;
+  if (B <= 2) return dispatch_zb<2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+  return dispatch_zb<4>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
 }

@@ -135,7 +135,8 @@ int sffn_forward_path(int act, int q4, int B, int D, int F);
  * (population) variance of x[b, :] -- the parameter-free normalisation between stacked layers, applied as the
  * input is loaded.
  * Outputs: mask (every word written, bits >= F zero); logits [B, F] fp32 if
- * non-NULL. Uses the workspace. Two kernels (three for B > 1 with x_norm: the tokens are normalised first). */
+ * non-NULL. Uses the workspace. Two kernels for B <= 8 (h, then z; a normalised input is normalised as it is
+ * loaded); for B > 8 three (partial h over shares of d, their sum, z), after a normalisation pass with x_norm. */
 int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F,
                  int r, float t, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream);
 

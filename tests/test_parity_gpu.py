@@ -111,6 +111,17 @@ def test_tiny_neuron_counts(gpu_ready, F, B):
         check(case, x, res, t=t)
 
 
+@pytest.mark.parametrize("r", [8, 136, 1024])
+@pytest.mark.parametrize("B", [1, 2, 5, 8])
+def test_predictor_rank_extremes(gpu_ready, r, B):
+    # every stage-2 shape class: one chunk round (r = 8), a ragged last round (r = 136), the largest rank
+    wl = small("c1", D=256, F=300, r=r, L=1, density=0.3)
+    case = make_case(wl, 0, gpu_ready)
+    x = _x(wl, B, 1)
+    say(f"[rank {r} B {B}]")
+    check(case, x, run_gpu(case, torch.from_numpy(x).to(gpu_ready)))
+
+
 @pytest.mark.parametrize("B", [1, 6])
 def test_minimum_d_q4(gpu_ready, B):
     wl = small("c5", D=32, F=200, r=8, L=1, density=0.5)
