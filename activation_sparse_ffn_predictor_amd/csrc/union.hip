@@ -109,6 +109,9 @@ __device__ __forceinline__ void split_xraw(const XRaw& r, half8& hi, half8& lo) 
 
 // k blocks whose loads are issued together (one memory round trip per chunk), by token tiles
 template <int NTT> struct KChunk { static constexpr int CH = NTT == 1 ? 8 : (NTT == 2 ? 4 : 2); };
+#ifndef SFFN_ROWS_CH1
+#define SFFN_ROWS_CH1 4
+#endif
 
 constexpr int NTK = 512;            // 8 waves split the k dimension
 constexpr int KW = NTK / 64;
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
   for (int t = 0; t < NTT; ++t) { au[t] = f32x4{0.f, 0.f, 0.f, 0.f}; ag[t] = au[t]; }
   // Double-buffered chunks of CH k blocks: the next chunk's weight rows (or nibbles and scales) and x tiles are
   // issued before the current chunk's matrix-core work, so consecutive round trips overlap.
-  constexpr int CH = KChunk<NTT>::CH / 2 > 0 ? KChunk<NTT>::CH / 2 : 1;
+  constexpr int CH = NTT == 1 ? SFFN_ROWS_CH1 : (KChunk<NTT>::CH / 2 > 0 ? KChunk<NTT>::CH / 2 : 1);
   struct Chunk {
     uint4 wu[CH], wg[CH];
     uint2 qu[CH], qg[CH];
@@ -433,8 +436,8 @@ constexpr int DS_K = 64;             // active rows per step (two 32-row MFMA k 
 // Partial y over a slice of 128 columns; part_out: [KS][B][D]. Row split ks takes the steps s = ks, ks + KS, ...
 // of DS_K consecutive dense indices, reading the ids the row kernel wrote to active[]. All of the block's ids are
 // staged in LDS first (one round trip, speculatively up to F); then every step's weight tile, scales and
-// activations are loaded into registers one step ahead, so each step's round trip overlaps the previous step's
-// matrix-core work.
+// activations are loaded into registers ahead of use: two steps ahead in two register sets taken in turn (up to
+// 32 tokens), else one step ahead, so each step's round trip overlaps the matrix-core work before it.
 template <int NTT, bool Q4>
 __global__ __launch_bounds__(DN_T) void k_mt_down(const void* __restrict__ Wd, const void* __restrict__ Sd,
                                                   const int32_t* __restrict__ active,
@@ -455,31 +458,55 @@ __global__ __launch_bounds__(DN_T) void k_mt_down(const void* __restrict__ Wd, c
   const Buf ba(abuf, (uint32_t)F * B * 4u);
   const Buf bid(active, (uint32_t)F * 4u);
   const Buf bn(n_active, 4u);
-  // round 1: the count and all of this block's ids (speculatively, bounded by F)
+  // round 1: all of this block's ids (speculatively, bounded by F: 8 per thread per round, one round for
+  // M DS_K <= 4096) and the count, issued after the first round's ids so that one wait covers both
+  int v[8];
+  auto ids_load = [&](int e0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int e = e0 + threadIdx.x + DN_T * k;
+      const int i = (ks + KS * (e / DS_K)) * DS_K + (e % DS_K);
+      v[k] = (int)bid.ldu(boff(e < M * DS_K && i < F, (uint32_t)i * 4u));
+    }
+  };
+  auto ids_store = [&](int e0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int e = e0 + threadIdx.x + DN_T * k;
+      if (e < M * DS_K) ids_lds[e] = v[k];
+    }
+  };
+  ids_load(0);
   const int nraw = (int)bn.ldu(0u);
-  for (int e = threadIdx.x; e < M * DS_K; e += DN_T) {
-    const int i = (ks + KS * (e / DS_K)) * DS_K + (e % DS_K);
-    ids_lds[e] = (int)bid.ldu(boff(i < F, (uint32_t)i * 4u));
+  ids_store(0);
+  for (int e0 = 8 * DN_T; e0 < M * DS_K; e0 += 8 * DN_T) {
+    ids_load(e0);
+    ids_store(e0);
   }
   const int n = min(max(nraw, 0), F);
   __syncthreads();
   // staging roles: fp16 tiles as 2 x (32 rows x 16 parts of 8 columns); Q4 as 64 rows x 8 half-blocks, scales
   // as 64 rows x 4 blocks; activations 8 per thread
-  struct Regs { uint4 w16[2]; uint2 nib; float sc; float av[8]; };
+  // two register sets (loads two steps ahead) up to 32 tokens; beyond, the registers they take would leave
+  // one block per CU instead of two
+  constexpr bool TWO_SETS = NTT <= 2;
+  constexpr int NT16 = 16 * NTT;                       // token slots of the activation tile
+  constexpr int NAV = DS_K * NT16 / DN_T;              // activation loads per thread per step (2 NTT)
+  struct Regs { uint4 w16[2]; uint2 nib; float sc; float av[NAV]; };
   auto load_step = [&](int m, Regs& R) {
     const int base = (ks + KS * m) * DS_K;           // dense index of the step's first row
     if constexpr (Q4) {
       const int row = threadIdx.x >> 3, part = threadIdx.x & 7;
       const int i = base + row;
       const bool ok = i < n;
-      const uint32_t id = ok ? (uint32_t)ids_lds[m * DS_K + row] : 0u;
+      const uint32_t id = (uint32_t)ids_lds[ok ? m * DS_K + row : 0];   // i < n: step m is one of the M staged
       const int q = part >> 1, hh = part & 1;
       const int blk = (c0 >> 5) + q;
       R.nib = bw.ld8(boff(ok && blk < nblk, id * (uint32_t)(D >> 1) + (uint32_t)blk * 16u + hh * 8u));
       const int srow = threadIdx.x >> 2, sq = threadIdx.x & 3;
       const int si = base + srow;
       const bool sok = threadIdx.x < DS_K * 4 && si < n && (c0 >> 5) + sq < nblk;
-      const uint32_t sid = sok ? (uint32_t)ids_lds[m * DS_K + srow] : 0u;
+      const uint32_t sid = (uint32_t)ids_lds[sok ? m * DS_K + srow : 0];
       R.sc = bs.ldh(boff(sok, (sid * nblk + (c0 >> 5) + sq) * 2u));
     } else {
 #pragma unroll
@@ -488,14 +515,14 @@ __global__ __launch_bounds__(DN_T) void k_mt_down(const void* __restrict__ Wd, c
         const int i = base + row;
         const int cc = c0 + part * 8;
         const bool ok = i < n && cc < D;
-        const uint32_t id = i < n ? (uint32_t)ids_lds[m * DS_K + row] : 0u;
+        const uint32_t id = (uint32_t)ids_lds[i < n ? m * DS_K + row : 0];
         R.w16[p] = bw.ld16(boff(ok, (id * D + cc) * 2u));
       }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int e = threadIdx.x + DN_T * k;            // DS_K * 64 = 8 * DN_T entries
-      const int kr = e >> 6, tok = e & 63;
+    for (int k = 0; k < NAV; ++k) {
+      const int e = threadIdx.x + DN_T * k;            // DS_K * NT16 = NAV * DN_T entries
+      const int kr = e / NT16, tok = e % NT16;
       const int i = base + kr;
       R.av[k] = ba.ldf(boff(i < n && tok < B, ((uint32_t)i * B + tok) * 4u));
     }
@@ -520,22 +547,20 @@ __global__ __launch_bounds__(DN_T) void k_mt_down(const void* __restrict__ Wd, c
       }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NAV; ++k) {
       const int e = threadIdx.x + DN_T * k;
-      at[e >> 6][e & 63] = R.av[k];
+      at[e / NT16][e % NT16] = R.av[k];
     }
   };
   f32x4 acc[NTT];
 #pragma unroll
   for (int t = 0; t < NTT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  Regs R;
-  int m = 0;
-  if ((ks + KS * m) * DS_K < n) load_step(m, R);
-  while ((ks + KS * m) * DS_K < n) {                   // block-uniform
+  // one step: tile to LDS, the step two ahead into the freed registers (branch-free: rows past n read 0), then
+  // the matrix-core work while two steps' loads are in flight
+  auto step = [&](Regs& R, int mm) {
     store_step(R);
     __syncthreads();
-    const bool more = (ks + KS * (m + 1)) * DS_K < n;
-    if (more) load_step(m + 1, R);                     // in flight during this step's matrix-core work
+    load_step(mm + (TWO_SETS ? 2 : 1), R);
 #pragma unroll
     for (int kc = 0; kc < DS_K / 32; ++kc) {
       // B operand: rows k = 8*(l/16)+i of column 16w + l%16 (read transposed from LDS)
@@ -558,7 +583,24 @@ __global__ __launch_bounds__(DN_T) void k_mt_down(const void* __restrict__ Wd, c
       }
     }
     __syncthreads();
-    ++m;
+  };
+  // steps of this block: m with (ks + KS m) DS_K < n; taken in pairs so that every loop iteration issues and
+  // waits for the same loads (the wait before each tile store then leaves the other set in flight)
+  const int nst = max(0, ((n + DS_K - 1) / DS_K - ks + KS - 1) / KS);
+  if constexpr (TWO_SETS) {
+    Regs R0, R1;
+    load_step(0, R0);
+    load_step(1, R1);
+    int m = 0;
+    for (; m + 1 < nst; m += 2) {
+      step(R0, m);
+      step(R1, m + 1);
+    }
+    if (m < nst) step(R0, m);
+  } else {
+    Regs R0;
+    load_step(0, R0);
+    for (int m = 0; m < nst; ++m) step(R0, m);
   }
   // D layout: lane l holds tokens 16t + 4(l/16) + i of column 16w + l%16
   const int col = c0 + w * 16 + (lane & 15);
