@@ -109,9 +109,6 @@ __device__ __forceinline__ void split_xraw(const XRaw& r, half8& hi, half8& lo) 
 
 // k blocks whose loads are issued together (one memory round trip per chunk), by token tiles
 template <int NTT> struct KChunk { static constexpr int CH = NTT == 1 ? 8 : (NTT == 2 ? 4 : 2); };
-#ifndef SFFN_ROWS_CH1
-#define SFFN_ROWS_CH1 4
-#endif
 
 constexpr int NTK = 512;            // 8 waves split the k dimension
 constexpr int KW = NTK / 64;
@@ -321,7 +318,9 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
   for (int t = 0; t < NTT; ++t) { au[t] = f32x4{0.f, 0.f, 0.f, 0.f}; ag[t] = au[t]; }
   // Double-buffered chunks of CH k blocks: the next chunk's weight rows (or nibbles and scales) and x tiles are
   // issued before the current chunk's matrix-core work, so consecutive round trips overlap.
-  constexpr int CH = NTT == 1 ? SFFN_ROWS_CH1 : (KChunk<NTT>::CH / 2 > 0 ? KChunk<NTT>::CH / 2 : 1);
+  // one token tile: 2 k blocks per chunk, so that the fp16 kernels stay within 128 VGPRs and two blocks share a
+  // CU (more rows in flight per CU than longer chunks give)
+  constexpr int CH = NTT == 1 ? 2 : (KChunk<NTT>::CH / 2 > 0 ? KChunk<NTT>::CH / 2 : 1);
   struct Chunk {
     uint4 wu[CH], wg[CH];
     uint2 qu[CH], qg[CH];
