@@ -26,8 +26,12 @@ Readings where the pages are silent (each is also listed in the design notes):
     active iff sigmoid(z) > t, i.e. z > ln(t / (1 - t)); strict inequality.
   * union over a batch of tokens: one mask M = OR over tokens; every token is
     computed over M.
-  * ReLU FFN: a_k = max(0, W_up[k] x + b_up[k]); ReGLU: a_k =
-    max(0, W_gate[k] x + b_gate[k]) * (W_up[k] x); y = W_down a, no down bias.
+  * ReLU FFN: a_k = max(0, W_up[k] x + b_up[k]); squared ReLU: a_k =
+    max(0, W_up[k] x + b_up[k])^2; ReGLU: a_k = max(0, W_gate[k] x + b_gate[k]) * (W_up[k] x);
+    y = W_down a, no down bias.
+  * always-active prefix: the neurons stored first are the hottest ones ("Neuron placement and
+    management"); a layer may declare its first n_hot stored neurons always active, and they join the
+    predicted set whatever their logits (the GPU then reads no predictor rows for them).
   * Q4_0: blocks of 32 consecutive weights along d_model in every neuron's
     row (W_gate, W_up) or column (W_down), w = (q - 8) * s.
   * layer chaining: parameter-free normalisation of each token, x' = (y - mean(y)) / sqrt(var(y) + 1e-6)
@@ -128,14 +132,16 @@ def band_neurons(z: np.ndarray, t: float, eps: float = BAND) -> np.ndarray:
 # ----------------------------------------------------------------------------- FFN
 def activations(act: str, x: np.ndarray, w: Dict[str, np.ndarray]) -> np.ndarray:
     """Dense neuron activations a [B, F] (fp64).
-    relu : a = max(0, W_up x + b_up)
-    reglu: a = max(0, W_gate x + b_gate) * (W_up x)"""
+    relu  : a = max(0, W_up x + b_up)
+    sqrelu: a = max(0, W_up x + b_up)^2   (squared ReLU, Indonesian digest, summary bullets)
+    reglu : a = max(0, W_gate x + b_gate) * (W_up x)"""
     x = np.atleast_2d(np.asarray(x, dtype=np.float64))
     u = x @ w["W_up"].T
-    if act == "relu":
+    if act in ("relu", "sqrelu"):
         if "b_up" in w:
             u = u + w["b_up"][None, :]
-        return np.maximum(u, 0.0)
+        a = np.maximum(u, 0.0)
+        return a * a if act == "sqrelu" else a
     if act == "reglu":
         g = x @ w["W_gate"].T
         if "b_gate" in w:
@@ -164,20 +170,31 @@ def layer_norm(y: np.ndarray, eps: float = NORM_EPS) -> np.ndarray:
     return c / np.sqrt(np.mean(c * c, axis=1, keepdims=True) + eps)
 
 
-def layer(act: str, x: np.ndarray, w: Dict[str, np.ndarray], t: float = 0.5) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """One sparse-FFN layer for a batch x [B, D]: returns (z [B,F], union mask [F], y [B,D])."""
+def with_hot_prefix(mask: np.ndarray, n_hot: int) -> np.ndarray:
+    """The computed set when the first n_hot stored neurons are always active: M | {k < n_hot}."""
+    m = np.array(mask, dtype=bool, copy=True)
+    m[:max(0, int(n_hot))] = True
+    return m
+
+
+def layer(act: str, x: np.ndarray, w: Dict[str, np.ndarray], t: float = 0.5,
+          n_hot: int = 0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One sparse-FFN layer for a batch x [B, D]: returns (z [B,F], computed mask [F], y [B,D]). The computed
+    mask is the union of the tokens' predicted masks, plus the first n_hot stored neurons when n_hot > 0."""
     z = predictor_logits(w["P1"], w["P2"], x, w.get("c"))
-    m = union_mask(token_masks(z, t))
+    m = with_hot_prefix(union_mask(token_masks(z, t)), n_hot)
     return z, m, ffn_masked(act, x, w, m)
 
 
-def stack(act: str, x: np.ndarray, layers, t: float = 0.5):
-    """Decode step through a stack: layer l consumes x_l, and x_{l+1} = layer_norm(y_l).
-    Returns the list of (z, mask, y) per layer."""
+def stack(act: str, x: np.ndarray, layers, t: float = 0.5, n_hot=0):
+    """Decode step through a stack: layer l consumes x_l, and x_{l+1} = layer_norm(y_l). ``n_hot`` is one
+    always-active prefix length for every layer or a sequence of one per layer. Layers may differ in predictor
+    rank. Returns the list of (z, mask, y) per layer."""
     out = []
     xl = np.atleast_2d(np.asarray(x, dtype=np.float64))
-    for w in layers:
-        z, m, y = layer(act, xl, w, t)
+    hots = list(n_hot) if np.ndim(n_hot) else [int(n_hot)] * len(layers)
+    for w, nh in zip(layers, hots):
+        z, m, y = layer(act, xl, w, t, nh)
         out.append((z, m, y))
         xl = layer_norm(y)
     return out

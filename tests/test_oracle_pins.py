@@ -24,22 +24,23 @@ def _dyadic(rng, shape, lim=32, den=16):
     return rng.integers(-lim, lim + 1, size=shape).astype(np.float64) / den
 
 
-def _exact_layer(act, x, P1, P2, c, Wg, bg, Wu, bu, Wd, tau=F0):
-    """Scalar loops over exact rationals: the layer written out from its definition."""
+def _exact_layer(act, x, P1, P2, c, Wg, bg, Wu, bu, Wd, tau=F0, n_hot=0):
+    """Scalar loops over exact rationals: the layer written out from its definition (the first n_hot stored
+    neurons are computed whatever the predictor says)."""
     Fr = lambda v: Fraction(float(v))  # noqa: E731  (inputs are dyadic, conversion is exact)
     B, D = x.shape
     r, F = P1.shape[0], P2.shape[0]
     h = [[sum((Fr(P1[j, d]) * Fr(x[b, d]) for d in range(D)), F0) for j in range(r)] for b in range(B)]
     z = [[sum((Fr(P2[k, j]) * h[b][j] for j in range(r)), F0) + (Fr(c[k]) if c is not None else F0)
           for k in range(F)] for b in range(B)]
-    mask = [any(z[b][k] > tau for b in range(B)) for k in range(F)]
+    mask = [k < n_hot or any(z[b][k] > tau for b in range(B)) for k in range(F)]
     a = [[F0] * F for _ in range(B)]
     for b in range(B):
         for k in range(F):
             u = sum((Fr(Wu[k, d]) * Fr(x[b, d]) for d in range(D)), F0)
-            if act == "relu":
+            if act in ("relu", "sqrelu"):
                 pre = u + (Fr(bu[k]) if bu is not None else F0)
-                a[b][k] = pre if pre > 0 else F0
+                a[b][k] = (pre if act == "relu" else pre * pre) if pre > 0 else F0
             else:
                 g = sum((Fr(Wg[k, d]) * Fr(x[b, d]) for d in range(D)), F0) + (Fr(bg[k]) if bg is not None else F0)
                 a[b][k] = (g if g > 0 else F0) * u
@@ -69,22 +70,28 @@ def _tiny_case(seed, act, B, D=8, F=16, r=4, with_c=True, tie=True):
     return x, w
 
 
-def check_brute_force(act, B, seed, with_c=True):
+def check_brute_force(act, B, seed, with_c=True, n_hot=0):
     x, w = _tiny_case(seed, act, B, with_c=with_c)
-    z, m, y = sf.layer(act, x, w, 0.5)
+    z, m, y = sf.layer(act, x, w, 0.5, n_hot)
     ez, em, ey = _exact_layer(act, x, w["P1"], w["P2"], w.get("c"), w.get("W_gate"), w.get("b_gate"), w["W_up"],
-                              w.get("b_up"), w["W_down"])
+                              w.get("b_up"), w["W_down"], n_hot=n_hot)
     ok = all(Fraction(float(z[b, k])) == ez[b][k] for b in range(B) for k in range(z.shape[1]))
     ok &= [bool(v) for v in m] == em
     ok &= all(Fraction(float(y[b, d])) == ey[b][d] for b in range(B) for d in range(y.shape[1]))
     return ok
 
 
-@pytest.mark.parametrize("act", ["relu", "reglu"])
+@pytest.mark.parametrize("act", ["relu", "sqrelu", "reglu"])
 @pytest.mark.parametrize("B", [1, 2, 3])
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_brute_force_exact(act, B, seed):
     assert check_brute_force(act, B, seed)
+
+
+@pytest.mark.parametrize("act", ["relu", "sqrelu", "reglu"])
+@pytest.mark.parametrize("n_hot", [1, 5, 16])
+def test_brute_force_hot_prefix(act, n_hot):
+    assert check_brute_force(act, 2, 3, n_hot=n_hot)
 
 
 def test_brute_force_no_predictor_bias():
@@ -155,6 +162,50 @@ def test_closed_form_relu_two_neurons():
     assert m.tolist() == [False, True] and y.tolist() == [[0.0, 0.0]]
 
 
+def test_closed_form_sqrelu_two_neurons():
+    # u = W_up x + b = (2, -0.5) -> a = (4, 0); y = W_down a = (1*4, 3*4)
+    x = np.array([[3.0, -1.0]])
+    w = {"P1": np.array([[1.0, 1.0]]), "P2": np.array([[1.0], [1.0]]), "c": np.array([0.0, 0.0]),
+         "W_up": np.eye(2), "b_up": np.array([-1.0, 0.5]), "W_down": np.array([[1.0, 0.0], [3.0, 2.0]])}
+    _, m, y = sf.layer("sqrelu", x, w, 0.5)
+    assert m.tolist() == [True, True] and y.tolist() == [[4.0, 12.0]]
+
+
+def check_hot_prefix_closed_form():
+    # the predictor skips neuron 0 (z = -3); declared always active, it is computed anyway
+    x = np.array([[3.0, -1.0]])
+    w = {"P1": np.array([[1.0, 1.0]]), "P2": np.array([[1.0], [1.0]]), "c": np.array([-5.0, 0.0]),
+         "W_up": np.eye(2), "b_up": np.array([-1.0, 0.5]), "W_down": np.array([[1.0, 0.0], [3.0, 2.0]])}
+    _, m0, y0 = sf.layer("relu", x, w, 0.5)
+    ok = m0.tolist() == [False, True] and y0.tolist() == [[0.0, 0.0]]
+    _, m1, y1 = sf.layer("relu", x, w, 0.5, n_hot=1)
+    ok &= m1.tolist() == [True, True] and y1.tolist() == [[2.0, 6.0]]
+    w["c"] = np.array([0.0, -5.0])                         # a hot prefix never removes a predicted neuron
+    _, m2, _ = sf.layer("relu", x, w, 0.5, n_hot=1)
+    return ok and m2.tolist() == [True, False]
+
+
+def test_closed_form_hot_prefix():
+    assert check_hot_prefix_closed_form()
+
+
+def test_hot_prefix_everything_is_dense():
+    x, w = _tiny_case(9, "reglu", 2)
+    _, m, y = sf.layer("reglu", x, w, 1.0 - 1e-15, n_hot=16)   # the predictor marks nothing, the prefix all
+    assert m.all() and np.array_equal(y, sf.ffn_dense("reglu", x, w))
+
+
+def test_hot_prefix_nested():
+    x, w = _tiny_case(10, "relu", 3, tie=False)
+    prev = None
+    for n_hot in range(0, 17):
+        _, m, _ = sf.layer("relu", x, w, 0.5, n_hot)
+        assert m[:n_hot].all()
+        if prev is not None:
+            assert np.all(m >= prev) and (m.sum() - prev.sum()) <= 1
+        prev = m
+
+
 def test_closed_form_reglu():
     x = np.array([[1.0, 2.0]])
     w = {"P1": np.array([[1.0, 0.0]]), "P2": np.array([[1.0], [-1.0], [2.0]]), "c": np.zeros(3),
@@ -213,6 +264,12 @@ def test_all_active_matches_torch_linear():
         torch.relu(torch.nn.functional.linear(tx, torch.from_numpy(w["W_up"]), torch.from_numpy(w["b_gate"]))),
         torch.from_numpy(w["W_down"])).numpy()
     assert np.max(np.abs(y2 - ref2)) <= 1e-12 * np.max(np.abs(ref2))
+    _, _, y3 = sf.layer("sqrelu", x, w2, 1e-300)
+    ref3 = torch.nn.functional.linear(
+        torch.square(torch.relu(torch.nn.functional.linear(tx, torch.from_numpy(w["W_up"]),
+                                                           torch.from_numpy(w["b_gate"])))),
+        torch.from_numpy(w["W_down"])).numpy()
+    assert np.max(np.abs(y3 - ref3)) <= 1e-12 * np.max(np.abs(ref3))
 
 
 def test_none_active_gives_zero():
@@ -260,7 +317,7 @@ def check_true_mask_equals_dense(act="reglu", seed=7):
             and np.max(np.abs(y_masked - sparse_loop)) <= 1e-12 * np.max(np.abs(y_dense)))
 
 
-@pytest.mark.parametrize("act", ["relu", "reglu"])
+@pytest.mark.parametrize("act", ["relu", "sqrelu", "reglu"])
 def test_true_mask_equals_dense(act):
     assert check_true_mask_equals_dense(act)
 
@@ -328,9 +385,11 @@ def check_layer_norm():
 
 
 def _all_pins():
-    return check_layer_norm() and (all(check_brute_force(act, B, s) for act in ("relu", "reglu") for B in (1, 3) for s in (0, 1))
-            and check_q4_exact() and check_true_mask_equals_dense("relu") and check_true_mask_equals_dense("reglu")
-            and check_permutation_invariance())
+    return check_layer_norm() and (all(check_brute_force(act, B, s) for act in ("relu", "sqrelu", "reglu")
+                                       for B in (1, 3) for s in (0, 1))
+            and all(check_brute_force(act, 2, 3, n_hot=n) for act in ("relu", "reglu") for n in (1, 5))
+            and check_q4_exact() and all(check_true_mask_equals_dense(a) for a in ("relu", "sqrelu", "reglu"))
+            and check_permutation_invariance() and check_hot_prefix_closed_form())
 
 
 def test_unmutated_oracle_passes_all_pins():
@@ -371,6 +430,31 @@ def _mut_relu_no_bias(act, x, w):
     return np.maximum(x @ w["W_gate"].T + w["b_gate"][None, :], 0.0) * (x @ w["W_up"].T)
 
 
+def _mut_sqrelu_unsquared(act, x, w):
+    x = np.atleast_2d(x)
+    if act == "reglu":
+        return np.maximum(x @ w["W_gate"].T + w["b_gate"][None, :], 0.0) * (x @ w["W_up"].T)
+    return np.maximum(x @ w["W_up"].T + w["b_up"][None, :], 0.0)   # squared ReLU left unsquared
+
+
+def _mut_sqrelu_square_before_relu(act, x, w):
+    x = np.atleast_2d(x)
+    if act == "reglu":
+        return np.maximum(x @ w["W_gate"].T + w["b_gate"][None, :], 0.0) * (x @ w["W_up"].T)
+    u = x @ w["W_up"].T + w["b_up"][None, :]
+    return (u * u) if act == "sqrelu" else np.maximum(u, 0.0)
+
+
+def _mut_hot_prefix_off_by_one(mask, n_hot):
+    m = np.array(mask, dtype=bool, copy=True)
+    m[:max(0, int(n_hot) - 1)] = True
+    return m
+
+
+def _mut_hot_prefix_ignored(mask, n_hot):
+    return np.array(mask, dtype=bool, copy=True)
+
+
 def _mut_q4_offset(q, s):
     q = np.asarray(q).astype(np.float64)
     return (q - 7.0) * np.repeat(np.asarray(s, dtype=np.float64), 32, axis=1)
@@ -396,6 +480,10 @@ def _mut_mask_first_token(masks):
     ("token_masks", _mut_threshold_ge),
     ("activations", _mut_reglu_swapped),
     ("activations", _mut_relu_no_bias),
+    ("activations", _mut_sqrelu_unsquared),
+    ("activations", _mut_sqrelu_square_before_relu),
+    ("with_hot_prefix", _mut_hot_prefix_off_by_one),
+    ("with_hot_prefix", _mut_hot_prefix_ignored),
     ("dequant_q4_rows", _mut_q4_offset),
     ("ffn_masked", _mut_mask_ignored),
     ("union_mask", _mut_mask_first_token),
