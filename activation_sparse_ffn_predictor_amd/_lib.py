@@ -12,11 +12,12 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsffn.so")
 
-ACT_RELU, ACT_REGLU = 0, 1
-ACTS = {"relu": ACT_RELU, "reglu": ACT_REGLU}
+ACT_RELU, ACT_REGLU, ACT_SQRELU = 0, 1, 2
+ACTS = {"relu": ACT_RELU, "reglu": ACT_REGLU, "sqrelu": ACT_SQRELU}
 
 EXPORTS = ("sffn_status_string", "sffn_last_error", "sffn_workspace_size", "sffn_mask_words", "sffn_predict",
-           "sffn_forward", "sffn_forward_q4", "sffn_profile_begin", "sffn_profile_end", "sffn_forward_path")
+           "sffn_predict_hot", "sffn_forward", "sffn_forward_q4", "sffn_profile_begin", "sffn_profile_end",
+           "sffn_forward_path")
 K_PRED_H, K_PRED_Z, K_ROWS, K_COLS = 0, 1, 2, 3
 
 
@@ -48,6 +49,8 @@ def lib() -> ctypes.CDLL:
         h.sffn_mask_words.argtypes, h.sffn_mask_words.restype = [i32], i32
         h.sffn_predict.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp]
         h.sffn_predict.restype = i32
+        h.sffn_predict_hot.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
+        h.sffn_predict_hot.restype = i32
         h.sffn_forward.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         h.sffn_forward.restype = i32
         h.sffn_forward_q4.argtypes = [i32, _Q4, vp, _Q4, vp, _Q4, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -92,11 +95,17 @@ def mask_words(F: int) -> int:
     return int(lib().sffn_mask_words(F))
 
 
-def predict(P1, P2, c, x, t: float, mask, ws, logits=None, x_norm: bool = False, stream=None):
-    """sffn_predict. P1 [r, D] fp16, P2 [F, r] fp16, c [F] fp32 or None, x [B, D] fp32, mask [ceil(F/64)]
-    int64 (bit pattern), ws uint8 workspace, logits [B, F] fp32 or None."""
+def predict(P1, P2, c, x, t: float, mask, ws, logits=None, x_norm: bool = False, stream=None, n_hot: int = 0):
+    """sffn_predict (n_hot = 0) or sffn_predict_hot (stored neurons 0 .. n_hot-1 always active). P1 [r, D] fp16,
+    P2 [F, r] fp16, c [F] fp32 or None, x [B, D] fp32, mask [ceil(F/64)] int64 (bit pattern), ws uint8
+    workspace, logits [B, F] fp32 or None."""
     B, D = x.shape
     F, r = P2.shape
+    if n_hot:
+        rc = lib().sffn_predict_hot(_p(P1), _p(P2), _p(c), _p(x), int(bool(x_norm)), B, D, F, r, float(t), int(n_hot),
+                                    _p(mask), _p(logits), _p(ws), _nbytes(ws), _stream(stream, x))
+        _check(rc, "sffn_predict_hot")
+        return
     rc = lib().sffn_predict(_p(P1), _p(P2), _p(c), _p(x), int(bool(x_norm)), B, D, F, r, float(t), _p(mask), _p(logits),
                             _p(ws), _nbytes(ws), _stream(stream, x))
     _check(rc, "sffn_predict")

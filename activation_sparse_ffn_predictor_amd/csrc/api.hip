@@ -206,17 +206,19 @@ size_t sffn_workspace_size(int B, int D, int F, int r) {
 int sffn_mask_words(int F) { return F < 1 ? 0 : (F + 63) / 64; }
 
 int sffn_forward_path(int act, int q4, int B, int D, int F) {
-  if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU) return -1;
+  if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU && act != SFFN_ACT_SQRELU) return -1;
   if (sffn_fused_ok(B, D, F, act, q4 != 0)) return SFFN_PATH_FUSED;
   return decode_batch(B, D, F) ? SFFN_PATH_DECODE : SFFN_PATH_UNION;
 }
 
-int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F, int r,
-                 float t, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream) {
+static int predict_impl(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D,
+                        int F, int r, float t, int n_hot, uint64_t* mask, float* logits, void* ws, size_t ws_bytes,
+                        void* stream) {
   g_err[0] = 0;
   if (!P1 || !P2 || !x || !mask) return fail(SFFN_ERR_NULL, "predict: P1, P2, x and mask are required");
   int s = check_common(B, D, F);
   if (s) return s;
+  if (n_hot < 0 || n_hot > F) return fail(SFFN_ERR_ARG, "n_hot=%d outside 0..F=%d", n_hot, F);
   if (r < 8 || r > MAX_R || r % 8) return fail(SFFN_ERR_SHAPE, "r=%d: need 8 <= r <= %d, r %% 8 == 0", r, MAX_R);
   if ((long)B * r > MAX_BR) return fail(SFFN_ERR_SHAPE, "B*r=%ld > %d", (long)B * r, MAX_BR);
   if (!(t > 0.f && t < 1.f)) return fail(SFFN_ERR_ARG, "threshold t=%g outside (0, 1)", (double)t);
@@ -229,14 +231,14 @@ int sffn_predict(const void* P1, const void* P2, const float* c, const float* x,
   float* h = ws_hbuf(ws, B, D, F);
   hipError_t e;
   if (B == 1) {
-    e = sffn_launch_predict(P1, P2, c, x, x_norm, B, D, F, r, tau, mask, logits, h, st);
+    e = sffn_launch_predict(P1, P2, c, x, x_norm, B, D, F, r, tau, n_hot, mask, logits, h, st);
   } else if (B <= 8) {
     // a few tokens: h in one kernel (each P1 row read once with every token, normalisation folded in), then z
     e = sffn_launch_predict_hb(P1, x, x_norm, B, D, r, h, st);
     // z: vector-ALU kernel for up to 4 tokens, matrix-core kernel beyond (measured: equal at 4, faster at 8)
     if (e == hipSuccess)
-      e = B <= 4 ? sffn_launch_predict_zb(P2, c, h, B, F, r, tau, mask, logits, st)
-                 : sffn_launch_predict_mt(P1, P2, c, x, B, D, F, r, tau, mask, logits, h, nullptr, 0, st);
+      e = B <= 4 ? sffn_launch_predict_zb(P2, c, h, B, F, r, tau, n_hot, mask, logits, st)
+                 : sffn_launch_predict_mt(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, h, nullptr, 0, st);
   } else {
     const float* xin = x;
     e = hipSuccess;
@@ -248,16 +250,28 @@ int sffn_predict(const void* P1, const void* P2, const float* c, const float* x,
     // (KS_MAX * B * D floats >= ksh * B * r)
     const int ksh = std::max(1, std::min({KS_MAX, D / 32 > 0 ? D / 32 : 1, (KS_MAX * D) / r}));
     if (e == hipSuccess)
-      e = sffn_launch_predict_mt(P1, P2, c, xin, B, D, F, r, tau, mask, logits, h, ws_part(ws, B, D, F), ksh, st);
+      e = sffn_launch_predict_mt(P1, P2, c, xin, B, D, F, r, tau, n_hot, mask, logits, h, ws_part(ws, B, D, F), ksh,
+                                 st);
   }
   return e == hipSuccess ? SFFN_OK : hip_fail(e, "predict launch");
+}
+
+int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F, int r,
+                 float t, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream) {
+  return predict_impl(P1, P2, c, x, x_norm, B, D, F, r, t, 0, mask, logits, ws, ws_bytes, stream);
+}
+
+int sffn_predict_hot(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F,
+                     int r, float t, int n_hot, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream) {
+  return predict_impl(P1, P2, c, x, x_norm, B, D, F, r, t, n_hot, mask, logits, ws, ws_bytes, stream);
 }
 
 int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W_up, const float* b_up,
                  const void* W_downT, const float* x, int x_norm, int B, int D, int F, const uint64_t* mask,
                  int32_t* active, int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU) return fail(SFFN_ERR_ACT, "unknown activation %d", act);
+  if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU && act != SFFN_ACT_SQRELU)
+    return fail(SFFN_ERR_ACT, "unknown activation %d", act);
   if (act == SFFN_ACT_REGLU && !W_gate) return fail(SFFN_ERR_ACT, "ReGLU needs W_gate");
   if (!W_up || !W_downT || !x || !mask || !active || !n_active || !y)
     return fail(SFFN_ERR_NULL, "forward: W_up, W_downT, x, mask, active, n_active and y are required");
@@ -291,7 +305,8 @@ int sffn_forward_q4(int act, sffn_q4 W_gate, const float* b_gate, sffn_q4 W_up, 
                     const float* x, int x_norm, int B, int D, int F, const uint64_t* mask, int32_t* active,
                     int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU) return fail(SFFN_ERR_ACT, "unknown activation %d", act);
+  if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU && act != SFFN_ACT_SQRELU)
+    return fail(SFFN_ERR_ACT, "unknown activation %d", act);
   if (act == SFFN_ACT_REGLU && (!W_gate.q || !W_gate.s)) return fail(SFFN_ERR_ACT, "ReGLU needs W_gate");
   if (!W_up.q || !W_up.s || !W_downT.q || !W_downT.s || !x || !mask || !active || !n_active || !y)
     return fail(SFFN_ERR_NULL, "forward_q4: W_up, W_downT, x, mask, active, n_active and y are required");

@@ -356,11 +356,12 @@ bool sffn_prof_events(int kid, hipEvent_t* start, hipEvent_t* stop);
 
 // ---- launchers (host side), defined in the kernel files; return hipError_t of the launch
 hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D,
-                               int F, int r, float tau, uint64_t* mask, float* logits, float* hbuf, hipStream_t st);
+                               int F, int r, float tau, int n_hot, uint64_t* mask, float* logits, float* hbuf,
+                               hipStream_t st);
 hipError_t sffn_launch_predict_hb(const void* P1, const float* x, int x_norm, int B, int D, int r, float* hbuf,
                                   hipStream_t st);
 hipError_t sffn_launch_predict_zb(const void* P2, const float* c, const float* hbuf, int B, int F, int r, float tau,
-                                  uint64_t* mask, float* logits, hipStream_t st);
+                                  int n_hot, uint64_t* mask, float* logits, hipStream_t st);
 hipError_t sffn_launch_forward(int act, const void* Wg, const float* bg, const void* Wu, const float* bu,
                                const void* WdT, const float* x, int x_norm, int B, int D, int F, const uint64_t* mask,
                                int32_t* active, int32_t* n_active, float* y, float* abuf, hipStream_t st);
@@ -381,8 +382,8 @@ hipError_t sffn_launch_fused_q4(int act, const uint8_t* qg, const void* sg, cons
 // multi-token (union-mask) path, matrix cores (union.hip)
 hipError_t sffn_launch_norm_tokens(const float* x, int B, int D, float* xn, hipStream_t st);
 hipError_t sffn_launch_predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F,
-                                  int r, float tau, uint64_t* mask, float* logits, float* hbuf, float* hpart, int KSH,
-                                  hipStream_t st);
+                                  int r, float tau, int n_hot, uint64_t* mask, float* logits, float* hbuf,
+                                  float* hpart, int KSH, hipStream_t st);
 hipError_t sffn_launch_rows_mt(int act, bool q4, const void* Wg, const void* Sg, const float* bg, const void* Wu,
                                const void* Su, const float* bu, const float* x, int B, int D, int F,
                                const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf, hipStream_t st);

@@ -129,6 +129,7 @@ __global__ __launch_bounds__(NT_UP) void k_upgate(const uint4* __restrict__ Wg, 
         a = fmaxf(g, 0.f) * u;
       } else {
         a = fmaxf(u + bias, 0.f);
+        if (ACT == 2) a *= a;
       }
       if (lane == 0) abuf[(size_t)i * B + b] = a;
     }
@@ -301,8 +302,10 @@ hipError_t forward_b(int act, const void* Wg, const float* bg, const void* Wu, c
                      const float* x, int x_norm, int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active,
                      float* y, float* abuf, hipStream_t st) {
   const int nch = (D / 8 + 63) / 64;
-  hipError_t e = act == 1 ? dispatch_up<B, 1>(nch, Wg, bg, Wu, bu, x, x_norm, D, F, mask, active, n_active, abuf, st)
-                          : dispatch_up<B, 0>(nch, Wg, bg, Wu, bu, x, x_norm, D, F, mask, active, n_active, abuf, st);
+  hipError_t e =
+      act == 1   ? dispatch_up<B, 1>(nch, Wg, bg, Wu, bu, x, x_norm, D, F, mask, active, n_active, abuf, st)
+      : act == 2 ? dispatch_up<B, 2>(nch, Wg, bg, Wu, bu, x, x_norm, D, F, mask, active, n_active, abuf, st)
+                 : dispatch_up<B, 0>(nch, Wg, bg, Wu, bu, x, x_norm, D, F, mask, active, n_active, abuf, st);
   if (e != hipSuccess) return e;
   return launch_down<B>(WdT, active, n_active, abuf, D, F, y, st);
 }

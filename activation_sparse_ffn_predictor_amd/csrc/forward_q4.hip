@@ -158,6 +158,7 @@ __global__ __launch_bounds__(NT_UP) void k_upgate_q4(const uint4* __restrict__ q
         a = fmaxf(g, 0.f) * u;
       } else {
         a = fmaxf(u + bias, 0.f);
+        if (ACT == 2) a *= a;
       }
       if (lane == 0) abuf[(size_t)i * B + b] = a;
     }
@@ -336,9 +337,10 @@ hipError_t forward_b(int act, const uint8_t* qg, const void* sg, const float* bg
                      const float* bu, const uint8_t* qd, const void* sd, const float* x, int x_norm, int D, int F,
                      const uint64_t* mask, int32_t* active, int32_t* n_active, float* y, float* abuf, hipStream_t st) {
   const int nq = (D / 32 + 63) / 64;
-  hipError_t e = act == 1
-                     ? dispatch_up<B, 1>(nq, qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st)
-                     : dispatch_up<B, 0>(nq, qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st);
+  hipError_t e =
+      act == 1   ? dispatch_up<B, 1>(nq, qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st)
+      : act == 2 ? dispatch_up<B, 2>(nq, qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st)
+                 : dispatch_up<B, 0>(nq, qg, sg, bg, qu, su, bu, x, x_norm, D, F, mask, active, n_active, abuf, st);
   if (e != hipSuccess) return e;
   const int slices = (D + QSW - 1) / QSW;
   const int grid = SFFN_DOWN_XCD ? (slices + 7) / 8 * 8 : slices;

@@ -148,6 +148,7 @@ __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, c
         a = fmaxf(g, 0.f) * u;
       } else {
         a = fmaxf(u + bias, 0.f);
+        if (ACT == 2) a *= a;
       }
       if (lane == 0) { av[w] = a; active[blk + G * k] = id; }
     } else if (lane == 0) {
@@ -372,6 +373,7 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
           a = fmaxf(g, 0.f) * u;
         } else {
           a = fmaxf(u + bias[r], 0.f);
+          if (ACT == 2) a *= a;
         }
         if (lane == 0) { av[w + FW * r] = a; active[blk + G * (k0 + w + FW * r)] = idr[r]; }
       } else if (lane == 0) {
@@ -479,7 +481,7 @@ hipError_t dispatch_fused(const void* Wg, const float* bg, const void* Wu, const
   if (nch <= 4) FU(4, 1);          // D <= 2048
   if (nch <= 8) FU(8, 1);          // D <= 4096
   if (nch <= 10) FU(10, 2);        // D <= 5120
-  if constexpr (ACT == 0) FU(16, 2);  // D <= 8192 (ReLU: one matrix; ReGLU rows this wide keep two kernels)
+  if constexpr (ACT != 1) FU(16, 2);  // D <= 8192 (ReLU, squared ReLU: one matrix; ReGLU rows this wide keep two kernels)
   return hipErrorInvalidValue;
 #undef FU
 }
@@ -524,6 +526,11 @@ hipError_t sffn_launch_fused_q4(int act, const uint8_t* qg, const void* sg, cons
     if (nq <= 2) FQ(1, 2);
     FQ(1, 4);
   }
+  if (act == 2) {
+    if (nq <= 1) FQ(2, 1);
+    if (nq <= 2) FQ(2, 2);
+    FQ(2, 4);
+  }
   if (nq <= 1) FQ(0, 1);
   if (nq <= 2) FQ(0, 2);
   FQ(0, 4);
@@ -535,12 +542,15 @@ hipError_t sffn_launch_fused_q4(int act, const uint8_t* qg, const void* sg, cons
 bool sffn_fused_ok(int B, int D, int F, int act, bool q4) {
   if (B != 1 || F > 32768) return false;
   if (q4) return D <= 8192;
-  return D <= 5120 || (act == 0 && D <= 8192);
+  return D <= 5120 || (act != 1 && D <= 8192);
 }
 
 hipError_t sffn_launch_fused(int act, const void* Wg, const float* bg, const void* Wu, const float* bu,
                              const void* WdT, const float* x, int x_norm, int D, int F, const uint64_t* mask,
                              int32_t* active, int32_t* n_active, float* part, int G, float* y, hipStream_t st) {
-  return act == 1 ? dispatch_fused<1>(Wg, bg, Wu, bu, WdT, x, x_norm, D, F, mask, active, n_active, part, G, y, st)
-                  : dispatch_fused<0>(Wg, bg, Wu, bu, WdT, x, x_norm, D, F, mask, active, n_active, part, G, y, st);
+  switch (act) {
+    case 1: return dispatch_fused<1>(Wg, bg, Wu, bu, WdT, x, x_norm, D, F, mask, active, n_active, part, G, y, st);
+    case 2: return dispatch_fused<2>(Wg, bg, Wu, bu, WdT, x, x_norm, D, F, mask, active, n_active, part, G, y, st);
+    default: return dispatch_fused<0>(Wg, bg, Wu, bu, WdT, x, x_norm, D, F, mask, active, n_active, part, G, y, st);
+  }
 }

@@ -188,7 +188,7 @@ __global__ __launch_bounds__(NTB) void k_pred_hb(const uint4* __restrict__ P1, c
 // take the matrix-core kernels).
 template <int LPR, int ROUNDS>
 __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, const float* __restrict__ c,
-                                               const float* __restrict__ h, int F, int r, float tau,
+                                               const float* __restrict__ h, int F, int r, float tau, int n_hot,
                                                uint64_t* __restrict__ mask, float* __restrict__ logits) {
   constexpr int RPI = 64 / LPR;        // rows per load instruction
   constexpr int RPW = 16;              // rows per wave = one 16-bit quarter of a mask word
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
     for (int i = 0; i < NI; ++i) {
       const int k = base + i * RPI + rsub;
       const int cc = q * LPR + csub;
-      wv[q][i] = bp.ld16(boff(k < F && cc < cpr, ((uint32_t)k * cpr + cc) * 16u));
+      wv[q][i] = bp.ld16(boff(k < F && k >= n_hot && cc < cpr, ((uint32_t)k * cpr + cc) * 16u));
     }
   float hv[ROUNDS][8];
 #pragma unroll
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int k = base + i * RPI + rsub;
-    cb[i] = bc.ldf(boff(k < F, (uint32_t)k * 4u));
+    cb[i] = bc.ldf(boff(k < F && k >= n_hot, (uint32_t)k * 4u));
   }
   __builtin_amdgcn_sched_barrier(0);
   // decisions: instruction i, row group q sits at lane q * LPR
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
     for (int q = 0; q < ROUNDS; ++q) acc += dot8(wv[q][i], hv[q]);
     acc = group_sum<LPR>(acc);
     const int k = base + i * RPI + rsub;
-    const float z = acc + cb[i];
+    const float z = k < n_hot ? INFINITY : acc + cb[i];   // the always-active prefix: no row was read
     const bool on = csub == 0 && k < F && z > tau;
     if (logits && csub == 0 && k < F) logits[k] = z;
     const unsigned long long bal = __ballot(on);
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(NT) void k_pred_z(const uint4* __restrict__ P2, con
 template <int LPR, int ROUNDS, int TB>
 __global__ __launch_bounds__(NT) void k_pred_zb(const uint4* __restrict__ P2, const float* __restrict__ c,
                                                 const float* __restrict__ h, int B, int F, int r, float tau,
-                                                uint64_t* __restrict__ mask, float* __restrict__ logits) {
+                                                int n_hot, uint64_t* __restrict__ mask, float* __restrict__ logits) {
   constexpr int RPI = 64 / LPR;
   constexpr int RPW = 16;
   constexpr int NI = RPW / RPI;
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(NT) void k_pred_zb(const uint4* __restrict__ P2, co
     for (int i = 0; i < NI; ++i) {
       const int k = base + i * RPI + rsub;
       const int cc = q * LPR + csub;
-      wv[q][i] = bp.ld16(boff(k < F && cc < cpr, ((uint32_t)k * cpr + cc) * 16u));
+      wv[q][i] = bp.ld16(boff(k < F && k >= n_hot && cc < cpr, ((uint32_t)k * cpr + cc) * 16u));
     }
   float4 hl[NHL];
 #pragma unroll
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(NT) void k_pred_zb(const uint4* __restrict__ P2, co
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int k = base + i * RPI + rsub;
-    cb[i] = bc.ldf(boff(k < F, (uint32_t)k * 4u));
+    cb[i] = bc.ldf(boff(k < F && k >= n_hot, (uint32_t)k * 4u));
   }
 #pragma unroll
   for (int l = 0; l < NHL; ++l)
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(NT) void k_pred_zb(const uint4* __restrict__ P2, co
     for (int i = 0; i < NI; ++i) {
       const float s = group_sum<LPR>(acc[i]);
       const int k = base + i * RPI + rsub;
-      const float z = s + cb[i];
+      const float z = k < n_hot ? INFINITY : s + cb[i];
       if (logits && csub == 0 && k < F) logits[(size_t)t * F + k] = z;
       any[i] = any[i] || z > tau;
     }
@@ -350,19 +350,19 @@ hipError_t launch_hb(const void* P1, const float* x, int x_norm, int B, int D, i
 }
 
 template <int LPR, int ROUNDS>
-hipError_t launch_z(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, uint64_t* mask,
-                    float* logits, hipStream_t st) {
+hipError_t launch_z(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, int n_hot,
+                    uint64_t* mask, float* logits, hipStream_t st) {
   const int grid = (F + 63) / 64;
-  SFFN_LAUNCH(1, (k_pred_z<LPR, ROUNDS>), dim3(grid), dim3(NT), 0, st, (const uint4*)P2, c, h, F, r, tau, mask,
+  SFFN_LAUNCH(1, (k_pred_z<LPR, ROUNDS>), dim3(grid), dim3(NT), 0, st, (const uint4*)P2, c, h, F, r, tau, n_hot, mask,
               logits);
   return hipGetLastError();
 }
 
 template <int LPR, int ROUNDS, int TB>
-hipError_t launch_zb(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, uint64_t* mask,
-                     float* logits, hipStream_t st) {
+hipError_t launch_zb(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, int n_hot,
+                     uint64_t* mask, float* logits, hipStream_t st) {
   SFFN_LAUNCH(1, (k_pred_zb<LPR, ROUNDS, TB>), dim3((F + 63) / 64), dim3(NT), 0, st, (const uint4*)P2, c, h, B, F, r,
-              tau, mask, logits);
+              tau, n_hot, mask, logits);
   return hipGetLastError();
 }
 
@@ -377,9 +377,9 @@ int z_shape(int r) {
 }
 
 template <int TB>
-hipError_t dispatch_zb(const void* P2, const float* c, const float* h, int B, int F, int r, float tau,
+hipError_t dispatch_zb(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, int n_hot,
                        uint64_t* mask, float* logits, hipStream_t st) {
-#define ZB(L, R) return launch_zb<L, R, TB>(P2, c, h, B, F, r, tau, mask, logits, st)
+#define ZB(L, R) return launch_zb<L, R, TB>(P2, c, h, B, F, r, tau, n_hot, mask, logits, st)
   switch (z_shape(r)) {
     case 801: ZB(8, 1);
     case 802: ZB(8, 2);
@@ -403,7 +403,8 @@ hipError_t dispatch_zb(const void* P2, const float* c, const float* h, int B, in
 }  // namespace
 
 hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D,
-                               int F, int r, float tau, uint64_t* mask, float* logits, float* hbuf, hipStream_t st) {
+                               int F, int r, float tau, int n_hot, uint64_t* mask, float* logits, float* hbuf,
+                               hipStream_t st) {
   if (B != 1) return hipErrorInvalidValue;   // batches of several tokens take the matrix-core kernels
   const int nch = (D / 8 + NTH - 1) / NTH;   // 16-byte chunks per thread (D <= 16384: at most 8)
   hipError_t e;
@@ -415,20 +416,20 @@ hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, c
   else e = launch_h<8>(P1, x, x_norm, B, D, r, hbuf, st);
   if (e != hipSuccess) return e;
   switch (z_shape(r)) {
-    case 801: return launch_z<8, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 802: return launch_z<8, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 804: return launch_z<8, 4>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 808: return launch_z<8, 8>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 816: return launch_z<8, 16>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 1601: return launch_z<16, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 1602: return launch_z<16, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 1604: return launch_z<16, 4>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 1608: return launch_z<16, 8>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 3201: return launch_z<32, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 3202: return launch_z<32, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 3204: return launch_z<32, 4>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 6401: return launch_z<64, 1>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-    case 6402: return launch_z<64, 2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+    case 801: return launch_z<8, 1>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 802: return launch_z<8, 2>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 804: return launch_z<8, 4>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 808: return launch_z<8, 8>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 816: return launch_z<8, 16>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 1601: return launch_z<16, 1>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 1602: return launch_z<16, 2>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 1604: return launch_z<16, 4>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 1608: return launch_z<16, 8>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 3201: return launch_z<32, 1>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 3202: return launch_z<32, 2>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 3204: return launch_z<32, 4>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 6401: return launch_z<64, 1>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+    case 6402: return launch_z<64, 2>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -455,8 +456,8 @@ hipError_t sffn_launch_predict_hb(const void* P1, const float* x, int x_norm, in
 // Stage 2 for 2 <= B <= 4 tokens: logits [B][F] (optional) and the union mask from h [B][r]. (At 8 tokens the
 // matrix-core kernel is the faster one.)
 hipError_t sffn_launch_predict_zb(const void* P2, const float* c, const float* hbuf, int B, int F, int r, float tau,
-                                  uint64_t* mask, float* logits, hipStream_t st) {
+                                  int n_hot, uint64_t* mask, float* logits, hipStream_t st) {
   if (B < 2 || B > 4) return hipErrorInvalidValue;
-  if (B <= 2) return dispatch_zb<2>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
-  return dispatch_zb<4>(P2, c, hbuf, B, F, r, tau, mask, logits, st);
+  if (B <= 2) return dispatch_zb<2>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
+  return dispatch_zb<4>(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, st);
 }

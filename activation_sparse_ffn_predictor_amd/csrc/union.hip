@@ -178,7 +178,8 @@ __global__ __launch_bounds__(NTK) void k_mt_h(const uint4* __restrict__ P1, cons
 template <int NTT>
 __global__ __launch_bounds__(256) void k_mt_z(const uint4* __restrict__ P2, const float* __restrict__ c,
                                               const float* __restrict__ h, int B, int F, int r, float tau,
-                                              uint64_t* __restrict__ mask, float* __restrict__ logits) {
+                                              int n_hot, uint64_t* __restrict__ mask,
+                                              float* __restrict__ logits) {
   __shared__ uint32_t bits16[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int k0 = blockIdx.x * 64 + w * 16;
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(256) void k_mt_z(const uint4* __restrict__ P2, cons
     for (int q = 0; q < CH; ++q) {
       const int kb = c0 + q;
       const int k = kb * 32 + (lane >> 4) * 8;
-      av[q] = bp.ld16(boff(kb < KB && row < F && k < r, ((uint32_t)row * r + k) * 2u));
+      av[q] = bp.ld16(boff(kb < KB && row < F && row >= n_hot && k < r, ((uint32_t)row * r + k) * 2u));
 #pragma unroll
       for (int t = 0; t < NTT; ++t) hr[q][t] = load_xraw(bh, B, kb < KB ? r : 0, t, kb);
     }
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(256) void k_mt_z(const uint4* __restrict__ P2, cons
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int kk = k0 + (lane >> 4) * 4 + i;
-    cb[i] = bc.ldf(boff(kk < F, (uint32_t)kk * 4u));
+    cb[i] = bc.ldf(boff(kk < F && kk >= n_hot, (uint32_t)kk * 4u));
   }
   uint32_t word = 0;
 #pragma unroll
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(256) void k_mt_z(const uint4* __restrict__ P2, cons
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       const int tok = t * 16 + (lane & 15);
-      const float z = acc[t][i] + cb[i];
+      const float z = kk < n_hot ? INFINITY : acc[t][i] + cb[i];   // always-active prefix: no row was read
       const bool valid = tok < B && kk < F;
       if (valid && logits) logits[(size_t)tok * F + kk] = z;
       any = any || (valid && z > tau);
@@ -269,7 +270,7 @@ __device__ __forceinline__ int locate_lane(const uint64_t* words, const int* rof
 constexpr int WMAXU = 2;
 
 // Active-row gather with fused activation, 16 dense indices per block, k split over 8 waves.
-// Q4: W = nibble planes + scale planes. ACT 1 = ReGLU (gate + up), 0 = ReLU (up).
+// Q4: W = nibble planes + scale planes. ACT 1 = ReGLU (gate + up), 0 = ReLU (up), 2 = squared ReLU (up).
 template <int NTT, int ACT, bool Q4>
 __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, const void* __restrict__ Sg,
                                                  const float* __restrict__ bg, const void* __restrict__ Wu,
@@ -277,8 +278,9 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
                                                  const float* __restrict__ x, int B, int D, int F,
                                                  const uint64_t* __restrict__ mask, int32_t* __restrict__ active,
                                                  int32_t* __restrict__ n_active, float* __restrict__ abuf) {
+  constexpr bool GT = ACT == 1;                        // gated (ReGLU): a gate row per neuron
   extern __shared__ uint64_t lds64[];
-  __shared__ f32x4 part[KW][ACT + 1][NTT][64];
+  __shared__ f32x4 part[KW][GT ? 2 : 1][NTT][64];
   __shared__ int ids16[16];
   const int nw = (F + 63) >> 6;
   const int wpt = (nw + NTK - 1) / NTK;
@@ -307,8 +309,8 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
   const int nblk = D >> 5;
   const uint32_t wbytes = Q4 ? (uint32_t)F * (uint32_t)(D >> 1) : (uint32_t)F * D * 2u;
   const uint32_t sbytes = (uint32_t)F * nblk * 2u;
-  const Buf bwu(Wu, wbytes), bwg(ACT ? Wg : Wu, ACT ? wbytes : 0u);
-  const Buf bsu(Q4 ? Su : Wu, Q4 ? sbytes : 0u), bsg(Q4 && ACT ? Sg : Wu, Q4 && ACT ? sbytes : 0u);
+  const Buf bwu(Wu, wbytes), bwg(GT ? Wg : Wu, GT ? wbytes : 0u);
+  const Buf bsu(Q4 ? Su : Wu, Q4 ? sbytes : 0u), bsg(Q4 && GT ? Sg : Wu, Q4 && GT ? sbytes : 0u);
   // rows of this lane's 4 outputs (D layout): 4*(l/16)+i
   int idr[4];
 #pragma unroll
@@ -336,18 +338,18 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
       if constexpr (Q4) {
         const uint32_t o = (uint32_t)(ok ? idl : 0) * (uint32_t)(D >> 1) + (uint32_t)kb * 16u + ((lane >> 4) & 1) * 8u;
         C.qu[q] = bwu.ld8(boff(ok, o));
-        if (ACT) C.qg[q] = bwg.ld8(boff(ok, o));
+        if (GT) C.qg[q] = bwg.ld8(boff(ok, o));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool okr = kb < kb1 && idr[i] >= 0;
           const uint32_t so = ((uint32_t)(okr ? idr[i] : 0) * nblk + kb) * 2u;
           C.su[q][i] = bsu.ldh(boff(okr, so));
-          if (ACT) C.sg[q][i] = bsg.ldh(boff(okr, so));
+          if (GT) C.sg[q][i] = bsg.ldh(boff(okr, so));
         }
       } else {
         const uint32_t o = ((uint32_t)(ok ? idl : 0) * D + k) * 2u;
         C.wu[q] = bwu.ld16(boff(ok, o));
-        if (ACT) C.wg[q] = bwg.ld16(boff(ok, o));
+        if (GT) C.wg[q] = bwg.ld16(boff(ok, o));
       }
 #pragma unroll
       for (int t = 0; t < NTT; ++t) C.xr[q][t] = load_xraw(bx, B, kb < kb1 ? D : 0, t, kb);
@@ -359,10 +361,10 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
       half8 a_u, a_g;
       if constexpr (Q4) {
         a_u = q4_to_half8(C.qu[q], lane >> 4);
-        if (ACT) a_g = q4_to_half8(C.qg[q], lane >> 4);
+        if (GT) a_g = q4_to_half8(C.qg[q], lane >> 4);
       } else {
         a_u = __builtin_bit_cast(half8, C.wu[q]);
-        if (ACT) a_g = __builtin_bit_cast(half8, C.wg[q]);
+        if (GT) a_g = __builtin_bit_cast(half8, C.wg[q]);
       }
 #pragma unroll
       for (int t = 0; t < NTT; ++t) {
@@ -373,14 +375,14 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
           const f32x4 pu = mfma16(a_u, xl, mfma16(a_u, xh, z));
 #pragma unroll
           for (int i = 0; i < 4; ++i) au[t][i] = fmaf(C.su[q][i], pu[i], au[t][i]);
-          if (ACT) {
+          if (GT) {
             const f32x4 pg = mfma16(a_g, xl, mfma16(a_g, xh, z));
 #pragma unroll
             for (int i = 0; i < 4; ++i) ag[t][i] = fmaf(C.sg[q][i], pg[i], ag[t][i]);
           }
         } else {
           au[t] = mfma16(a_u, xl, mfma16(a_u, xh, au[t]));
-          if (ACT) ag[t] = mfma16(a_g, xl, mfma16(a_g, xh, ag[t]));
+          if (GT) ag[t] = mfma16(a_g, xl, mfma16(a_g, xh, ag[t]));
         }
       }
     }
@@ -399,29 +401,33 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
 #pragma unroll
   for (int t = 0; t < NTT; ++t) {
     part[w][0][t][lane] = au[t];
-    if (ACT) part[w][ACT][t][lane] = ag[t];
+    if (GT) part[w][1][t][lane] = ag[t];
   }
   __syncthreads();
   if (w == 0) {
-    const float* bp = ACT ? bg : bu;
+    const float* bp = GT ? bg : bu;
     float bias[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) bias[i] = (bp && idr[i] >= 0) ? bp[idr[i]] : 0.f;
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       f32x4 u = part[0][0][t][lane], g = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (ACT) g = part[0][ACT][t][lane];
+      if (GT) g = part[0][1][t][lane];
       for (int ww = 1; ww < KW; ++ww) {
         u += part[ww][0][t][lane];
-        if (ACT) g += part[ww][ACT][t][lane];
+        if (GT) g += part[ww][1][t][lane];
       }
       const int tok = t * 16 + (lane & 15);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ii = i0 + (lane >> 4) * 4 + i;
         float a;
-        if (ACT) a = fmaxf(g[i] + bias[i], 0.f) * u[i];
-        else a = fmaxf(u[i] + bias[i], 0.f);
+        if (GT) {
+          a = fmaxf(g[i] + bias[i], 0.f) * u[i];
+        } else {
+          a = fmaxf(u[i] + bias[i], 0.f);
+          if (ACT == 2) a *= a;
+        }
         if (tok < B && ii < n) abuf[(size_t)ii * B + tok] = a;
       }
     }
@@ -622,7 +628,8 @@ __global__ void k_sum_parts(const float* __restrict__ part, int KS, int n, float
 
 template <int NTT>
 hipError_t predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F, int r,
-                      float tau, uint64_t* mask, float* logits, float* hbuf, float* hpart, int KSH, hipStream_t st) {
+                      float tau, int n_hot, uint64_t* mask, float* logits, float* hbuf, float* hpart, int KSH,
+                      hipStream_t st) {
   hipError_t e;
   if (KSH > 0) {                                       // else hbuf holds h already
     SFFN_LAUNCH(0, k_mt_h<NTT>, dim3((r + 15) / 16, KSH), dim3(NTK), 0, st, (const uint4*)P1, x, B, D, r, hpart);
@@ -633,8 +640,8 @@ hipError_t predict_mt(const void* P1, const void* P2, const float* c, const floa
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  SFFN_LAUNCH(1, k_mt_z<NTT>, dim3((F + 63) / 64), dim3(256), 0, st, (const uint4*)P2, c, hbuf, B, F, r, tau, mask,
-              logits);
+  SFFN_LAUNCH(1, k_mt_z<NTT>, dim3((F + 63) / 64), dim3(256), 0, st, (const uint4*)P2, c, hbuf, B, F, r, tau, n_hot,
+              mask, logits);
   return hipGetLastError();
 }
 
@@ -690,14 +697,14 @@ hipError_t sffn_launch_norm_tokens(const float* x, int B, int D, float* xn, hipS
 }
 
 hipError_t sffn_launch_predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F,
-                                  int r, float tau, uint64_t* mask, float* logits, float* hbuf, float* hpart, int KSH,
-                                  hipStream_t st) {
+                                  int r, float tau, int n_hot, uint64_t* mask, float* logits, float* hbuf,
+                                  float* hpart, int KSH, hipStream_t st) {
   const int ntt = (B + 15) / 16;
   switch (ntt) {
-    case 1: return predict_mt<1>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, hpart, KSH, st);
-    case 2: return predict_mt<2>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, hpart, KSH, st);
-    case 3: return predict_mt<3>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, hpart, KSH, st);
-    case 4: return predict_mt<4>(P1, P2, c, x, B, D, F, r, tau, mask, logits, hbuf, hpart, KSH, st);
+    case 1: return predict_mt<1>(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, hbuf, hpart, KSH, st);
+    case 2: return predict_mt<2>(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, hbuf, hpart, KSH, st);
+    case 3: return predict_mt<3>(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, hbuf, hpart, KSH, st);
+    case 4: return predict_mt<4>(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, hbuf, hpart, KSH, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -709,7 +716,9 @@ hipError_t sffn_launch_rows_mt(int act, bool q4, const void* Wg, const void* Sg,
 #define RMT(N, A, Q) return rows_mt<N, A, Q>(Wg, Sg, bg, Wu, Su, bu, x, B, D, F, mask, active, n_active, abuf, st)
 #define RMT_A(N) \
   if (act == 1) { if (q4) RMT(N, 1, true); RMT(N, 1, false); } \
-  else { if (q4) RMT(N, 0, true); RMT(N, 0, false); }
+  if (act == 2) { if (q4) RMT(N, 2, true); RMT(N, 2, false); } \
+  if (q4) RMT(N, 0, true); \
+  RMT(N, 0, false);
   switch (ntt) {
     case 1: RMT_A(1)
     case 2: RMT_A(2)

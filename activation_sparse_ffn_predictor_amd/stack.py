@@ -4,6 +4,10 @@ library's normalise-on-load option (a parameter-free LayerNorm). A step can be c
 
 The pages' decode touches the whole model for every token (Turkish article, motivation section); the stack
 is the FFN part of that, with the neuron order of every layer chosen hot-first (pack.hot_first_perm).
+
+Layers may differ in predictor rank (Turkish article, "Adaptive sparsity predictors": the predictor is sized per
+layer), and with ``hot_prefix`` each layer's saturated neurons, stored first, are declared always active so the
+predictor reads no rows for them (sffn_predict_hot).
 """
 from __future__ import annotations
 
@@ -20,13 +24,15 @@ from .pack import hot_first_perm, pack_layer
 
 class SparseFFNStack:
     def __init__(self, wl: sg.Workload, device="cuda:0", layers: Optional[List[int]] = None, with_c: bool = True,
-                 max_batch: int = 1, seed: int = sg.MASTER_SEED):
+                 max_batch: int = 1, seed: int = sg.MASTER_SEED, hot_prefix: bool = False):
         self.wl = wl
         self.device = torch.device(device)
         self.layer_ids = list(range(wl.L)) if layers is None else list(layers)
         self.q4 = wl.wdtype == "q4"
         self.with_c = with_c
         self.max_batch = max_batch
+        self.ranks = [wl.rank(l) for l in self.layer_ids]
+        self.n_hot = [sg.saturated_count(wl, l, seed) if hot_prefix else 0 for l in self.layer_ids]
         self.layers: List[Dict[str, torch.Tensor]] = []
         for l in self.layer_ids:
             logical = sg.layer_device(wl, l, self.device, seed=seed, with_c=with_c)
@@ -40,7 +46,8 @@ class SparseFFNStack:
         self.active = torch.zeros((L, F), dtype=torch.int32, device=self.device)
         self.n_active = torch.zeros((L,), dtype=torch.int32, device=self.device)
         self.y = torch.zeros((L, max_batch, D), dtype=torch.float32, device=self.device)
-        self.ws = torch.zeros(_lib.workspace_size(max_batch, D, F, wl.r), dtype=torch.uint8, device=self.device)
+        self.ws = torch.zeros(_lib.workspace_size(max_batch, D, F, max(self.ranks)), dtype=torch.uint8,
+                              device=self.device)
         self.x_in = torch.zeros((max_batch, D), dtype=torch.float32, device=self.device)
         self.graphs = {}
 
@@ -48,7 +55,8 @@ class SparseFFNStack:
     def layer_call(self, i: int, x: torch.Tensor, x_norm: bool, y: torch.Tensor, logits=None):
         """Predict + forward of stored layer i on input x [B, D]; writes self.mask[i], active[i], n_active[i], y."""
         t, wl = self.layers[i], self.wl
-        _lib.predict(t["P1"], t["P2"], t.get("c"), x, wl.t, self.mask[i], self.ws, logits=logits, x_norm=x_norm)
+        _lib.predict(t["P1"], t["P2"], t.get("c"), x, wl.t, self.mask[i], self.ws, logits=logits, x_norm=x_norm,
+                     n_hot=self.n_hot[i])
         if self.q4:
             g = (t["Q_gate"], t["S_gate"]) if wl.act == "reglu" else None
             _lib.forward_q4(wl.act, g, t.get("b_gate"), (t["Q_up"], t["S_up"]), t.get("b_up"),
@@ -87,5 +95,7 @@ class SparseFFNStack:
         return wl.n_mats * row
 
     def predictor_bytes(self) -> int:
+        """Predictor bytes one step reads over the whole stack: P1, and the rows of P2 outside the always-active
+        prefix."""
         wl = self.wl
-        return 2 * (wl.r * wl.D + wl.F * wl.r)
+        return sum(2 * (r * wl.D + (wl.F - h) * r) for r, h in zip(self.ranks, self.n_hot))

@@ -40,6 +40,12 @@ def parse():
     ap.add_argument("--workload", "--config", default="relullama_7b",
                     help="toy_relu | relullama_7b | llama2_13b | falcon_40b | llama2_70b_q4 (or c1..c5)")
     ap.add_argument("--batch", type=int, default=1, help="tokens per decode step (union mask when > 1)")
+    ap.add_argument("--act", choices=("relu", "sqrelu", "reglu"), default=None,
+                    help="activation instead of the workload's own (same shapes)")
+    ap.add_argument("--hot-prefix", action="store_true",
+                    help="declare each layer's saturated neurons (stored first) always active: no predictor rows")
+    ap.add_argument("--rank-schedule", choices=("fixed", "adaptive"), default="fixed",
+                    help="adaptive: predictor ranks cycle over 0.5, 1, 1.5, 1 times the workload's rank by layer")
     ap.add_argument("--profile-steps", type=int, default=8, help="eager steps per profiled kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--prompt", type=int, default=None,
@@ -148,11 +154,15 @@ def main():
     from activation_sparse_ffn_predictor_amd.stack import SparseFFNStack
 
     wl = sg.workload(args.workload)
+    if args.act and args.act != wl.act:
+        wl = sg.custom(wl, act=args.act, name=f"{wl.name}_{args.act}")
+    if args.rank_schedule == "adaptive":
+        wl = sg.with_rank_schedule(wl)
     B = args.batch
     PB = wl.prompt if args.prompt is None else args.prompt
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
-    stack = SparseFFNStack(wl, dev, max_batch=max(B, PB))
+    stack = SparseFFNStack(wl, dev, max_batch=max(B, PB), hot_prefix=args.hot_prefix)
     L = len(stack.layers)
     setup_s = time.perf_counter() - t0
     print(f"# setup: {wl.name}, {L} layers resident, {setup_s:.1f} s", file=sys.stderr, flush=True)
@@ -228,7 +238,7 @@ def main():
     n_mean = n_acc.cpu().numpy().astype(np.float64) / K          # mean active rows per layer per step
     row_bytes = stack.active_weight_bytes_per_row()
     active_bytes_step = float(n_mean.sum()) * row_bytes
-    pred_bytes_step = L * stack.predictor_bytes()
+    pred_bytes_step = stack.predictor_bytes()
     tok_s = B * K / (ms_total * 1e-3)
 
     # ---- per-kernel durations: P eager steps of the same stack on the timed inputs; every launch of the
@@ -261,7 +271,8 @@ def main():
     else:
         bytes_rows = n_prof * rows_mats * one_row                # per launch of kernel 2
         bytes_cols = n_prof * one_row                            # per launch of kernel 3
-    kb = {0: np.full(len(prof[0]), 2.0 * wl.r * wl.D), 1: np.full(len(prof[1]), 2.0 * wl.F * wl.r),
+    ranks, hots = np.asarray(stack.ranks, np.float64), np.asarray(stack.n_hot, np.float64)
+    kb = {0: np.tile(2.0 * ranks * wl.D, P), 1: np.tile(2.0 * (wl.F - hots) * ranks, P),   # launches in layer order
           2: bytes_rows, 3: bytes_cols}
     tot = {k: float(prof[k].sum()) for k in prof}
     dom = max(tot, key=tot.get)
@@ -288,9 +299,10 @@ def main():
         "dtype": "f16" if not stack.q4 else "q4_0",
         "accumulate": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "d_model": wl.D, "d_ffn": wl.F, "rank": wl.r, "layers": L, "batch": B,
+        "config": {"workload": wl.name, "d_model": wl.D, "d_ffn": wl.F,
+                   "rank": wl.r if not wl.ranks else list(wl.ranks), "layers": L, "batch": B,
                    "activation": wl.act, "weights": "fp16" if not stack.q4 else "q4_0", "density_target": wl.density,
-                   "graph": not args.no_graph},
+                   "hot_prefix_per_layer": round(float(np.mean(stack.n_hot)), 1), "graph": not args.no_graph},
         "active_weight_gbs": round(active_bytes_step / (ms_step * 1e-3) / 1e9, 1),
         "forward_active_gbs": round(fwd_gbs, 1),
         "all_bytes_gbs": round((active_bytes_step + pred_bytes_step) / (ms_step * 1e-3) / 1e9, 1),

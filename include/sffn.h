@@ -17,7 +17,7 @@
  *   - "Neuron placement and management" (same article): neurons are stored in
  *     a chosen order and a table maps each back to its original position;
  *   - summary bullets and "Limitations/FAQ" (Indonesian digest): ReLU-family
- *     FFNs (ReLU, ReGLU); "Quantization": INT4 Q4_0 weights.
+ *     FFNs (ReLU, ReGLU, squared ReLU); "Quantization": INT4 Q4_0 weights.
  *
  * Notation. D = d_model, F = d_ffn (neurons), r = predictor rank, B = tokens
  * of one call (1 for decode; B > 1 computes every token over the union of the
@@ -93,7 +93,8 @@ typedef enum {
 
 typedef enum {
   SFFN_ACT_RELU = 0,   /* a_k = max(0, W_up[k] x + b_up[k])                        */
-  SFFN_ACT_REGLU = 1   /* a_k = max(0, W_gate[k] x + b_gate[k]) * (W_up[k] x)      */
+  SFFN_ACT_REGLU = 1,  /* a_k = max(0, W_gate[k] x + b_gate[k]) * (W_up[k] x)      */
+  SFFN_ACT_SQRELU = 2  /* a_k = max(0, W_up[k] x + b_up[k])^2  (squared ReLU; operands as for RELU) */
 } sffn_act;
 
 /* One Q4_0 matrix (device pointers, layout above). */
@@ -140,12 +141,22 @@ int sffn_forward_path(int act, int q4, int B, int D, int F);
 int sffn_predict(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F,
                  int r, float t, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream);
 
+/* sffn_predict with an always-active prefix ("Neuron placement and management", Turkish article: neurons are
+ * stored in a chosen order, here hottest first). Stored neurons 0 .. n_hot-1 are set in the mask whatever the
+ * predictor would say, and their rows of P2 and entries of c are never read (P2 and c must still span all F
+ * rows; only rows >= n_hot are loaded). Their logits, if requested, are written as +infinity. Every other
+ * neuron is decided exactly as by sffn_predict, which is this call with n_hot = 0. SFFN_ERR_ARG if n_hot is
+ * outside 0..F. */
+int sffn_predict_hot(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F,
+                     int r, float t, int n_hot, uint64_t* mask, float* logits, void* ws, size_t ws_bytes,
+                     void* stream);
+
 /* Neuron-aware sparse FFN over the neurons set in `mask` ("Neuron-aware operator").
  *   compaction: active[0 .. n) = ascending stored ids of the set bits, *n_active = n
  *   a[b, j]  = act(row active[j] of W_gate / W_up, xn[b, :])   (only active rows are read)
  *   y[b, :]  = sum_j a[b, j] * W_downT[active[j], :]          (only active rows are read)
  * xn as in sffn_predict. W_gate / b_gate are used (and required) for REGLU only;
- * b_up may be NULL (0). active [F] int32 and n_active [1] int32 are device
+ * RELU and SQRELU read W_up and b_up; b_up may be NULL (0). active [F] int32 and n_active [1] int32 are device
  * outputs; y [B, D] is overwritten. Uses the workspace. Two kernels; the union kernels add a sum of the row-split partials (and a normalisation pass for x_norm). */
 int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W_up, const float* b_up,
                  const void* W_downT, const float* x, int x_norm, int B, int D, int F, const uint64_t* mask,

@@ -5,5 +5,5 @@ import this package. The GPU library and its Python binding never do.
 """
 from .sparse_ffn import (  # noqa: F401
     BAND, NORM_EPS, activations, band_neurons, dequant_q4_cols, dequant_q4_rows, ffn_dense, ffn_masked, layer,
-    logical_weights, predictor_logits, layer_norm, stack, threshold_logit, token_masks, union_mask,
+    logical_weights, predictor_logits, layer_norm, stack, threshold_logit, token_masks, union_mask, with_hot_prefix,
 )

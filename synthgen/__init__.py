@@ -61,7 +61,7 @@ class Workload:
     F: int              # d_ffn (neurons)
     r: int              # predictor rank
     L: int              # layers
-    act: str            # "relu" (W_up + b_up, W_down) or "reglu" (W_gate + b_gate, W_up, W_down)
+    act: str            # "relu" / "sqrelu" (W_up + b_up, W_down) or "reglu" (W_gate + b_gate, W_up, W_down)
     wdtype: str         # "f16" or "q4"
     sigma_w: float      # weight std (fp16 workloads)
     sigma_p: float      # predictor factor std
@@ -71,6 +71,11 @@ class Workload:
     steps: int = 128    # decode steps
     prompt: int = 0     # prompt tokens handled as one union-mask batch (0 = none)
     t: float = 0.5      # predictor sigmoid threshold
+    ranks: Optional[Tuple[int, ...]] = None   # per-layer predictor ranks, cycled over layers (None: r everywhere)
+
+    def rank(self, layer: int) -> int:
+        """Predictor rank of one layer."""
+        return self.ranks[layer % len(self.ranks)] if self.ranks else self.r
 
     @property
     def n_mats(self) -> int:
@@ -84,9 +89,9 @@ class Workload:
             return math.sqrt(self.D * var_q * e_s2)
         return self.sigma_w * math.sqrt(self.D)
 
-    def logit_std(self) -> float:
-        """Std of one predictor logit (P2 P1 x)[k] for x ~ N(0, I)."""
-        return self.sigma_p ** 2 * math.sqrt(self.r * self.D)
+    def logit_std(self, layer: int = 0) -> float:
+        """Std of one predictor logit (P2 P1 x)[k] for x ~ N(0, I) at the layer's rank."""
+        return self.sigma_p ** 2 * math.sqrt(self.rank(layer) * self.D)
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -109,6 +114,17 @@ ALIASES = {"c1": "toy_relu", "c2": "relullama_7b", "c3": "llama2_13b", "c4": "fa
 
 def workload(name: str) -> Workload:
     return WORKLOADS[ALIASES.get(name, name)]
+
+
+# Per-layer rank schedule: multiples of the base rank, cycled over the layers (mean 1, so the stack holds as many
+# predictor bytes as with the base rank everywhere). A stand-in for ranks sized per layer; no training is done.
+RANK_FACTORS = (0.5, 1.0, 1.5, 1.0)
+
+
+def with_rank_schedule(base: Workload, factors: Sequence[float] = RANK_FACTORS) -> Workload:
+    """Copy of a workload whose layers cycle through ranks factor * r (multiples of 8); r becomes the largest."""
+    ranks = tuple(max(8, int(round(f * base.r / 8.0)) * 8) for f in factors)
+    return custom(base, r=max(ranks), ranks=ranks, name=base.name + "_adaptive_rank")
 
 
 def custom(base: Workload, **kw) -> Workload:
@@ -238,6 +254,12 @@ def neuron_probs(wl: Workload, layer: int, seed: int = MASTER_SEED) -> np.ndarra
     return p_by_rank[neuron_ranks(wl, layer, seed) - 1]
 
 
+def saturated_count(wl: Workload, layer: int, seed: int = MASTER_SEED) -> int:
+    """Neurons of one layer whose activation probability sits at the cap (the hottest ones; stored first in a
+    hot-first order)."""
+    return int(np.count_nonzero(neuron_probs(wl, layer, seed) >= ZIPF_CAP))
+
+
 def _ndtri(p: np.ndarray) -> np.ndarray:
     from scipy.special import ndtri
     return ndtri(p)
@@ -252,13 +274,13 @@ def act_bias(wl: Workload, layer: int, seed: int = MASTER_SEED) -> np.ndarray:
 def predictor_bias(wl: Workload, layer: int, seed: int = MASTER_SEED) -> np.ndarray:
     """Calibrated predictor bias c_k = logit_std * Phi^-1(p_k): the predictor marks neuron k with
     probability p_k for x ~ N(0, I) at threshold 0.5. fp32."""
-    return (wl.logit_std() * _ndtri(neuron_probs(wl, layer, seed))).astype(np.float32)
+    return (wl.logit_std(layer) * _ndtri(neuron_probs(wl, layer, seed))).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------- logical layer tensors
-def layer_shapes(wl: Workload) -> Dict[str, Tuple[Tuple[int, ...], str, int]]:
+def layer_shapes(wl: Workload, layer: int = 0) -> Dict[str, Tuple[Tuple[int, ...], str, int]]:
     """name -> (shape, dtype, tag) of the logical tensors of one layer."""
-    D, F, r = wl.D, wl.F, wl.r
+    D, F, r = wl.D, wl.F, wl.rank(layer)
     s = {"P1": ((r, D), "f16", TAG_P1), "P2": ((F, r), "f16", TAG_P2)}
     if wl.wdtype == "f16":
         if wl.act == "reglu":
@@ -292,7 +314,7 @@ def layer_host(wl: Workload, layer: int, seed: int = MASTER_SEED, names: Optiona
     """Logical tensors of one layer as host numpy arrays (fp16 / uint8 / fp32)."""
     key = key_seed(wl.index, seed)
     out: Dict[str, np.ndarray] = {}
-    for name, (shape, dt, tag) in layer_shapes(wl).items():
+    for name, (shape, dt, tag) in layer_shapes(wl, layer).items():
         if names is not None and name not in names:
             continue
         a = np.empty(shape, dtype={"f16": np.float16, "u8": np.uint8}[dt])
@@ -314,7 +336,7 @@ def layer_device(wl: Workload, layer: int, device="cuda", seed: int = MASTER_SEE
     key = key_seed(wl.index, seed)
     tdt = {"f16": torch.float16, "u8": torch.uint8}
     out = {}
-    for name, (shape, dt, tag) in layer_shapes(wl).items():
+    for name, (shape, dt, tag) in layer_shapes(wl, layer).items():
         t = torch.empty(shape, dtype=tdt[dt], device=device)
         _fill_named(name, t, wl, layer, key, tag)
         out[name] = t

@@ -6,7 +6,9 @@ Comparison rules (the pages leave ties open; the design notes list them):
     token clearly above it), which may go either way;
   * compaction: active[0:n] is strictly ascending, in range, and equal to the set bits of the mask;
   * y: per token, max |y_gpu - y_ref| <= 2e-3 * max |y_ref|, where y_ref is the oracle's masked FFN under the
-    oracle mask with band neurons set as the GPU decided (either decision is valid); y_ref == 0 => y_gpu == 0.
+    oracle mask with band neurons set as the GPU decided (either decision is valid); y_ref == 0 => y_gpu == 0;
+  * always-active prefix (n_hot > 0): the first n_hot stored neurons must be set (they are never band neurons)
+    and their logits are +infinity.
 """
 from __future__ import annotations
 
@@ -65,7 +67,7 @@ def host_case(wl, layer=0, perm=None):
     return LayerCase(wl, layer, host, oracle.logical_weights(host), {}, np.asarray(p))
 
 
-def run_gpu(case: LayerCase, x: torch.Tensor, x_norm=False, t=None, want_logits=True):
+def run_gpu(case: LayerCase, x: torch.Tensor, x_norm=False, t=None, want_logits=True, n_hot=0):
     wl, d = case.wl, case.dev
     B, D = x.shape
     dev = x.device
@@ -76,7 +78,7 @@ def run_gpu(case: LayerCase, x: torch.Tensor, x_norm=False, t=None, want_logits=
     logits = torch.full((B, wl.F), float("nan"), dtype=torch.float32, device=dev) if want_logits else None
     ws = torch.zeros(_lib.workspace_size(B, D, wl.F, wl.r), dtype=torch.uint8, device=dev)
     tt = wl.t if t is None else t
-    _lib.predict(d["P1"], d["P2"], d.get("c"), x, tt, mask, ws, logits=logits, x_norm=x_norm)
+    _lib.predict(d["P1"], d["P2"], d.get("c"), x, tt, mask, ws, logits=logits, x_norm=x_norm, n_hot=n_hot)
     if wl.wdtype == "q4":
         g = (d["Q_gate"], d["S_gate"]) if wl.act == "reglu" else None
         _lib.forward_q4(wl.act, g, d.get("b_gate"), (d["Q_up"], d["S_up"]), d.get("b_up"), (d["Q_downT"], d["S_downT"]),
@@ -95,7 +97,7 @@ def mask_bits(words: np.ndarray, F: int) -> np.ndarray:
     return bits[:F].astype(bool)
 
 
-def check(case: LayerCase, x_host: np.ndarray, res: dict, x_norm=False, t=None, tol=Y_TOL):
+def check(case: LayerCase, x_host: np.ndarray, res: dict, x_norm=False, t=None, tol=Y_TOL, n_hot=0):
     """Compare one GPU layer result with the oracle; raise AssertionError with details on mismatch.
     Returns a dict of statistics."""
     wl, F = case.wl, case.wl.F
@@ -104,6 +106,13 @@ def check(case: LayerCase, x_host: np.ndarray, res: dict, x_norm=False, t=None, 
     z = oracle.predictor_logits(case.w["P1"], case.w["P2"], xo, case.w.get("c"))
     m_ref = oracle.union_mask(oracle.token_masks(z, tt))
     band = oracle.band_neurons(z, tt)
+    hot = np.zeros(F, dtype=bool)                       # original ids of the always-active stored prefix
+    hot[case.perm[:n_hot]] = True
+    if n_hot:
+        stored = oracle.with_hot_prefix(m_ref[case.perm], n_hot)   # the oracle's rule, in stored order
+        m_ref = np.zeros(F, dtype=bool)
+        m_ref[case.perm[stored]] = True
+        band &= ~hot
     # GPU set in original ids
     bits = mask_bits(res["mask"], F)
     # bits beyond F must be zero
@@ -136,7 +145,9 @@ def check(case: LayerCase, x_host: np.ndarray, res: dict, x_norm=False, t=None, 
             assert err <= tol * ymax, f"token {b}: max err {err:.3e} > {tol} * {ymax:.3e}"
             errs.append(err / ymax)
     if res.get("logits") is not None:
-        lerr = np.max(np.abs(res["logits"][:, case.perm.argsort()] - z)) if F else 0.0
+        lg = res["logits"][:, case.perm.argsort()]    # back to original ids
+        assert np.all(np.isposinf(lg[:, hot])), "logits of the always-active prefix are not +inf"
+        lerr = np.max(np.abs(lg[:, ~hot] - z[:, ~hot])) if (~hot).any() else 0.0
     else:
         lerr = None
     return dict(n=n, band=int(band.sum()), flips=int((m_gpu != m_ref).sum()), rel_err=max(errs) if errs else 0.0,

@@ -133,3 +133,32 @@ def test_forward_path_routing():
     assert _lib.forward_path("reglu", False, 4, 5120, 13824) == _lib.PATH_UNION
     assert _lib.forward_path("relu", True, 64, 8192, 28672) == _lib.PATH_UNION
     assert _lib.lib().sffn_forward_path(5, 0, 1, 64, 64) == -1
+
+
+def _predict_hot(**kw):
+    a = dict(P1=A, P2=A, c=None, x=A, x_norm=0, B=1, D=512, F=2048, r=64, t=0.5, n_hot=10, mask=A, logits=None, ws=A,
+             ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return _lib.lib().sffn_predict_hot(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_hot=-1), 6), (dict(n_hot=2049), 6), (dict(P2=None), 1), (dict(r=12), 2), (dict(t=1.5), 6),
+    (dict(mask=MIS), 3), (dict(ws_bytes=8), 4),
+    (dict(n_hot=0, ws_bytes=8), 4), (dict(n_hot=2048, ws_bytes=8), 4), (dict(B=9, n_hot=5, ws_bytes=8), 4),
+])
+def test_predict_hot_rejects(kw, status):
+    # n_hot in 0..F passes validation (the fake workspace size is what fails in the last three)
+    assert _predict_hot(**kw) == status
+
+
+def test_squared_relu_is_accepted_on_every_path():
+    assert _forward(act=2, ws_bytes=16) == 4
+    assert _forward(act=2, B=3, ws_bytes=16) == 4
+    assert _forward_q4(act=2, Wg=_lib._Q4(None, None), bg=None, bu=A, ws_bytes=16) == 4
+    assert _lib.forward_path("sqrelu", False, 1, 8192, 32768) == _lib.PATH_FUSED   # as ReLU: up to D = 8192
+    assert _lib.forward_path("sqrelu", False, 1, 8704, 1000) == _lib.PATH_DECODE
+    assert _lib.forward_path("sqrelu", True, 1, 8192, 28672) == _lib.PATH_FUSED
+    assert _lib.forward_path("sqrelu", False, 2, 4096, 11008) == _lib.PATH_DECODE
+    assert _lib.forward_path("sqrelu", False, 4, 4096, 11008) == _lib.PATH_UNION
+    assert _lib.forward_path(3, False, 1, 512, 2048) == -1

@@ -22,19 +22,35 @@ def _check_stack(stack, cases, x0, B):
     for i, case in enumerate(cases):
         res = _layer_results(stack, i, B)
         xin = x0 if i == 0 else stack.y[i - 1, :B].cpu().numpy()
-        stats.append(check(case, xin, res, x_norm=i > 0))
+        stats.append(check(case, xin, res, x_norm=i > 0, n_hot=stack.n_hot[i]))
     return stats
 
 
 CASES = [("c2", 1, 3, 0), ("c3", 1, 3, 0), ("c3", 4, 3, 0), ("c4", 1, 2, 0), ("c5", 1, 2, 0), ("c5", 64, 2, 1)]
+# per-layer predictor ranks (0.5, 1, 1.5, 1 times the base rank) with the always-active prefix, and a
+# squared-ReLU stack of the Falcon-40B shape
+VARIANTS = [("c3", 1, 4, 0, "adaptive+hot"), ("c3", 8, 4, 0, "adaptive+hot"), ("c5", 1, 4, 0, "adaptive+hot"),
+            ("c4", 1, 4, 0, "adaptive+hot+sqrelu"), ("c4", 4, 2, 0, "sqrelu")]
 
 
-@pytest.mark.parametrize("name,B,nl,prompt", CASES, ids=[f"{c[0]}-B{c[1]}" for c in CASES])
-def test_graph_replay_matches_oracle(gpu_ready, name, B, nl, prompt):
+def _variant(name, opts):
     wl = sg.workload(name)
+    if "sqrelu" in opts:
+        wl = sg.custom(wl, act="sqrelu")
+    if "adaptive" in opts:
+        wl = sg.with_rank_schedule(wl)
+    return wl, "hot" in opts
+
+
+@pytest.mark.parametrize("name,B,nl,prompt,opts", [c + ("",) for c in CASES] + VARIANTS,
+                         ids=[f"{c[0]}-B{c[1]}" for c in CASES] + [f"{c[0]}-B{c[1]}-{c[4]}" for c in VARIANTS])
+def test_graph_replay_matches_oracle(gpu_ready, name, B, nl, prompt, opts):
+    wl, hot = _variant(name, opts)
     layers = list(range(nl))
-    say(f"[stack {name} B={B}] building {nl} layers")
-    stack = SparseFFNStack(wl, gpu_ready, layers=layers, max_batch=B)
+    say(f"[stack {name} B={B} {opts}] building {nl} layers, ranks {[wl.rank(l) for l in layers]}")
+    stack = SparseFFNStack(wl, gpu_ready, layers=layers, max_batch=B, hot_prefix=hot)
+    if hot:
+        assert min(stack.n_hot) > 0
     cases = [host_case(wl, l) for l in layers]
     tag = sg.TAG_X_PROMPT if prompt else sg.TAG_X_DECODE
     xs = [sg.inputs(wl, s, B, tag=tag) for s in range(3)]

@@ -103,3 +103,39 @@ def test_fp16_conversion_is_round_to_nearest_even():
         with np.errstate(over="ignore"):
             ref = v.astype(np.float16).view(np.uint16)
         assert np.array_equal(ours, ref)
+
+
+def test_rank_schedule_shapes_and_calibration():
+    base = sg.workload("c3")
+    wl = sg.with_rank_schedule(base)
+    assert wl.ranks == (128, 256, 384, 256) and wl.r == 384
+    assert np.mean(wl.ranks) == base.r                       # same predictor bytes as the fixed rank on average
+    for layer, r in enumerate((128, 256, 384, 256, 128)):
+        assert wl.rank(layer) == r
+        shapes = sg.layer_shapes(wl, layer)
+        assert shapes["P1"][0] == (r, wl.D) and shapes["P2"][0] == (wl.F, r)
+    # at rank 128 the first 128 rows of P1 equal the base workload's (the generator is counter-based)
+    small = sg.custom(sg.with_rank_schedule(sg.workload("c1")), F=256)
+    t0 = sg.layer_host(small, 0, names=["P1"])
+    tb = sg.layer_host(sg.custom(sg.workload("c1"), F=256), 0, names=["P1"])
+    assert np.array_equal(t0["P1"], tb["P1"][:small.rank(0)])
+
+
+def test_rank_schedule_predictor_density():
+    # the calibrated bias follows each layer's rank: the predictor still marks about the target share
+    wl = sg.custom(sg.with_rank_schedule(sg.workload("c1")), F=1024)
+    X = np.stack([sg.inputs(wl, s, 1, tag=sg.TAG_X_TEST)[0] for s in range(512)]).astype(np.float64)
+    for layer in range(4):
+        t = sg.layer_host(wl, layer, names=["P1", "P2"])
+        assert t["P1"].shape == (wl.rank(layer), wl.D)
+        z = (X @ t["P1"].astype(np.float64).T) @ t["P2"].astype(np.float64).T + t["c"][None, :]
+        assert abs((z > 0).mean() - wl.density) < 0.015, layer
+
+
+def test_saturated_count_is_the_hot_first_prefix():
+    from activation_sparse_ffn_predictor_amd.pack import hot_first_perm
+    wl = sg.workload("c2")
+    p = sg.neuron_probs(wl, 3)
+    n = sg.saturated_count(wl, 3)
+    perm = hot_first_perm(p)
+    assert n > 0 and np.all(p[perm[:n]] >= sg.ZIPF_CAP) and np.all(p[perm[n:]] < sg.ZIPF_CAP)
