@@ -17,7 +17,7 @@ ACTS = {"relu": ACT_RELU, "reglu": ACT_REGLU, "sqrelu": ACT_SQRELU}
 
 EXPORTS = ("sffn_status_string", "sffn_last_error", "sffn_workspace_size", "sffn_mask_words", "sffn_predict",
            "sffn_predict_hot", "sffn_forward", "sffn_forward_q4", "sffn_profile_begin", "sffn_profile_end",
-           "sffn_forward_path")
+           "sffn_forward_path", "sffn_decode", "sffn_decode_path")
 K_PRED_H, K_PRED_Z, K_ROWS, K_COLS = 0, 1, 2, 3
 
 
@@ -55,6 +55,10 @@ def lib() -> ctypes.CDLL:
         h.sffn_forward.restype = i32
         h.sffn_forward_q4.argtypes = [i32, _Q4, vp, _Q4, vp, _Q4, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         h.sffn_forward_q4.restype = i32
+        h.sffn_decode.argtypes = [i32, vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp,
+                                  vp, vp, sz, vp]
+        h.sffn_decode.restype = i32
+        h.sffn_decode_path.argtypes, h.sffn_decode_path.restype = [i32, i32, i32, i32, i32], i32
         h.sffn_profile_begin.argtypes, h.sffn_profile_begin.restype = [i32, i32], i32
         h.sffn_forward_path.argtypes, h.sffn_forward_path.restype = [i32, i32, i32, i32, i32], i32
         h.sffn_profile_end.argtypes, h.sffn_profile_end.restype = [ctypes.POINTER(ctypes.c_float), i32], i32
@@ -133,6 +137,25 @@ def forward_q4(act, W_gate, b_gate, W_up, b_up, W_downT, x, mask, active, n_acti
                                _Q4(*map(_p, W_downT)), _p(x), int(bool(x_norm)), B, D, F, _p(mask), _p(active),
                                _p(n_active), _p(y), _p(ws), _nbytes(ws), _stream(stream, x))
     _check(rc, "sffn_forward_q4")
+
+
+def decode(act, P1, P2, c, t: float, W_gate, b_gate, W_up, b_up, W_downT, x, mask, active, n_active, y, ws,
+           x_norm: bool = False, n_hot: int = 0, logits=None, stream=None):
+    """sffn_decode: predictor and sparse FFN of one layer for one token (x [1, D]); fp16 weights as in forward."""
+    B, D = x.shape
+    F, r = P2.shape
+    rc = lib().sffn_decode(ACTS.get(act, act), _p(P1), _p(P2), _p(c), float(t), int(n_hot), _p(W_gate), _p(b_gate),
+                           _p(W_up), _p(b_up), _p(W_downT), _p(x), int(bool(x_norm)), D, F, r, _p(mask), _p(active),
+                           _p(n_active), _p(y), _p(logits), _p(ws), _nbytes(ws), _stream(stream, x))
+    _check(rc, "sffn_decode")
+
+
+DECODE_SEPARATE, DECODE_FOLDED = 0, 1
+
+
+def decode_path(act, q4: bool, D: int, F: int, r: int) -> int:
+    """DECODE_FOLDED if sffn_decode runs the predictor's second stage inside the row gather for these sizes."""
+    return int(lib().sffn_decode_path(ACTS.get(act, act), int(bool(q4)), D, F, r))
 
 
 PATH_DECODE, PATH_FUSED, PATH_UNION = 0, 1, 2

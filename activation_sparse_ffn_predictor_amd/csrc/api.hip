@@ -66,9 +66,12 @@ int union_splits(int D) {
 }
 
 // Workspace layout, each part 256-byte aligned:
-//   [activations a: F * B fp32][B > 1: normalised x: B * D fp32]
+//   [activations a: F * B fp32; for B == 1 at least the decision bitmaps of the folded single-token layer]
+//   [B > 1: normalised x: B * D fp32]
 //   [partial y: KS_MAX * B * D fp32 for B > 1, G_FUSED * D fp32 for B == 1][predictor h: B * r fp32]
-size_t ws_a_bytes(int B, int F) { return align256((size_t)F * B * sizeof(float)); }
+size_t ws_a_bytes(int B, int F) {
+  return align256(std::max((size_t)F * B * sizeof(float), B == 1 ? sffn_decode_dec_bytes(G_FUSED) : (size_t)0));
+}
 size_t ws_xn_bytes(int B, int D) { return B > 1 ? align256((size_t)B * D * sizeof(float)) : 0; }
 size_t ws_part_bytes(int B, int D) {
   return align256((size_t)(B > 1 ? KS_MAX * B : G_FUSED) * D * sizeof(float));
@@ -264,6 +267,50 @@ int sffn_predict(const void* P1, const void* P2, const float* c, const float* x,
 int sffn_predict_hot(const void* P1, const void* P2, const float* c, const float* x, int x_norm, int B, int D, int F,
                      int r, float t, int n_hot, uint64_t* mask, float* logits, void* ws, size_t ws_bytes, void* stream) {
   return predict_impl(P1, P2, c, x, x_norm, B, D, F, r, t, n_hot, mask, logits, ws, ws_bytes, stream);
+}
+
+int sffn_decode_path(int act, int q4, int D, int F, int r) {
+  if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU && act != SFFN_ACT_SQRELU) return -1;
+  return !q4 && sffn_decode_ok(act, D, F, r, G_FUSED) ? SFFN_DECODE_FOLDED : SFFN_DECODE_SEPARATE;
+}
+
+int sffn_decode(int act, const void* P1, const void* P2, const float* c, float t, int n_hot, const void* W_gate,
+                const float* b_gate, const void* W_up, const float* b_up, const void* W_downT, const float* x,
+                int x_norm, int D, int F, int r, uint64_t* mask, int32_t* active, int32_t* n_active, float* y,
+                float* logits, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU && act != SFFN_ACT_SQRELU)
+    return fail(SFFN_ERR_ACT, "unknown activation %d", act);
+  if (act == SFFN_ACT_REGLU && !W_gate) return fail(SFFN_ERR_ACT, "ReGLU needs W_gate");
+  if (!sffn_decode_ok(act, D, F, r, G_FUSED)) {        // the separate predictor and forward calls
+    int s = predict_impl(P1, P2, c, x, x_norm, 1, D, F, r, t, n_hot, mask, logits, ws, ws_bytes, stream);
+    if (s) return s;
+    return sffn_forward(act, W_gate, b_gate, W_up, b_up, W_downT, x, x_norm, 1, D, F, mask, active, n_active, y, ws,
+                        ws_bytes, stream);
+  }
+  if (!P1 || !P2 || !x || !mask || !W_up || !W_downT || !active || !n_active || !y)
+    return fail(SFFN_ERR_NULL, "decode: P1, P2, x, W_up, W_downT, mask, active, n_active and y are required");
+  int s = check_common(1, D, F);
+  if (s) return s;
+  if (r < 8 || r > MAX_R || r % 8) return fail(SFFN_ERR_SHAPE, "r=%d: need 8 <= r <= %d, r %% 8 == 0", r, MAX_R);
+  if (!(t > 0.f && t < 1.f)) return fail(SFFN_ERR_ARG, "threshold t=%g outside (0, 1)", (double)t);
+  if (n_hot < 0 || n_hot > F) return fail(SFFN_ERR_ARG, "n_hot=%d outside 0..F=%d", n_hot, F);
+  if (!al(P1, 16) || !al(P2, 16) || !al(x, 16) || !al(mask, 8) || (c && !al(c, 4)) || (logits && !al(logits, 4)) ||
+      (act == SFFN_ACT_REGLU && !al(W_gate, 16)) || !al(W_up, 16) || !al(W_downT, 16) || !al(active, 4) ||
+      !al(n_active, 4) || !al(y, 16) || (b_gate && !al(b_gate, 4)) || (b_up && !al(b_up, 4)))
+    return fail(SFFN_ERR_ALIGN, "decode: misaligned pointer");
+  s = check_ws(ws, ws_bytes, sffn_workspace_size(1, D, F, r));
+  if (s) return s;
+  const float tau = (float)log((double)t / (1.0 - (double)t));
+  const bool g = act == SFFN_ACT_REGLU;
+  hipStream_t st = (hipStream_t)stream;
+  float* h = ws_hbuf(ws, 1, D, F);
+  hipError_t e = sffn_launch_predict_h(P1, x, x_norm, D, r, h, st);
+  if (e == hipSuccess)
+    e = sffn_launch_decode(act, P2, c, h, r, tau, n_hot, g ? W_gate : nullptr, g ? b_gate : nullptr, W_up,
+                           g ? nullptr : b_up, W_downT, x, x_norm, D, F, (uint32_t*)ws_abuf(ws), logits,
+                           ws_part(ws, 1, D, F), G_FUSED, mask, active, n_active, y, st);
+  return e == hipSuccess ? SFFN_OK : hip_fail(e, "decode launch");
 }
 
 int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W_up, const float* b_up,

@@ -222,6 +222,15 @@ __device__ __forceinline__ void stage_norm(float* xs, int nb, int D, float* red)
   __syncthreads();
 }
 
+// Workgroup barrier for LDS data only: waits for this wave's LDS accesses, not for its outstanding global loads
+// (those stay in flight across the barrier). The empty asm keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maximum (no wait)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on XCD i % 8) and every XCD has its own
 // L2. For a grid of G = 8 * per workgroups, xcd_slice maps workgroup i to slice (i % 8) * per + i / 8, so
 // neighbouring slices -- which share cache lines when a slice is narrower than a line -- run on one XCD and
@@ -378,6 +387,16 @@ hipError_t sffn_launch_fused_q4(int act, const uint8_t* qg, const void* sg, cons
                                 const void* su, const float* bu, const uint8_t* qd, const void* sd, const float* x,
                                 int x_norm, int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active,
                                 float* part, int G, float* y, hipStream_t st);
+
+// single-token layer with the predictor's second stage folded into the row gather (decode.hip)
+bool sffn_decode_ok(int act, int D, int F, int r, int G);
+size_t sffn_decode_dec_bytes(int G);
+hipError_t sffn_launch_decode(int act, const void* P2, const float* c, const float* h, int r, float tau, int n_hot,
+                              const void* Wg, const float* bg, const void* Wu, const float* bu, const void* WdT,
+                              const float* x, int x_norm, int D, int F, uint32_t* dec, float* logits, float* part,
+                              int G, uint64_t* mask, int32_t* active, int32_t* n_active, float* y, hipStream_t st);
+hipError_t sffn_launch_predict_h(const void* P1, const float* x, int x_norm, int D, int r, float* hbuf,
+                                 hipStream_t st);
 
 // multi-token (union-mask) path, matrix cores (union.hip)
 hipError_t sffn_launch_norm_tokens(const float* x, int B, int D, float* xn, hipStream_t st);

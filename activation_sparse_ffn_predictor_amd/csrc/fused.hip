@@ -32,15 +32,6 @@ constexpr int WMAX_F = 1;            // mask words per thread kept in LDS (nw <=
 #define SFFN_Q4_FUSED_RPW 1          // Q4_0 rows per wave per pass (measured best at the 70B shape: 1, over 2 and 3)
 #endif
 
-// Workgroup barrier for LDS data only: waits for this wave's LDS accesses, not for its outstanding global loads
-// (those stay in flight across the barrier). The empty asm keeps the compiler from moving memory accesses across.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maximum (no wait)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <int ACT, int NCH, int DCH>
 __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, const float* __restrict__ bg,
                                                  const uint4* __restrict__ Wu, const float* __restrict__ bu,

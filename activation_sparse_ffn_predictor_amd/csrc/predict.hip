@@ -434,6 +434,18 @@ hipError_t sffn_launch_predict(const void* P1, const void* P2, const float* c, c
   }
 }
 
+// Stage 1 alone for one token: h[j] (fp32, [r]) with the optional normalisation folded in.
+hipError_t sffn_launch_predict_h(const void* P1, const float* x, int x_norm, int D, int r, float* hbuf,
+                                 hipStream_t st) {
+  const int nch = (D / 8 + NTH - 1) / NTH;
+  if (nch <= 1) return launch_h<1>(P1, x, x_norm, 1, D, r, hbuf, st);
+  if (nch <= 2) return launch_h<2>(P1, x, x_norm, 1, D, r, hbuf, st);
+  if (nch <= 3) return launch_h<3>(P1, x, x_norm, 1, D, r, hbuf, st);
+  if (nch <= 4) return launch_h<4>(P1, x, x_norm, 1, D, r, hbuf, st);
+  if (nch <= 6) return launch_h<6>(P1, x, x_norm, 1, D, r, hbuf, st);
+  return launch_h<8>(P1, x, x_norm, 1, D, r, hbuf, st);
+}
+
 // Stage 1 for 2 <= B <= 8 tokens: h[b][j] (fp32, [B][r]) with the optional per-token normalisation folded in.
 hipError_t sffn_launch_predict_hb(const void* P1, const float* x, int x_norm, int B, int D, int r, float* hbuf,
                                   hipStream_t st) {

@@ -24,13 +24,14 @@ from .pack import hot_first_perm, pack_layer
 
 class SparseFFNStack:
     def __init__(self, wl: sg.Workload, device="cuda:0", layers: Optional[List[int]] = None, with_c: bool = True,
-                 max_batch: int = 1, seed: int = sg.MASTER_SEED, hot_prefix: bool = False):
+                 max_batch: int = 1, seed: int = sg.MASTER_SEED, hot_prefix: bool = False, fold_predictor: bool = True):
         self.wl = wl
         self.device = torch.device(device)
         self.layer_ids = list(range(wl.L)) if layers is None else list(layers)
         self.q4 = wl.wdtype == "q4"
         self.with_c = with_c
         self.max_batch = max_batch
+        self.fold_predictor = fold_predictor
         self.ranks = [wl.rank(l) for l in self.layer_ids]
         self.n_hot = [sg.saturated_count(wl, l, seed) if hot_prefix else 0 for l in self.layer_ids]
         self.layers: List[Dict[str, torch.Tensor]] = []
@@ -55,6 +56,12 @@ class SparseFFNStack:
     def layer_call(self, i: int, x: torch.Tensor, x_norm: bool, y: torch.Tensor, logits=None):
         """Predict + forward of stored layer i on input x [B, D]; writes self.mask[i], active[i], n_active[i], y."""
         t, wl = self.layers[i], self.wl
+        if self.fold_predictor and x.shape[0] == 1 and not self.q4:
+            # one token, fp16: sffn_decode (predictor stage 2 folded into the row gather where it applies)
+            _lib.decode(wl.act, t["P1"], t["P2"], t.get("c"), wl.t, t.get("W_gate"), t.get("b_gate"), t["W_up"],
+                        t.get("b_up"), t["W_downT"], x, self.mask[i], self.active[i], self.n_active[i:i + 1], y,
+                        self.ws, x_norm=x_norm, n_hot=self.n_hot[i], logits=logits)
+            return
         _lib.predict(t["P1"], t["P2"], t.get("c"), x, wl.t, self.mask[i], self.ws, logits=logits, x_norm=x_norm,
                      n_hot=self.n_hot[i])
         if self.q4:
@@ -65,6 +72,11 @@ class SparseFFNStack:
         else:
             _lib.forward(wl.act, t.get("W_gate"), t.get("b_gate"), t["W_up"], t.get("b_up"), t["W_downT"], x,
                          self.mask[i], self.active[i], self.n_active[i:i + 1], y, self.ws, x_norm=x_norm)
+
+    def folded(self, i: int, B: int) -> bool:
+        """Whether layer i's call for B tokens runs the predictor's second stage inside the row gather."""
+        return (self.fold_predictor and B == 1 and not self.q4
+                and _lib.decode_path(self.wl.act, False, self.wl.D, self.wl.F, self.ranks[i]) == _lib.DECODE_FOLDED)
 
     # ------------------------------------------------------------------ decode step
     def step(self, B: int = 1):

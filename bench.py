@@ -30,6 +30,8 @@ KERNEL_NAMES = {0: "predictor h = P1 x", 1: "predictor z = P2 h + c, threshold, 
                 2: "compaction + W_gate/W_up row gather + activation", 3: "W_downT column gather"}
 FUSED_NAMES = {2: "compaction + W_gate/W_up/W_downT row gather + activation (fused)",
                3: "sum of the per-block partials of y"}
+FOLDED_NAMES = {2: "predictor z = P2 h + c, threshold + W_gate/W_up/W_downT row gather + activation (folded)",
+                3: "sum of the per-block partials of y + mask and id assembly"}
 
 
 def parse():
@@ -44,6 +46,8 @@ def parse():
                     help="activation instead of the workload's own (same shapes)")
     ap.add_argument("--hot-prefix", action="store_true",
                     help="declare each layer's saturated neurons (stored first) always active: no predictor rows")
+    ap.add_argument("--separate-predictor", action="store_true",
+                    help="single tokens: predictor and forward as separate calls (no folded predictor stage 2)")
     ap.add_argument("--rank-schedule", choices=("fixed", "adaptive"), default="fixed",
                     help="adaptive: predictor ranks cycle over 0.5, 1, 1.5, 1 times the workload's rank by layer")
     ap.add_argument("--profile-steps", type=int, default=8, help="eager steps per profiled kernel")
@@ -59,7 +63,8 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("common.h", "api.hip", "predict.hip", "forward.hip", "forward_q4.hip", "union.hip", "fused.hip")
+KERNEL_SOURCES = ("common.h", "api.hip", "predict.hip", "forward.hip", "forward_q4.hip", "union.hip", "fused.hip",
+                  "decode.hip")
 
 
 def kernel_source_hash() -> str:
@@ -162,7 +167,8 @@ def main():
     PB = wl.prompt if args.prompt is None else args.prompt
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
-    stack = SparseFFNStack(wl, dev, max_batch=max(B, PB), hot_prefix=args.hot_prefix)
+    stack = SparseFFNStack(wl, dev, max_batch=max(B, PB), hot_prefix=args.hot_prefix,
+                           fold_predictor=not args.separate_predictor)
     L = len(stack.layers)
     setup_s = time.perf_counter() - t0
     print(f"# setup: {wl.name}, {L} layers resident, {setup_s:.1f} s", file=sys.stderr, flush=True)
@@ -255,6 +261,7 @@ def main():
                 nlog.append(stack.n_active.cpu().numpy().astype(np.float64))
         prof[kid] = np.asarray(_lib.profile_end(P * L), dtype=np.float64)
     torch.cuda.synchronize()
+    prof = {k: v for k, v in prof.items() if len(v)}   # the folded layers launch no separate stage-2 kernel
     mean_us = {k: float(v.mean() * 1e3) for k, v in prof.items()}
     # algorithmic bytes per launch (active rows actually read by the profiled launches)
     n_prof = np.concatenate(nlog) if nlog else np.zeros(1)
@@ -264,21 +271,26 @@ def main():
         one_row = 2 * wl.D
     rows_mats = wl.n_mats - 1
     path = _lib.forward_path(wl.act, stack.q4, B, wl.D, wl.F)
+    ranks, hots = np.asarray(stack.ranks, np.float64), np.asarray(stack.n_hot, np.float64)
+    fold = np.tile(np.array([stack.folded(i, B) for i in range(L)]), P)   # launches: P steps x L layers
+    p2_bytes = np.tile(2.0 * (wl.F - hots) * ranks, P)
     if path == _lib.PATH_FUSED:
-        # kernel 2 gathers gate/up and W_downT rows; kernel 3 adds the per-block partial sums of y
-        bytes_rows = n_prof * wl.n_mats * one_row
-        bytes_cols = (np.minimum(n_prof, 256) * wl.D + B * wl.D) * 4.0
+        # kernel 2 gathers gate/up and W_downT rows (folded: after reading the block's P2 rows); kernel 3 adds
+        # the per-block partial sums of y (folded: all 256 of them, and assembles the mask and ids)
+        bytes_rows = n_prof * wl.n_mats * one_row + np.where(fold, p2_bytes, 0.0)
+        bytes_cols = (np.where(fold, 256.0, np.minimum(n_prof, 256)) * wl.D + B * wl.D) * 4.0
     else:
         bytes_rows = n_prof * rows_mats * one_row                # per launch of kernel 2
         bytes_cols = n_prof * one_row                            # per launch of kernel 3
-    ranks, hots = np.asarray(stack.ranks, np.float64), np.asarray(stack.n_hot, np.float64)
-    kb = {0: np.tile(2.0 * ranks * wl.D, P), 1: np.tile(2.0 * (wl.F - hots) * ranks, P),   # launches in layer order
+    kb = {0: np.tile(2.0 * ranks * wl.D, P), 1: p2_bytes[~fold],   # launches in layer order
           2: bytes_rows, 3: bytes_cols}
     tot = {k: float(prof[k].sum()) for k in prof}
     dom = max(tot, key=tot.get)
     m = min(len(kb[dom]), len(prof[dom]))
     achieved = float(kb[dom][:m].sum() / (prof[dom][:m].sum() * 1e-3) / 1e9)       # GB/s
-    names = {**KERNEL_NAMES, **(FUSED_NAMES if path == _lib.PATH_FUSED else {})}
+    names = {**KERNEL_NAMES, **(FUSED_NAMES if path == _lib.PATH_FUSED else {}), **(FOLDED_NAMES if fold.all() else {})}
+    if fold.any() and not fold.all():
+        names[2] += " (folded with the predictor in some layers)"
     fwd_us = mean_us[2] + mean_us[3]
     fwd_gbs = (float(n_prof.mean()) * row_bytes) / (fwd_us * 1e-6) / 1e9
 
@@ -302,7 +314,8 @@ def main():
         "config": {"workload": wl.name, "d_model": wl.D, "d_ffn": wl.F,
                    "rank": wl.r if not wl.ranks else list(wl.ranks), "layers": L, "batch": B,
                    "activation": wl.act, "weights": "fp16" if not stack.q4 else "q4_0", "density_target": wl.density,
-                   "hot_prefix_per_layer": round(float(np.mean(stack.n_hot)), 1), "graph": not args.no_graph},
+                   "hot_prefix_per_layer": round(float(np.mean(stack.n_hot)), 1),
+                   "predictor_folded_layers": int(fold[:L].sum()), "graph": not args.no_graph},
         "active_weight_gbs": round(active_bytes_step / (ms_step * 1e-3) / 1e9, 1),
         "forward_active_gbs": round(fwd_gbs, 1),
         "all_bytes_gbs": round((active_bytes_step + pred_bytes_step) / (ms_step * 1e-3) / 1e9, 1),

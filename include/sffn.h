@@ -57,7 +57,8 @@
  * batch results match the decode kernels' to within fp32 rounding.
  *
  * Workspace (sffn_workspace_size bytes, 256-byte parts, caller-owned, no
- * state kept between calls): activations a [F, B] fp32; for B > 1 the
+ * state kept between calls): activations a [F, B] fp32 (for B == 1 at least
+ * 4 KiB: sffn_decode keeps its per-block decision bitmaps there); for B > 1 the
  * normalised inputs [B, D]; partial sums of y, [256, D] fp32 for B == 1 (one
  * per block of the fused kernel) or [8, B, D] for B > 1 (row splits; the
  * union predictor also keeps its partial h there); the predictor's h [B, r]
@@ -168,10 +169,27 @@ int sffn_forward_q4(int act, sffn_q4 W_gate, const float* b_gate, sffn_q4 W_up, 
                     const float* x, int x_norm, int B, int D, int F, const uint64_t* mask, int32_t* active,
                     int32_t* n_active, float* y, void* ws, size_t ws_bytes, void* stream);
 
+/* One decode step of one layer for a single token: sffn_predict_hot (n_hot = 0: sffn_predict) followed by
+ * sffn_forward, with the same operands, outputs and results ("Adaptive sparsity predictors" and "Neuron-aware
+ * operator", Turkish article). mask, active, n_active, y and logits (if non-NULL) are written as the two calls
+ * would write them. Where sffn_decode_path says SFFN_DECODE_FOLDED, the predictor's second stage runs inside
+ * the row gather: each of the 256 workgroups decides the neurons it owns (stored neurons k with k % 256 equal to
+ * its index) and gathers the active ones at once, so the layer takes three kernels instead of four and one
+ * dependent round trip less; the mask and the ascending ids are assembled while the partial sums of y are added.
+ * Otherwise the two calls run as they are. fp16 weights only (the Q4_0 forward keeps its separate calls). Uses
+ * the workspace of sffn_workspace_size(1, D, F, r). Errors as sffn_predict and sffn_forward. */
+enum { SFFN_DECODE_SEPARATE = 0, SFFN_DECODE_FOLDED = 1 };
+int sffn_decode_path(int act, int q4, int D, int F, int r);   /* -1 for an unknown activation */
+int sffn_decode(int act, const void* P1, const void* P2, const float* c, float t, int n_hot, const void* W_gate,
+                const float* b_gate, const void* W_up, const float* b_up, const void* W_downT, const float* x,
+                int x_norm, int D, int F, int r, uint64_t* mask, int32_t* active, int32_t* n_active, float* y,
+                float* logits, void* ws, size_t ws_bytes, void* stream);
+
 /* Per-launch timing of one kernel (profiling aid; not needed for computing).
  * kernel: SFFN_K_PRED_H (P1 x), SFFN_K_PRED_Z (P2 h + c, threshold, mask), SFFN_K_ROWS (compaction + W_gate /
  * W_up row gather + activation), SFFN_K_COLS (W_downT column gather; in the union path the row-split down
- * projection, not the sum of its partials).
+ * projection, not the sum of its partials). In a folded sffn_decode the folded kernel (predictor stage 2 + row
+ * gather) is SFFN_K_ROWS and the sum of partials with the mask assembly SFFN_K_COLS.
  * Between sffn_profile_begin and sffn_profile_end, every launch of that kernel made by the calling thread, up
  * to max_launches of them, is issued with a pair of HIP events that take the kernel's own start and end
  * timestamps (hipExtLaunchKernelGGL): the kernel's time on the device, without host-side queueing. The events

@@ -92,6 +92,26 @@ def run_gpu(case: LayerCase, x: torch.Tensor, x_norm=False, t=None, want_logits=
                 logits=None if logits is None else logits.cpu().numpy().astype(np.float64))
 
 
+def run_decode(case: LayerCase, x: torch.Tensor, x_norm=False, t=None, want_logits=True, n_hot=0):
+    """One token through sffn_decode (predictor and forward in one call); outputs as run_gpu."""
+    wl, d = case.wl, case.dev
+    B, D = x.shape
+    dev = x.device
+    mask = torch.full((_lib.mask_words(wl.F),), -1, dtype=torch.int64, device=dev)   # garbage-filled outputs
+    active = torch.full((wl.F,), -7, dtype=torch.int32, device=dev)
+    n_active = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    y = torch.full((B, D), float("nan"), dtype=torch.float32, device=dev)
+    logits = torch.full((B, wl.F), float("nan"), dtype=torch.float32, device=dev) if want_logits else None
+    ws = torch.full((_lib.workspace_size(B, D, wl.F, wl.r),), 0xA5, dtype=torch.uint8, device=dev)
+    _lib.decode(wl.act, d["P1"], d["P2"], d.get("c"), wl.t if t is None else t, d.get("W_gate"), d.get("b_gate"),
+                d["W_up"], d.get("b_up"), d["W_downT"], x, mask, active, n_active, y, ws, x_norm=x_norm, n_hot=n_hot,
+                logits=logits)
+    torch.cuda.synchronize(dev)
+    return dict(mask=mask.cpu().numpy().view(np.uint64), active=active.cpu().numpy(), n=int(n_active.item()),
+                y=y.cpu().numpy().astype(np.float64),
+                logits=None if logits is None else logits.cpu().numpy().astype(np.float64))
+
+
 def mask_bits(words: np.ndarray, F: int) -> np.ndarray:
     bits = np.unpackbits(words.astype("<u8").view(np.uint8), bitorder="little")
     return bits[:F].astype(bool)

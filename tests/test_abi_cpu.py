@@ -162,3 +162,34 @@ def test_squared_relu_is_accepted_on_every_path():
     assert _lib.forward_path("sqrelu", False, 2, 4096, 11008) == _lib.PATH_DECODE
     assert _lib.forward_path("sqrelu", False, 4, 4096, 11008) == _lib.PATH_UNION
     assert _lib.forward_path(3, False, 1, 512, 2048) == -1
+
+
+def _decode(**kw):
+    a = dict(act=1, P1=A, P2=A, c=None, t=0.5, n_hot=0, Wg=A, bg=A, Wu=A, bu=None, WdT=A, x=A, x_norm=0, D=512, F=2048,
+             r=64, mask=A, active=A, n_active=A, y=A, logits=None, ws=A, ws_bytes=1 << 24, stream=None)
+    a.update(kw)
+    return _lib.lib().sffn_decode(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(act=5), 5), (dict(Wg=None), 5), (dict(P1=None), 1), (dict(y=None), 1), (dict(active=None), 1),
+    (dict(r=12), 2), (dict(r=2048), 2), (dict(t=0.0), 6), (dict(n_hot=-1), 6), (dict(n_hot=2049), 6),
+    (dict(P2=MIS), 3), (dict(y=A + 4), 3), (dict(ws=A + 16), 3), (dict(ws_bytes=1000), 4),
+    # sizes outside the folded kernel take the separate calls and fail there the same way
+    (dict(D=8192, ws_bytes=1000), 4), (dict(F=40000, D=64, ws_bytes=1000), 4), (dict(D=8192, n_hot=-2), 6),
+])
+def test_decode_rejects(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_decode_paths_and_workspace():
+    assert _lib.decode_path("reglu", False, 4096, 11008, 256) == _lib.DECODE_FOLDED
+    assert _lib.decode_path("reglu", False, 4096, 11008, 384) == _lib.DECODE_SEPARATE   # 8 rounds per row
+    assert _lib.decode_path("reglu", False, 5120, 13824, 256) == _lib.DECODE_SEPARATE   # rows wider than 4096
+    assert _lib.decode_path("relu", False, 4096, 32768, 512) == _lib.DECODE_SEPARATE   # 2 row steps x 8 rounds
+    assert _lib.decode_path("relu", False, 4096, 32768, 64) == _lib.DECODE_FOLDED      # 2 row steps x 1 round
+    assert _lib.decode_path("reglu", False, 8192, 1000, 64) == _lib.DECODE_SEPARATE    # ReGLU wider than 5120
+    assert _lib.decode_path("relu", True, 512, 1000, 64) == _lib.DECODE_SEPARATE       # Q4_0
+    assert _lib.decode_path(9, False, 512, 1000, 64) == -1
+    # one token: the activation region holds at least the 256 workgroups' 16-byte decision bitmaps
+    assert _lib.workspace_size(1, 64, 1, 8) == 4096 + 256 * 64 * 4 + 256
