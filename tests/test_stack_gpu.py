@@ -29,7 +29,8 @@ def _check_stack(stack, cases, x0, B):
 CASES = [("c2", 1, 3, 0), ("c3", 1, 3, 0), ("c3", 4, 3, 0), ("c4", 1, 2, 0), ("c5", 1, 2, 0), ("c5", 64, 2, 1)]
 # per-layer predictor ranks (0.5, 1, 1.5, 1 times the base rank) with the always-active prefix, and a
 # squared-ReLU stack of the Falcon-40B shape
-VARIANTS = [("c3", 1, 4, 0, "adaptive+hot"), ("c3", 8, 4, 0, "adaptive+hot"), ("c5", 1, 4, 0, "adaptive+hot"),
+VARIANTS = [("c2", 1, 4, 0, "adaptive+hot"), ("c2", 1, 3, 0, "separate"),
+            ("c3", 1, 4, 0, "adaptive+hot"), ("c3", 8, 4, 0, "adaptive+hot"), ("c5", 1, 4, 0, "adaptive+hot"),
             ("c4", 1, 4, 0, "adaptive+hot+sqrelu"), ("c4", 4, 2, 0, "sqrelu")]
 
 
@@ -48,9 +49,13 @@ def test_graph_replay_matches_oracle(gpu_ready, name, B, nl, prompt, opts):
     wl, hot = _variant(name, opts)
     layers = list(range(nl))
     say(f"[stack {name} B={B} {opts}] building {nl} layers, ranks {[wl.rank(l) for l in layers]}")
-    stack = SparseFFNStack(wl, gpu_ready, layers=layers, max_batch=B, hot_prefix=hot)
+    stack = SparseFFNStack(wl, gpu_ready, layers=layers, max_batch=B, hot_prefix=hot,
+                           fold_predictor="separate" not in opts)
     if hot:
         assert min(stack.n_hot) > 0
+    if name == "c2" and B == 1 and "separate" not in opts:
+        # the 7B shape folds the predictor where a layer's rank allows: rank 384 does not
+        assert [stack.folded(i, B) for i in range(nl)] == [wl.rank(l) != 384 for l in layers]
     cases = [host_case(wl, l) for l in layers]
     tag = sg.TAG_X_PROMPT if prompt else sg.TAG_X_DECODE
     xs = [sg.inputs(wl, s, B, tag=tag) for s in range(3)]
