@@ -14,7 +14,7 @@
 // compared with tau (the always-active prefix k < n_hot is forced on; its P2 rows and biases are never loaded:
 // their offsets are out of range, which reads 0 without a memory request). A ballot gives each wave's 8
 // decisions per row step; they land in an LDS bitmap of the block's rows, and the block's active neurons, in
-// ascending order, are picked from it by rank select. The gather that follows is that of k_fused1: per pass of 8
+// ascending order, are picked from it by rank select. The gather that follows is k_fused1's (rowgather.h): per pass of 8
 // rows each wave issues its row of W_gate / W_up and every thread its chunks of the pass's 8 W_downT rows, all
 // together; x is normalised and staged while they are in flight; the activations go through LDS and every thread
 // adds a_i W_downT[id_i, its chunks] in row order into the block's partial sum of y. Every block writes its
@@ -23,6 +23,7 @@
 // assemble the blocks' bitmaps into the mask words and write the ascending ids of the set bits to active[] and
 // their count to n_active.
 #include "common.h"
+#include "rowgather.h"
 
 using namespace sffn;
 
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(NT_D) void k_decode1(const uint4* __restrict__ P2, 
   int* bids = reinterpret_cast<int*>(bits8 + ZS * FWD);              // [32 * JW] the block's active neuron ids
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int G = gridDim.x, blk = blockIdx.x;
-  const int nc = D >> 3, n4 = D >> 2;
+  const int n4 = D >> 2;
   const int cpr = r >> 3;                              // 16-byte chunks per P2 row
   constexpr int XPT = (128 * NCH + NT_D - 1) / NT_D;
   const int rsub = lane / ZL, csub = lane % ZL;
@@ -137,108 +138,8 @@ __global__ __launch_bounds__(NT_D) void k_decode1(const uint4* __restrict__ P2, 
   if ((int)threadIdx.x < JW) dec[threadIdx.x * G + blk] = bw[threadIdx.x];
   lds_barrier();
 
-  const uint32_t wbytes = (uint32_t)F * (uint32_t)D * 2u;
-  const Buf bwu(Wu, wbytes), bwd(WdT, wbytes);
-  const Buf bwg(ACT == 1 ? (const void*)Wg : (const void*)Wu, ACT == 1 ? wbytes : 0u);
-  const float* bp_ = ACT == 1 ? bg : bu;
-  const Buf bbias(bp_ ? (const void*)bp_ : (const void*)Wu, bp_ ? (uint32_t)F * 4u : 0u);   // no bias: 0
-  float acc[DCH][8];
-#pragma unroll
-  for (int q = 0; q < DCH; ++q)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
-  const bool wq_last = (int)__builtin_amdgcn_readfirstlane(threadIdx.x) + NT_D * (DCH - 1) < nc;   // wave-uniform
-
-  bool first = true;
-  for (int k0 = 0; k0 < nrow; k0 += FWD) {             // passes (block-uniform); row k0 + w on wave w
-    const int k = k0 + w;
-    const bool have = k < nrow;                        // wave-uniform
-    // round 2: this wave's neuron, its gate/up rows and bias; then the pass's W_downT rows, all issued together
-    int id = -1;
-    uint4 wu[NCH], wg[NCH];
-    float bias = 0.f;
-    if (have) {
-      id = bids[k];
-#pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        const int cm = lane + 64 * m;
-        const uint32_t o = boff(cm < nc, ((uint32_t)id * nc + cm) * 16u);
-        wu[m] = bwu.ld16(o);
-        if (ACT == 1) wg[m] = bwg.ld16(o);
-      }
-      bias = bbias.ldf((uint32_t)id * 4u);
-    }
-    uint4 wd[FWD][DCH];
-#pragma unroll
-    for (int j = 0; j < FWD; ++j) {
-      const int idj = k0 + j < nrow ? bids[k0 + j] : -1;
-#pragma unroll
-      for (int q = 0; q < DCH; ++q) {
-        const int cq = threadIdx.x + NT_D * q;
-        if (q == DCH - 1 && !wq_last) {                // chunks past the row end on this whole wave: no load
-          wd[j][q] = make_uint4(0u, 0u, 0u, 0u);
-          continue;
-        }
-        wd[j][q] = bwd.ld16(boff(idj >= 0 && cq < nc, ((uint32_t)(idj >= 0 ? idj : 0) * nc + cq) * 16u));
-      }
-    }
-    if (first) {                                       // x: normalised and staged while the rows are in flight
-      if (x_norm) block_norm_regs<NT_D, XPT>(xv4, n4, x0, red);
-      stage_store<NT_D, XPT>(xs, n4, xv4);
-      lds_barrier();
-      first = false;
-    }
-    if (have) {
-      float au = 0.f, ag = 0.f;
-#pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        const int cm = lane + 64 * m;
-        if (cm < nc) {
-          const float4* xp = reinterpret_cast<const float4*>(xs + 8 * cm);
-          const float4 xa = xp[0], xb = xp[1];
-          const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-          au += dot8(wu[m], xv);
-          if (ACT == 1) ag += dot8(wg[m], xv);
-        }
-      }
-      const float u = wave_sum(au);
-      float a;
-      if (ACT == 1) {
-        const float g = wave_sum(ag) + bias;
-        a = fmaxf(g, 0.f) * u;
-      } else {
-        a = fmaxf(u + bias, 0.f);
-        if (ACT == 2) a *= a;
-      }
-      if (lane == 0) av[w] = a;
-    } else if (lane == 0) {
-      av[w] = 0.f;
-    }
-    lds_barrier();
-    // column gather of the pass, rows in wave order
-#pragma unroll
-    for (int j = 0; j < FWD; ++j) {
-      const float aj = av[j];
-#pragma unroll
-      for (int q = 0; q < DCH; ++q) {
-        float wf[8];
-        f16x8_to_f32(wd[j][q], wf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(aj, wf[e], acc[q][e]);
-      }
-    }
-    lds_barrier();                                     // ids / av are rewritten by the next pass
-  }
-  float* pb = part + (size_t)blockIdx.x * D;           // every block writes its partial (zeros without rows)
-#pragma unroll
-  for (int q = 0; q < DCH; ++q) {
-    const int cq = threadIdx.x + NT_D * q;
-    if (cq < nc) {
-      float4* o = reinterpret_cast<float4*>(pb + 8 * cq);
-      o[0] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
-      o[1] = make_float4(acc[q][4], acc[q][5], acc[q][6], acc[q][7]);
-    }
-  }
+  gather_rows<ACT, NCH, DCH, NT_D, XPT, false>(bids, nrow, Wg, bg, Wu, bu, WdT, D, F, x_norm, x0, xv4, xs, red, av,
+                                               part, nullptr, 0, 0);   // every block writes its partial
 }
 
 constexpr int NT_S = 512;            // 32 columns x 16 groups of blocks

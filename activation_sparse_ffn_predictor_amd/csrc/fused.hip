@@ -8,7 +8,8 @@
 // k_fused1 (G >= 64 blocks of 8 waves): round 1 loads x and the mask words; a block scan gives each thread the
 // set bits before its mask word. Dense index i goes to block i % G, so every block gets a near-equal share. A
 // block's rows are G apart in dense order, so a mask word holds at most one of them: each thread finds its word's
-// one by a rank select, and the block has the ids of all its rows in LDS at once. Per pass of 8 rows, each wave
+// one by a rank select, and the block has the ids of all its rows in LDS at once. The gather (rowgather.h,
+// shared with the folded kernel of decode.hip): per pass of 8 rows, each wave
 // issues the loads of its row of W_gate / W_up and every thread the loads of its 16-byte chunks of the pass's 8
 // rows of W_downT, all together and before x is normalised and staged. Each wave reduces its row dot products to
 // the activation a_i; the 8 activations go through LDS and every thread adds a_i * W_downT[id_i, its chunks] in
@@ -20,6 +21,7 @@
 // column, each summed in block order, then the groups in order); all of a thread's loads are issued together.
 // Every sum has a fixed order, so the results do not depend on timing.
 #include "common.h"
+#include "rowgather.h"
 
 using namespace sffn;
 
@@ -48,8 +50,6 @@ __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, c
   float* red = av + FW;                                                  // [2 * FW] normalisation scratch
   float* xs = red + 2 * FW + 4;                                          // [D] x (16-byte aligned)
   int* bids = reinterpret_cast<int*>(xs + D);                            // [ceil(F / G)] the block's row ids
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int nc = D >> 3;
   const int n4 = D >> 2;
   constexpr int XPT = (128 * NCH + NT_F - 1) / NT_F;   // float4 of x per thread: D / 4 <= 128 * NCH
 
@@ -61,115 +61,13 @@ __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, c
   if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
   const int G = gridDim.x;
   if ((int)blockIdx.x >= n) return;                    // block-uniform: no row here; its partial is never read
-  const uint32_t wbytes = (uint32_t)F * (uint32_t)D * 2u;
-  const Buf bwu(Wu, wbytes), bwd(WdT, wbytes);
-  const Buf bwg(ACT == 1 ? (const void*)Wg : (const void*)Wu, ACT == 1 ? wbytes : 0u);
-  const float* bp = ACT == 1 ? bg : bu;
-  const Buf bbias(bp ? (const void*)bp : (const void*)Wu, bp ? (uint32_t)F * 4u : 0u);   // no bias: 0
-
-  float acc[DCH][8];
-#pragma unroll
-  for (int q = 0; q < DCH; ++q)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
-
   // the block's rows: dense indices blk + G * k, k < nrow, their ids in LDS (one rank select per mask word)
   const int blk = blockIdx.x;
   const int nrow = (n - blk + G - 1) / G;
   block_row_ids(wl, roff, nw, blk, G, bids);
   lds_barrier();
-  const bool wq_last = (int)__builtin_amdgcn_readfirstlane(threadIdx.x) + NT_F * (DCH - 1) < nc;   // wave-uniform
-
-  bool first = true;
-  for (int k0 = 0; k0 < nrow; k0 += FW) {              // passes (block-uniform); row k0 + w on wave w
-    const int k = k0 + w;
-    const bool have = k < nrow;                        // wave-uniform
-    // round 2: this wave's neuron, its gate/up rows and bias; then the block's W_downT rows, all issued together
-    int id = -1;
-    uint4 wu[NCH], wg[NCH];
-    float bias = 0.f;
-    if (have) {
-      id = bids[k];
-#pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        const int c = lane + 64 * m;
-        const uint32_t o = boff(c < nc, ((uint32_t)id * nc + c) * 16u);
-        wu[m] = bwu.ld16(o);
-        if (ACT == 1) wg[m] = bwg.ld16(o);
-      }
-      bias = bbias.ldf((uint32_t)id * 4u);
-    }
-    uint4 wd[FW][DCH];
-#pragma unroll
-    for (int j = 0; j < FW; ++j) {
-      const int idj = k0 + j < nrow ? bids[k0 + j] : -1;
-#pragma unroll
-      for (int q = 0; q < DCH; ++q) {
-        const int c = threadIdx.x + NT_F * q;
-        if (q == DCH - 1 && !wq_last) {                // chunks past the row end on this whole wave: no load
-          wd[j][q] = make_uint4(0u, 0u, 0u, 0u);
-          continue;
-        }
-        wd[j][q] = bwd.ld16(boff(idj >= 0 && c < nc, ((uint32_t)(idj >= 0 ? idj : 0) * nc + c) * 16u));
-      }
-    }
-    if (first) {                                       // x: normalised and staged while the rows are in flight
-      if (x_norm) block_norm_regs<NT_F, XPT>(xv4, n4, x0, red);
-      stage_store<NT_F, XPT>(xs, n4, xv4);
-      lds_barrier();
-      first = false;
-    }
-    if (have) {
-      float au = 0.f, ag = 0.f;
-#pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        const int c = lane + 64 * m;
-        if (c < nc) {
-          const float4* xp = reinterpret_cast<const float4*>(xs + 8 * c);
-          const float4 xa = xp[0], xb = xp[1];
-          const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-          au += dot8(wu[m], xv);
-          if (ACT == 1) ag += dot8(wg[m], xv);
-        }
-      }
-      const float u = wave_sum(au);
-      float a;
-      if (ACT == 1) {
-        const float g = wave_sum(ag) + bias;
-        a = fmaxf(g, 0.f) * u;
-      } else {
-        a = fmaxf(u + bias, 0.f);
-        if (ACT == 2) a *= a;
-      }
-      if (lane == 0) { av[w] = a; active[blk + G * k] = id; }
-    } else if (lane == 0) {
-      av[w] = 0.f;
-    }
-    lds_barrier();
-    // column gather of the pass, rows in wave order
-#pragma unroll
-    for (int j = 0; j < FW; ++j) {
-      const float aj = av[j];
-#pragma unroll
-      for (int q = 0; q < DCH; ++q) {
-        float wf[8];
-        f16x8_to_f32(wd[j][q], wf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(aj, wf[e], acc[q][e]);
-      }
-    }
-    lds_barrier();                                     // ids / av are rewritten by the next pass
-  }
-  float* pb = part + (size_t)blockIdx.x * D;
-#pragma unroll
-  for (int q = 0; q < DCH; ++q) {
-    const int c = threadIdx.x + NT_F * q;
-    if (c < nc) {
-      float4* o = reinterpret_cast<float4*>(pb + 8 * c);
-      o[0] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
-      o[1] = make_float4(acc[q][4], acc[q][5], acc[q][6], acc[q][7]);
-    }
-  }
+  gather_rows<ACT, NCH, DCH, NT_F, XPT, true>(bids, nrow, Wg, bg, Wu, bu, WdT, D, F, x_norm, x0, xv4, xs, red, av,
+                                              part, active, blk, G);
 }
 
 // sum over half a Q4 block of q_e * x_e: nib = the block's 16 nibble bytes (byte k: low nibble = element k, high
