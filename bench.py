@@ -120,23 +120,47 @@ def cpu_baseline(wl, B: int, budget_s: float):
         threads = os.cpu_count() or 1
     layers = [0, 1] if wl.L > 1 else [0]
     ws = [oracle.logical_weights(sg.layer_host(wl, l)) for l in layers]
-    times, n = [], 0
     t_start = time.perf_counter()
-    step = 0
-    while time.perf_counter() - t_start < budget_s:
-        for w in ws:
-            x = sg.inputs(wl, step, B)
-            t0 = time.perf_counter()
-            oracle.layer(wl.act, x, w, wl.t)
-            times.append(time.perf_counter() - t0)
-            n += 1
-        step += 1
-    per_layer = float(np.median(times))
+
+    def sample(seconds):
+        times, n, step = [], 0, 0
+        t0s = time.perf_counter()
+        while time.perf_counter() - t0s < seconds:
+            for w in ws:
+                x = sg.inputs(wl, step, B)
+                t0 = time.perf_counter()
+                oracle.layer(wl.act, x, w, wl.t)
+                times.append(time.perf_counter() - t0)
+                n += 1
+            step += 1
+        return float(np.median(times)), n
+
+    per_layer, n = sample(budget_s)
+    one = None
+    try:                                               # the same oracle on one BLAS thread, a shorter sample
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one, _ = sample(budget_s / 3.0)
+    except Exception:  # noqa: BLE001
+        pass
     tok_s = B / (per_layer * wl.L)
     return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} layer evaluations of {wl.name} (layers {layers}, {B} token(s) each, fp64 NumPy dense FFN "
                       f"+ predictor), median {per_layer * 1e3:.1f} ms per layer, extrapolated to {wl.L} layers",
+            "value_1_thread": None if one is None else round(B / (one * wl.L), 4),
+            "cpu_model": _cpu_model(),
             "seconds": round(time.perf_counter() - t_start, 2)}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
