@@ -59,6 +59,12 @@ bool decode_batch(int B, int D, int F) {
   return B == 2 || ((B == 4 || B == 8) && F > MAX_F_UNION);
 }
 
+// k shares of the union row kernel: 5..16 tokens split k in two (twice the blocks, each half as long, spread
+// more evenly over the CUs when the row tiles number a little over one per CU); a small kernel then forms the
+// activations. Measured at the 13B shape: 8 tokens 2738 -> 2847 tokens/s; 4 tokens 1964 -> 1862, so up to 4
+// tokens keep one share.
+int union_ksp(int B) { return B > 4 && B <= 16 ? 2 : 1; }
+
 // Row splits of the union down projection: enough blocks of 128 columns x KS splits to cover the chip twice.
 int union_splits(int D) {
   const int cb = (D + 127) / 128;
@@ -76,7 +82,12 @@ size_t ws_xn_bytes(int B, int D) { return B > 1 ? align256((size_t)B * D * sizeo
 size_t ws_part_bytes(int B, int D) {
   return align256((size_t)(B > 1 ? KS_MAX * B : G_FUSED) * D * sizeof(float));
 }
-size_t ws_forward_bytes(int B, int D, int F) { return ws_a_bytes(B, F) + ws_xn_bytes(B, D) + ws_part_bytes(B, D); }
+// B > 1: partial pre-activations of the k-split union row kernel, [KSP_MAX][2][F][B] fp32
+constexpr int KSP_MAX = 2;
+size_t ws_pre_bytes(int B, int F) { return B > 1 ? align256((size_t)KSP_MAX * 2 * F * B * sizeof(float)) : 0; }
+size_t ws_forward_bytes(int B, int D, int F) {
+  return ws_a_bytes(B, F) + ws_xn_bytes(B, D) + ws_part_bytes(B, D) + ws_pre_bytes(B, F);
+}
 
 int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   if (!ws) return fail(SFFN_ERR_NULL, "workspace is NULL");
@@ -96,6 +107,9 @@ float* ws_abuf(void* ws) { return (float*)ws; }
 float* ws_xn(void* ws, int B, int F) { return (float*)((char*)ws + ws_a_bytes(B, F)); }
 float* ws_part(void* ws, int B, int D, int F) { return (float*)((char*)ws + ws_a_bytes(B, F) + ws_xn_bytes(B, D)); }
 float* ws_hbuf(void* ws, int B, int D, int F) { return (float*)((char*)ws + ws_forward_bytes(B, D, F)); }
+float* ws_pre(void* ws, int B, int D, int F) {
+  return (float*)((char*)ws + ws_a_bytes(B, F) + ws_xn_bytes(B, D) + ws_part_bytes(B, D));
+}
 
 struct Prof {
   int kernel = -1;
@@ -137,7 +151,7 @@ hipError_t run_union(int act, bool q4, const void* Wg, const void* Sg, const flo
     xin = ws_xn(ws, B, F);
   }
   hipError_t e = sffn_launch_rows_mt(act, q4, Wg, Sg, bg, Wu, Su, bu, xin, B, D, F, mask, active, n_active,
-                                     ws_abuf(ws), st);
+                                     ws_abuf(ws), ws_pre(ws, B, D, F), union_ksp(B), st);
   if (e != hipSuccess) return e;
   return sffn_launch_down_mt(q4, Wd, Sd, active, n_active, ws_abuf(ws), B, D, F, ws_part(ws, B, D, F),
                              union_splits(D), y, st);

@@ -405,7 +405,8 @@ hipError_t sffn_launch_predict_mt(const void* P1, const void* P2, const float* c
                                   float* hpart, int KSH, hipStream_t st);
 hipError_t sffn_launch_rows_mt(int act, bool q4, const void* Wg, const void* Sg, const float* bg, const void* Wu,
                                const void* Su, const float* bu, const float* x, int B, int D, int F,
-                               const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf, hipStream_t st);
+                               const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf, float* pre,
+                               int KSP, hipStream_t st);
 hipError_t sffn_launch_down_mt(bool q4, const void* Wd, const void* Sd, const int32_t* active,
                                const int32_t* n_active, const float* abuf, int B, int D, int F, float* part, int KS,
                                float* y, hipStream_t st);

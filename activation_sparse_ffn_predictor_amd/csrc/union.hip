@@ -271,13 +271,20 @@ constexpr int WMAXU = 2;
 
 // Active-row gather with fused activation, 16 dense indices per block, k split over 8 waves.
 // Q4: W = nibble planes + scale planes. ACT 1 = ReGLU (gate + up), 0 = ReLU (up), 2 = squared ReLU (up).
+// KSP > 1 splits k over KSP blocks per 16 rows, block t * KSP + ks taking share ks (the shares of a tile are
+// neighbours in dispatch order, so both start with the first blocks; with the shares in a second grid dimension
+// they came after every first share, most of them blocks without rows, and 8 tokens gained nothing): each
+// writes its partial pre-activations
+// (up, and gate for ReGLU, no bias) to pre[(ks * 2 + mat) * F * B + i * B + token] and k_act_combine applies
+// the activation; with KSP = 1 the block writes the activations itself.
 template <int NTT, int ACT, bool Q4>
 __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, const void* __restrict__ Sg,
                                                  const float* __restrict__ bg, const void* __restrict__ Wu,
                                                  const void* __restrict__ Su, const float* __restrict__ bu,
                                                  const float* __restrict__ x, int B, int D, int F,
                                                  const uint64_t* __restrict__ mask, int32_t* __restrict__ active,
-                                                 int32_t* __restrict__ n_active, float* __restrict__ abuf) {
+                                                 int32_t* __restrict__ n_active, float* __restrict__ abuf,
+                                                 float* __restrict__ pre, int KSP) {
   constexpr bool GT = ACT == 1;                        // gated (ReGLU): a gate row per neuron
   extern __shared__ uint64_t lds64[];
   __shared__ f32x4 part[KW][GT ? 2 : 1][NTT][64];
@@ -290,21 +297,24 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
   int* tmp = roff + NTK;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = mask_prefix<NTK, WMAXU>(mask, nw, F, wpt, words_lds ? wl : nullptr, roff, tmp);
+  const int ksp = blockIdx.x % KSP;
   if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
-  const int i0 = blockIdx.x * 16;
+  const int i0 = (blockIdx.x / KSP) * 16;
   if (i0 >= n) return;
   const uint64_t* words = words_lds ? wl : mask;
   if (threadIdx.x < 16) {
     const int i = i0 + threadIdx.x;
     const int id = i < n ? locate_lane(words, roff, NTK, wpt, nw, F, i) : -1;
     ids16[threadIdx.x] = id;
-    if (id >= 0) active[i] = id;
+    if (id >= 0 && ksp == 0) active[i] = id;
   }
   __syncthreads();
   const int idl = ids16[lane & 15];                      // A-operand row of this lane (-1: none)
   const int KB = (D + 31) / 32;
-  const int kpw = (KB + KW - 1) / KW;
-  const int kb0 = w * kpw, kb1 = min(KB, kb0 + kpw);
+  const int KBh = (KB + KSP - 1) / KSP;                  // k blocks of this block's share
+  const int kbs = ksp * KBh, kbe = min(KB, kbs + KBh);
+  const int kpw = (kbe - kbs + KW - 1) / KW;
+  const int kb0 = kbs + w * kpw, kb1 = min(kbe, kb0 + kpw);
   const Buf bx(x, (uint32_t)B * D * 4u);
   const int nblk = D >> 5;
   const uint32_t wbytes = Q4 ? (uint32_t)F * (uint32_t)(D >> 1) : (uint32_t)F * D * 2u;
@@ -404,7 +414,27 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
     if (GT) part[w][1][t][lane] = ag[t];
   }
   __syncthreads();
-  if (w == 0) {
+  if (w == 0 && KSP > 1) {                             // partial pre-activations of this share of k
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+      f32x4 u = part[0][0][t][lane], g = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (GT) g = part[0][1][t][lane];
+      for (int ww = 1; ww < KW; ++ww) {
+        u += part[ww][0][t][lane];
+        if (GT) g += part[ww][1][t][lane];
+      }
+      const int tok = t * 16 + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ii = i0 + (lane >> 4) * 4 + i;
+        if (tok < B && ii < n) {
+          const size_t e = (size_t)ii * B + tok;
+          pre[(size_t)(2 * ksp) * F * B + e] = u[i];
+          if (GT) pre[(size_t)(2 * ksp + 1) * F * B + e] = g[i];
+        }
+      }
+    }
+  } else if (w == 0) {
     const float* bp = GT ? bg : bu;
     float bias[4];
 #pragma unroll
@@ -432,6 +462,34 @@ __global__ __launch_bounds__(NTK) void k_mt_rows(const void* __restrict__ Wg, co
       }
     }
   }
+}
+
+// Activations from the k-split partials of k_mt_rows: entry e = i * B + token of the n * B active ones,
+// a = act(sum over the KSP shares in order, bias of neuron active[i]).
+template <int ACT>
+__global__ __launch_bounds__(256) void k_act_combine(const float* __restrict__ pre, int KSP,
+                                                     const int32_t* __restrict__ active,
+                                                     const int32_t* __restrict__ n_active,
+                                                     const float* __restrict__ bias, int B, int F,
+                                                     float* __restrict__ abuf) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int n = min(max(*n_active, 0), F);
+  if (e >= n * B) return;
+  const size_t FB = (size_t)F * B;
+  float u = 0.f, g = 0.f;
+  for (int k = 0; k < KSP; ++k) {
+    u += pre[(size_t)(2 * k) * FB + e];
+    if (ACT == 1) g += pre[(size_t)(2 * k + 1) * FB + e];
+  }
+  const float b = bias ? bias[active[e / B]] : 0.f;
+  float a;
+  if (ACT == 1) {
+    a = fmaxf(g + b, 0.f) * u;
+  } else {
+    a = fmaxf(u + b, 0.f);
+    if (ACT == 2) a *= a;
+  }
+  abuf[e] = a;
 }
 
 constexpr int DN_T = 512;            // 8 waves
@@ -648,7 +706,7 @@ hipError_t predict_mt(const void* P1, const void* P2, const float* c, const floa
 template <int NTT, int ACT, bool Q4>
 hipError_t rows_mt(const void* Wg, const void* Sg, const float* bg, const void* Wu, const void* Su, const float* bu,
                    const float* x, int B, int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active,
-                   float* abuf, hipStream_t st) {
+                   float* abuf, float* pre, int KSP, hipStream_t st) {
   const int nw = (F + 63) / 64;
   const int wpt = (nw + NTK - 1) / NTK;
   const size_t lds = (wpt <= WMAXU ? (size_t)((nw + 1) & ~1) * 8 : 0) + (NTK + NTK / 64 + 4) * sizeof(int);
@@ -658,8 +716,13 @@ hipError_t rows_mt(const void* Wg, const void* Sg, const float* bg, const void* 
     if (ea != hipSuccess) return ea;
   }
   if (lds > avail) return hipErrorInvalidValue;
-  SFFN_LAUNCH(2, (k_mt_rows<NTT, ACT, Q4>), dim3((F + 15) / 16), dim3(NTK), lds, st, Wg, Sg, bg, Wu, Su, bu, x, B,
-                     D, F, mask, active, n_active, abuf);
+  if (KSP < 1 || (KSP > 1 && !pre)) return hipErrorInvalidValue;
+  SFFN_LAUNCH(2, (k_mt_rows<NTT, ACT, Q4>), dim3((F + 15) / 16 * KSP), dim3(NTK), lds, st, Wg, Sg, bg, Wu, Su, bu, x,
+              B, D, F, mask, active, n_active, abuf, pre, KSP);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || KSP == 1) return e;
+  hipLaunchKernelGGL(k_act_combine<ACT>, dim3((F * B + 255) / 256), dim3(256), 0, st, pre, KSP, active, n_active,
+                     ACT == 1 ? bg : bu, B, F, abuf);
   return hipGetLastError();
 }
 
@@ -711,9 +774,11 @@ hipError_t sffn_launch_predict_mt(const void* P1, const void* P2, const float* c
 
 hipError_t sffn_launch_rows_mt(int act, bool q4, const void* Wg, const void* Sg, const float* bg, const void* Wu,
                                const void* Su, const float* bu, const float* x, int B, int D, int F,
-                               const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf, hipStream_t st) {
+                               const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf, float* pre,
+                               int KSP, hipStream_t st) {
   const int ntt = (B + 15) / 16;
-#define RMT(N, A, Q) return rows_mt<N, A, Q>(Wg, Sg, bg, Wu, Su, bu, x, B, D, F, mask, active, n_active, abuf, st)
+#define RMT(N, A, Q) \
+  return rows_mt<N, A, Q>(Wg, Sg, bg, Wu, Su, bu, x, B, D, F, mask, active, n_active, abuf, pre, KSP, st)
 #define RMT_A(N) \
   if (act == 1) { if (q4) RMT(N, 1, true); RMT(N, 1, false); } \
   if (act == 2) { if (q4) RMT(N, 2, true); RMT(N, 2, false); } \

@@ -61,8 +61,9 @@
  * 4 KiB: sffn_decode keeps its per-block decision bitmaps there); for B > 1 the
  * normalised inputs [B, D]; partial sums of y, [256, D] fp32 for B == 1 (one
  * per block of the fused kernel) or [8, B, D] for B > 1 (row splits; the
- * union predictor also keeps its partial h there); the predictor's h [B, r]
- * fp32 last. One workspace may serve the predict and
+ * union predictor also keeps its partial h there); for B > 1 the partial
+ * pre-activations of the k-split union row kernel, [2, 2, F, B] fp32; the
+ * predictor's h [B, r] fp32 last. One workspace may serve the predict and
  * forward calls of a layer in turn on one stream; calls that overlap in time
  * need separate workspaces.
  *

@@ -42,8 +42,8 @@ def test_status_strings_and_sizes():
     assert _lib.mask_words(1) == 1 and _lib.mask_words(64) == 1 and _lib.mask_words(65) == 2
     # [a: F*B fp32][B > 1: xn B*D fp32][partial y: 8*B*D fp32 (B > 1) or 256*D fp32 (B = 1)][h: B*r fp32]
     assert _lib.workspace_size(1, 4096, 11008, 256) == 44032 + 256 * 4096 * 4 + 1024
-    assert _lib.workspace_size(8, 512, 100, 64) == 3328 + 16384 + 131072 + 2048
-    assert _lib.workspace_size(3, 40, 7, 8) == 256 + 512 + 3840 + 256
+    assert _lib.workspace_size(8, 512, 100, 64) == 3328 + 16384 + 131072 + 12800 + 2048   # + k-split partials
+    assert _lib.workspace_size(3, 40, 7, 8) == 256 + 512 + 3840 + 512 + 256
 
 
 A = 0x10000          # fake, 256-byte aligned, never dereferenced
