@@ -329,6 +329,7 @@ def main():
         "warmup": W,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
+        "us_per_layer": round(float(np.median(per_step)) * 1e3 / L, 3),   # FFN-layer time: median step / layers
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
