@@ -193,3 +193,18 @@ def test_decode_paths_and_workspace():
     assert _lib.decode_path(9, False, 512, 1000, 64) == -1
     # one token: the activation region holds at least the 256 workgroups' 16-byte decision bitmaps
     assert _lib.workspace_size(1, 64, 1, 8) == 4096 + 256 * 64 * 4 + 256
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # the product path has no non-HIP implementation: without libsffn.so every call raises
+    monkeypatch.setattr(_lib, "_handle", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libsffn.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.workspace_size(1, 64, 64, 8)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2", "--steps", "1"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stdout

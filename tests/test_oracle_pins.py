@@ -492,3 +492,26 @@ def _mut_mask_first_token(masks):
 def test_planted_mistake_is_caught(monkeypatch, name, mutant):
     monkeypatch.setattr(sf, name, mutant)
     assert not _all_pins()
+
+
+def test_stack_with_per_layer_prefix_and_rank():
+    # a stack whose layers differ in predictor rank and always-active prefix equals the layers called in turn,
+    # each on the normalised output of the previous one
+    rng = np.random.default_rng(21)
+    D, F = 12, 20
+    layers = []
+    for r in (2, 5, 3):
+        layers.append({"P1": rng.standard_normal((r, D)), "P2": rng.standard_normal((F, r)),
+                       "c": rng.standard_normal(F) - 1.0, "W_gate": rng.standard_normal((F, D)),
+                       "b_gate": rng.standard_normal(F), "W_up": rng.standard_normal((F, D)),
+                       "W_down": rng.standard_normal((D, F))})
+    x = rng.standard_normal((2, D))
+    hots = [0, 4, F]
+    out = sf.stack("reglu", x, layers, 0.5, n_hot=hots)
+    xl = x
+    for (z, m, y), w, nh in zip(out, layers, hots):
+        z2, m2, y2 = sf.layer("reglu", xl, w, 0.5, nh)
+        assert np.array_equal(z, z2) and np.array_equal(m, m2) and np.array_equal(y, y2)
+        assert m[:nh].all()
+        xl = sf.layer_norm(y2)
+    assert out[2][1].all()                               # a prefix of every neuron: the dense layer
