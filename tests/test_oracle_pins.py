@@ -377,6 +377,93 @@ def test_band_rule():
     assert b.tolist() == [True, False, False, True, True]
 
 
+# ----------------------------------------------------------------------------- logical weights
+def _q4_tiny(seed=31, D=64, F=64):
+    """A tiny Q4_0 ReGLU layer with planted codes and scales: every plane draws its own values, so a plane routed
+    to the wrong logical matrix, or a scale plane read in the wrong orientation, changes some element."""
+    rng = np.random.default_rng(seed)
+    t = {"P1": rng.integers(-8, 8, size=(4, D)).astype(np.float16) / np.float16(8),
+         "P2": rng.integers(-8, 8, size=(F, 4)).astype(np.float16) / np.float16(8),
+         "Q_gate": rng.integers(0, 16, size=(F, D)).astype(np.uint8),
+         "S_gate": (rng.integers(1, 200, size=(F, D // 32)) / 1024.0).astype(np.float16),
+         "Q_up": rng.integers(0, 16, size=(F, D)).astype(np.uint8),
+         "S_up": (rng.integers(200, 400, size=(F, D // 32)) / 1024.0).astype(np.float16),
+         "Q_down": rng.integers(0, 16, size=(D, F)).astype(np.uint8),
+         "S_down": (rng.integers(400, 600, size=(D // 32, F)) / 1024.0).astype(np.float16),
+         "b_gate": rng.standard_normal(F).astype(np.float32), "c": rng.standard_normal(F).astype(np.float32)}
+    return t
+
+
+def _fp16_tiny(seed=32, D=16, F=24):
+    rng = np.random.default_rng(seed)
+    return {"P1": rng.standard_normal((4, D)).astype(np.float16), "P2": rng.standard_normal((F, 4)).astype(np.float16),
+            "W_gate": rng.standard_normal((F, D)).astype(np.float16),
+            "W_up": rng.standard_normal((F, D)).astype(np.float16),
+            "W_down": rng.standard_normal((D, F)).astype(np.float16),
+            "b_gate": rng.standard_normal(F).astype(np.float32), "c": rng.standard_normal(F).astype(np.float32)}
+
+
+def check_logical_weights():
+    """Every logical matrix is the element-wise exact value of the plane it is named after: Q4_0 as
+    (q - 8) * s with the scale of the element's 32-block along d_model (rows of W_gate / W_up, columns of
+    W_down), fp16 upcast unchanged; biases and predictor factors pass through."""
+    Fr = lambda v: Fraction(float(v))  # noqa: E731
+    try:
+        t = _q4_tiny()
+        w = sf.logical_weights(t)
+        F, D = t["Q_up"].shape
+        ok = set(w) == {"P1", "P2", "W_gate", "W_up", "W_down", "b_gate", "c"}
+        for name, q, s in (("W_gate", t["Q_gate"], t["S_gate"]), ("W_up", t["Q_up"], t["S_up"])):
+            ok &= w[name].shape == (F, D)
+            ok &= all(Fr(w[name][k, d]) == (int(q[k, d]) - 8) * Fr(s[k, d // 32]) for k in range(F) for d in range(D))
+        ok &= w["W_down"].shape == (D, F)
+        ok &= all(Fr(w["W_down"][d, k]) == (int(t["Q_down"][d, k]) - 8) * Fr(t["S_down"][d // 32, k])
+                  for d in range(D) for k in range(F))
+        for name in ("P1", "P2", "b_gate", "c"):
+            ok &= np.array_equal(w[name], t[name].astype(np.float64))
+        t = _fp16_tiny()
+        w = sf.logical_weights(t)
+        ok &= set(w) == {"P1", "P2", "W_gate", "W_up", "W_down", "b_gate", "c"}
+        for name in t:
+            ok &= w[name].dtype == np.float64 and w[name].shape == t[name].shape
+            ok &= all(Fr(a) == Fr(b) for a, b in zip(w[name].ravel(), t[name].ravel()))
+        return bool(ok)
+    except (KeyError, AssertionError, ValueError, IndexError):
+        return False
+
+
+def test_logical_weights_planes():
+    assert check_logical_weights()
+
+
+# ----------------------------------------------------------------------------- stack (closed form)
+def check_stack_closed_form():
+    """Two ReLU layers worked by hand. Layer 1 (rank 1): x = (3, -1), h = 2, z = (2, 2), both neurons computed,
+    u = (2, -0.5), a = (2, 0), y1 = (2, 6). The next input is y1 centred and scaled: mean 4, variance 4, so
+    x2 = (-2, 2) / sqrt(4 + eps) = (-s, s). Layer 2 (rank 2, first neuron always active): h = x2,
+    z = (-s, -s), so the predictor marks nothing and only neuron 0 is computed; u = (s, s), a = (s, 0),
+    y2 = (s, 2 s)."""
+    s = 2.0 / np.sqrt(4.0 + sf.NORM_EPS)
+    l1 = {"P1": np.array([[1.0, 1.0]]), "P2": np.array([[1.0], [1.0]]), "c": np.array([0.0, 0.0]),
+          "W_up": np.eye(2), "b_up": np.array([-1.0, 0.5]), "W_down": np.array([[1.0, 0.0], [3.0, 2.0]])}
+    l2 = {"P1": np.eye(2), "P2": np.array([[1.0, 0.0], [0.0, -1.0]]), "c": np.array([0.0, 0.0]),
+          "W_up": np.array([[-1.0, 0.0], [0.0, 1.0]]), "b_up": np.array([0.0, 0.0]),
+          "W_down": np.array([[1.0, 0.0], [2.0, 5.0]])}
+    try:
+        out = sf.stack("relu", np.array([[3.0, -1.0]]), [l1, l2], 0.5, n_hot=[0, 1])
+        (z1, m1, y1), (z2, m2, y2) = out
+        ok = len(out) == 2 and z1.tolist() == [[2.0, 2.0]] and m1.tolist() == [True, True]
+        ok &= y1.tolist() == [[2.0, 6.0]] and m2.tolist() == [True, False]
+        ok &= np.allclose(z2, [[-s, -s]], rtol=1e-15, atol=0) and np.allclose(y2, [[s, 2 * s]], rtol=1e-15, atol=0)
+        return bool(ok)
+    except (KeyError, ValueError, IndexError):
+        return False
+
+
+def test_stack_two_layers_closed_form():
+    assert check_stack_closed_form()
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 def check_layer_norm():
     y = np.array([[3.0, -1.0]])
@@ -389,7 +476,8 @@ def _all_pins():
                                        for B in (1, 3) for s in (0, 1))
             and all(check_brute_force(act, 2, 3, n_hot=n) for act in ("relu", "reglu") for n in (1, 5))
             and check_q4_exact() and all(check_true_mask_equals_dense(a) for a in ("relu", "sqrelu", "reglu"))
-            and check_permutation_invariance() and check_hot_prefix_closed_form())
+            and check_permutation_invariance() and check_hot_prefix_closed_form()
+            and check_logical_weights() and check_stack_closed_form())
 
 
 def test_unmutated_oracle_passes_all_pins():
@@ -473,6 +561,55 @@ def _mut_mask_first_token(masks):
     return np.atleast_2d(masks)[0]
 
 
+def _mut_lw_gate_up_swapped(t):
+    w = _LW(t)
+    if "Q_gate" in t:
+        w["W_gate"] = sf.dequant_q4_rows(t["Q_up"], t["S_up"])
+        w["W_up"] = sf.dequant_q4_rows(t["Q_gate"], t["S_gate"])
+    return w
+
+
+def _mut_lw_scales_swapped(t):
+    w = _LW(t)
+    if "Q_gate" in t:
+        w["W_gate"] = sf.dequant_q4_rows(t["Q_gate"], t["S_up"])
+        w["W_up"] = sf.dequant_q4_rows(t["Q_up"], t["S_gate"])
+    return w
+
+
+def _mut_lw_down_scale_transposed(t):
+    w = _LW(t)
+    if "Q_down" in t:                                  # scale blocks taken along d_ffn instead of d_model
+        w["W_down"] = sf.dequant_q4_rows(t["Q_down"], np.asarray(t["S_down"]).T)
+    return w
+
+
+def _mut_lw_fp16_gate_up_swapped(t):
+    w = _LW(t)
+    if "W_gate" in t:
+        w["W_gate"], w["W_up"] = w["W_up"], w["W_gate"]
+    return w
+
+
+def _mut_stack_unnormalised(act, x, layers, t=0.5, n_hot=0):
+    out, xl = [], np.atleast_2d(np.asarray(x, dtype=np.float64))
+    hots = list(n_hot) if np.ndim(n_hot) else [int(n_hot)] * len(layers)
+    for w, nh in zip(layers, hots):
+        z, m, y = sf.layer(act, xl, w, t, nh)
+        out.append((z, m, y))
+        xl = y                                         # next layer fed the raw output
+    return out
+
+
+def _mut_stack_first_prefix_everywhere(act, x, layers, t=0.5, n_hot=0):
+    hots = list(n_hot) if np.ndim(n_hot) else [int(n_hot)] * len(layers)
+    return _STACK(act, x, layers, t, [hots[0]] * len(layers))
+
+
+_LW = sf.logical_weights
+_STACK = sf.stack
+
+
 @pytest.mark.parametrize("name,mutant", [
     ("predictor_logits", _mut_predictor_transposed),
     ("predictor_logits", _mut_predictor_no_bias),
@@ -488,30 +625,15 @@ def _mut_mask_first_token(masks):
     ("ffn_masked", _mut_mask_ignored),
     ("union_mask", _mut_mask_first_token),
     ("layer_norm", _mut_norm_uncentred),
+    ("logical_weights", _mut_lw_gate_up_swapped),
+    ("logical_weights", _mut_lw_scales_swapped),
+    ("logical_weights", _mut_lw_down_scale_transposed),
+    ("logical_weights", _mut_lw_fp16_gate_up_swapped),
+    ("stack", _mut_stack_unnormalised),
+    ("stack", _mut_stack_first_prefix_everywhere),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, mutant):
     monkeypatch.setattr(sf, name, mutant)
     assert not _all_pins()
 
 
-def test_stack_with_per_layer_prefix_and_rank():
-    # a stack whose layers differ in predictor rank and always-active prefix equals the layers called in turn,
-    # each on the normalised output of the previous one
-    rng = np.random.default_rng(21)
-    D, F = 12, 20
-    layers = []
-    for r in (2, 5, 3):
-        layers.append({"P1": rng.standard_normal((r, D)), "P2": rng.standard_normal((F, r)),
-                       "c": rng.standard_normal(F) - 1.0, "W_gate": rng.standard_normal((F, D)),
-                       "b_gate": rng.standard_normal(F), "W_up": rng.standard_normal((F, D)),
-                       "W_down": rng.standard_normal((D, F))})
-    x = rng.standard_normal((2, D))
-    hots = [0, 4, F]
-    out = sf.stack("reglu", x, layers, 0.5, n_hot=hots)
-    xl = x
-    for (z, m, y), w, nh in zip(out, layers, hots):
-        z2, m2, y2 = sf.layer("reglu", xl, w, 0.5, nh)
-        assert np.array_equal(z, z2) and np.array_equal(m, m2) and np.array_equal(y, y2)
-        assert m[:nh].all()
-        xl = sf.layer_norm(y2)
-    assert out[2][1].all()                               # a prefix of every neuron: the dense layer
