@@ -10,7 +10,8 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsffn.so")
+# SFFN_LIB_PATH selects another build of the same library (the host-sanitized one of the CPU checks)
+LIB_PATH = os.environ.get("SFFN_LIB_PATH") or os.path.join(HERE, "libsffn.so")
 
 ACT_RELU, ACT_REGLU, ACT_SQRELU = 0, 1, 2
 ACTS = {"relu": ACT_RELU, "reglu": ACT_REGLU, "sqrelu": ACT_SQRELU}
@@ -154,7 +155,8 @@ DECODE_SEPARATE, DECODE_FOLDED = 0, 1
 
 
 def decode_path(act, q4: bool, D: int, F: int, r: int) -> int:
-    """DECODE_FOLDED if sffn_decode runs the predictor's second stage inside the row gather for these sizes."""
+    """Which kernels sffn_decode runs for these sizes: DECODE_FOLDED (h, then the predictor's second stage inside
+    the fused gather, then the sum of partials) or DECODE_SEPARATE (the sffn_predict and sffn_forward calls)."""
     return int(lib().sffn_decode_path(ACTS.get(act, act), int(bool(q4)), D, F, r))
 
 

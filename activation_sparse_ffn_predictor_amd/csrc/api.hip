@@ -40,6 +40,13 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool al(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Predictor rank and P2 [F, r] fp16: the kernels address P2 with 31-bit byte offsets (buffer loads).
+int check_rank(int F, int r) {
+  if (r < 8 || r > MAX_R || r % 8) return fail(SFFN_ERR_SHAPE, "r=%d: need 8 <= r <= %d, r %% 8 == 0", r, MAX_R);
+  if ((size_t)F * r * 2 >= MAX_TENSOR) return fail(SFFN_ERR_SHAPE, "F=%d, r=%d: P2 reaches 2 GiB", F, r);
+  return SFFN_OK;
+}
+
 int check_common(int B, int D, int F) {
   if (B < 1 || B > MAX_B) return fail(SFFN_ERR_SHAPE, "B=%d outside [1, %d]", B, MAX_B);
   if (D < 8 || D > MAX_D || D % 8) return fail(SFFN_ERR_SHAPE, "D=%d: need 8 <= D <= %d, D %% 8 == 0", D, MAX_D);
@@ -236,7 +243,8 @@ static int predict_impl(const void* P1, const void* P2, const float* c, const fl
   int s = check_common(B, D, F);
   if (s) return s;
   if (n_hot < 0 || n_hot > F) return fail(SFFN_ERR_ARG, "n_hot=%d outside 0..F=%d", n_hot, F);
-  if (r < 8 || r > MAX_R || r % 8) return fail(SFFN_ERR_SHAPE, "r=%d: need 8 <= r <= %d, r %% 8 == 0", r, MAX_R);
+  s = check_rank(F, r);
+  if (s) return s;
   if ((long)B * r > MAX_BR) return fail(SFFN_ERR_SHAPE, "B*r=%ld > %d", (long)B * r, MAX_BR);
   if (!(t > 0.f && t < 1.f)) return fail(SFFN_ERR_ARG, "threshold t=%g outside (0, 1)", (double)t);
   if (!al(P1, 16) || !al(P2, 16) || !al(x, 16) || !al(mask, 8) || (c && !al(c, 4)) || (logits && !al(logits, 4)))
@@ -296,7 +304,8 @@ int sffn_decode(int act, const void* P1, const void* P2, const float* c, float t
   if (act != SFFN_ACT_RELU && act != SFFN_ACT_REGLU && act != SFFN_ACT_SQRELU)
     return fail(SFFN_ERR_ACT, "unknown activation %d", act);
   if (act == SFFN_ACT_REGLU && !W_gate) return fail(SFFN_ERR_ACT, "ReGLU needs W_gate");
-  if (!sffn_decode_ok(act, D, F, r, G_FUSED)) {        // the separate predictor and forward calls
+  const int path = sffn_decode_path(act, 0, D, F, r);
+  if (path == SFFN_DECODE_SEPARATE) {                  // the separate predictor and forward calls
     int s = predict_impl(P1, P2, c, x, x_norm, 1, D, F, r, t, n_hot, mask, logits, ws, ws_bytes, stream);
     if (s) return s;
     return sffn_forward(act, W_gate, b_gate, W_up, b_up, W_downT, x, x_norm, 1, D, F, mask, active, n_active, y, ws,
@@ -306,7 +315,8 @@ int sffn_decode(int act, const void* P1, const void* P2, const float* c, float t
     return fail(SFFN_ERR_NULL, "decode: P1, P2, x, W_up, W_downT, mask, active, n_active and y are required");
   int s = check_common(1, D, F);
   if (s) return s;
-  if (r < 8 || r > MAX_R || r % 8) return fail(SFFN_ERR_SHAPE, "r=%d: need 8 <= r <= %d, r %% 8 == 0", r, MAX_R);
+  s = check_rank(F, r);
+  if (s) return s;
   if (!(t > 0.f && t < 1.f)) return fail(SFFN_ERR_ARG, "threshold t=%g outside (0, 1)", (double)t);
   if (n_hot < 0 || n_hot > F) return fail(SFFN_ERR_ARG, "n_hot=%d outside 0..F=%d", n_hot, F);
   if (!al(P1, 16) || !al(P2, 16) || !al(x, 16) || !al(mask, 8) || (c && !al(c, 4)) || (logits && !al(logits, 4)) ||

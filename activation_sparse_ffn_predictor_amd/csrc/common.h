@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <mutex>
+
 namespace sffn {
 
 constexpr int WAVE = 64;
@@ -348,6 +350,27 @@ inline hipError_t allow_dynamic_lds(const void* func, size_t* avail) {
   *avail = total > fa.sharedSizeBytes ? total - fa.sharedSizeBytes : 0;
   return hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)*avail);
 }
+
+#ifndef SFFN_MAX_DEVICES
+#define SFFN_MAX_DEVICES 64
+#endif
+// The dynamic LDS limit of one kernel, set on the current device by its first launch there. Thread-safe: the
+// attribute is set exactly once per device (std::call_once), and every caller then reads the stored result.
+// One static instance per kernel (a function-local static of the launcher).
+struct LdsLimit {
+  std::once_flag once[SFFN_MAX_DEVICES];
+  size_t avail[SFFN_MAX_DEVICES] = {};
+  hipError_t err[SFFN_MAX_DEVICES] = {};
+  hipError_t get(const void* func, size_t* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SFFN_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [&] { err[dev] = allow_dynamic_lds(func, &avail[dev]); });
+    *out = avail[dev];
+    return err[dev];
+  }
+};
 
 // ---- profiling hook (api.hip): while kernel id `kid` is being profiled (sffn_profile_begin), hands out the next
 // pair of events. The launch then records the kernel's own start and end timestamps into them

@@ -243,11 +243,10 @@ hipError_t launch_decode(const void* P2, const float* c, const float* h, int r, 
                          int D, int F, uint32_t* dec, float* logits, float* part, int G, uint64_t* mask,
                          int32_t* active, int32_t* n_active, float* y, hipStream_t st) {
   const size_t lds = (1024 + (size_t)D + FWD + 2 * FWD + 4) * sizeof(float) + ZS * FWD + 32 * JW * sizeof(int);
-  static size_t avail = 0;
-  if (!avail) {
-    hipError_t ea = allow_dynamic_lds((const void*)k_decode1<ACT, NCH, DCH>, &avail);
-    if (ea != hipSuccess) return ea;
-  }
+  static LdsLimit lds_limit;   // per kernel, set once per device
+  size_t avail = 0;
+  hipError_t ea = lds_limit.get((const void*)k_decode1<ACT, NCH, DCH>, &avail);
+  if (ea != hipSuccess) return ea;
   if (lds > avail || G != GD) return hipErrorInvalidValue;
   SFFN_LAUNCH(2, (k_decode1<ACT, NCH, DCH>), dim3(G), dim3(NT_D), lds, st, (const uint4*)P2, c, h, r, z_log_rounds(r), tau,
               n_hot, (const uint4*)Wg, bg, (const uint4*)Wu, bu, (const uint4*)WdT, x, x_norm, D, F, dec, logits,

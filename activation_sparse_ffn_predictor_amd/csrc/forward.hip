@@ -255,11 +255,10 @@ hipError_t launch_up(const void* Wg, const float* bg, const void* Wu, const floa
   const size_t lds_scan = (wpt <= WMAX ? (size_t)((nw + 1) & ~1) * 8 : 0) + (NT_UP + NT_UP / 64 + 4) * sizeof(int);
   const int grid = std::max(1, std::min((F + 3) / 4, SFFN_UP_GRID));
   const size_t lds = lds_scan + ((size_t)B * D + 2 * (NT_UP / 64) * B) * sizeof(float);
-  static size_t avail = 0;
-  if (!avail) {
-    hipError_t ea = allow_dynamic_lds((const void*)k_upgate<B, ACT, NCH>, &avail);
-    if (ea != hipSuccess) return ea;
-  }
+  static LdsLimit lds_limit;   // per kernel, set once per device
+  size_t avail = 0;
+  hipError_t ea = lds_limit.get((const void*)k_upgate<B, ACT, NCH>, &avail);
+  if (ea != hipSuccess) return ea;
   if (lds > avail) return hipErrorInvalidValue;
   SFFN_LAUNCH(2, (k_upgate<B, ACT, NCH>), dim3(grid), dim3(NT_UP), lds, st, (const uint4*)Wg, bg,
               (const uint4*)Wu, bu, x, x_norm, D, F, mask, active, n_active, abuf);

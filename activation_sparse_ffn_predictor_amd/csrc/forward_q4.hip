@@ -307,11 +307,10 @@ hipError_t launch_up(const uint8_t* qg, const void* sg, const float* bg, const u
   const int wpt = (nw + NT_UP - 1) / NT_UP;
   const size_t lds = (wpt <= WMAX ? (size_t)((nw + 1) & ~1) * 8 : 0) + (NT_UP + NT_UP / 64 + 4) * sizeof(int) +
                      ((size_t)B * D + (size_t)B * nblk + 2 * (NT_UP / 64) * B) * sizeof(float);
-  static size_t avail = 0;
-  if (!avail) {
-    hipError_t ea = allow_dynamic_lds((const void*)k_upgate_q4<B, ACT, NQ>, &avail);
-    if (ea != hipSuccess) return ea;
-  }
+  static LdsLimit lds_limit;   // per kernel, set once per device
+  size_t avail = 0;
+  hipError_t ea = lds_limit.get((const void*)k_upgate_q4<B, ACT, NQ>, &avail);
+  if (ea != hipSuccess) return ea;
   if (lds > avail) return hipErrorInvalidValue;
   const int grid = std::max(1, std::min((F + 3) / 4, SFFN_UP_GRID));
   SFFN_LAUNCH(2, (k_upgate_q4<B, ACT, NQ>), dim3(grid), dim3(NT_UP), lds, st, (const uint4*)qg,

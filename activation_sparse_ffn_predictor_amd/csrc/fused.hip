@@ -345,11 +345,10 @@ hipError_t launch_fused(const void* Wg, const float* bg, const void* Wu, const f
   if (G < 64) return hipErrorInvalidValue;            // one owned row per mask word at most
   const size_t lds = (size_t)((nw + 1) & ~1) * 8 + (NT_F + NT_F / 64 + 4) * sizeof(int) +
                      (FW + 2 * FW + 4 + (size_t)D) * sizeof(float) + ((size_t)(F + G - 1) / G) * sizeof(int) + 16;
-  static size_t avail = 0;
-  if (!avail) {
-    hipError_t ea = allow_dynamic_lds((const void*)k_fused1<ACT, NCH, DCH>, &avail);
-    if (ea != hipSuccess) return ea;
-  }
+  static LdsLimit lds_limit;   // per kernel, set once per device
+  size_t avail = 0;
+  hipError_t ea = lds_limit.get((const void*)k_fused1<ACT, NCH, DCH>, &avail);
+  if (ea != hipSuccess) return ea;
   if (lds > avail) return hipErrorInvalidValue;
   SFFN_LAUNCH(2, (k_fused1<ACT, NCH, DCH>), dim3(G), dim3(NT_F), lds, st, (const uint4*)Wg, bg, (const uint4*)Wu, bu,
               (const uint4*)WdT, x, x_norm, D, F, mask, active, n_active, part);
@@ -387,11 +386,10 @@ hipError_t launch_fused_q4(const uint8_t* qg, const void* sg, const float* bg, c
   const size_t lds = (size_t)((nw + 1) & ~1) * 8 + (NT_F + NT_F / 64 + 4) * sizeof(int) +
                      (NS + 2 * FW + 4 + (size_t)D + nblk) * sizeof(float) + ((size_t)(F + G - 1) / G) * sizeof(int) +
                      16 + (size_t)NS * ((nblk + 63) / 64) * 1024 + 16;   // + the pass's nibble rows
-  static size_t avail = 0;
-  if (!avail) {
-    hipError_t ea = allow_dynamic_lds((const void*)k_fused1_q4<ACT, NQ, RPW>, &avail);
-    if (ea != hipSuccess) return ea;
-  }
+  static LdsLimit lds_limit;   // per kernel, set once per device
+  size_t avail = 0;
+  hipError_t ea = lds_limit.get((const void*)k_fused1_q4<ACT, NQ, RPW>, &avail);
+  if (ea != hipSuccess) return ea;
   if (lds > avail || G > SG * SPG) return hipErrorInvalidValue;
   SFFN_LAUNCH(2, (k_fused1_q4<ACT, NQ, RPW>), dim3(G), dim3(NT_F), lds, st, (const uint4*)qg, (const _Float16*)sg, bg,
               (const uint4*)qu, (const _Float16*)su, bu, qd, (const _Float16*)sd, x, x_norm, D, F, mask, active,

@@ -710,11 +710,10 @@ hipError_t rows_mt(const void* Wg, const void* Sg, const float* bg, const void* 
   const int nw = (F + 63) / 64;
   const int wpt = (nw + NTK - 1) / NTK;
   const size_t lds = (wpt <= WMAXU ? (size_t)((nw + 1) & ~1) * 8 : 0) + (NTK + NTK / 64 + 4) * sizeof(int);
-  static size_t avail = 0;
-  if (!avail) {
-    hipError_t ea = allow_dynamic_lds((const void*)k_mt_rows<NTT, ACT, Q4>, &avail);
-    if (ea != hipSuccess) return ea;
-  }
+  static LdsLimit lds_limit;   // per kernel, set once per device
+  size_t avail = 0;
+  hipError_t ea = lds_limit.get((const void*)k_mt_rows<NTT, ACT, Q4>, &avail);
+  if (ea != hipSuccess) return ea;
   if (lds > avail) return hipErrorInvalidValue;
   if (KSP < 1 || (KSP > 1 && !pre)) return hipErrorInvalidValue;
   SFFN_LAUNCH(2, (k_mt_rows<NTT, ACT, Q4>), dim3((F + 15) / 16 * KSP), dim3(NTK), lds, st, Wg, Sg, bg, Wu, Su, bu, x,
@@ -731,11 +730,10 @@ hipError_t down_mt(const void* Wd, const void* Sd, const int32_t* active, const 
                    int B, int D, int F, float* part, int KS, float* y, hipStream_t st) {
   const int M = (F + DS_K * KS - 1) / (DS_K * KS);
   const size_t lds = (size_t)M * DS_K * sizeof(int);
-  static size_t avail = 0;
-  if (!avail) {
-    hipError_t ea = allow_dynamic_lds((const void*)k_mt_down<NTT, Q4>, &avail);
-    if (ea != hipSuccess) return ea;
-  }
+  static LdsLimit lds_limit;   // per kernel, set once per device
+  size_t avail = 0;
+  hipError_t ea = lds_limit.get((const void*)k_mt_down<NTT, Q4>, &avail);
+  if (ea != hipSuccess) return ea;
   if (lds > avail) return hipErrorInvalidValue;
   SFFN_LAUNCH(3, (k_mt_down<NTT, Q4>), dim3((D + DS_COLS - 1) / DS_COLS, KS), dim3(DN_T), lds, st, Wd, Sd, active,
               n_active, abuf, B, D, F, part);

@@ -73,10 +73,16 @@ class SparseFFNStack:
             _lib.forward(wl.act, t.get("W_gate"), t.get("b_gate"), t["W_up"], t.get("b_up"), t["W_downT"], x,
                          self.mask[i], self.active[i], self.n_active[i:i + 1], y, self.ws, x_norm=x_norm)
 
+    def decode_path(self, i: int, B: int) -> int:
+        """The kernels of layer i's call for B tokens: _lib.DECODE_FOLDED when sffn_decode runs the predictor's
+        second stage inside the row gather, else DECODE_SEPARATE (sffn_predict, then the forward call)."""
+        if not (self.fold_predictor and B == 1 and not self.q4):
+            return _lib.DECODE_SEPARATE
+        return _lib.decode_path(self.wl.act, False, self.wl.D, self.wl.F, self.ranks[i])
+
     def folded(self, i: int, B: int) -> bool:
-        """Whether layer i's call for B tokens runs the predictor's second stage inside the row gather."""
-        return (self.fold_predictor and B == 1 and not self.q4
-                and _lib.decode_path(self.wl.act, False, self.wl.D, self.wl.F, self.ranks[i]) == _lib.DECODE_FOLDED)
+        """Whether layer i's call for B tokens runs the predictor's second stage in the row-gather kernel."""
+        return self.decode_path(i, B) != _lib.DECODE_SEPARATE
 
     # ------------------------------------------------------------------ decode step
     def step(self, B: int = 1):

@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", "--config", default="relullama_7b",
+    ap.add_argument("--workload", "--config", default="falcon_40b",
                     help="toy_relu | relullama_7b | llama2_13b | falcon_40b | llama2_70b_q4 (or c1..c5)")
     ap.add_argument("--batch", type=int, default=1, help="tokens per decode step (union mask when > 1)")
     ap.add_argument("--act", choices=("relu", "sqrelu", "reglu"), default=None,
@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--prompt", type=int, default=None,
                     help="prompt tokens timed as one union batch (default: the workload's own, 64 for the 70B)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--also", default="llama2_13b",
+                    help="comma-separated workloads measured after the headline one at the same batch, steps and "
+                         "warm-up (decode only, no CPU sample), reported under 'also'; 'none' for none")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of replaying a graph")
     ap.add_argument("--copy-only", type=float, default=None, metavar="MIB",
                     help="only copy MIB mebibytes device to device 8 times and exit (the reference transfer that "
@@ -109,15 +112,12 @@ def copy_only(mib: float):
 
 def cpu_baseline(wl, B: int, budget_s: float):
     """The oracle (plain fp64 NumPy dense FFN + predictor) timed on this host over a bounded sample of the same
-    workload: whole layers, B tokens per evaluation, until the time budget is spent; extrapolated to the stack."""
+    workload: whole layers, B tokens per evaluation, until the time budget is spent; extrapolated to the stack.
+    BLAS runs on every core of this process's affinity mask; a shorter second sample runs on one thread."""
     import numpy as np
     import oracle
     import synthgen as sg
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+    cores = len(os.sched_getaffinity(0))
     layers = [0, 1] if wl.L > 1 else [0]
     ws = [oracle.logical_weights(sg.layer_host(wl, l)) for l in layers]
     t_start = time.perf_counter()
@@ -135,46 +135,47 @@ def cpu_baseline(wl, B: int, budget_s: float):
             step += 1
         return float(np.median(times)), n
 
-    per_layer, n = sample(budget_s)
-    one = None
-    try:                                               # the same oracle on one BLAS thread, a shorter sample
-        from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):
+    blas_threads, one = None, None
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        with threadpool_limits(limits=cores):
+            blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+            per_layer, n = sample(budget_s)
+        with threadpool_limits(limits=1):               # the same oracle on one BLAS thread, a shorter sample
             one, _ = sample(budget_s / 3.0)
-    except Exception:  # noqa: BLE001
-        pass
+    except ImportError:
+        per_layer, n = sample(budget_s)
     tok_s = B / (per_layer * wl.L)
-    return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": int(blas_threads or cores), "kind": "oracle",
             "sample": f"{n} layer evaluations of {wl.name} (layers {layers}, {B} token(s) each, fp64 NumPy dense FFN "
                       f"+ predictor), median {per_layer * 1e3:.1f} ms per layer, extrapolated to {wl.L} layers",
+            "affinity_cores": cores, "blas_threads": blas_threads,
             "value_1_thread": None if one is None else round(B / (one * wl.L), 4),
             "cpu_model": _cpu_model(),
             "seconds": round(time.perf_counter() - t_start, 2)}
 
 
 def _cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it: model name, family / model / stepping, logical CPUs."""
+    info, ncpu = {}, 0
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "processor":
+                    ncpu += 1
+                elif k in ("model name", "cpu family", "model", "stepping", "vendor_id") and k not in info:
+                    info[k] = v
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    return (f"{info.get('model name', 'unknown')} ({info.get('vendor_id', '?')} family {info.get('cpu family', '?')} "
+            f"model {info.get('model', '?')} stepping {info.get('stepping', '?')}, {ncpu} logical CPUs visible)")
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs the sparse-FFN stack on one GPU; --gpus must be 1"}),
-              flush=True)
-        sys.exit(2)
-
-    if args.copy_only is not None:
-        copy_only(args.copy_only)
-        return
-
+def measure(wl, B: int, args, with_prompt: bool):
+    """Build the resident stack of ``wl`` and time its decode steps (and, if asked, its prompt); returns the
+    fields of the JSON line for this workload."""
     import numpy as np
     import torch
 
@@ -182,13 +183,7 @@ def main():
     from activation_sparse_ffn_predictor_amd import _lib
     from activation_sparse_ffn_predictor_amd.stack import SparseFFNStack
 
-    wl = sg.workload(args.workload)
-    if args.act and args.act != wl.act:
-        wl = sg.custom(wl, act=args.act, name=f"{wl.name}_{args.act}")
-    if args.rank_schedule == "adaptive":
-        wl = sg.with_rank_schedule(wl)
-    B = args.batch
-    PB = wl.prompt if args.prompt is None else args.prompt
+    PB = (wl.prompt if args.prompt is None else args.prompt) if with_prompt else 0
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
     stack = SparseFFNStack(wl, dev, max_batch=max(B, PB), hot_prefix=args.hot_prefix,
@@ -297,6 +292,7 @@ def main():
     path = _lib.forward_path(wl.act, stack.q4, B, wl.D, wl.F)
     ranks, hots = np.asarray(stack.ranks, np.float64), np.asarray(stack.n_hot, np.float64)
     fold = np.tile(np.array([stack.folded(i, B) for i in range(L)]), P)   # launches: P steps x L layers
+    sep = ~fold
     p2_bytes = np.tile(2.0 * (wl.F - hots) * ranks, P)
     if path == _lib.PATH_FUSED:
         # kernel 2 gathers gate/up and W_downT rows (folded: after reading the block's P2 rows); kernel 3 adds
@@ -306,7 +302,7 @@ def main():
     else:
         bytes_rows = n_prof * rows_mats * one_row                # per launch of kernel 2
         bytes_cols = n_prof * one_row                            # per launch of kernel 3
-    kb = {0: np.tile(2.0 * ranks * wl.D, P), 1: p2_bytes[~fold],   # launches in layer order
+    kb = {0: np.tile(2.0 * ranks * wl.D, P), 1: p2_bytes[sep],   # launches in layer order
           2: bytes_rows, 3: bytes_cols}
     tot = {k: float(prof[k].sum()) for k in prof}
     dom = max(tot, key=tot.get)
@@ -320,22 +316,12 @@ def main():
 
     tr = traffic_for(wl.name, B, names[dom], float(kb[dom][:m].mean()))
     traffic, traffic_detail = tr if tr else (None, None)
-    out = {
-        "metric": METRIC,
+    res = {
         "value": round(tok_s, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
         "us_per_layer": round(float(np.median(per_step)) * 1e3 / L, 3),   # FFN-layer time: median step / layers
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "f16" if not stack.q4 else "q4_0",
-        "accumulate": "f32",
-        "data": "synthetic",
         "config": {"workload": wl.name, "d_model": wl.D, "d_ffn": wl.F,
                    "rank": wl.r if not wl.ranks else list(wl.ranks), "layers": L, "batch": B,
                    "activation": wl.act, "weights": "fp16" if not stack.q4 else "q4_0", "density_target": wl.density,
@@ -343,17 +329,75 @@ def main():
                    "predictor_folded_layers": int(fold[:L].sum()), "graph": not args.no_graph},
         "active_weight_gbs": round(active_bytes_step / (ms_step * 1e-3) / 1e9, 1),
         "forward_active_gbs": round(fwd_gbs, 1),
+        # the spec quantity: active-weight bytes over the forward kernels' time, against the 8 TB/s peak
+        "active_weight_frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
         "all_bytes_gbs": round((active_bytes_step + pred_bytes_step) / (ms_step * 1e-3) / 1e9, 1),
         "active_rows_per_layer": round(float(n_mean.mean()), 1),
         "density": round(float(n_mean.mean()) / wl.F, 4),
         "kernel_us": {names[k]: round(v, 3) for k, v in mean_us.items()},
         "kernel_timing": timing,
         "prompt": prompt,
+        # every algorithmic byte the dominant kernel reads or writes per launch (for a folded layer its P2 rows
+        # too, for the fused kernel its partial sums of y), over that kernel's own launch time
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "traffic_detail": traffic_detail},
         "wall_s": round(wall, 3),
         "setup_s": round(setup_s, 1),
+    }
+    del stack, X, n_acc
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs the sparse-FFN stack on one GPU; --gpus must be 1"}),
+              flush=True)
+        sys.exit(2)
+
+    if args.copy_only is not None:
+        copy_only(args.copy_only)
+        return
+
+    import synthgen as sg
+
+    wl = sg.workload(args.workload)
+    if args.act and args.act != wl.act:
+        wl = sg.custom(wl, act=args.act, name=f"{wl.name}_{args.act}")
+    if args.rank_schedule == "adaptive":
+        wl = sg.with_rank_schedule(wl)
+    B = args.batch
+    head = measure(wl, B, args, with_prompt=True)
+    also = []
+    for name in [a for a in args.also.split(",") if a and a != "none"]:
+        other = sg.workload(name)
+        if other.name == wl.name:
+            continue
+        r = measure(other, B, args, with_prompt=False)
+        also.append({k: r[k] for k in ("value", "ms_per_step", "us_per_layer", "forward_active_gbs",
+                                       "active_weight_frac", "active_weight_gbs", "all_bytes_gbs",
+                                       "active_rows_per_layer", "kernel_us", "roofline")}
+                    | {"workload": other.name, "batch": B, "unit": "tokens/s"})
+    out = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "accumulate": "f32",
+        "data": "synthetic",
+        **{k: v for k, v in head.items() if k not in ("value", "ms_per_step", "dtype")},
+        "also": also,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, B, args.cpu_seconds)

@@ -79,6 +79,8 @@ def _forward_q4(**kw):
     (dict(t=0.0), 6), (dict(t=1.0), 6), (dict(t=float("nan")), 6),
     (dict(P1=MIS), 3), (dict(x=MIS), 3), (dict(ws=A + 16), 3),
     (dict(ws_bytes=100), 4),
+    # P2 [F, r] fp16 of 4 GiB: the kernels address it with 31-bit byte offsets, so the shape is refused
+    (dict(D=256, F=1 << 21, r=1024), 2), (dict(D=256, F=1 << 20, r=1024), 2),
 ])
 def test_predict_rejects(kw, status):
     assert _predict(**kw) == status
@@ -177,6 +179,8 @@ def _decode(**kw):
     (dict(P2=MIS), 3), (dict(y=A + 4), 3), (dict(ws=A + 16), 3), (dict(ws_bytes=1000), 4),
     # sizes outside the folded kernel take the separate calls and fail there the same way
     (dict(D=8192, ws_bytes=1000), 4), (dict(F=40000, D=64, ws_bytes=1000), 4), (dict(D=8192, n_hot=-2), 6),
+    # P2 of 4 GiB (folded and separate routes alike)
+    (dict(D=256, F=1 << 21, r=1024), 2), (dict(act=0, Wg=None, bg=None, bu=A, D=64, F=1 << 21, r=1024), 2),
 ])
 def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
@@ -208,3 +212,9 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2", "--steps", "1"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stdout
+
+
+def test_p2_just_below_the_limit_passes_validation():
+    # F * r * 2 = 2 GiB - 2 KiB: accepted; the fake workspace size is what fails
+    assert _predict(D=256, F=(1 << 20) - 1, r=1024, ws_bytes=16) == 4
+    assert _predict_hot(D=256, F=(1 << 20) - 1, r=1024, n_hot=0, ws_bytes=16) == 4

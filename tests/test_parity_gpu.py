@@ -87,6 +87,28 @@ def test_permutation_invariance(gpu_ready, perm):
     assert np.max(np.abs(ys[0] - ys[1])) <= 1e-5 * np.max(np.abs(ys[0]))
 
 
+@pytest.mark.parametrize("name,wl", [SMALL[1], SMALL[2]], ids=[SMALL[1][0], SMALL[2][0]])
+@pytest.mark.parametrize("B", [4, 16])
+@pytest.mark.parametrize("perm", ["identity", "random"])
+def test_permutation_invariance_batches(gpu_ready, name, wl, B, perm):
+    # union batches (matrix-core kernels): another stored neuron order gives the same set of original neurons and
+    # the same outputs up to summation order
+    x = _x(wl, B, 4)
+    ys, sets = [], []
+    for p in ("hot", perm):
+        case = make_case(wl, 0, gpu_ready, perm=p)
+        say(f"[{name}] B={B} perm={p}")
+        res = run_gpu(case, torch.from_numpy(x).to(gpu_ready))
+        check(case, x, res)
+        ys.append(res["y"])
+        ids = res["active"][:res["n"]]
+        sets.append(set(case.perm[ids].tolist()))
+    # each run matched the oracle outside the band (check), so the sets can differ only in band neurons; with
+    # equal sets the outputs agree up to summation order
+    if sets[0] == sets[1]:
+        assert np.max(np.abs(ys[0] - ys[1])) <= 2e-3 * np.max(np.abs(ys[0]))
+
+
 @pytest.mark.parametrize("t,expect", [(1e-30, "all"), (1.0 - 1e-7, "none")])
 def test_all_and_none_active(gpu_ready, t, expect):
     wl = SMALL[0][1]
