@@ -18,7 +18,8 @@ ACTS = {"relu": ACT_RELU, "reglu": ACT_REGLU, "sqrelu": ACT_SQRELU}
 
 EXPORTS = ("sffn_status_string", "sffn_last_error", "sffn_workspace_size", "sffn_mask_words", "sffn_predict",
            "sffn_predict_hot", "sffn_forward", "sffn_forward_q4", "sffn_profile_begin", "sffn_profile_end",
-           "sffn_forward_path", "sffn_decode", "sffn_decode_path")
+           "sffn_forward_path", "sffn_decode", "sffn_decode_path", "sffn_decode_noalloc",
+           "sffn_noalloc_scratch_bytes")
 K_PRED_H, K_PRED_Z, K_ROWS, K_COLS = 0, 1, 2, 3
 
 
@@ -59,6 +60,10 @@ def lib() -> ctypes.CDLL:
         h.sffn_decode.argtypes = [i32, vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp,
                                   vp, vp, sz, vp]
         h.sffn_decode.restype = i32
+        h.sffn_decode_noalloc.argtypes = [i32, vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp,
+                                          vp, vp, vp, vp]
+        h.sffn_decode_noalloc.restype = i32
+        h.sffn_noalloc_scratch_bytes.argtypes, h.sffn_noalloc_scratch_bytes.restype = [], sz
         h.sffn_decode_path.argtypes, h.sffn_decode_path.restype = [i32, i32, i32, i32, i32], i32
         h.sffn_profile_begin.argtypes, h.sffn_profile_begin.restype = [i32, i32], i32
         h.sffn_forward_path.argtypes, h.sffn_forward_path.restype = [i32, i32, i32, i32, i32], i32
@@ -149,6 +154,22 @@ def decode(act, P1, P2, c, t: float, W_gate, b_gate, W_up, b_up, W_downT, x, mas
                            _p(W_up), _p(b_up), _p(W_downT), _p(x), int(bool(x_norm)), D, F, r, _p(mask), _p(active),
                            _p(n_active), _p(y), _p(logits), _p(ws), _nbytes(ws), _stream(stream, x))
     _check(rc, "sffn_decode")
+
+
+def decode_noalloc(act, P1, P2, c, t: float, W_gate, b_gate, W_up, b_up, W_downT, x, mask, active, n_active, y,
+                   x_norm: bool = False, n_hot: int = 0, logits=None, stream=None):
+    """sffn_decode_noalloc: sffn_decode with the library's own per-GPU device scratch as its workspace (no
+    allocation; calls that overlap in time on one GPU race on the scratch)."""
+    B, D = x.shape
+    F, r = P2.shape
+    rc = lib().sffn_decode_noalloc(ACTS.get(act, act), _p(P1), _p(P2), _p(c), float(t), int(n_hot), _p(W_gate),
+                                   _p(b_gate), _p(W_up), _p(b_up), _p(W_downT), _p(x), int(bool(x_norm)), D, F, r,
+                                   _p(mask), _p(active), _p(n_active), _p(y), _p(logits), _stream(stream, x))
+    _check(rc, "sffn_decode_noalloc")
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().sffn_noalloc_scratch_bytes())
 
 
 DECODE_SEPARATE, DECODE_FOLDED = 0, 1

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/sffn.h"
 #include "common.h"
@@ -35,6 +36,9 @@ constexpr int MAX_F_UNION = 32768;   // union kernels compact the whole mask in 
 constexpr int KS_MAX = 8;            // row splits of the union down projection
 constexpr int G_FUSED = 256;         // blocks (= partial sums of y) of the fused single-token forward
 constexpr size_t MAX_TENSOR = (size_t)1 << 31;   // buffer loads address each tensor with 31-bit byte offsets
+#ifndef SFFN_NOALLOC_SCRATCH_BYTES
+#define SFFN_NOALLOC_SCRATCH_BYTES (16u << 20)   // device scratch of sffn_decode_noalloc, per GPU
+#endif
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -335,6 +339,64 @@ int sffn_decode(int act, const void* P1, const void* P2, const float* c, float t
                            g ? nullptr : b_up, W_downT, x, x_norm, D, F, (uint32_t*)ws_abuf(ws), logits,
                            ws_part(ws, 1, D, F), G_FUSED, mask, active, n_active, y, st);
   return e == hipSuccess ? SFFN_OK : hip_fail(e, "decode launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device scratch of sffn_decode_noalloc: one array per GPU, allocated with the code object when the library is
+// loaded on that device and kept until the process ends. In host code `scratch` names a host-side stand-in, not
+// device memory: kernels and copies only ever get the per-device address from hipGetSymbolAddress.
+constexpr size_t NOALLOC_BYTES = (size_t)SFFN_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[NOALLOC_BYTES];
+
+struct ScratchAddr {
+  std::once_flag once[SFFN_MAX_DEVICES];
+  void* ptr[SFFN_MAX_DEVICES] = {};
+  hipError_t err[SFFN_MAX_DEVICES] = {};
+};
+ScratchAddr g_scratch;
+
+// The current device's address of `scratch`, looked up once per device (with that device current).
+hipError_t scratch_addr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SFFN_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::call_once(g_scratch.once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch.err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch.ptr[dev] = g_scratch.err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch.err[dev] != hipSuccess) return g_scratch.err[dev];
+  if (!g_scratch.ptr[dev] || !al(g_scratch.ptr[dev], 256)) return hipErrorInvalidSymbol;
+  *out = g_scratch.ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sffn_noalloc_scratch_bytes(void) { return NOALLOC_BYTES; }
+
+int sffn_decode_noalloc(int act, const void* P1, const void* P2, const float* c, float t, int n_hot,
+                        const void* W_gate, const float* b_gate, const void* W_up, const float* b_up,
+                        const void* W_downT, const float* x, int x_norm, int D, int F, int r, uint64_t* mask,
+                        int32_t* active, int32_t* n_active, float* y, float* logits, void* stream) {
+  g_err[0] = 0;
+  if (D < 1 || F < 1 || r < 1) return fail(SFFN_ERR_SHAPE, "decode_noalloc: D=%d, F=%d, r=%d", D, F, r);
+  const size_t need = sffn_workspace_size(1, D, F, r);
+  if (need > NOALLOC_BYTES)
+    return fail(SFFN_ERR_WORKSPACE,
+                "decode_noalloc: D=%d, F=%d, r=%d need %zu bytes of scratch, beyond its fixed %zu; use sffn_decode "
+                "with a workspace", D, F, r, need, NOALLOC_BYTES);
+  void* ws = nullptr;
+  const hipError_t e = scratch_addr(&ws);
+  if (e != hipSuccess) return hip_fail(e, "decode_noalloc: scratch address");
+  return sffn_decode(act, P1, P2, c, t, n_hot, W_gate, b_gate, W_up, b_up, W_downT, x, x_norm, D, F, r, mask, active,
+                     n_active, y, logits, ws, NOALLOC_BYTES, stream);
 }
 
 int sffn_forward(int act, const void* W_gate, const float* b_gate, const void* W_up, const float* b_up,

@@ -186,6 +186,21 @@ int sffn_decode(int act, const void* P1, const void* P2, const float* c, float t
                 int x_norm, int D, int F, int r, uint64_t* mask, int32_t* active, int32_t* n_active, float* y,
                 float* logits, void* ws, size_t ws_bytes, void* stream);
 
+/* sffn_decode without a workspace argument, for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same operands, outputs and results as
+ * sffn_decode. Its workspace is a scratch array of sffn_noalloc_scratch_bytes() bytes (16 MiB) in the library's
+ * own device memory: one per GPU, allocated when the library is loaded on that GPU and held until the process
+ * ends. The call allocates nothing. Sizes whose workspace (sffn_workspace_size(1, D, F, r)) exceeds the scratch
+ * return SFFN_ERR_WORKSPACE before anything is enqueued (D = 8192, F = 32768, r = 1024 need 8.1 MiB). Every call
+ * on one GPU shares that GPU's scratch, which keeps the last call's contents (no call needs them): calls that
+ * overlap in time on one GPU (several streams or host threads) race on it and must be serialised by the caller.
+ * The first call on a device looks up the scratch's address there (SFFN_ERR_HIP if that fails). */
+size_t sffn_noalloc_scratch_bytes(void);
+int sffn_decode_noalloc(int act, const void* P1, const void* P2, const float* c, float t, int n_hot,
+                        const void* W_gate, const float* b_gate, const void* W_up, const float* b_up,
+                        const void* W_downT, const float* x, int x_norm, int D, int F, int r, uint64_t* mask,
+                        int32_t* active, int32_t* n_active, float* y, float* logits, void* stream);
+
 /* Per-launch timing of one kernel (profiling aid; not needed for computing).
  * kernel: SFFN_K_PRED_H (P1 x), SFFN_K_PRED_Z (P2 h + c, threshold, mask), SFFN_K_ROWS (compaction + W_gate /
  * W_up row gather + activation), SFFN_K_COLS (W_downT column gather; in the union path the row-split down

@@ -218,3 +218,14 @@ def test_p2_just_below_the_limit_passes_validation():
     # F * r * 2 = 2 GiB - 2 KiB: accepted; the fake workspace size is what fails
     assert _predict(D=256, F=(1 << 20) - 1, r=1024, ws_bytes=16) == 4
     assert _predict_hot(D=256, F=(1 << 20) - 1, r=1024, n_hot=0, ws_bytes=16) == 4
+
+
+def test_decode_noalloc_validates_sizes_first():
+    h = _lib.lib()
+    assert h.sffn_noalloc_scratch_bytes() == 16 << 20
+    args = dict(act=0, P1=A, P2=A, c=None, t=0.5, n_hot=0, Wg=None, bg=None, Wu=A, bu=A, WdT=A, x=A, x_norm=0,
+                D=16384, F=1 << 20, r=8, mask=A, active=A, n_active=A, y=A, logits=None, stream=None)
+    assert h.sffn_decode_noalloc(*args.values()) == 4                        # scratch too small for these sizes
+    assert "scratch" in h.sffn_last_error().decode()
+    args.update(D=0)
+    assert h.sffn_decode_noalloc(*args.values()) == 2
