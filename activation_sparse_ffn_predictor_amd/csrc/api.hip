@@ -35,6 +35,10 @@ constexpr int MAX_BD_VALU = SFFN_MAX_BD_VALU;   // decode-batch kernels (B in {2
 constexpr int MAX_F_UNION = 32768;   // union kernels compact the whole mask in one block
 constexpr int KS_MAX = 8;            // row splits of the union down projection
 constexpr int G_FUSED = 256;         // blocks (= partial sums of y) of the fused single-token forward
+#ifndef SFFN_UNION_EXACT
+#define SFFN_UNION_EXACT 1
+#endif
+constexpr bool UNION_EXACT = SFFN_UNION_EXACT != 0;   // union row kernel: tokens as fp16 hi + lo, scales on fp32
 constexpr size_t MAX_TENSOR = (size_t)1 << 31;   // buffer loads address each tensor with 31-bit byte offsets
 #ifndef SFFN_NOALLOC_SCRATCH_BYTES
 #define SFFN_NOALLOC_SCRATCH_BYTES (16u << 20)   // device scratch of sffn_decode_noalloc, per GPU
@@ -93,11 +97,17 @@ size_t ws_xn_bytes(int B, int D) { return B > 1 ? align256((size_t)B * D * sizeo
 size_t ws_part_bytes(int B, int D) {
   return align256((size_t)(B > 1 ? KS_MAX * B : G_FUSED) * D * sizeof(float));
 }
-// B > 1: partial pre-activations of the k-split union row kernel, [KSP_MAX][2][F][B] fp32
-constexpr int KSP_MAX = 2;
-size_t ws_pre_bytes(int B, int F) { return B > 1 ? align256((size_t)KSP_MAX * 2 * F * B * sizeof(float)) : 0; }
+// B > 1: partial pre-activations of the union row kernel's k shares, [KS][2][F][B] fp32 (KS > 1 up to 32 tokens)
+size_t ws_pre_bytes(int B, int F) {
+  const int ks = sffn_ur_shares(B);
+  return B > 1 && ks > 1 ? align256((size_t)ks * 2 * F * B * sizeof(float)) : 0;
+}
+// B > 1: the union row kernel's token fragments (two fp16 planes) and the tokens' powers of two (16 per tile)
+size_t ws_xf_bytes(int B, int D) {
+  return B > 1 ? align256(sffn_ur_xf_bytes(B, D, true)) + align256((size_t)((B + 15) / 16) * 16 * sizeof(float)) : 0;
+}
 size_t ws_forward_bytes(int B, int D, int F) {
-  return ws_a_bytes(B, F) + ws_xn_bytes(B, D) + ws_part_bytes(B, D) + ws_pre_bytes(B, F);
+  return ws_a_bytes(B, F) + ws_xn_bytes(B, D) + ws_part_bytes(B, D) + ws_pre_bytes(B, F) + ws_xf_bytes(B, D);
 }
 
 int check_ws(const void* ws, size_t ws_bytes, size_t need) {
@@ -120,6 +130,10 @@ float* ws_part(void* ws, int B, int D, int F) { return (float*)((char*)ws + ws_a
 float* ws_hbuf(void* ws, int B, int D, int F) { return (float*)((char*)ws + ws_forward_bytes(B, D, F)); }
 float* ws_pre(void* ws, int B, int D, int F) {
   return (float*)((char*)ws + ws_a_bytes(B, F) + ws_xn_bytes(B, D) + ws_part_bytes(B, D));
+}
+void* ws_xf(void* ws, int B, int D, int F) { return (char*)ws_pre(ws, B, D, F) + ws_pre_bytes(B, F); }
+float* ws_xs(void* ws, int B, int D, int F) {
+  return (float*)((char*)ws_xf(ws, B, D, F) + align256(sffn_ur_xf_bytes(B, D, true)));
 }
 
 struct Prof {
@@ -155,14 +169,9 @@ namespace {
 hipError_t run_union(int act, bool q4, const void* Wg, const void* Sg, const float* bg, const void* Wu, const void* Su,
                      const float* bu, const void* Wd, const void* Sd, const float* x, int x_norm, int B, int D, int F,
                      const uint64_t* mask, int32_t* active, int32_t* n_active, float* y, void* ws, hipStream_t st) {
-  const float* xin = x;
-  if (x_norm) {
-    hipError_t e = sffn_launch_norm_tokens(x, B, D, ws_xn(ws, B, F), st);
-    if (e != hipSuccess) return e;
-    xin = ws_xn(ws, B, F);
-  }
-  hipError_t e = sffn_launch_rows_mt(act, q4, Wg, Sg, bg, Wu, Su, bu, xin, B, D, F, mask, active, n_active,
-                                     ws_abuf(ws), ws_pre(ws, B, D, F), union_ksp(B), st);
+  hipError_t e = sffn_launch_rows_ur(act, q4, UNION_EXACT, Wg, Sg, bg, Wu, Su, bu, x, x_norm, B, D, F, mask, active,
+                                     n_active, ws_abuf(ws), ws_xf(ws, B, D, F), ws_xs(ws, B, D, F),
+                                     ws_pre(ws, B, D, F), st);
   if (e != hipSuccess) return e;
   return sffn_launch_down_mt(q4, Wd, Sd, active, n_active, ws_abuf(ws), B, D, F, ws_part(ws, B, D, F),
                              union_splits(D), y, st);

@@ -430,6 +430,16 @@ hipError_t sffn_launch_rows_mt(int act, bool q4, const void* Wg, const void* Sg,
                                const void* Su, const float* bu, const float* x, int B, int D, int F,
                                const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf, float* pre,
                                int KSP, hipStream_t st);
+// union row gather tiled over 64 rows with every token tile (union_rows.hip): token fragments from x (normalised
+// when x_norm) into xf (sffn_ur_xf_bytes) and the tokens' powers of two into xs, then the row kernel
+size_t sffn_ur_xf_bytes(int B, int D, bool exact);
+int sffn_ur_shares(int B);   // k shares per 64 union rows (> 1: partial pre-activations in `pre`, then combined)
+hipError_t sffn_launch_rows_ur(int act, bool q4, bool exact, const void* Wg, const void* Sg, const float* bg,
+                               const void* Wu, const void* Su, const float* bu, const float* x, int x_norm, int B,
+                               int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf,
+                               void* xf, float* xs, float* pre, hipStream_t st);
+hipError_t sffn_launch_act_combine(int act, const float* pre, int KSP, const int32_t* active, const int32_t* n_active,
+                                   const float* bias, int B, int F, float* abuf, hipStream_t st);
 hipError_t sffn_launch_down_mt(bool q4, const void* Wd, const void* Sd, const int32_t* active,
                                const int32_t* n_active, const float* abuf, int B, int D, int F, float* part, int KS,
                                float* y, hipStream_t st);

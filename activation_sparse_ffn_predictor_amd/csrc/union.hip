@@ -746,6 +746,16 @@ hipError_t down_mt(const void* Wd, const void* Sd, const int32_t* active, const 
 
 }  // namespace
 
+// Activations from KSP shares of partial pre-activations (row kernels with a k split); see k_act_combine.
+hipError_t sffn_launch_act_combine(int act, const float* pre, int KSP, const int32_t* active, const int32_t* n_active,
+                                   const float* bias, int B, int F, float* abuf, hipStream_t st) {
+  const dim3 grid((F * B + 255) / 256);
+  if (act == 1) hipLaunchKernelGGL(k_act_combine<1>, grid, dim3(256), 0, st, pre, KSP, active, n_active, bias, B, F, abuf);
+  else if (act == 2) hipLaunchKernelGGL(k_act_combine<2>, grid, dim3(256), 0, st, pre, KSP, active, n_active, bias, B, F, abuf);
+  else hipLaunchKernelGGL(k_act_combine<0>, grid, dim3(256), 0, st, pre, KSP, active, n_active, bias, B, F, abuf);
+  return hipGetLastError();
+}
+
 // ---- entry points used by the C ABI for B > 1
 hipError_t sffn_launch_norm_tokens(const float* x, int B, int D, float* xn, hipStream_t st) {
   const int xpt = (D / 4 + NTN - 1) / NTN;

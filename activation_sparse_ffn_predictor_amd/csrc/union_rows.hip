@@ -1,0 +1,410 @@
+// Multi-token row gather on the matrix cores, tiled so that the token operand is read once per 64 union rows.
+//
+// PowerInfer pages, Turkish article, "Neuron-aware operator": only the rows of W_gate / W_up of predicted-active
+// neurons are read; with several tokens the masks are merged and each union row is read once for all of them.
+// Per layer this is a GEMM of the union rows [n x D] with the tokens [D x B] (n up to F, B <= 64), on
+// v_mfma_f32_16x16x32_f16 (A: 16 rows x 32 k, lane l: row l % 16, 8 k values of lane group j = l / 16; B: 32 k x 16
+// tokens, lane l: token l % 16, the same 8 k values; D: lane l holds rows 4 (l / 16) + i of token l % 16).
+//
+// k order. A dot product may take its k terms in any order, so the MFMA k slots are assigned to suit the loads:
+// k blocks of 32 go in quads; in MFMA q (0..3) of quad g, lane group j takes elements 8 q .. 8 q + 7 of k block
+// 4 g + j. A lane therefore holds one whole k block of its row per quad: one 16-byte load of Q4_0 nibbles (or four
+// of fp16), and the four lanes of a row read 64 (256) contiguous bytes of it. The token fragments are written in
+// the same order.
+//
+// k_split_x (one workgroup per token slot): normalises the token (optional, as every entry point's x_norm),
+// scales it by a power of two 2^-e with 2^e the smallest power above max |x| (exact, and it keeps every value
+// inside fp16's range), and writes the B-operand fragments, fragment f = (quad, q, token tile) as 64 lanes x 16
+// bytes, so a wave reads one as a contiguous kilobyte. EXACT adds a plane of fp16 residuals (x = hi + lo, the
+// single-token kernels' fp32 to within 2^-22); without it the operand is fp16(x).
+//
+// k_ur (workgroups of 4 waves, 64 dense indices each, one 16-row tile per wave, every token tile; KS workgroups
+// per 64 rows split the quads): the workgroup's union rows come from the mask (block scan of the words' popcounts,
+// then a search per row). Quads are walked in chunks; per chunk each thread loads a share of the chunk's token
+// fragments (into registers, then LDS, double-buffered: all four waves read them) and its row's k blocks of
+// weights (Q4_0 nibbles and block scales, or fp16); loads run two chunks ahead of the matrix-core work in a ring
+// of three register sets. The chunk count is padded to a multiple of three (the padding reads nothing:
+// out-of-range buffer loads return 0). Q4_0 weights become exact fp16 (q - 8) through the exponent trick (0x64qq
+// is 1024 + q in fp16), times the block scale in fp16 (one rounding per weight; the whole block's scale is one
+// lane's, so no per-block fp32 step is needed). fp16 weights enter as they are; with EXACT each token operand is
+// two fp16 halves and every product is exact. The epilogue undoes the token's power of two and, with one
+// share, adds the bias and applies the activation; with KS shares each writes its partial pre-activations and
+// k_act_combine (union.hip) adds them in share order.
+#include "common.h"
+
+using namespace sffn;
+
+#define GT_BIAS(A, bg, bu) ((A) == 1 ? (bg) : (bu))
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const half8& a, const half8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Q4_0: elements 8 q .. 8 q + 7 of a 32-element block as exact fp16 (q - 8). w = the block's 16 nibble bytes (byte
+// i: element i low, element 16 + i high): q = 0, 1 take the low nibbles of bytes 8 q .., q = 2, 3 the high nibbles
+// of bytes 8 (q - 2) ... Each byte goes under the fp16 exponent pattern 0x64 (0x64nn = 1024 + n exactly), then
+// 1032 is subtracted.
+__device__ __forceinline__ half8 q4_half8(const uint4& w, int q) {
+  const uint32_t px = (q & 1) ? w.z : w.x, py = (q & 1) ? w.w : w.y;
+  const uint32_t sh = (uint32_t)(q >> 1) * 4u;
+  const uint32_t w0 = (px >> sh) & 0x0F0F0F0Fu, w1 = (py >> sh) & 0x0F0F0F0Fu;
+  const uint32_t e = 0x64646464u;
+  // v_perm_b32 byte pool: selector 0..3 = second source's bytes, 4..7 = first source's bytes
+  const uint32_t h0 = __builtin_amdgcn_perm(w0, e, 0x00050004u), h1 = __builtin_amdgcn_perm(w0, e, 0x00070006u);
+  const uint32_t h2 = __builtin_amdgcn_perm(w1, e, 0x00050004u), h3 = __builtin_amdgcn_perm(w1, e, 0x00070006u);
+  const half2v off = {(_Float16)1032.f, (_Float16)1032.f};
+  const half2v a0 = __builtin_bit_cast(half2v, h0) - off, a1 = __builtin_bit_cast(half2v, h1) - off;
+  const half2v a2 = __builtin_bit_cast(half2v, h2) - off, a3 = __builtin_bit_cast(half2v, h3) - off;
+  half8 r;
+  r[0] = a0[0]; r[1] = a0[1]; r[2] = a1[0]; r[3] = a1[1];
+  r[4] = a2[0]; r[5] = a2[1]; r[6] = a3[0]; r[7] = a3[1];
+  return r;
+}
+
+constexpr int NTX = 256;
+
+// One workgroup per token slot tok < NTT * 16 (slots >= B are zero). xf: [KB][NTT][NH][64] uint4, NH = 2 with EXACT
+// (hi, lo). xs[tok] = 2^e, the power of two the fragments are divided by.
+template <int XPT, bool EXACT>
+__global__ __launch_bounds__(NTX) void k_split_x(const float* __restrict__ x, int x_norm, int B, int D, int NTT,
+                                                 uint4* __restrict__ xf, float* __restrict__ xs) {
+  constexpr int NH = EXACT ? 2 : 1;
+  __shared__ float red[2 * (NTX / 64) + 4];
+  const int tok = blockIdx.x;
+  const bool real = tok < B;
+  const int n4 = real ? D >> 2 : 0;                    // padding slots load nothing (all zero)
+  const float* xb = x + (size_t)(real ? tok : 0) * D;
+  float4 v[XPT];
+  stage_load<NTX, XPT>(xb, n4, v);
+  if (real && x_norm) block_norm_regs<NTX, XPT>(v, n4, xb[0], red);
+  float m = 0.f;
+#pragma unroll
+  for (int k = 0; k < XPT; ++k)
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[k].x), fabsf(v[k].y)), fmaxf(fabsf(v[k].z), fabsf(v[k].w))));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, WAVE));
+  __syncthreads();                                     // red may still be read by block_norm_regs' last step
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < NTX / 64; ++i) mx = fmaxf(mx, red[i]);
+  int ex = 0;
+  if (mx > 0.f) (void)frexpf(mx, &ex);                 // mx = f 2^ex, f in [0.5, 1): |x| 2^-ex < 1
+  const float inv = ldexpf(1.f, -ex);
+  if (threadIdx.x == 0) xs[tok] = ldexpf(1.f, ex);
+  const int t = tok >> 4, tl = tok & 15;
+  // element e: k block kb = e / 32 (quad kb / 4, lane group kb % 4), fragment q = (e % 32) / 8; float4 i holds
+  // elements 4 i .. 4 i + 3, half i % 2 of an 8-element group
+  auto slot = [&](int kb, int q, int h) {
+    return (((size_t)((kb >> 2) * 4 + q) * NTT + t) * NH + h) * 64 + (size_t)((kb & 3) * 16 + tl);
+  };
+#pragma unroll
+  for (int k = 0; k < XPT; ++k) {
+    const int i = k * NTX + (int)threadIdx.x;
+    if (i < (D >> 2)) {
+      const int kb = i >> 3, q = (i >> 1) & 3, hf = i & 1;
+      const float a[4] = {v[k].x * inv, v[k].y * inv, v[k].z * inv, v[k].w * inv};
+      _Float16 hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (_Float16)a[e];
+        lo[e] = (_Float16)(a[e] - (float)hi[e]);
+      }
+      uint2* dh = reinterpret_cast<uint2*>(xf + slot(kb, q, 0)) + hf;
+      *dh = make_uint2(__builtin_bit_cast(uint32_t, half2v{hi[0], hi[1]}),
+                       __builtin_bit_cast(uint32_t, half2v{hi[2], hi[3]}));
+      if (EXACT) {
+        uint2* dl = reinterpret_cast<uint2*>(xf + slot(kb, q, 1)) + hf;
+        *dl = make_uint2(__builtin_bit_cast(uint32_t, half2v{lo[0], lo[1]}),
+                         __builtin_bit_cast(uint32_t, half2v{lo[2], lo[3]}));
+      }
+    }
+  }
+  // 8-element groups at or past D, up to the end of the last quad, are zero
+  const int KQ = (D + 127) >> 7;                       // quads
+  for (int gi = (D >> 3) + (int)threadIdx.x; gi < KQ * 16; gi += NTX) {
+    xf[slot(gi >> 2, gi & 3, 0)] = make_uint4(0u, 0u, 0u, 0u);
+    if (EXACT) xf[slot(gi >> 2, gi & 3, 1)] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+constexpr int NTR = 256;             // 4 waves
+constexpr int RTB = 64;              // union rows per workgroup (a 16-row tile per wave)
+constexpr int WMAXR = 2;             // mask words per thread kept in LDS (F <= 32768)
+
+// k blocks per chunk: 8 for Q4_0 (two quads: 32 bytes of a row per lane and matrix), 4 for fp16 (a quad: 64 bytes)
+template <bool Q4> struct URChunk { static constexpr int KC = Q4 ? 8 : 4; };
+
+template <int NTT, int ACT, bool Q4, bool EXACT>
+__global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
+                                            const float* __restrict__ bg, const void* __restrict__ Wu,
+                                            const void* __restrict__ Su, const float* __restrict__ bu,
+                                            const uint4* __restrict__ xf, const float* __restrict__ xsc, int B,
+                                            int D, int F, const uint64_t* __restrict__ mask,
+                                            int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                                            float* __restrict__ abuf, float* __restrict__ pre, int KS) {
+  static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
+  constexpr bool GT = ACT == 1;                        // ReGLU: a gate row per neuron
+  constexpr int NH = EXACT ? 2 : 1;                    // token fragment planes (hi, lo)
+  constexpr int KC = URChunk<Q4>::KC;
+  constexpr int QC = KC / 4;                           // quads per chunk
+  constexpr int XV = KC * NTT * NH * 64 / NTR;         // uint4 of token fragments per thread per chunk
+  static_assert(XV * NTR == KC * NTT * NH * 64, "fragment share");
+  constexpr int WV = Q4 ? QC : 4 * QC;                 // uint4 of weights per lane and matrix per chunk
+  __shared__ uint64_t wl[WMAXR * NTR];                 // mask words
+  __shared__ int roff[NTR];
+  __shared__ int tmp[NTR / 64 + 4];
+  __shared__ int ids[RTB];
+  __shared__ uint4 xl[2][KC * NTT * NH * 64];          // token fragments of two chunks
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nw = (F + 63) >> 6;
+  const int wpt = (nw + NTR - 1) / NTR;
+  const int n = mask_prefix<NTR, WMAXR>(mask, nw, F, wpt, wl, roff, tmp);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
+  const int ks = blockIdx.x % KS;                      // the shares of 64 rows are neighbours in dispatch order
+  const int i0 = (blockIdx.x / KS) * RTB;
+  if (i0 >= n) return;                                 // block-uniform
+  if (threadIdx.x < RTB) {
+    const int i = i0 + threadIdx.x;
+    int id = -1;
+    if (i < n) {                                       // the (i - roff)-th set bit after word range T * wpt
+      int lo = 0, hi = NTR - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (roff[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      int rem = i - roff[lo];
+      for (int tw = lo * wpt; tw < nw; ++tw) {
+        const int cnt = __popcll(wl[tw]);
+        if (rem < cnt) { id = tw * 64 + select_bit(wl[tw], rem); break; }
+        rem -= cnt;
+      }
+      if (ks == 0) active[i] = id;
+    }
+    ids[threadIdx.x] = id;
+  }
+  __syncthreads();
+  const int idl = ids[w * 16 + (lane & 15)];           // this lane's A-operand row (-1: none)
+  const int jq = lane >> 4;                            // lane group: the k block of a quad this lane holds
+  const int KB = (D + 31) >> 5, nblk = D >> 5;
+  const int KQ = (KB + 3) >> 2;                        // quads
+  const int KQS = (KQ + KS - 1) / KS;                  // quads of one share
+  const int q0 = ks * KQS, q1 = min(KQ, q0 + KQS);     // this share's quads
+  const int nch = ((max(q1 - q0, 0) + QC - 1) / QC + 2) / 3 * 3;   // chunks, padded to rounds of three
+  const Buf bx(xf, (uint32_t)q1 * 4u * NTT * NH * 1024u);           // quads past the share read 0
+  const uint32_t wbytes = Q4 ? (uint32_t)F * (uint32_t)(D >> 1) : (uint32_t)F * (uint32_t)D * 2u;
+  const uint32_t sbytes = Q4 ? (uint32_t)F * (uint32_t)nblk * 2u : 0u;
+  const Buf bwu(Wu, wbytes), bwg(GT ? Wg : Wu, GT ? wbytes : 0u);
+  const Buf bsu(Q4 ? Su : Wu, sbytes), bsg(Q4 && GT ? Sg : Wu, GT ? sbytes : 0u);
+  const uint32_t row = (uint32_t)(idl >= 0 ? idl : 0);
+
+  struct Set {
+    uint4 xv[XV];
+    uint4 wu[WV], wg[WV];
+    _Float16 su[Q4 ? QC : 1], sg[Q4 ? QC : 1];
+  };
+  auto load = [&](int c, Set& S) {
+    const int g0 = q0 + c * QC;                        // first quad of the chunk
+#pragma unroll
+    for (int m = 0; m < XV; ++m)
+      S.xv[m] = bx.ld16(((uint32_t)g0 * 4u * NTT * NH * 64 + (uint32_t)(m * NTR) + threadIdx.x) * 16u);
+#pragma unroll
+    for (int gq = 0; gq < QC; ++gq) {
+      const int kb = (g0 + gq) * 4 + jq;               // this lane's k block of the quad
+      const bool ok = g0 + gq < q1 && kb < KB && idl >= 0;
+      if constexpr (Q4) {
+        const uint32_t o = row * (uint32_t)(D >> 1) + (uint32_t)kb * 16u;
+        S.wu[gq] = bwu.ld16(boff(ok, o));
+        if (GT) S.wg[gq] = bwg.ld16(boff(ok, o));
+        const uint32_t so = (row * nblk + kb) * 2u;
+        S.su[gq] = bsu.ldh16(boff(ok, so));
+        if (GT) S.sg[gq] = bsg.ldh16(boff(ok, so));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {                  // elements 8 q .. 8 q + 7 of the lane's k block
+          const int k = kb * 32 + q * 8;
+          const uint32_t o = (row * (uint32_t)D + (uint32_t)k) * 2u;
+          S.wu[gq * 4 + q] = bwu.ld16(boff(ok && k < D, o));
+          if (GT) S.wg[gq * 4 + q] = bwg.ld16(boff(ok && k < D, o));
+        }
+      }
+    }
+  };
+  auto store_x = [&](const Set& S, int buf) {
+#pragma unroll
+    for (int m = 0; m < XV; ++m) xl[buf][m * NTR + threadIdx.x] = S.xv[m];
+  };
+  f32x4 au[NTT], ag[NTT];
+#pragma unroll
+  for (int t = 0; t < NTT; ++t) { au[t] = f32x4{0.f, 0.f, 0.f, 0.f}; ag[t] = au[t]; }
+  auto compute = [&](const Set& S, int buf) {
+#pragma unroll
+    for (int gq = 0; gq < QC; ++gq) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        half8 a_u, a_g;
+        if constexpr (Q4) {                            // fp16((q - 8) s): one rounding per weight
+          const half8 su8 = {S.su[gq], S.su[gq], S.su[gq], S.su[gq], S.su[gq], S.su[gq], S.su[gq], S.su[gq]};
+          a_u = q4_half8(S.wu[gq], q) * su8;
+          if (GT) {
+            const half8 sg8 = {S.sg[gq], S.sg[gq], S.sg[gq], S.sg[gq], S.sg[gq], S.sg[gq], S.sg[gq], S.sg[gq]};
+            a_g = q4_half8(S.wg[gq], q) * sg8;
+          }
+        } else {
+          a_u = __builtin_bit_cast(half8, S.wu[gq * 4 + q]);
+          if (GT) a_g = __builtin_bit_cast(half8, S.wg[gq * 4 + q]);
+        }
+#pragma unroll
+        for (int t = 0; t < NTT; ++t) {
+          const int f = ((gq * 4 + q) * NTT + t) * NH;
+          const half8 xh = __builtin_bit_cast(half8, xl[buf][f * 64 + lane]);
+          if constexpr (EXACT) {
+            const half8 xo = __builtin_bit_cast(half8, xl[buf][(f + 1) * 64 + lane]);
+            au[t] = mfma16(a_u, xo, mfma16(a_u, xh, au[t]));
+            if (GT) ag[t] = mfma16(a_g, xo, mfma16(a_g, xh, ag[t]));
+          } else {
+            au[t] = mfma16(a_u, xh, au[t]);
+            if (GT) ag[t] = mfma16(a_g, xh, ag[t]);
+          }
+        }
+      }
+    }
+  };
+  // three register sets in turn: step c loads chunk c + 2, computes chunk c (its tokens in LDS buffer c % 2) and
+  // stages chunk c + 1's tokens into the other buffer
+  Set S0, S1, S2;
+  load(0, S0);
+  load(1, S1);
+  store_x(S0, 0);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 3) {                   // nch is a multiple of 3
+    load(c + 2, S2);
+    compute(S0, c & 1);
+    store_x(S1, (c + 1) & 1);
+    __syncthreads();
+    load(c + 3, S0);
+    compute(S1, (c + 1) & 1);
+    store_x(S2, c & 1);
+    __syncthreads();
+    load(c + 4, S1);
+    compute(S2, c & 1);
+    store_x(S0, (c + 1) & 1);
+    __syncthreads();
+  }
+  // epilogue: the token's power of two back; one share: bias and activation, else the partial pre-activations
+  int idr[4];                                          // the rows of this lane's 4 outputs (D layout)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) idr[i] = ids[w * 16 + (lane >> 4) * 4 + i];
+  const float* bp = GT ? bg : bu;
+  float bias[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bias[i] = (bp && idr[i] >= 0) ? bp[idr[i]] : 0.f;
+  const size_t FB = (size_t)F * B;
+#pragma unroll
+  for (int t = 0; t < NTT; ++t) {
+    const int tok = t * 16 + (lane & 15);
+    if (tok >= B) continue;
+    const float sx = xsc[tok];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ii = i0 + w * 16 + (lane >> 4) * 4 + i;
+      if (ii >= n) continue;
+      const float u = au[t][i] * sx, g = ag[t][i] * sx;
+      const size_t e = (size_t)ii * B + tok;
+      if (KS > 1) {
+        pre[(size_t)(2 * ks) * FB + e] = u;
+        if (GT) pre[(size_t)(2 * ks + 1) * FB + e] = g;
+        continue;
+      }
+      float a;
+      if (GT) {
+        a = fmaxf(g + bias[i], 0.f) * u;
+      } else {
+        a = fmaxf(u + bias[i], 0.f);
+        if (ACT == 2) a *= a;
+      }
+      abuf[e] = a;
+    }
+  }
+}
+
+template <int XPT, bool EXACT>
+hipError_t launch_split_x(const float* x, int x_norm, int B, int D, int NTT, uint4* xf, float* xs, hipStream_t st) {
+  hipLaunchKernelGGL((k_split_x<XPT, EXACT>), dim3(NTT * 16), dim3(NTX), 0, st, x, x_norm, B, D, NTT, xf, xs);
+  return hipGetLastError();
+}
+
+template <int NTT, int ACT, bool Q4, bool EXACT>
+hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void* Wu, const void* Su, const float* bu,
+                     const float* x, int x_norm, int B, int D, int F, const uint64_t* mask, int32_t* active,
+                     int32_t* n_active, float* abuf, uint4* xf, float* xs, float* pre, int KS, hipStream_t st) {
+  const int xpt = (D / 4 + NTX - 1) / NTX;
+  hipError_t e;
+  static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
+  if (xpt <= 1) e = launch_split_x<1, EXACT>(x, x_norm, B, D, NTT, xf, xs, st);
+  else if (xpt <= 2) e = launch_split_x<2, EXACT>(x, x_norm, B, D, NTT, xf, xs, st);
+  else if (xpt <= 4) e = launch_split_x<4, EXACT>(x, x_norm, B, D, NTT, xf, xs, st);
+  else if (xpt <= 8) e = launch_split_x<8, EXACT>(x, x_norm, B, D, NTT, xf, xs, st);
+  else if (xpt <= 16) e = launch_split_x<16, EXACT>(x, x_norm, B, D, NTT, xf, xs, st);
+  else return hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
+  if ((F + 63) / 64 > WMAXR * NTR || KS < 1 || (KS > 1 && !pre)) return hipErrorInvalidValue;
+  SFFN_LAUNCH(2, (k_ur<NTT, ACT, Q4, EXACT>), dim3((F + RTB - 1) / RTB * KS), dim3(NTR), 0, st, Wg, Sg, bg, Wu, Su, bu,
+              (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, pre, KS);
+  e = hipGetLastError();
+  if (e != hipSuccess || KS == 1) return e;
+  return sffn_launch_act_combine(ACT, pre, KS, active, n_active, GT_BIAS(ACT, bg, bu), B, F, abuf, st);
+}
+
+// Q4_0 rows always take fp16 tokens (the weights are rounded to fp16 with their scale); fp16 rows take them as
+// two halves when EXACT
+template <int NTT, bool EXACT>
+hipError_t ur_act(int act, bool q4, const void* Wg, const void* Sg, const float* bg, const void* Wu, const void* Su,
+                  const float* bu, const float* x, int x_norm, int B, int D, int F, const uint64_t* mask,
+                  int32_t* active, int32_t* n_active, float* abuf, uint4* xf, float* xs, float* pre, int KS,
+                  hipStream_t st) {
+#define UR(A, Q, E) return launch_ur<NTT, A, Q, E>(Wg, Sg, bg, Wu, Su, bu, x, x_norm, B, D, F, mask, active, \
+                                                   n_active, abuf, xf, xs, pre, KS, st)
+  if (act == 1) { if (q4) UR(1, true, false); UR(1, false, EXACT); }
+  if (act == 2) { if (q4) UR(2, true, false); UR(2, false, EXACT); }
+  if (q4) UR(0, true, false);
+  UR(0, false, EXACT);
+#undef UR
+}
+
+}  // namespace
+
+// Bytes of the token fragments k_split_x writes for B tokens of D values (EXACT: two planes): whole quads of k blocks.
+size_t sffn_ur_xf_bytes(int B, int D, bool exact) {
+  return (size_t)((D + 127) / 128) * 4 * ((B + 15) / 16) * (exact ? 2 : 1) * 1024;
+}
+
+// Shares of the k range per 64 union rows: few tokens mean few union rows, so more shares keep the CUs busy.
+int sffn_ur_shares(int B) { return B <= 8 ? 8 : (B <= 16 ? 4 : (B <= 32 ? 2 : 1)); }
+
+hipError_t sffn_launch_rows_ur(int act, bool q4, bool exact, const void* Wg, const void* Sg, const float* bg,
+                               const void* Wu, const void* Su, const float* bu, const float* x, int x_norm, int B,
+                               int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf,
+                               void* xf, float* xs, float* pre, hipStream_t st) {
+  const int ntt = (B + 15) / 16;
+  const int KS = sffn_ur_shares(B);
+#define URN(N) return exact ? ur_act<N, true>(act, q4, Wg, Sg, bg, Wu, Su, bu, x, x_norm, B, D, F, mask, active,   \
+                                              n_active, abuf, (uint4*)xf, xs, pre, KS, st)                      \
+                            : ur_act<N, false>(act, q4, Wg, Sg, bg, Wu, Su, bu, x, x_norm, B, D, F, mask, active,  \
+                                               n_active, abuf, (uint4*)xf, xs, pre, KS, st)
+  switch (ntt) {
+    case 1: URN(1);
+    case 2: URN(2);
+    case 3: URN(3);
+    case 4: URN(4);
+    default: return hipErrorInvalidValue;
+  }
+#undef URN
+}
