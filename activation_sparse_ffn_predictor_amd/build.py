@@ -8,8 +8,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsffn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "predict.hip", "forward.hip", "forward_q4.hip", "union.hip", "union_rows.hip", "fused.hip",
-           "decode.hip"]
+SOURCES = ["api.hip", "predict.hip", "forward.hip", "forward_q4.hip", "union.hip", "union_rows.hip", "union_down.hip",
+           "fused.hip", "decode.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic (scalar fp32 only).
 HIPFLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

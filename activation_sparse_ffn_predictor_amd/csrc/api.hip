@@ -33,7 +33,8 @@ constexpr int MAX_B = 64, MAX_D = 16384, MAX_F = 1 << 22, MAX_R = 1024, MAX_BR =
 #endif
 constexpr int MAX_BD_VALU = SFFN_MAX_BD_VALU;   // decode-batch kernels (B in {2, 4, 8}): B * D <= this
 constexpr int MAX_F_UNION = 32768;   // union kernels compact the whole mask in one block
-constexpr int KS_MAX = 8;            // row splits of the union down projection
+constexpr int KS_MAX = 8;            // k shares of the multi-token predictor's first stage
+constexpr int UD_KS_MAX = 16;        // row shares of the union down projection
 constexpr int G_FUSED = 256;         // blocks (= partial sums of y) of the fused single-token forward
 #ifndef SFFN_UNION_EXACT
 #define SFFN_UNION_EXACT 1
@@ -74,28 +75,21 @@ bool decode_batch(int B, int D, int F) {
   return B == 2 || ((B == 4 || B == 8) && F > MAX_F_UNION);
 }
 
-// k shares of the union row kernel: 5..16 tokens split k in two (twice the blocks, each half as long, spread
-// more evenly over the CUs when the row tiles number a little over one per CU); a small kernel then forms the
-// activations. Measured at the 13B shape: 8 tokens 2738 -> 2847 tokens/s; 4 tokens 1964 -> 1862, so up to 4
-// tokens keep one share.
-int union_ksp(int B) { return B > 4 && B <= 16 ? 2 : 1; }
-
-// Row splits of the union down projection: enough blocks of 128 columns x KS splits to cover the chip twice.
-int union_splits(int D) {
-  const int cb = (D + 127) / 128;
-  return std::min(KS_MAX, std::max(1, (512 + cb - 1) / cb));
-}
-
 // Workspace layout, each part 256-byte aligned:
-//   [activations a: F * B fp32; for B == 1 at least the decision bitmaps of the folded single-token layer]
+//   [activations a: F * B fp32, for B > 1 at least the union kernels' 64-row tiles of 16-token tiles
+//    (ceil(F / 64) 64 x ceil(B / 16) 16 fp32); for B == 1 at least the decision bitmaps of the folded single-token
+//    layer]
 //   [B > 1: normalised x: B * D fp32]
-//   [partial y: KS_MAX * B * D fp32 for B > 1, G_FUSED * D fp32 for B == 1][predictor h: B * r fp32]
+//   [partial y: UD_KS_MAX * B * D fp32 for B > 1, G_FUSED * D fp32 for B == 1][predictor h: B * r fp32]
 size_t ws_a_bytes(int B, int F) {
-  return align256(std::max((size_t)F * B * sizeof(float), B == 1 ? sffn_decode_dec_bytes(G_FUSED) : (size_t)0));
+  const size_t tiles = B > 1 ? (size_t)((F + 63) / 64) * 64 * ((B + 15) / 16) * 16 * sizeof(float) : 0;
+  return align256(std::max({(size_t)F * B * sizeof(float), tiles,
+                            B == 1 ? sffn_decode_dec_bytes(G_FUSED) : (size_t)0}));
 }
 size_t ws_xn_bytes(int B, int D) { return B > 1 ? align256((size_t)B * D * sizeof(float)) : 0; }
 size_t ws_part_bytes(int B, int D) {
-  return align256((size_t)(B > 1 ? KS_MAX * B : G_FUSED) * D * sizeof(float));
+  static_assert(UD_KS_MAX >= KS_MAX, "the partials region serves both");
+  return align256((size_t)(B > 1 ? UD_KS_MAX * B : G_FUSED) * D * sizeof(float));
 }
 // B > 1: partial pre-activations of the union row kernel's k shares, [KS][2][F][B] fp32 (KS > 1 up to 32 tokens)
 size_t ws_pre_bytes(int B, int F) {
@@ -106,8 +100,11 @@ size_t ws_pre_bytes(int B, int F) {
 size_t ws_xf_bytes(int B, int D) {
   return B > 1 ? align256(sffn_ur_xf_bytes(B, D, true)) + align256((size_t)((B + 15) / 16) * 16 * sizeof(float)) : 0;
 }
+// B > 1: the row kernels' largest |activation| per 64 union rows and token, [ceil(F / 64)][B] fp32
+size_t ws_bmax_bytes(int B, int F) { return B > 1 ? align256((size_t)((F + 63) / 64) * B * sizeof(float)) : 0; }
 size_t ws_forward_bytes(int B, int D, int F) {
-  return ws_a_bytes(B, F) + ws_xn_bytes(B, D) + ws_part_bytes(B, D) + ws_pre_bytes(B, F) + ws_xf_bytes(B, D);
+  return ws_a_bytes(B, F) + ws_xn_bytes(B, D) + ws_part_bytes(B, D) + ws_pre_bytes(B, F) + ws_xf_bytes(B, D) +
+         ws_bmax_bytes(B, F);
 }
 
 int check_ws(const void* ws, size_t ws_bytes, size_t need) {
@@ -135,6 +132,7 @@ void* ws_xf(void* ws, int B, int D, int F) { return (char*)ws_pre(ws, B, D, F) +
 float* ws_xs(void* ws, int B, int D, int F) {
   return (float*)((char*)ws_xf(ws, B, D, F) + align256(sffn_ur_xf_bytes(B, D, true)));
 }
+float* ws_bmax(void* ws, int B, int D, int F) { return (float*)((char*)ws_xf(ws, B, D, F) + ws_xf_bytes(B, D)); }
 
 struct Prof {
   int kernel = -1;
@@ -170,11 +168,11 @@ hipError_t run_union(int act, bool q4, const void* Wg, const void* Sg, const flo
                      const float* bu, const void* Wd, const void* Sd, const float* x, int x_norm, int B, int D, int F,
                      const uint64_t* mask, int32_t* active, int32_t* n_active, float* y, void* ws, hipStream_t st) {
   hipError_t e = sffn_launch_rows_ur(act, q4, UNION_EXACT, Wg, Sg, bg, Wu, Su, bu, x, x_norm, B, D, F, mask, active,
-                                     n_active, ws_abuf(ws), ws_xf(ws, B, D, F), ws_xs(ws, B, D, F),
-                                     ws_pre(ws, B, D, F), st);
+                                     n_active, ws_abuf(ws), ws_bmax(ws, B, D, F), ws_xf(ws, B, D, F),
+                                     ws_xs(ws, B, D, F), ws_pre(ws, B, D, F), st);
   if (e != hipSuccess) return e;
-  return sffn_launch_down_mt(q4, Wd, Sd, active, n_active, ws_abuf(ws), B, D, F, ws_part(ws, B, D, F),
-                             union_splits(D), y, st);
+  return sffn_launch_down_ud(q4, UNION_EXACT, Wd, Sd, active, n_active, ws_abuf(ws), ws_bmax(ws, B, D, F), B, D, F,
+                             ws_part(ws, B, D, F), sffn_ud_shares(D, UD_KS_MAX), y, st);
 }
 
 }  // namespace

@@ -89,6 +89,9 @@ struct Buf {
   __device__ __forceinline__ _Float16 ldh16(uint32_t off) const {  // one fp16 value
     return __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
   }
+  __device__ __forceinline__ uint32_t ldu16(uint32_t off) const {  // one 16-bit value, zero-extended
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+  }
   __device__ __forceinline__ float ldh(uint32_t off) const {  // one fp16 value, widened
     const unsigned short b = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
     return (float)__builtin_bit_cast(_Float16, b);
@@ -426,10 +429,6 @@ hipError_t sffn_launch_norm_tokens(const float* x, int B, int D, float* xn, hipS
 hipError_t sffn_launch_predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F,
                                   int r, float tau, int n_hot, uint64_t* mask, float* logits, float* hbuf,
                                   float* hpart, int KSH, hipStream_t st);
-hipError_t sffn_launch_rows_mt(int act, bool q4, const void* Wg, const void* Sg, const float* bg, const void* Wu,
-                               const void* Su, const float* bu, const float* x, int B, int D, int F,
-                               const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf, float* pre,
-                               int KSP, hipStream_t st);
 // union row gather tiled over 64 rows with every token tile (union_rows.hip): token fragments from x (normalised
 // when x_norm) into xf (sffn_ur_xf_bytes) and the tokens' powers of two into xs, then the row kernel
 size_t sffn_ur_xf_bytes(int B, int D, bool exact);
@@ -437,9 +436,15 @@ int sffn_ur_shares(int B);   // k shares per 64 union rows (> 1: partial pre-act
 hipError_t sffn_launch_rows_ur(int act, bool q4, bool exact, const void* Wg, const void* Sg, const float* bg,
                                const void* Wu, const void* Su, const float* bu, const float* x, int x_norm, int B,
                                int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf,
-                               void* xf, float* xs, float* pre, hipStream_t st);
+                               float* bmax, void* xf, float* xs, float* pre, hipStream_t st);
+// activations (octet order, 64-row tiles written whole) from the k shares' partial pre-activations, and the
+// largest |a| per 64 rows and token into bmax
 hipError_t sffn_launch_act_combine(int act, const float* pre, int KSP, const int32_t* active, const int32_t* n_active,
-                                   const float* bias, int B, int F, float* abuf, hipStream_t st);
-hipError_t sffn_launch_down_mt(bool q4, const void* Wd, const void* Sd, const int32_t* active,
-                               const int32_t* n_active, const float* abuf, int B, int D, int F, float* part, int KS,
-                               float* y, hipStream_t st);
+                                   const float* bias, int B, int F, float* abuf, float* bmax, hipStream_t st);
+hipError_t sffn_launch_sum_parts(const float* part, int KS, int n, float* y, hipStream_t st);
+// union down projection on the matrix cores (union_down.hip): KS shares of the union rows, each with its tokens'
+// power-of-two scale from bmax, partial sums into part [KS][B][D], then y = their sum
+int sffn_ud_shares(int D, int ks_max);
+hipError_t sffn_launch_down_ud(bool q4, bool exact, const void* Wd, const void* Sd, const int32_t* active,
+                               const int32_t* n_active, const float* abuf, const float* bmax, int B, int D, int F,
+                               float* part, int KS, float* y, hipStream_t st);

@@ -1,0 +1,344 @@
+// Multi-token down projection on the matrix cores: y[b, :] = sum over union rows i of a[i, b] W_downT[active[i], :].
+//
+// PowerInfer pages, Turkish article, "Neuron-aware operator": only the columns of W_down (rows of W_downT) of the
+// union neurons are read, each once for all tokens. As a GEMM, M = tokens, N = D columns, K = union rows, on
+// v_mfma_f32_16x16x32_f16 (A: 16 tokens x 32 rows, lane l: token l % 16, rows 8 (l / 16) .. + 8; B: 32 rows x 16
+// columns, lane l: column l % 16, the same rows; D: lane l holds tokens 4 (l / 16) + i of column l % 16).
+//
+// Activations arrive from the row kernels in octet order: a[i, b] at float ((i / 8) * BP + b) * 8 + i % 8, BP the
+// token count rounded up to 16, rows past the union and tokens past B zero. An A-operand lane (8 consecutive rows of
+// one token) is then 32 contiguous bytes, and a step's 64 rows x BP tokens one contiguous block.
+// The weights are stored neuron-major (a neuron's row runs along D) while a B-operand lane needs 8 neurons at one
+// column, so every tile is transposed once on its way through LDS.
+// k_ud (workgroups of 4 waves, 256 columns x every token tile, KS workgroups over the union rows, split by the
+// device-side union size): the workgroup stages the ids of its share of union rows in LDS, then walks them in steps
+// of 64. Per step each thread loads a 4-neuron x 16-column piece of W_downT (Q4_0: 8 nibble bytes and the block
+// scale per neuron; fp16: two 16-byte loads per neuron) and NTT 16-byte pieces of the activations, and writes them,
+// converted to fp16, as operand fragments into LDS (8 bytes per column and 4 neurons; 8 bytes per token and 4 rows).
+// Loads run three steps ahead of the matrix-core work in four register sets, with no branch in the loop: rows past
+// the union and steps past the share read neuron 0's weights against zero activations. The fragment
+// buffers are double-buffered with one barrier per step. Each wave multiplies its 64 columns by every token tile.
+// Activations enter multiplied by a per-token power of two 2^(15 - e), with 2^e above their largest magnitude over
+// the workgroup's share of rows (from the per-64-row maxima the row kernels write), so every value lies inside
+// fp16's range with its full precision; the partial sums are scaled back before they are written. Q4_0 weights
+// enter as fp16((q - 8) s) (one rounding) with fp16 activations; fp16 weights enter exactly, with the activations as
+// one fp16 operand or, EXACT, as two halves (hi + lo). k_sum_parts (union.hip) adds the KS partials in fixed order.
+#include "common.h"
+
+using namespace sffn;
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const half8& a, const half8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+constexpr int NTD = 256;             // 4 waves
+constexpr int CTD = 256;             // columns per workgroup: 16 column tiles, 4 per wave
+constexpr int KSTD = 64;             // union rows per step: 2 MFMA k chunks
+constexpr int UD_PAD = 7;            // steps of ids past a share: the ring reads up to 6 steps beyond its last
+
+// 8 nibbles (one byte each, low or high half of the block's bytes) as exact fp16 (q - 8)
+__device__ __forceinline__ void nib8_half(uint32_t px, uint32_t py, uint32_t sh, half2v (&o)[4]) {
+  const uint32_t w0 = (px >> sh) & 0x0F0F0F0Fu, w1 = (py >> sh) & 0x0F0F0F0Fu;
+  const uint32_t e = 0x64646464u;   // v_perm_b32: selector 0..3 = second source's bytes, 4..7 = first source's
+  const half2v off = {(_Float16)1032.f, (_Float16)1032.f};
+  o[0] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(w0, e, 0x00050004u)) - off;
+  o[1] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(w0, e, 0x00070006u)) - off;
+  o[2] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(w1, e, 0x00050004u)) - off;
+  o[3] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(w1, e, 0x00070006u)) - off;
+}
+
+template <int NTT, bool Q4, bool EXACT>
+__global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const void* __restrict__ Sd,
+                                            const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
+                                            const float* __restrict__ abuf, const float* __restrict__ bmax, int B,
+                                            int D, int F, int M, float* __restrict__ part) {
+  // M: the most 64-row steps one share can hold (sizes the ids in LDS, with UD_PAD steps of padding)
+  static_assert(!(Q4 && EXACT), "Q4_0 weights take fp16 activations");
+  constexpr int NHA = EXACT ? 2 : 1;                   // activation planes (hi, lo)
+  constexpr int BP = NTT * 16;                         // token stride of the activations
+  extern __shared__ __align__(16) int ids[];           // [(M + UD_PAD) * KSTD] ids of this share's union rows
+  __shared__ uint4 Bl[2][2][16][64];                   // weight fragments [buffer][k chunk][column tile][slot]
+  __shared__ uint4 Al[2][2][NTT][NHA][64];             // activation fragments [buffer][k chunk][token tile][plane]
+  __shared__ float smx[4][64];
+  __shared__ float inv_s[64];                          // per token: 2^(15 - e), max |a| < 2^e over this share
+  __shared__ float scl[64];                            // and its inverse 2^(e - 15)
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int KS = gridDim.y, ks = blockIdx.y;
+  const int c0 = blockIdx.x * CTD;
+  const int nblk = D >> 5;
+  // the union rows in KS shares of whole 64-row blocks
+  const int n = min(max((int)Buf(n_active, 4u).ldu(0u), 0), F);
+  const int Mn = min(((n + 63) / 64 + KS - 1) / KS, M);
+  const int total = Mn * KSTD;
+  const int ibase = ks * total;                        // dense index of this workgroup's first row
+  // the row-block maxima of this share and the ids (0 past the union and past the share) in one round trip
+  {
+    const Buf bm(bmax, (uint32_t)((F + 63) >> 6) * (uint32_t)B * 4u);
+    const Buf bid(active, (uint32_t)n * 4u);
+    const int tok = threadIdx.x & 63, sub = threadIdx.x >> 6;
+    float m = 0.f;
+    for (int b0 = 0; b0 < Mn; b0 += 32) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int b = b0 + sub + 4 * k;
+        v[k] = bm.ldf(boff(b < Mn && tok < B, ((uint32_t)(ks * Mn + b) * (uint32_t)B + (uint32_t)tok) * 4u));
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int b = b0 + sub + 4 * k;
+        if (ibase + 64 * b < n) m = fmaxf(m, v[k]);    // row blocks past n hold stale maxima
+      }
+    }
+    smx[sub][tok] = m;
+    const int tot_p = total + UD_PAD * KSTD;
+    for (int e0 = 0; e0 < tot_p; e0 += 8 * NTD) {
+      int v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = e0 + (int)threadIdx.x + NTD * k;
+        v[k] = (int)bid.ldu(boff(e < total, (uint32_t)(ibase + e) * 4u));   // 0 past the share
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = e0 + (int)threadIdx.x + NTD * k;
+        if (e < tot_p) ids[e] = v[k];
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int t = threadIdx.x;
+    const float mx = fmaxf(fmaxf(smx[0][t], smx[1][t]), fmaxf(smx[2][t], smx[3][t]));
+    int ex = 0;
+    if (mx > 0.f) (void)frexpf(mx, &ex);
+    const int p = min(15 - ex, 126);
+    inv_s[t] = ldexpf(1.f, p);
+    scl[t] = ldexpf(1.f, -p);
+  }
+  __syncthreads();
+  const int nst = (max(0, min(total, n - ibase)) + KSTD - 1) / KSTD;   // steps with rows
+  const int nst4 = (nst + 3) / 4 * 4;                  // padded to rounds of four
+
+  // weight roles: neuron quad nq = t / 16 (neurons 4 nq .. + 3 of the step), column unit cu = t % 16: 32-column
+  // block wb = cu / 2, offset wo = 8 (cu % 2): columns 32 wb + wo + (0..7) and 32 wb + 16 + wo + (0..7), which Q4_0
+  // holds in the low and high nibbles of the same 8 bytes
+  const int nq = threadIdx.x >> 4, cu = threadIdx.x & 15;
+  const int wb = cu >> 1, wo = (cu & 1) * 8;
+  const int kcw = nq >> 3, lgw = (nq >> 1) & 3, hfw = nq & 1;   // fragment k chunk, lane group, 8-byte half
+  const uint32_t nbytes = Q4 ? (uint32_t)F * (uint32_t)(D >> 1) : (uint32_t)F * (uint32_t)D * 2u;
+  const Buf bw(Wd, nbytes);
+  const Buf bs(Q4 ? Sd : Wd, Q4 ? (uint32_t)F * (uint32_t)nblk * 2u : 0u);
+  const int jb = (c0 >> 5) + wb;                       // the weights' 32-column block
+  const int cl = c0 + 32 * wb + wo;
+  // per-thread column part of every weight offset; OOB (>= 2^31, above any tensor) for columns past D
+  const uint32_t rowb = Q4 ? (uint32_t)(D >> 1) : (uint32_t)D * 2u;
+  const uint32_t cb0 = Q4 ? (jb < nblk ? (uint32_t)jb * 16u + (uint32_t)wo : OOB) : (cl < D ? (uint32_t)cl * 2u : OOB);
+  const uint32_t cb1 = Q4 ? 0u : (cl + 16 < D ? (uint32_t)(cl + 16) * 2u : OOB);
+  const uint32_t cbs = jb < nblk ? (uint32_t)jb * 2u : OOB;
+  // activation roles: piece j (of NTT) is 16 bytes g = 256 j + t of the step's block: octet g / (2 BP), token
+  // (g / 2) % BP, half g % 2 (rows 4 (g % 2) .. + 3 of the octet)
+  const int nr = min(((n + 63) >> 6) << 6, ((F + 63) >> 6) << 6);
+  const Buf ba(abuf, (uint32_t)nr * (uint32_t)BP * 4u);   // rows past the union's last 64-row block read 0
+  uint32_t aoff[NTT];
+  float asc[NTT];
+  int aslot[NTT];                                      // Al slot offset in uint2 units within [buffer][plane 0]
+#pragma unroll
+  for (int j = 0; j < NTT; ++j) {
+    const int g = 256 * j + (int)threadIdx.x;
+    const int oc = g / (2 * BP), tk = (g >> 1) % BP, h = g & 1;
+    aoff[j] = ((uint32_t)((ibase >> 3) + oc) * (uint32_t)BP + (uint32_t)tk) * 32u + (uint32_t)h * 16u;
+    asc[j] = inv_s[tk];
+    const int kc = oc >> 2, lg = oc & 3;
+    aslot[j] = ((((kc * NTT + (tk >> 4)) * NHA) * 64) + (tk & 15) + 16 * lg) * 2 + h;
+  }
+  const uint32_t astep = (uint32_t)KSTD * (uint32_t)BP * 4u;   // bytes of one step's activations
+
+  struct Set {
+    uint2 q[Q4 ? 4 : 1];                               // Q4_0: 8 nibble bytes per neuron
+    uint32_t s[Q4 ? 4 : 1];                            // Q4_0: the block scale's fp16 bits
+    uint4 h[Q4 ? 1 : 4][2];                            // fp16: 8 + 8 columns per neuron
+    float4 a[NTT];
+  };
+  auto load = [&](int st, Set& S) {
+    const int4 id4 = *reinterpret_cast<const int4*>(&ids[st * KSTD + 4 * nq]);
+    const uint32_t id[4] = {(uint32_t)id4.x, (uint32_t)id4.y, (uint32_t)id4.z, (uint32_t)id4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (Q4) {
+        S.q[e] = bw.ld8(id[e] * rowb + cb0);
+        S.s[e] = bs.ldu16(id[e] * (uint32_t)nblk * 2u + cbs);
+      } else {
+        S.h[e][0] = bw.ld16(id[e] * rowb + cb0);
+        S.h[e][1] = bw.ld16(id[e] * rowb + cb1);
+      }
+    }
+    const uint32_t ast = st < nst ? (uint32_t)st * astep : OOB;   // steps past the share's rows read zeros
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) S.a[j] = ba.ldf4(aoff[j] + ast);
+  };
+  // fragment slots: a column tile's 64 slots hold (lane group g, column c) at 16 g + (c ^ (tile / 2 % 8)), so
+  // the staging writes of a half-wave (16 columns x 2 halves) fall in distinct banks; a 16-lane read stays a
+  // permutation of one 256-byte row
+  auto stage = [&](const Set& S, int buf) {
+    half2v lo[4][4], hi[4][4];                         // [neuron][column pair]: columns wo.., 16 + wo..
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (Q4) {
+        nib8_half(S.q[e].x, S.q[e].y, 0u, lo[e]);
+        nib8_half(S.q[e].x, S.q[e].y, 4u, hi[e]);
+        const half2v s2 = __builtin_bit_cast(half2v, S.s[e] * 0x10001u);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) { lo[e][p] = lo[e][p] * s2; hi[e][p] = hi[e][p] * s2; }
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          lo[e][p] = __builtin_bit_cast(half2v, (&S.h[e][0].x)[p]);
+          hi[e][p] = __builtin_bit_cast(half2v, (&S.h[e][1].x)[p]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int ln = 16 * lgw + ((wo + c) ^ wb);
+      const half4 vlo = {lo[0][c >> 1][c & 1], lo[1][c >> 1][c & 1], lo[2][c >> 1][c & 1], lo[3][c >> 1][c & 1]};
+      const half4 vhi = {hi[0][c >> 1][c & 1], hi[1][c >> 1][c & 1], hi[2][c >> 1][c & 1], hi[3][c >> 1][c & 1]};
+      reinterpret_cast<uint2*>(&Bl[buf][kcw][2 * wb][ln])[hfw] = __builtin_bit_cast(uint2, vlo);
+      reinterpret_cast<uint2*>(&Bl[buf][kcw][2 * wb + 1][ln])[hfw] = __builtin_bit_cast(uint2, vhi);
+    }
+    uint2* al = reinterpret_cast<uint2*>(&Al[buf][0][0][0][0]);
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) {
+      const float v[4] = {S.a[j].x * asc[j], S.a[j].y * asc[j], S.a[j].z * asc[j], S.a[j].w * asc[j]};
+      half4 vh, vl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vh[e] = (_Float16)v[e];
+        vl[e] = (_Float16)(v[e] - (float)vh[e]);
+      }
+      al[aslot[j]] = __builtin_bit_cast(uint2, vh);
+      if (EXACT) al[aslot[j] + 128] = __builtin_bit_cast(uint2, vl);   // the lo plane: 64 slots further
+    }
+  };
+  f32x4 acc[NTT][4];
+#pragma unroll
+  for (int t = 0; t < NTT; ++t)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      half8 bop[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int tile = 4 * w + c;
+        bop[c] = __builtin_bit_cast(half8, Bl[buf][kc][tile][(lane & 48) | ((lane & 15) ^ ((tile >> 1) & 7))]);
+      }
+#pragma unroll
+      for (int t = 0; t < NTT; ++t) {
+        const half8 ah = __builtin_bit_cast(half8, Al[buf][kc][t][0][lane]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[t][c] = mfma16(ah, bop[c], acc[t][c]);
+        if constexpr (EXACT) {
+          const half8 al = __builtin_bit_cast(half8, Al[buf][kc][t][NHA - 1][lane]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[t][c] = mfma16(al, bop[c], acc[t][c]);
+        }
+      }
+    }
+  };
+  // four register sets: a phase loads step s + 3, computes step s (fragments in buffer s % 2) and stages step s + 1
+  Set S0, S1, S2, S3;
+  load(0, S0);
+  load(1, S1);
+  load(2, S2);
+  stage(S0, 0);
+  __syncthreads();
+  for (int s = 0; s < nst4; s += 4) {
+    load(s + 3, S3);
+    compute(0);
+    stage(S1, 1);
+    __syncthreads();
+    load(s + 4, S0);
+    compute(1);
+    stage(S2, 0);
+    __syncthreads();
+    load(s + 5, S1);
+    compute(0);
+    stage(S3, 1);
+    __syncthreads();
+    load(s + 6, S2);
+    compute(1);
+    stage(S0, 0);
+    __syncthreads();
+  }
+  // partial sums with the tokens' powers of two undone: lane l holds tokens 4 (l / 16) + i of column l % 16 of
+  // column tile 4 w + c
+#pragma unroll
+  for (int t = 0; t < NTT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = t * 16 + (lane >> 4) * 4 + i;
+      if (tok >= B) continue;
+      const float sc = scl[tok];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int col = c0 + 64 * w + 16 * c + (lane & 15);
+        if (col < D) part[((size_t)ks * B + tok) * D + col] = acc[t][c][i] * sc;
+      }
+    }
+}
+
+template <int NTT, bool Q4, bool EXACT>
+hipError_t launch_ud(const void* Wd, const void* Sd, const int32_t* active, const int32_t* n_active,
+                     const float* abuf, const float* bmax, int B, int D, int F, float* part, int KS, float* y,
+                     hipStream_t st) {
+  const int M = (F + KSTD * KS - 1) / (KSTD * KS);     // steps per workgroup at most
+  const size_t lds = (size_t)(M + UD_PAD) * KSTD * sizeof(int);
+  static LdsLimit lds_limit;   // per kernel, set once per device
+  size_t avail = 0;
+  hipError_t ea = lds_limit.get((const void*)k_ud<NTT, Q4, EXACT>, &avail);
+  if (ea != hipSuccess) return ea;
+  if (lds > avail) return hipErrorInvalidValue;
+  SFFN_LAUNCH(3, (k_ud<NTT, Q4, EXACT>), dim3((D + CTD - 1) / CTD, KS), dim3(NTD), lds, st, Wd, Sd, active, n_active,
+              abuf, bmax, B, D, F, M, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return sffn_launch_sum_parts(part, KS, B * D, y, st);
+}
+
+template <int NTT>
+hipError_t ud_q(bool q4, bool exact, const void* Wd, const void* Sd, const int32_t* active, const int32_t* n_active,
+                const float* abuf, const float* bmax, int B, int D, int F, float* part, int KS, float* y,
+                hipStream_t st) {
+  if (q4) return launch_ud<NTT, true, false>(Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
+  if (exact) return launch_ud<NTT, false, true>(Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
+  return launch_ud<NTT, false, false>(Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
+}
+
+}  // namespace
+
+// Shares of the union rows for the down projection: enough workgroups of 256 columns to cover the CUs once.
+int sffn_ud_shares(int D, int ks_max) {
+  const int ct = (D + CTD - 1) / CTD;
+  return std::max(1, std::min(ks_max, (256 + ct - 1) / ct));
+}
+
+hipError_t sffn_launch_down_ud(bool q4, bool exact, const void* Wd, const void* Sd, const int32_t* active,
+                               const int32_t* n_active, const float* abuf, const float* bmax, int B, int D, int F,
+                               float* part, int KS, float* y, hipStream_t st) {
+  switch ((B + 15) / 16) {
+    case 1: return ud_q<1>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
+    case 2: return ud_q<2>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
+    case 3: return ud_q<3>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
+    case 4: return ud_q<4>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
+    default: return hipErrorInvalidValue;
+  }
+}

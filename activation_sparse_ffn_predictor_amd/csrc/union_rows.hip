@@ -67,6 +67,12 @@ __device__ __forceinline__ half8 q4_half8(const uint4& w, int q) {
   return r;
 }
 
+// eight copies of the fp16 value whose bits are the low half of s
+__device__ __forceinline__ half8 splat8(uint32_t s) {
+  const uint32_t d = s * 0x10001u;
+  return __builtin_bit_cast(half8, make_uint4(d, d, d, d));
+}
+
 constexpr int NTX = 256;
 
 // One workgroup per token slot tok < NTT * 16 (slots >= B are zero). xf: [KB][NTT][NH][64] uint4, NH = 2 with EXACT
@@ -149,7 +155,8 @@ __global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const v
                                             const uint4* __restrict__ xf, const float* __restrict__ xsc, int B,
                                             int D, int F, const uint64_t* __restrict__ mask,
                                             int32_t* __restrict__ active, int32_t* __restrict__ n_active,
-                                            float* __restrict__ abuf, float* __restrict__ pre, int KS) {
+                                            float* __restrict__ abuf, float* __restrict__ bmax,
+                                            float* __restrict__ pre, int KS) {
   static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
   constexpr bool GT = ACT == 1;                        // ReGLU: a gate row per neuron
   constexpr int NH = EXACT ? 2 : 1;                    // token fragment planes (hi, lo)
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const v
   struct Set {
     uint4 xv[XV];
     uint4 wu[WV], wg[WV];
-    _Float16 su[Q4 ? QC : 1], sg[Q4 ? QC : 1];
+    uint32_t su[Q4 ? QC : 1], sg[Q4 ? QC : 1];         // block scales' fp16 bits (32-bit: kept in registers)
   };
   auto load = [&](int c, Set& S) {
     const int g0 = q0 + c * QC;                        // first quad of the chunk
@@ -224,8 +231,8 @@ __global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const v
         S.wu[gq] = bwu.ld16(boff(ok, o));
         if (GT) S.wg[gq] = bwg.ld16(boff(ok, o));
         const uint32_t so = (row * nblk + kb) * 2u;
-        S.su[gq] = bsu.ldh16(boff(ok, so));
-        if (GT) S.sg[gq] = bsg.ldh16(boff(ok, so));
+        S.su[gq] = bsu.ldu16(boff(ok, so));
+        if (GT) S.sg[gq] = bsg.ldu16(boff(ok, so));
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {                  // elements 8 q .. 8 q + 7 of the lane's k block
@@ -251,12 +258,8 @@ __global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const v
       for (int q = 0; q < 4; ++q) {
         half8 a_u, a_g;
         if constexpr (Q4) {                            // fp16((q - 8) s): one rounding per weight
-          const half8 su8 = {S.su[gq], S.su[gq], S.su[gq], S.su[gq], S.su[gq], S.su[gq], S.su[gq], S.su[gq]};
-          a_u = q4_half8(S.wu[gq], q) * su8;
-          if (GT) {
-            const half8 sg8 = {S.sg[gq], S.sg[gq], S.sg[gq], S.sg[gq], S.sg[gq], S.sg[gq], S.sg[gq], S.sg[gq]};
-            a_g = q4_half8(S.wg[gq], q) * sg8;
-          }
+          a_u = q4_half8(S.wu[gq], q) * splat8(S.su[gq]);
+          if (GT) a_g = q4_half8(S.wg[gq], q) * splat8(S.sg[gq]);
         } else {
           a_u = __builtin_bit_cast(half8, S.wu[gq * 4 + q]);
           if (GT) a_g = __builtin_bit_cast(half8, S.wg[gq * 4 + q]);
@@ -307,31 +310,55 @@ __global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const v
 #pragma unroll
   for (int i = 0; i < 4; ++i) bias[i] = (bp && idr[i] >= 0) ? bp[idr[i]] : 0.f;
   const size_t FB = (size_t)F * B;
+  float amx[NTT];                                      // largest |a| of this lane's rows, per token tile
 #pragma unroll
   for (int t = 0; t < NTT; ++t) {
+    amx[t] = 0.f;
     const int tok = t * 16 + (lane & 15);
-    if (tok >= B) continue;
-    const float sx = xsc[tok];
+    const int r0 = i0 + w * 16 + (lane >> 4) * 4;      // this lane's 4 rows: half an octet
+    const float sx = tok < B ? xsc[tok] : 0.f;
+    float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ii = i0 + w * 16 + (lane >> 4) * 4 + i;
-      if (ii >= n) continue;
+      const int ii = r0 + i;
       const float u = au[t][i] * sx, g = ag[t][i] * sx;
-      const size_t e = (size_t)ii * B + tok;
+      float a = 0.f;
       if (KS > 1) {
-        pre[(size_t)(2 * ks) * FB + e] = u;
-        if (GT) pre[(size_t)(2 * ks + 1) * FB + e] = g;
+        if (tok < B && ii < n) {
+          const size_t e = (size_t)ii * B + tok;
+          pre[(size_t)(2 * ks) * FB + e] = u;
+          if (GT) pre[(size_t)(2 * ks + 1) * FB + e] = g;
+        }
         continue;
       }
-      float a;
       if (GT) {
         a = fmaxf(g + bias[i], 0.f) * u;
       } else {
         a = fmaxf(u + bias[i], 0.f);
         if (ACT == 2) a *= a;
       }
-      abuf[e] = a;
+      a4[i] = (tok < B && ii < n) ? a : 0.f;           // the 64-row tile is written whole: zeros past n and B
+      amx[t] = fmaxf(amx[t], fabsf(a4[i]));
     }
+    if (KS == 1)   // octet order: ((row / 8) * 16 NTT + token) * 8 + row % 8
+      *reinterpret_cast<float4*>(&abuf[((size_t)(r0 >> 3) * (NTT * 16) + tok) * 8 + (r0 & 7)]) =
+          make_float4(a4[0], a4[1], a4[2], a4[3]);
+  }
+  if (KS > 1) return;                                  // k_act_combine writes the maxima
+  // the workgroup's largest |a| per token: over the lane groups (rows), then over the waves
+  __syncthreads();                                     // xl is free: every wave is past its last chunk
+  float* smx = reinterpret_cast<float*>(&xl[0][0]);    // [4 waves][64 tokens]
+#pragma unroll
+  for (int t = 0; t < NTT; ++t) {
+    float m = amx[t];
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (lane < 16) smx[w * 64 + t * 16 + lane] = m;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < B) {
+    const int t = threadIdx.x;
+    bmax[(size_t)(i0 / RTB) * B + t] = fmaxf(fmaxf(smx[t], smx[64 + t]), fmaxf(smx[128 + t], smx[192 + t]));
   }
 }
 
@@ -344,7 +371,8 @@ hipError_t launch_split_x(const float* x, int x_norm, int B, int D, int NTT, uin
 template <int NTT, int ACT, bool Q4, bool EXACT>
 hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void* Wu, const void* Su, const float* bu,
                      const float* x, int x_norm, int B, int D, int F, const uint64_t* mask, int32_t* active,
-                     int32_t* n_active, float* abuf, uint4* xf, float* xs, float* pre, int KS, hipStream_t st) {
+                     int32_t* n_active, float* abuf, float* bmax, uint4* xf, float* xs, float* pre, int KS,
+                     hipStream_t st) {
   const int xpt = (D / 4 + NTX - 1) / NTX;
   hipError_t e;
   static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
@@ -357,10 +385,10 @@ hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void
   if (e != hipSuccess) return e;
   if ((F + 63) / 64 > WMAXR * NTR || KS < 1 || (KS > 1 && !pre)) return hipErrorInvalidValue;
   SFFN_LAUNCH(2, (k_ur<NTT, ACT, Q4, EXACT>), dim3((F + RTB - 1) / RTB * KS), dim3(NTR), 0, st, Wg, Sg, bg, Wu, Su, bu,
-              (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, pre, KS);
+              (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
   e = hipGetLastError();
   if (e != hipSuccess || KS == 1) return e;
-  return sffn_launch_act_combine(ACT, pre, KS, active, n_active, GT_BIAS(ACT, bg, bu), B, F, abuf, st);
+  return sffn_launch_act_combine(ACT, pre, KS, active, n_active, GT_BIAS(ACT, bg, bu), B, F, abuf, bmax, st);
 }
 
 // Q4_0 rows always take fp16 tokens (the weights are rounded to fp16 with their scale); fp16 rows take them as
@@ -368,10 +396,10 @@ hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void
 template <int NTT, bool EXACT>
 hipError_t ur_act(int act, bool q4, const void* Wg, const void* Sg, const float* bg, const void* Wu, const void* Su,
                   const float* bu, const float* x, int x_norm, int B, int D, int F, const uint64_t* mask,
-                  int32_t* active, int32_t* n_active, float* abuf, uint4* xf, float* xs, float* pre, int KS,
-                  hipStream_t st) {
+                  int32_t* active, int32_t* n_active, float* abuf, float* bmax, uint4* xf, float* xs, float* pre,
+                  int KS, hipStream_t st) {
 #define UR(A, Q, E) return launch_ur<NTT, A, Q, E>(Wg, Sg, bg, Wu, Su, bu, x, x_norm, B, D, F, mask, active, \
-                                                   n_active, abuf, xf, xs, pre, KS, st)
+                                                   n_active, abuf, bmax, xf, xs, pre, KS, st)
   if (act == 1) { if (q4) UR(1, true, false); UR(1, false, EXACT); }
   if (act == 2) { if (q4) UR(2, true, false); UR(2, false, EXACT); }
   if (q4) UR(0, true, false);
@@ -392,13 +420,13 @@ int sffn_ur_shares(int B) { return B <= 8 ? 8 : (B <= 16 ? 4 : (B <= 32 ? 2 : 1)
 hipError_t sffn_launch_rows_ur(int act, bool q4, bool exact, const void* Wg, const void* Sg, const float* bg,
                                const void* Wu, const void* Su, const float* bu, const float* x, int x_norm, int B,
                                int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf,
-                               void* xf, float* xs, float* pre, hipStream_t st) {
+                               float* bmax, void* xf, float* xs, float* pre, hipStream_t st) {
   const int ntt = (B + 15) / 16;
   const int KS = sffn_ur_shares(B);
 #define URN(N) return exact ? ur_act<N, true>(act, q4, Wg, Sg, bg, Wu, Su, bu, x, x_norm, B, D, F, mask, active,   \
-                                              n_active, abuf, (uint4*)xf, xs, pre, KS, st)                      \
+                                              n_active, abuf, bmax, (uint4*)xf, xs, pre, KS, st)                      \
                             : ur_act<N, false>(act, q4, Wg, Sg, bg, Wu, Su, bu, x, x_norm, B, D, F, mask, active,  \
-                                               n_active, abuf, (uint4*)xf, xs, pre, KS, st)
+                                               n_active, abuf, bmax, (uint4*)xf, xs, pre, KS, st)
   switch (ntt) {
     case 1: URN(1);
     case 2: URN(2);

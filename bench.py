@@ -67,7 +67,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("common.h", "rowgather.h", "api.hip", "predict.hip", "forward.hip", "forward_q4.hip", "union.hip",
-                  "union_rows.hip", "fused.hip", "decode.hip")
+                  "union_rows.hip", "union_down.hip", "fused.hip", "decode.hip")
 
 
 def kernel_source_hash() -> str:

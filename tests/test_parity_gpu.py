@@ -60,6 +60,21 @@ def test_union_normalised_input(gpu_ready, name, wl, B):
     say("   ", st)
 
 
+@pytest.mark.parametrize("name,wl", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("B", [3, 40])
+@pytest.mark.parametrize("scale", [1e-4, 1e4])
+def test_union_token_range(gpu_ready, name, wl, B, scale):
+    # tokens far from unit size without normalisation: the activations reach about scale^2 (ReGLU, squared ReLU),
+    # beyond fp16's range either way, so the union kernels' per-token powers of two must carry them
+    case = make_case(wl, 0, gpu_ready)
+    x = scale * _x(wl, B, 7)
+    say(f"[{name}] union B={B} x*{scale:g}")
+    res = run_gpu(case, torch.from_numpy(x).to(gpu_ready))
+    st = check(case, x, res)
+    say("   ", st)
+    assert np.all(np.isfinite(res["y"]))
+
+
 @pytest.mark.parametrize("B", [3, 16])
 @pytest.mark.parametrize("t,expect", [(1e-30, "all"), (1.0 - 1e-7, "none")])
 def test_union_all_and_none_active(gpu_ready, B, t, expect):
