@@ -197,9 +197,15 @@ def measure(wl, B: int, args, with_prompt: bool):
     for s in range(W + K):
         sg.inputs(wl, s, B, tag=sg.TAG_X_DECODE, out=X[s])
     n_acc = torch.zeros(L, dtype=torch.int64, device=dev)
+    # the step's token(s) are taken from X by a step counter on the device, inside the replayed graph, so a
+    # step is one graph launch with no host-side copy between steps
+    step_idx = torch.zeros(1, dtype=torch.long, device=dev)
 
     def make_run(nb, acc):
         def body():
+            if acc is not None:
+                stack.x_in[:nb].copy_(X.index_select(0, step_idx)[0])
+                step_idx.add_(1)
             stack.step(nb)
             if acc is not None:
                 acc.add_(stack.n_active)
@@ -240,19 +246,18 @@ def measure(wl, B: int, args, with_prompt: bool):
         print(f"# prompt: {prompt}", file=sys.stderr, flush=True)
 
     # ---- decode steps: W warm-up replays, then K timed replays with an event between consecutive steps
-    stack.x_in[:B].copy_(X[0])
-    run = make_run(B, n_acc)
+    run = make_run(B, n_acc)                           # (the capture's eager warm-up step consumed X[0])
+    step_idx.zero_()
     for s in range(W):
-        stack.x_in[:B].copy_(X[s])
         run()
     torch.cuda.synchronize()
     n_acc.zero_()
+    step_idx.fill_(W)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for s in range(K):
         ev[s].record()
-        stack.x_in[:B].copy_(X[W + s])
         run()
     ev[K].record()
     torch.cuda.synchronize()
