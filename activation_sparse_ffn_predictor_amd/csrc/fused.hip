@@ -14,9 +14,11 @@
 // rows of W_downT, all together and before x is normalised and staged. Each wave reduces its row dot products to
 // the activation a_i; the 8 activations go through LDS and every thread adds a_i * W_downT[id_i, its chunks] in
 // row order. The block's partial sum of y over its rows is written to part[block][D].
-// k_fused1_q4: the same for Q4_0 rows (nibbles and fp16 block scales). x sits in LDS transposed, so the lane of a
-// Q4 block reads its 32 values of x without bank conflicts; the pass's W_downT nibble rows are loaded straight
-// into LDS (buffer loads with the LDS destination) instead of registers.
+// k_fused1_q4: the same for Q4_0 rows (nibbles and fp16 block scales). x is scaled by a power of two (from its
+// largest magnitude) and staged in LDS as fp16, in pieces laid out so that the lane of a Q4 block reads its 32
+// values without bank conflicts; each pair of nibbles becomes exact fp16 (q - 8) and meets its pair of x in a
+// packed dot product (v_dot2, exact products, fp32 sum). The pass's W_downT nibble rows are loaded straight into
+// LDS (buffer loads with the LDS destination) instead of registers.
 // k_sum_rows: y[d] = sum over blocks b < min(G, n) of part[b][d] in a fixed order (16 groups of blocks per
 // column, each summed in block order, then the groups in order); all of a thread's loads are issued together.
 // Every sum has a fixed order, so the results do not depend on timing.
@@ -70,22 +72,37 @@ __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, c
                                               part, active, blk, G);
 }
 
-// sum over half a Q4 block of q_e * x_e: nib = the block's 16 nibble bytes (byte k: low nibble = element k, high
-// nibble = element 16 + k); H = 0: elements 0..15 (low nibbles), H = 1: elements 16..31; xh = those 16 values of x
-template <int H>
-__device__ __forceinline__ float q4_dot_half(const uint4& nib, const float (&xh)[16]) {
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+
+// the fp16 value whose bits are the low half of s, widened
+__device__ __forceinline__ float h16f(uint32_t s) { return (float)__builtin_bit_cast(_Float16, (uint16_t)s); }
+
+// sum over a Q4 block of (q_e - 8) x_e: nib = the block's 16 nibble bytes (byte i: element i low, 16 + i high);
+// xp[j] = x[4 j .. 4 j + 3] as two fp16 pairs. v_perm_b32 puts each nibble byte under the exponent byte 0x64 (byte
+// pool: selector 0..3 = second source, 4..7 = first source), 1032 is subtracted exactly, and v_dot2 multiplies
+// the pairs (exact products) into an fp32 sum.
+__device__ __forceinline__ float q4_dot_x16(const uint4& nib, const half2v (&xp)[8][2]) {
   const uint32_t wds[4] = {nib.x, nib.y, nib.z, nib.w};
+  const uint32_t e = 0x64646464u;
+  const half2v off = {(_Float16)1032.f, (_Float16)1032.f};
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t q = (wds[k] >> (4 * H)) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) s = fmaf((float)((q >> (8 * b)) & 0xFF), xh[4 * k + b], s);
+    const uint32_t lo = wds[k] & 0x0F0F0F0Fu, hi = (wds[k] >> 4) & 0x0F0F0F0Fu;
+    const half2v a0 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(lo, e, 0x00050004u)) - off;
+    const half2v a1 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(lo, e, 0x00070006u)) - off;
+    const half2v a2 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hi, e, 0x00050004u)) - off;
+    const half2v a3 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hi, e, 0x00070006u)) - off;
+    s = __builtin_amdgcn_fdot2(a0, xp[k][0], s, false);
+    s = __builtin_amdgcn_fdot2(a1, xp[k][1], s, false);
+    s = __builtin_amdgcn_fdot2(a2, xp[4 + k][0], s, false);
+    s = __builtin_amdgcn_fdot2(a3, xp[4 + k][1], s, false);
   }
   return s;
 }
 
-// Q4_0 form: gate/up rows as nibbles + block scales (the "- 8" folded out with per-block sums of x); thread t owns
+// Q4_0 form: gate/up rows as nibbles + block scales, dotted with x in packed fp16 (q4_dot_x16); thread t owns
 // half-block t of every W_downT row (8 nibble bytes = 16 columns, and the block scale) and carries sum(a * s) for
 // the "- 8" of its columns. NQ: Q4 blocks per lane of a row; D <= 32 * NT_F (one half-block per thread).
 template <int ACT, int NQ, int RPW>
@@ -104,12 +121,10 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
   int* tmp = roff + NT_F;                                                // [NT_F/64 + 1] scan scratch
   constexpr int NS = FW * RPW;                                           // rows (slots) per pass
   float* av = reinterpret_cast<float*>(tmp + NT_F / 64 + 4);             // [NS] activations of the pass
-  float* red = av + NS;                                                  // [2 * FW] normalisation scratch
-  float* xs = red + 2 * FW + 4;                                          // [D] x (16-byte aligned)
-  float* xsum = xs + D;                                                  // [D / 32] per-block sums of x
-  const int nch_row = (nblk + 63) >> 6;                // 1 kB pieces (64 lanes x 16 bytes) of a nibble row
-  const uint32_t rstride = (uint32_t)nch_row * 1024u;
-  int* bids = reinterpret_cast<int*>(xsum + nblk);                      // [ceil(F / G)] the block's row ids
+  float* red = av + NS;                                                  // [3 * FW] normalisation / max scratch
+  uint2* xt = reinterpret_cast<uint2*>(red + 3 * FW + 4);                // [8][D / 32] x as fp16 pieces (16-B aligned)
+  int* bids = reinterpret_cast<int*>(xt + 8 * nblk);                    // [ceil(F / G)] the block's row ids
+  const uint32_t rstride = (uint32_t)NQ * 1024u;       // 1 kB pieces (64 lanes x 16 bytes) of a nibble row
   uint8_t* sdn = reinterpret_cast<uint8_t*>(lds64) +   // [NS][rstride] the pass's W_downT nibble rows
                  ((reinterpret_cast<uintptr_t>(bids + (F + gridDim.x - 1) / gridDim.x) -
                    reinterpret_cast<uintptr_t>(lds64) + 15) & ~(uintptr_t)15);
@@ -140,31 +155,41 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   float sas = 0.f;
 
-  // x: normalised, staged in LDS and summed per Q4 block during the first pass, while its rows are in flight
-  constexpr bool EARLY_X = false;
-  // x is stored transposed, xs[e * nblk + c] = x[32 c + e]: the lane that owns Q4 block c reads its 32 values as
-  // words c, c + nblk, ..., so a wave reads 64 consecutive words per step (no LDS bank conflicts)
+  // x: normalised, scaled by a power of two and staged in LDS as fp16 while the first pass's rows are in flight.
+  // The block's largest |x| sets the power 2^(15 - e) (2^e above it), so every value lies inside fp16's range with
+  // its full precision; the dot products are scaled back by 2^(e - 15).
+  // piece j of Q4 block c (x[32 c + 4 j .. + 3], four fp16) sits at xt[j * nblk + c]: the lane that owns block c
+  // reads its 8 pieces as words c, c + nblk, ..., so a wave reads 64 consecutive 8-byte words per step (no LDS
+  // bank conflicts)
+  float xinv = 1.f;
   auto stage_x = [&]() {
     if (x_norm) block_norm_regs<NT_F, XPT>(xv4, n4, x0, red);
+    float mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < XPT; ++k)
+      if (k * NT_F + (int)threadIdx.x < n4)
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv4[k].x), fabsf(xv4[k].y)), fmaxf(fabsf(xv4[k].z), fabsf(xv4[k].w))));
+    mx = wave_max(mx);
+    if (lane == 0) red[2 * FW + w] = mx;
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < FW; ++i) mx = fmaxf(mx, red[2 * FW + i]);
+    int ex = 0;
+    if (mx > 0.f) (void)frexpf(mx, &ex);
+    const int pw = min(15 - ex, 126);
+    const float xsc = ldexpf(1.f, pw);
+    xinv = ldexpf(1.f, -pw);
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
-      const int i = k * NT_F + (int)threadIdx.x;       // float4 i: elements 4 i .. 4 i + 3 of block i / 8
+      const int i = k * NT_F + (int)threadIdx.x;       // float4 i: piece i % 8 of block i / 8
       if (i < n4) {
-        float* d = xs + (4 * i & 31) * nblk + (i >> 3);
-        d[0] = xv4[k].x; d[nblk] = xv4[k].y; d[2 * nblk] = xv4[k].z; d[3 * nblk] = xv4[k].w;
+        const half4 hv = {(_Float16)(xv4[k].x * xsc), (_Float16)(xv4[k].y * xsc), (_Float16)(xv4[k].z * xsc),
+                          (_Float16)(xv4[k].w * xsc)};
+        xt[(i & 7) * nblk + (i >> 3)] = __builtin_bit_cast(uint2, hv);
       }
     }
     lds_barrier();
-    for (int t = threadIdx.x; t < nblk; t += NT_F) {
-      float v = 0.f;
-#pragma unroll
-      for (int e = 0; e < 32; e += 4)
-        v += (xs[e * nblk + t] + xs[(e + 1) * nblk + t]) + (xs[(e + 2) * nblk + t] + xs[(e + 3) * nblk + t]);
-      xsum[t] = v;
-    }
-    lds_barrier();
   };
-  if (EARLY_X) stage_x();
   // A pass takes NS = 8 * RPW rows: slot s (dense index k0 + G * s) runs on wave s % 8 as its row s / 8, so a
   // block with up to NS rows reads them all in one round trip. The wave of a slot also issues the loads of the
   // slot's W_downT nibble row straight into LDS (no registers), in the same round trip as its gate/up rows.
@@ -174,53 +199,55 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
   const int nrow = (n - blk + G - 1) / G;
   block_row_ids(wl, roff, nw, blk, G, bids);
   lds_barrier();
-  bool first = !EARLY_X;
-  for (int k0 = 0; k0 < nrow; k0 += NS) {              // passes (block-uniform); row k0 + s in slot s
+  struct Pass {
     int idr[RPW];
     uint4 nu[RPW][NQ], ng[RPW][NQ];
-    _Float16 fu[RPW][NQ], fg[RPW][NQ];                 // (fp16 kept as loaded: two per register)
+    uint32_t fu[RPW][NQ], fg[RPW][NQ];                 // block scales' fp16 bits (32-bit: kept in registers)
     float bias[RPW];
+    uint32_t ds[NS];                                   // this thread's block scale of every W_downT row (fp16 bits)
+  };
+  auto issue = [&](int k0, Pass& P) {                  // rows past nrow read nothing (out-of-range offsets)
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const int kr = k0 + w + FW * r;
       const bool have = kr < nrow;                     // wave-uniform
-      idr[r] = have ? bids[kr] : -1;
-      const uint32_t row = (uint32_t)(have ? idr[r] : 0);
+      P.idr[r] = have ? bids[kr] : -1;
+      const uint32_t row = (uint32_t)(have ? P.idr[r] : 0);
 #pragma unroll
       for (int m = 0; m < NQ; ++m) {
         const int c = lane + 64 * m;
         const bool ok = have && c < nblk;
         const uint32_t o = row * nblk + c;
-        nu[r][m] = bqu.ld16(boff(ok, o * 16u));
-        fu[r][m] = bsu.ldh16(boff(ok, o * 2u));
+        P.nu[r][m] = bqu.ld16(boff(ok, o * 16u));
+        P.fu[r][m] = bsu.ldu16(boff(ok, o * 2u));
         if (ACT == 1) {
-          ng[r][m] = bqg.ld16(boff(ok, o * 16u));
-          fg[r][m] = bsg.ldh16(boff(ok, o * 2u));
+          P.ng[r][m] = bqg.ld16(boff(ok, o * 16u));
+          P.fg[r][m] = bsg.ldu16(boff(ok, o * 2u));
         }
       }
-      bias[r] = bbias.ldf(boff(have, row * 4u));
+      P.bias[r] = bbias.ldf(boff(have, row * 4u));
       uint8_t* dst = sdn + (uint32_t)(wv + FW * r) * rstride;
-      for (int c = 0; c < nch_row; ++c) {              // the slot's nibble row, 1 kB per load
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) {                   // the slot's nibble row, 1 kB per load
         const uint32_t o = (uint32_t)c * 1024u + (uint32_t)lane * 16u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             bqd.r, (__attribute__((address_space(3))) void*)(dst + c * 1024), 16,
             boff(have && o < (uint32_t)nblk * 16u, row * (uint32_t)nblk * 16u + o), 0, 0, 0);
       }
     }
-    _Float16 ds[NS];                                   // this thread's block scale of every W_downT row
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int idj = k0 + j < nrow ? bids[k0 + j] : -1;
       const bool ok = idj >= 0 && hok;
       const uint32_t row = (uint32_t)(idj >= 0 ? idj : 0);
-      ds[j] = bsd.ldh16(boff(ok, (row * nblk + (hb >> 1)) * 2u));
+      P.ds[j] = bsd.ldu16(boff(ok, (row * nblk + (hb >> 1)) * 2u));
     }
-    if (first) {
-      stage_x();
-      first = false;
-    }
-    // dot products of the wave's rows: Q4 block m of the lane outer (its 32 values of x read once from LDS for all
-    // of the wave's rows), rows inner
+  };
+  auto compute = [&](int k0, const Pass& P) {
+    // dot products of the wave's rows: Q4 block m of the lane outer (its 8 pieces of x read once from LDS for
+    // all of the wave's rows), rows inner. A word of nibbles holds elements 4 k .. 4 k + 3 (low nibbles) and
+    // 16 + 4 k .. (high); each pair becomes exact fp16 (q - 8) (0x64qq is 1024 + q) and meets its pair of x in
+    // a packed dot product with fp32 accumulation.
     float au[RPW], ag[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) au[r] = ag[r] = 0.f;
@@ -228,43 +255,35 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
     for (int m = 0; m < NQ; ++m) {
       const int c = lane + 64 * m;
       if (c < nblk) {
-        float du[RPW], dg[RPW];                        // sum q_e x_e over the block, by row
+        half2v xp[8][2];
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) du[r] = dg[r] = 0.f;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {                  // the block's two halves, 16 values of x at a time
-          float xh[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) xh[e] = xs[(16 * h + e) * nblk + c];
-#pragma unroll
-          for (int r = 0; r < RPW; ++r) {
-            if (idr[r] >= 0) {                         // wave-uniform
-              du[r] += h ? q4_dot_half<1>(nu[r][m], xh) : q4_dot_half<0>(nu[r][m], xh);
-              if (ACT == 1) dg[r] += h ? q4_dot_half<1>(ng[r][m], xh) : q4_dot_half<0>(ng[r][m], xh);
-            }
-          }
+        for (int j = 0; j < 8; ++j) {
+          const uint2 v = xt[j * nblk + c];
+          xp[j][0] = __builtin_bit_cast(half2v, v.x);
+          xp[j][1] = __builtin_bit_cast(half2v, v.y);
         }
-        const float xsb = xsum[c];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-          au[r] = fmaf((float)fu[r][m], du[r] - 8.f * xsb, au[r]);
-          if (ACT == 1) ag[r] = fmaf((float)fg[r][m], dg[r] - 8.f * xsb, ag[r]);
+          if (P.idr[r] >= 0) {                         // wave-uniform
+            au[r] = fmaf(h16f(P.fu[r][m]), q4_dot_x16(P.nu[r][m], xp), au[r]);
+            if (ACT == 1) ag[r] = fmaf(h16f(P.fg[r][m]), q4_dot_x16(P.ng[r][m], xp), ag[r]);
+          }
         }
       }
     }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      if (idr[r] >= 0) {                               // wave-uniform
-        const float u = wave_sum(au[r]);
+      if (P.idr[r] >= 0) {                             // wave-uniform
+        const float u = wave_sum(au[r]) * xinv;
         float a;
         if (ACT == 1) {
-          const float g = wave_sum(ag[r]) + bias[r];
+          const float g = wave_sum(ag[r]) * xinv + P.bias[r];
           a = fmaxf(g, 0.f) * u;
         } else {
-          a = fmaxf(u + bias[r], 0.f);
+          a = fmaxf(u + P.bias[r], 0.f);
           if (ACT == 2) a *= a;
         }
-        if (lane == 0) { av[w + FW * r] = a; active[blk + G * (k0 + w + FW * r)] = idr[r]; }
+        if (lane == 0) { av[w + FW * r] = a; active[blk + G * (k0 + w + FW * r)] = P.idr[r]; }
       } else if (lane == 0) {
         av[w + FW * r] = 0.f;
       }
@@ -275,7 +294,7 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
     // 8 * half + e), e >= 8 the high nibble (block element 16 + 8 * half + e - 8)
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const float as_ = av[j] * (float)ds[j];
+      const float as_ = av[j] * h16f(P.ds[j]);
       sas += as_;
       const uint2 dj = hok ? *reinterpret_cast<const uint2*>(sdn + (uint32_t)j * rstride + hoff) : make_uint2(0u, 0u);
       const uint32_t wds[2] = {dj.x, dj.y};
@@ -289,7 +308,13 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
         }
       }
     }
-    lds_barrier();                                     // ids / av are rewritten by the next pass
+    lds_barrier();                                     // av is rewritten by the next pass
+  };
+  for (int k0 = 0; k0 < nrow; k0 += NS) {              // passes (block-uniform); row k0 + s in slot s
+    Pass P;
+    issue(k0, P);
+    if (k0 == 0) stage_x();                            // while the first pass's rows are in flight
+    compute(k0, P);
   }
   if (hok) {
     float* pb = part + (size_t)blockIdx.x * D + 32 * (hb >> 1) + 8 * (hb & 1);
@@ -382,10 +407,9 @@ hipError_t launch_fused_q4(const uint8_t* qg, const void* sg, const float* bg, c
   const int nw = (F + 63) / 64;
   constexpr int NS = FW * RPW;
   if (G < 64) return hipErrorInvalidValue;            // one owned row per mask word at most
-  const size_t nblk = (size_t)D / 32;
   const size_t lds = (size_t)((nw + 1) & ~1) * 8 + (NT_F + NT_F / 64 + 4) * sizeof(int) +
-                     (NS + 2 * FW + 4 + (size_t)D + nblk) * sizeof(float) + ((size_t)(F + G - 1) / G) * sizeof(int) +
-                     16 + (size_t)NS * ((nblk + 63) / 64) * 1024 + 16;   // + the pass's nibble rows
+                     (NS + 3 * FW + 4 + (size_t)D / 2) * sizeof(float) + ((size_t)(F + G - 1) / G) * sizeof(int) +
+                     16 + (size_t)NS * NQ * 1024;   // + the pass's nibble rows (16-byte aligned)
   static LdsLimit lds_limit;   // per kernel, set once per device
   size_t avail = 0;
   hipError_t ea = lds_limit.get((const void*)k_fused1_q4<ACT, NQ, RPW>, &avail);
