@@ -103,8 +103,8 @@ __device__ __forceinline__ float q4_dot_x16(const uint4& nib, const half2v (&xp)
 }
 
 // Q4_0 form: gate/up rows as nibbles + block scales, dotted with x in packed fp16 (q4_dot_x16); thread t owns
-// half-block t of every W_downT row (8 nibble bytes = 16 columns, and the block scale) and carries sum(a * s) for
-// the "- 8" of its columns. NQ: Q4 blocks per lane of a row; D <= 32 * NT_F (one half-block per thread).
+// half-block t of every W_downT row (8 nibble bytes = 16 columns, and the block scale), takes each nibble as the
+// exact fp16 1024 + q in an fp32 FMA, and carries sum(a * s) for the "- 1032" of its columns. NQ: Q4 blocks per lane of a row; D <= 32 * NT_F (one half-block per thread).
 template <int ACT, int NQ, int RPW>
 __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg, const _Float16* __restrict__ sg,
                                                     const float* __restrict__ bg, const uint4* __restrict__ qu,
@@ -299,13 +299,20 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
       const uint2 dj = hok ? *reinterpret_cast<const uint2*>(sdn + (uint32_t)j * rstride + hoff) : make_uint2(0u, 0u);
       const uint32_t wds[2] = {dj.x, dj.y};
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const uint32_t lo = wds[k] & 0x0F0F0F0Fu, hi = (wds[k] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          acc[4 * k + b] = fmaf(as_, (float)((lo >> (8 * b)) & 0xFF), acc[4 * k + b]);
-          acc[8 + 4 * k + b] = fmaf(as_, (float)((hi >> (8 * b)) & 0xFF), acc[8 + 4 * k + b]);
-        }
+      for (int k = 0; k < 2; ++k) {                    // nibbles as exact fp16 1024 + q (0x64qq), fp32 FMA with
+        const uint32_t lo = wds[k] & 0x0F0F0F0Fu, hi = (wds[k] >> 4) & 0x0F0F0F0Fu;   // fp16 operands
+        const half2v l0 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(lo, 0x64646464u, 0x00050004u));
+        const half2v l1 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(lo, 0x64646464u, 0x00070006u));
+        const half2v h0 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hi, 0x64646464u, 0x00050004u));
+        const half2v h1 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hi, 0x64646464u, 0x00070006u));
+        acc[4 * k + 0] = fmaf(as_, (float)l0[0], acc[4 * k + 0]);
+        acc[4 * k + 1] = fmaf(as_, (float)l0[1], acc[4 * k + 1]);
+        acc[4 * k + 2] = fmaf(as_, (float)l1[0], acc[4 * k + 2]);
+        acc[4 * k + 3] = fmaf(as_, (float)l1[1], acc[4 * k + 3]);
+        acc[8 + 4 * k + 0] = fmaf(as_, (float)h0[0], acc[8 + 4 * k + 0]);
+        acc[8 + 4 * k + 1] = fmaf(as_, (float)h0[1], acc[8 + 4 * k + 1]);
+        acc[8 + 4 * k + 2] = fmaf(as_, (float)h1[0], acc[8 + 4 * k + 2]);
+        acc[8 + 4 * k + 3] = fmaf(as_, (float)h1[1], acc[8 + 4 * k + 3]);
       }
     }
     lds_barrier();                                     // av is rewritten by the next pass
@@ -320,7 +327,7 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
     float* pb = part + (size_t)blockIdx.x * D + 32 * (hb >> 1) + 8 * (hb & 1);
     float4* lo = reinterpret_cast<float4*>(pb);
     float4* hi = reinterpret_cast<float4*>(pb + 16);
-    const float c8 = -8.f * sas;
+    const float c8 = -1032.f * sas;                    // the nibbles entered as 1024 + q
     lo[0] = make_float4(acc[0] + c8, acc[1] + c8, acc[2] + c8, acc[3] + c8);
     lo[1] = make_float4(acc[4] + c8, acc[5] + c8, acc[6] + c8, acc[7] + c8);
     hi[0] = make_float4(acc[8] + c8, acc[9] + c8, acc[10] + c8, acc[11] + c8);
