@@ -100,8 +100,11 @@ size_t ws_pre_bytes(int B, int F) {
 size_t ws_xf_bytes(int B, int D) {
   return B > 1 ? align256(sffn_ur_xf_bytes(B, D, true)) + align256((size_t)((B + 15) / 16) * 16 * sizeof(float)) : 0;
 }
-// B > 1: the row kernels' largest |activation| per 64 union rows and token, [ceil(F / 64)][B] fp32
-size_t ws_bmax_bytes(int B, int F) { return B > 1 ? align256((size_t)((F + 63) / 64) * B * sizeof(float)) : 0; }
+// B > 1: the row kernels' largest |activation| per row tile (16 or 64 union rows) and token, [tiles][B] fp32
+size_t ws_bmax_bytes(int B, int F) {
+  const int t = 1 << sffn_ur_bmax_shift(B);
+  return B > 1 ? align256((size_t)((F + t - 1) / t) * B * sizeof(float)) : 0;
+}
 size_t ws_forward_bytes(int B, int D, int F) {
   return ws_a_bytes(B, F) + ws_xn_bytes(B, D) + ws_part_bytes(B, D) + ws_pre_bytes(B, F) + ws_xf_bytes(B, D) +
          ws_bmax_bytes(B, F);
@@ -171,8 +174,8 @@ hipError_t run_union(int act, bool q4, const void* Wg, const void* Sg, const flo
                                      n_active, ws_abuf(ws), ws_bmax(ws, B, D, F), ws_xf(ws, B, D, F),
                                      ws_xs(ws, B, D, F), ws_pre(ws, B, D, F), st);
   if (e != hipSuccess) return e;
-  return sffn_launch_down_ud(q4, UNION_EXACT, Wd, Sd, active, n_active, ws_abuf(ws), ws_bmax(ws, B, D, F), B, D, F,
-                             ws_part(ws, B, D, F), sffn_ud_shares(D, UD_KS_MAX), y, st);
+  return sffn_launch_down_ud(q4, UNION_EXACT, Wd, Sd, active, n_active, ws_abuf(ws), ws_bmax(ws, B, D, F),
+                             sffn_ur_bmax_shift(B), B, D, F, ws_part(ws, B, D, F), sffn_ud_shares(D, UD_KS_MAX), y, st);
 }
 
 }  // namespace

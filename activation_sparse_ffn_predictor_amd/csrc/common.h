@@ -446,6 +446,7 @@ hipError_t sffn_launch_predict_mt(const void* P1, const void* P2, const float* c
 // when x_norm) into xf (sffn_ur_xf_bytes) and the tokens' powers of two into xs, then the row kernel
 size_t sffn_ur_xf_bytes(int B, int D, bool exact);
 int sffn_ur_shares(int B);   // k shares per 64 union rows (> 1: partial pre-activations in `pre`, then combined)
+int sffn_ur_bmax_shift(int B);   // log2 of the union rows per entry of the largest-|a| table
 hipError_t sffn_launch_rows_ur(int act, bool q4, bool exact, const void* Wg, const void* Sg, const float* bg,
                                const void* Wu, const void* Su, const float* bu, const float* x, int x_norm, int B,
                                int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf,
@@ -456,8 +457,8 @@ hipError_t sffn_launch_act_combine(int act, const float* pre, int KSP, const int
                                    const float* bias, int B, int F, float* abuf, float* bmax, hipStream_t st);
 hipError_t sffn_launch_sum_parts(const float* part, int KS, int n, float* y, hipStream_t st);
 // union down projection on the matrix cores (union_down.hip): KS shares of the union rows, each with its tokens'
-// power-of-two scale from bmax, partial sums into part [KS][B][D], then y = their sum
+// power-of-two scale from bmax (one entry per 2^rbs rows), partial sums into part [KS][B][D], then y = their sum
 int sffn_ud_shares(int D, int ks_max);
 hipError_t sffn_launch_down_ud(bool q4, bool exact, const void* Wd, const void* Sd, const int32_t* active,
-                               const int32_t* n_active, const float* abuf, const float* bmax, int B, int D, int F,
-                               float* part, int KS, float* y, hipStream_t st);
+                               const int32_t* n_active, const float* abuf, const float* bmax, int rbs, int B, int D,
+                               int F, float* part, int KS, float* y, hipStream_t st);

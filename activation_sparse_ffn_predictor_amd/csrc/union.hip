@@ -223,6 +223,8 @@ __global__ __launch_bounds__(256) void k_mt_z(const uint4* __restrict__ P2, cons
 // The 64 x BP tile (BP = B rounded up to 16) is written whole in octet order, a[i, b] at
 // ((i / 8) * BP + b) * 8 + i % 8, zero past n and B; bmax receives the tile's largest |a| per token,
 // bmax[(i / 64) * B + token].
+constexpr int KSP_MAX = 8;           // k shares of the union row kernel at most
+
 template <int ACT>
 __global__ __launch_bounds__(256) void k_act_combine(const float* __restrict__ pre, int KSP,
                                                      const int32_t* __restrict__ active,
@@ -236,16 +238,24 @@ __global__ __launch_bounds__(256) void k_act_combine(const float* __restrict__ p
   if (threadIdx.x < 64) smx[threadIdx.x] = 0u;
   __syncthreads();
   const int BP = (B + 15) & ~15;
-  const size_t FB = (size_t)F * B;
+  const uint32_t FB = (uint32_t)F * (uint32_t)B;
+  const Buf bp(pre, (uint32_t)KSP * 2u * FB * 4u);
   for (int q = (int)threadIdx.x; q < 64 * BP; q += 256) {
     const int b = (q >> 3) % BP, i = i0 + (q / (8 * BP)) * 8 + (q & 7);
     float a = 0.f;
     if (i < n && b < B) {
-      const size_t e = (size_t)i * B + b;
+      const uint32_t e = (uint32_t)i * (uint32_t)B + (uint32_t)b;
+      float vu[KSP_MAX], vg[KSP_MAX];                  // every share's loads in flight at once
+#pragma unroll
+      for (int k = 0; k < KSP_MAX; ++k) {
+        vu[k] = bp.ldf(boff(k < KSP, ((uint32_t)(2 * k) * FB + e) * 4u));
+        vg[k] = ACT == 1 ? bp.ldf(boff(k < KSP, ((uint32_t)(2 * k + 1) * FB + e) * 4u)) : 0.f;
+      }
       float u = 0.f, g = 0.f;
-      for (int k = 0; k < KSP; ++k) {
-        u += pre[(size_t)(2 * k) * FB + e];
-        if (ACT == 1) g += pre[(size_t)(2 * k + 1) * FB + e];
+#pragma unroll
+      for (int k = 0; k < KSP_MAX; ++k) {              // in share order (shares past KSP read 0)
+        u += vu[k];
+        if (ACT == 1) g += vg[k];
       }
       const float bi = bias ? bias[active[i]] : 0.f;
       if (ACT == 1) {
@@ -294,6 +304,7 @@ hipError_t predict_mt(const void* P1, const void* P2, const float* c, const floa
 // Activations from KSP shares of partial pre-activations (row kernels with a k split); see k_act_combine.
 hipError_t sffn_launch_act_combine(int act, const float* pre, int KSP, const int32_t* active, const int32_t* n_active,
                                    const float* bias, int B, int F, float* abuf, float* bmax, hipStream_t st) {
+  if (KSP < 1 || KSP > KSP_MAX || (size_t)KSP * 2 * F * B * 4 >= ((size_t)1 << 31)) return hipErrorInvalidValue;
   const dim3 grid((F + 63) / 64), blk(256);
   if (act == 1) hipLaunchKernelGGL(k_act_combine<1>, grid, blk, 0, st, pre, KSP, active, n_active, bias, B, F, abuf, bmax);
   else if (act == 2) hipLaunchKernelGGL(k_act_combine<2>, grid, blk, 0, st, pre, KSP, active, n_active, bias, B, F, abuf, bmax);

@@ -57,9 +57,10 @@ __device__ __forceinline__ void nib8_half(uint32_t px, uint32_t py, uint32_t sh,
 template <int NTT, bool Q4, bool EXACT>
 __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const void* __restrict__ Sd,
                                             const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
-                                            const float* __restrict__ abuf, const float* __restrict__ bmax, int B,
-                                            int D, int F, int M, float* __restrict__ part) {
-  // M: the most 64-row steps one share can hold (sizes the ids in LDS, with UD_PAD steps of padding)
+                                            const float* __restrict__ abuf, const float* __restrict__ bmax,
+                                            int rbs, int B, int D, int F, int M, float* __restrict__ part) {
+  // M: the most 64-row steps one share can hold (sizes the ids in LDS, with UD_PAD steps of padding); bmax holds
+  // the largest |a| per token of every row tile of 2^rbs rows (rbs = 4 or 6)
   static_assert(!(Q4 && EXACT), "Q4_0 weights take fp16 activations");
   constexpr int NHA = EXACT ? 2 : 1;                   // activation planes (hi, lo)
   constexpr int BP = NTT * 16;                         // token stride of the activations
@@ -80,21 +81,22 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
   const int ibase = ks * total;                        // dense index of this workgroup's first row
   // the row-block maxima of this share and the ids (0 past the union and past the share) in one round trip
   {
-    const Buf bm(bmax, (uint32_t)((F + 63) >> 6) * (uint32_t)B * 4u);
+    const Buf bm(bmax, (uint32_t)((F + (1 << rbs) - 1) >> rbs) * (uint32_t)B * 4u);
     const Buf bid(active, (uint32_t)n * 4u);
     const int tok = threadIdx.x & 63, sub = threadIdx.x >> 6;
+    const int ne = Mn << (6 - rbs);                    // table entries (row tiles of 2^rbs rows) of this share
     float m = 0.f;
-    for (int b0 = 0; b0 < Mn; b0 += 32) {
+    for (int b0 = 0; b0 < ne; b0 += 32) {
       float v[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int b = b0 + sub + 4 * k;
-        v[k] = bm.ldf(boff(b < Mn && tok < B, ((uint32_t)(ks * Mn + b) * (uint32_t)B + (uint32_t)tok) * 4u));
+        v[k] = bm.ldf(boff(b < ne && tok < B, ((uint32_t)(ks * ne + b) * (uint32_t)B + (uint32_t)tok) * 4u));
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int b = b0 + sub + 4 * k;
-        if (ibase + 64 * b < n) m = fmaxf(m, v[k]);    // row blocks past n hold stale maxima
+        if (ibase + (b << rbs) < n) m = fmaxf(m, v[k]);   // row tiles past n hold stale maxima
       }
     }
     smx[sub][tok] = m;
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
 
 template <int NTT, bool Q4, bool EXACT>
 hipError_t launch_ud(const void* Wd, const void* Sd, const int32_t* active, const int32_t* n_active,
-                     const float* abuf, const float* bmax, int B, int D, int F, float* part, int KS, float* y,
+                     const float* abuf, const float* bmax, int rbs, int B, int D, int F, float* part, int KS, float* y,
                      hipStream_t st) {
   const int M = (F + KSTD * KS - 1) / (KSTD * KS);     // steps per workgroup at most
   const size_t lds = (size_t)(M + UD_PAD) * KSTD * sizeof(int);
@@ -308,7 +310,7 @@ hipError_t launch_ud(const void* Wd, const void* Sd, const int32_t* active, cons
   if (ea != hipSuccess) return ea;
   if (lds > avail) return hipErrorInvalidValue;
   SFFN_LAUNCH(3, (k_ud<NTT, Q4, EXACT>), dim3((D + CTD - 1) / CTD, KS), dim3(NTD), lds, st, Wd, Sd, active, n_active,
-              abuf, bmax, B, D, F, M, part);
+              abuf, bmax, rbs, B, D, F, M, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return sffn_launch_sum_parts(part, KS, B * D, y, st);
@@ -316,11 +318,11 @@ hipError_t launch_ud(const void* Wd, const void* Sd, const int32_t* active, cons
 
 template <int NTT>
 hipError_t ud_q(bool q4, bool exact, const void* Wd, const void* Sd, const int32_t* active, const int32_t* n_active,
-                const float* abuf, const float* bmax, int B, int D, int F, float* part, int KS, float* y,
+                const float* abuf, const float* bmax, int rbs, int B, int D, int F, float* part, int KS, float* y,
                 hipStream_t st) {
-  if (q4) return launch_ud<NTT, true, false>(Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
-  if (exact) return launch_ud<NTT, false, true>(Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
-  return launch_ud<NTT, false, false>(Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
+  if (q4) return launch_ud<NTT, true, false>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
+  if (exact) return launch_ud<NTT, false, true>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
+  return launch_ud<NTT, false, false>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
 }
 
 }  // namespace
@@ -332,13 +334,14 @@ int sffn_ud_shares(int D, int ks_max) {
 }
 
 hipError_t sffn_launch_down_ud(bool q4, bool exact, const void* Wd, const void* Sd, const int32_t* active,
-                               const int32_t* n_active, const float* abuf, const float* bmax, int B, int D, int F,
-                               float* part, int KS, float* y, hipStream_t st) {
+                               const int32_t* n_active, const float* abuf, const float* bmax, int rbs, int B, int D,
+                               int F, float* part, int KS, float* y, hipStream_t st) {
+  if (rbs != 4 && rbs != 6) return hipErrorInvalidValue;
   switch ((B + 15) / 16) {
-    case 1: return ud_q<1>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
-    case 2: return ud_q<2>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
-    case 3: return ud_q<3>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
-    case 4: return ud_q<4>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, B, D, F, part, KS, y, st);
+    case 1: return ud_q<1>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
+    case 2: return ud_q<2>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
+    case 3: return ud_q<3>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
+    case 4: return ud_q<4>(q4, exact, Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
     default: return hipErrorInvalidValue;
   }
 }

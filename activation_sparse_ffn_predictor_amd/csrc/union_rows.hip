@@ -362,6 +362,188 @@ __global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const v
   }
 }
 
+// A few tokens (B <= UR16_MAX_B): 16 union rows per workgroup and the k range split over its 4 waves, so that a small
+// union still spreads over many workgroups without a second kernel to combine k shares. Wave w takes a contiguous
+// quarter of the quads; per quad each lane loads its row's k block (as in k_ur) and its own token fragments
+// straight from xf (no LDS staging: no two waves share a quad). Loads run two quads ahead in a ring of three
+// register sets. The waves' partial sums meet in LDS and wave 0 adds them in wave order, applies bias and
+// activation, and writes the tile (octet order, zeros past n and B) and its largest |a| per token
+// (bmax[(i0 / 16) * B + token]). Workgroups past the union but inside its last 64-row block write a zero tile.
+constexpr int R16 = 16;
+// Up to 4 tokens the 16-row kernel (k split over the waves of a workgroup) runs; from 5 tokens its token fragments,
+// read again by every 16-row workgroup, cost more than the k-share combine of the 64-row kernel. Measured at the
+// 13B shape: 4 tokens 1616 -> 1689 tokens/s with the 16-row kernel, 8 tokens 2552 -> 2398.
+constexpr int UR16_MAX_B = 4;
+
+
+template <int ACT, bool Q4, bool EXACT>
+__global__ __launch_bounds__(NTR) void k_ur16(const void* __restrict__ Wg, const void* __restrict__ Sg,
+                                              const float* __restrict__ bg, const void* __restrict__ Wu,
+                                              const void* __restrict__ Su, const float* __restrict__ bu,
+                                              const uint4* __restrict__ xf, const float* __restrict__ xsc, int B,
+                                              int D, int F, const uint64_t* __restrict__ mask,
+                                              int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                                              float* __restrict__ abuf, float* __restrict__ bmax) {
+  static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
+  constexpr bool GT = ACT == 1;                        // ReGLU: a gate row per neuron
+  constexpr int NH = EXACT ? 2 : 1;                    // token fragment planes (hi, lo)
+  constexpr int WV = Q4 ? 1 : 4;                       // uint4 of weights per lane and matrix per quad
+  __shared__ uint64_t wl[WMAXR * NTR];                 // mask words
+  __shared__ int roff[NTR];
+  __shared__ int tmp[NTR / 64 + 4];
+  __shared__ int ids[R16];
+  __shared__ f32x4 red[3][2][64];                      // waves 1..3's partial sums (up, gate)
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nw = (F + 63) >> 6;
+  const int wpt = (nw + NTR - 1) / NTR;
+  const int n = mask_prefix<NTR, WMAXR>(mask, nw, F, wpt, wl, roff, tmp);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
+  const int i0 = blockIdx.x * R16;
+  if (i0 >= n) {                                       // block-uniform
+    if (i0 < ((n + 63) & ~63)) {                       // inside the union's last 64-row block: a zero tile
+      const int r = threadIdx.x >> 4, tok = threadIdx.x & 15, i = i0 + r;
+      abuf[((size_t)(i >> 3) * 16 + tok) * 8 + (i & 7)] = 0.f;
+    }
+    return;
+  }
+  if (threadIdx.x < R16) {
+    const int i = i0 + threadIdx.x;
+    int id = -1;
+    if (i < n) {                                       // the (i - roff)-th set bit after word range T * wpt
+      int lo = 0, hi = NTR - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (roff[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      int rem = i - roff[lo];
+      for (int tw = lo * wpt; tw < nw; ++tw) {
+        const int cnt = __popcll(wl[tw]);
+        if (rem < cnt) { id = tw * 64 + select_bit(wl[tw], rem); break; }
+        rem -= cnt;
+      }
+      active[i] = id;
+    }
+    ids[threadIdx.x] = id;
+  }
+  __syncthreads();
+  const int idl = ids[lane & 15];                      // this lane's A-operand row (-1: none)
+  const int jq = lane >> 4;                            // lane group: the k block of a quad this lane holds
+  const int KB = (D + 31) >> 5, nblk = D >> 5;
+  const int KQ = (KB + 3) >> 2;                        // quads
+  const int KQW = (KQ + 3) >> 2;                       // quads of one wave
+  const int q0 = w * KQW, q1 = min(KQ, q0 + KQW);      // this wave's quads
+  const int nq3 = (max(q1 - q0, 0) + 2) / 3 * 3;       // padded to rounds of three (the padding reads nothing)
+  const Buf bx(xf, (uint32_t)KQ * 4u * (uint32_t)NH * 1024u);
+  const uint32_t wbytes = Q4 ? (uint32_t)F * (uint32_t)(D >> 1) : (uint32_t)F * (uint32_t)D * 2u;
+  const uint32_t sbytes = Q4 ? (uint32_t)F * (uint32_t)nblk * 2u : 0u;
+  const Buf bwu(Wu, wbytes), bwg(GT ? Wg : Wu, GT ? wbytes : 0u);
+  const Buf bsu(Q4 ? Su : Wu, sbytes), bsg(Q4 && GT ? Sg : Wu, GT ? sbytes : 0u);
+  const uint32_t row = (uint32_t)(idl >= 0 ? idl : 0);
+  struct Set {
+    uint4 wu[WV], wg[WV];
+    uint32_t su, sg;                                   // block scales' fp16 bits (32-bit: kept in registers)
+    uint4 xv[4][NH];
+  };
+  auto load = [&](int g, Set& S) {                     // quad g of the wave's range (past q1: nothing)
+    const int kb = g * 4 + jq;
+    const bool ok = g < q1 && kb < KB && idl >= 0;
+    if constexpr (Q4) {
+      const uint32_t o = row * (uint32_t)(D >> 1) + (uint32_t)kb * 16u;
+      S.wu[0] = bwu.ld16(boff(ok, o));
+      if (GT) S.wg[0] = bwg.ld16(boff(ok, o));
+      const uint32_t so = (row * nblk + kb) * 2u;
+      S.su = bsu.ldu16(boff(ok, so));
+      if (GT) S.sg = bsg.ldu16(boff(ok, so));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {                    // elements 8 q .. 8 q + 7 of the lane's k block
+        const int k = kb * 32 + q * 8;
+        const uint32_t o = (row * (uint32_t)D + (uint32_t)k) * 2u;
+        S.wu[q] = bwu.ld16(boff(ok && k < D, o));
+        if (GT) S.wg[q] = bwg.ld16(boff(ok && k < D, o));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        S.xv[q][h] = bx.ld16(boff(g < q1, (((uint32_t)(g * 4 + q) * NH + h) * 64u + lane) * 16u));
+  };
+  f32x4 au = {0.f, 0.f, 0.f, 0.f}, ag = au;
+  auto compute = [&](const Set& S) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      half8 a_u, a_g;
+      if constexpr (Q4) {                              // fp16((q - 8) s): one rounding per weight
+        a_u = q4_half8(S.wu[0], q) * splat8(S.su);
+        if (GT) a_g = q4_half8(S.wg[0], q) * splat8(S.sg);
+      } else {
+        a_u = __builtin_bit_cast(half8, S.wu[q]);
+        if (GT) a_g = __builtin_bit_cast(half8, S.wg[q]);
+      }
+      const half8 xh = __builtin_bit_cast(half8, S.xv[q][0]);
+      if constexpr (EXACT) {
+        const half8 xo = __builtin_bit_cast(half8, S.xv[q][NH - 1]);
+        au = mfma16(a_u, xo, mfma16(a_u, xh, au));
+        if (GT) ag = mfma16(a_g, xo, mfma16(a_g, xh, ag));
+      } else {
+        au = mfma16(a_u, xh, au);
+        if (GT) ag = mfma16(a_g, xh, ag);
+      }
+    }
+  };
+  Set S0, S1, S2;
+  load(q0, S0);
+  load(q0 + 1, S1);
+  for (int c = 0; c < nq3; c += 3) {                   // nq3 is a multiple of 3
+    load(q0 + c + 2, S2);
+    compute(S0);
+    load(q0 + c + 3, S0);
+    compute(S1);
+    load(q0 + c + 4, S1);
+    compute(S2);
+  }
+  // the waves' partial sums, added in wave order by wave 0
+  if (w > 0) {
+    red[w - 1][0][lane] = au;
+    if (GT) red[w - 1][1][lane] = ag;
+  }
+  __syncthreads();
+  if (w > 0) return;                                   // wave-uniform
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    au += red[k][0][lane];
+    if (GT) ag += red[k][1][lane];
+  }
+  // epilogue: lane l holds rows 4 (l / 16) + i of token l % 16; the token's power of two back, bias, activation
+  const int tok = lane & 15;
+  const int r0 = i0 + (lane >> 4) * 4;                 // this lane's 4 rows: half an octet
+  const float sx = tok < B ? xsc[tok] : 0.f;
+  const float* bp = GT ? bg : bu;
+  float a4[4], amx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ii = r0 + i;
+    const int id = ids[(lane >> 4) * 4 + i];
+    const float bias = (bp && id >= 0) ? bp[id] : 0.f;
+    const float u = au[i] * sx, g = ag[i] * sx;
+    float a;
+    if (GT) {
+      a = fmaxf(g + bias, 0.f) * u;
+    } else {
+      a = fmaxf(u + bias, 0.f);
+      if (ACT == 2) a *= a;
+    }
+    a4[i] = (tok < B && ii < n) ? a : 0.f;
+    amx = fmaxf(amx, fabsf(a4[i]));
+  }
+  *reinterpret_cast<float4*>(&abuf[((size_t)(r0 >> 3) * 16 + tok) * 8 + (r0 & 7)]) =
+      make_float4(a4[0], a4[1], a4[2], a4[3]);
+  amx = fmaxf(amx, __shfl_xor(amx, 16, 64));
+  amx = fmaxf(amx, __shfl_xor(amx, 32, 64));
+  if (lane < B) bmax[(size_t)(i0 / R16) * B + lane] = amx;
+}
+
 template <int XPT, bool EXACT>
 hipError_t launch_split_x(const float* x, int x_norm, int B, int D, int NTT, uint4* xf, float* xs, hipStream_t st) {
   hipLaunchKernelGGL((k_split_x<XPT, EXACT>), dim3(NTT * 16), dim3(NTX), 0, st, x, x_norm, B, D, NTT, xf, xs);
@@ -384,6 +566,11 @@ hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
   if ((F + 63) / 64 > WMAXR * NTR || KS < 1 || (KS > 1 && !pre)) return hipErrorInvalidValue;
+  if (NTT == 1 && B <= UR16_MAX_B) {                   // 16-row workgroups, k split over the waves
+    SFFN_LAUNCH(2, (k_ur16<ACT, Q4, EXACT>), dim3((F + R16 - 1) / R16), dim3(NTR), 0, st, Wg, Sg, bg, Wu, Su, bu,
+                (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax);
+    return hipGetLastError();
+  }
   SFFN_LAUNCH(2, (k_ur<NTT, ACT, Q4, EXACT>), dim3((F + RTB - 1) / RTB * KS), dim3(NTR), 0, st, Wg, Sg, bg, Wu, Su, bu,
               (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
   e = hipGetLastError();
@@ -415,7 +602,10 @@ size_t sffn_ur_xf_bytes(int B, int D, bool exact) {
 }
 
 // Shares of the k range per 64 union rows: few tokens mean few union rows, so more shares keep the CUs busy.
-int sffn_ur_shares(int B) { return B <= 8 ? 8 : (B <= 16 ? 4 : (B <= 32 ? 2 : 1)); }
+int sffn_ur_shares(int B) { return B <= UR16_MAX_B ? 1 : (B <= 8 ? 8 : (B <= 16 ? 4 : (B <= 32 ? 2 : 1))); }
+
+// log2 of the union rows per entry of the row kernels' largest-|a| table: 16-row tiles for the 16-row kernel, else 64
+int sffn_ur_bmax_shift(int B) { return B <= UR16_MAX_B ? 4 : 6; }
 
 hipError_t sffn_launch_rows_ur(int act, bool q4, bool exact, const void* Wg, const void* Sg, const float* bg,
                                const void* Wu, const void* Su, const float* bu, const float* x, int x_norm, int B,

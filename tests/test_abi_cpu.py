@@ -43,11 +43,11 @@ def test_status_strings_and_sizes():
     # [a: F*B fp32, for B > 1 at least ceil(F/64)*64 x ceil(B/16)*16 fp32][B > 1: xn B*D fp32]
     # [partial y: 16*B*D fp32 (B > 1) or 256*D fp32 (B = 1)][B > 1: k-share partials KS*2*F*B fp32]
     # [B > 1: token fragments, 2 planes of 4 ceil(D/128) x ceil(B/16) kB, + 16 powers of two per token tile]
-    # [B > 1: largest |a| per 64 union rows and token, ceil(F/64)*B fp32][h: B*r fp32]
+    # [B > 1: largest |a| per row tile (16 rows up to 4 tokens, else 64) and token][h: B*r fp32]
     assert _lib.workspace_size(1, 4096, 11008, 256) == 44032 + 256 * 4096 * 4 + 1024
-    # (k shares: 8 up to 8 tokens, 4 up to 16, 2 up to 32; token fragments in whole quads of 4 k blocks)
+    # (k shares: none up to 4 tokens, 8 up to 8, 4 up to 16, 2 up to 32; token fragments in whole quads of 4 k blocks)
     assert _lib.workspace_size(8, 512, 100, 64) == 8192 + 16384 + 262144 + 51200 + (32768 + 256) + 256 + 2048
-    assert _lib.workspace_size(3, 40, 7, 8) == 4096 + 512 + 7680 + 1536 + (8192 + 256) + 256 + 256
+    assert _lib.workspace_size(3, 40, 7, 8) == 4096 + 512 + 7680 + 0 + (8192 + 256) + 256 + 256
     assert _lib.workspace_size(64, 512, 100, 64) == 32768 + 131072 + 2097152 + 0 + (4 * 32768 + 256) + 512 + 16384
 
 
