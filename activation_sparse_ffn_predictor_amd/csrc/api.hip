@@ -35,6 +35,7 @@ constexpr int MAX_BD_VALU = SFFN_MAX_BD_VALU;   // decode-batch kernels (B in {2
 constexpr int MAX_F_UNION = 32768;   // union kernels compact the whole mask in one block
 constexpr int KS_MAX = 8;            // k shares of the multi-token predictor's first stage
 constexpr int UD_KS_MAX = 16;        // row shares of the union down projection
+constexpr int MZ_MIN_B = 17;         // tokens from which the predictor's stage 2 runs on pre-split h fragments
 constexpr int G_FUSED = 256;         // blocks (= partial sums of y) of the fused single-token forward
 #ifndef SFFN_UNION_EXACT
 #define SFFN_UNION_EXACT 1
@@ -277,7 +278,8 @@ static int predict_impl(const void* P1, const void* P2, const float* c, const fl
     // z: vector-ALU kernel for up to 4 tokens, matrix-core kernel beyond (measured: equal at 4, faster at 8)
     if (e == hipSuccess)
       e = B <= 4 ? sffn_launch_predict_zb(P2, c, h, B, F, r, tau, n_hot, mask, logits, st)
-                 : sffn_launch_predict_mt(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, h, nullptr, 0, st);
+                 : sffn_launch_predict_mt(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, h, nullptr, 0,
+                                          nullptr, nullptr, st);
   } else {
     const float* xin = x;
     e = hipSuccess;
@@ -288,9 +290,12 @@ static int predict_impl(const void* P1, const void* P2, const float* c, const fl
     // shares of d for the union predictor's first stage; their partial sums use the partials region
     // (KS_MAX * B * D floats >= ksh * B * r)
     const int ksh = std::max(1, std::min({KS_MAX, D / 32 > 0 ? D / 32 : 1, (KS_MAX * D) / r}));
+    // stage 2 on pre-split h fragments (in the union row kernel's token-fragment region, free until the forward
+    // call) from 17 tokens; below, its split launch costs more than the fragments save
+    const bool mz = B > MZ_MIN_B - 1 && sffn_ur_xf_bytes(B, r, true) <= sffn_ur_xf_bytes(B, D, true);
     if (e == hipSuccess)
       e = sffn_launch_predict_mt(P1, P2, c, xin, B, D, F, r, tau, n_hot, mask, logits, h, ws_part(ws, B, D, F), ksh,
-                                 st);
+                                 mz ? ws_xf(ws, B, D, F) : nullptr, mz ? ws_xs(ws, B, D, F) : nullptr, st);
   }
   return e == hipSuccess ? SFFN_OK : hip_fail(e, "predict launch");
 }

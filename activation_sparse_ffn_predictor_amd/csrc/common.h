@@ -439,9 +439,10 @@ hipError_t sffn_launch_predict_h(const void* P1, const float* x, int x_norm, int
 
 // multi-token (union-mask) path, matrix cores (union.hip)
 hipError_t sffn_launch_norm_tokens(const float* x, int B, int D, float* xn, hipStream_t st);
+// (hf, hs non-NULL: stage 2 through sffn_launch_predict_mz with those fragment buffers, else k_mt_z)
 hipError_t sffn_launch_predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F,
                                   int r, float tau, int n_hot, uint64_t* mask, float* logits, float* hbuf,
-                                  float* hpart, int KSH, hipStream_t st);
+                                  float* hpart, int KSH, void* hf, float* hs, hipStream_t st);
 // union row gather tiled over 64 rows with every token tile (union_rows.hip): token fragments from x (normalised
 // when x_norm) into xf (sffn_ur_xf_bytes) and the tokens' powers of two into xs, then the row kernel
 size_t sffn_ur_xf_bytes(int B, int D, bool exact);
@@ -451,6 +452,9 @@ hipError_t sffn_launch_rows_ur(int act, bool q4, bool exact, const void* Wg, con
                                const void* Wu, const void* Su, const float* bu, const float* x, int x_norm, int B,
                                int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf,
                                float* bmax, void* xf, float* xs, float* pre, hipStream_t st);
+// multi-token predictor stage 2 from h [B, r]: h split into fragments in hf (sffn_ur_xf_bytes(B, r, true)) and hs
+hipError_t sffn_launch_predict_mz(const void* P2, const float* c, const float* h, int B, int F, int r, float tau,
+                                  int n_hot, uint64_t* mask, float* logits, void* hf, float* hs, hipStream_t st);
 // activations (octet order, 64-row tiles written whole) from the k shares' partial pre-activations, and the
 // largest |a| per 64 rows and token into bmax
 hipError_t sffn_launch_act_combine(int act, const float* pre, int KSP, const int32_t* active, const int32_t* n_active,

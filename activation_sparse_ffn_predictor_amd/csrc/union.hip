@@ -283,7 +283,7 @@ __global__ void k_sum_parts(const float* __restrict__ part, int KS, int n, float
 template <int NTT>
 hipError_t predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F, int r,
                       float tau, int n_hot, uint64_t* mask, float* logits, float* hbuf, float* hpart, int KSH,
-                      hipStream_t st) {
+                      void* hf, float* hs, hipStream_t st) {
   hipError_t e;
   if (KSH > 0) {                                       // else hbuf holds h already
     SFFN_LAUNCH(0, k_mt_h<NTT>, dim3((r + 15) / 16, KSH), dim3(NTK), 0, st, (const uint4*)P1, x, B, D, r, hpart);
@@ -294,6 +294,8 @@ hipError_t predict_mt(const void* P1, const void* P2, const float* c, const floa
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (hf)                                              // h split once, P2 streamed on the 64-row tiling
+    return sffn_launch_predict_mz(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, hf, hs, st);
   SFFN_LAUNCH(1, k_mt_z<NTT>, dim3((F + 63) / 64), dim3(256), 0, st, (const uint4*)P2, c, hbuf, B, F, r, tau, n_hot,
               mask, logits);
   return hipGetLastError();
@@ -331,13 +333,15 @@ hipError_t sffn_launch_norm_tokens(const float* x, int B, int D, float* xn, hipS
 
 hipError_t sffn_launch_predict_mt(const void* P1, const void* P2, const float* c, const float* x, int B, int D, int F,
                                   int r, float tau, int n_hot, uint64_t* mask, float* logits, float* hbuf,
-                                  float* hpart, int KSH, hipStream_t st) {
+                                  float* hpart, int KSH, void* hf, float* hs, hipStream_t st) {
   const int ntt = (B + 15) / 16;
+#define PMT(N) return predict_mt<N>(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, hbuf, hpart, KSH, hf, hs, st)
   switch (ntt) {
-    case 1: return predict_mt<1>(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, hbuf, hpart, KSH, st);
-    case 2: return predict_mt<2>(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, hbuf, hpart, KSH, st);
-    case 3: return predict_mt<3>(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, hbuf, hpart, KSH, st);
-    case 4: return predict_mt<4>(P1, P2, c, x, B, D, F, r, tau, n_hot, mask, logits, hbuf, hpart, KSH, st);
+    case 1: PMT(1);
+    case 2: PMT(2);
+    case 3: PMT(3);
+    case 4: PMT(4);
     default: return hipErrorInvalidValue;
   }
+#undef PMT
 }

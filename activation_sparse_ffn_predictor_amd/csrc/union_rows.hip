@@ -544,6 +544,127 @@ __global__ __launch_bounds__(NTR) void k_ur16(const void* __restrict__ Wg, const
   if (lane < B) bmax[(size_t)(i0 / R16) * B + lane] = amx;
 }
 
+// The predictor's second stage for a batch of tokens on the same tiling (PowerInfer pages, Turkish article,
+// "Adaptive sparsity predictors": z = P2 h + c per token, a neuron marked if any token's z passes the threshold).
+// h [B, r] is first split by k_split_x into token fragments (scaled by a power of two per token, two fp16 planes);
+// k_mz then streams every row of P2 (64 neurons per workgroup, 16 per wave, 4 k blocks per chunk, two chunks
+// ahead in three register sets, the chunk's fragments shared through LDS) and takes exact products into fp32 sums.
+// Epilogue: z = sum * 2^e + c (the always-active prefix: +inf, its row never read), optional logits[token][neuron],
+// and the OR over tokens by ballot into the block's mask word.
+template <int NTT>
+__global__ __launch_bounds__(NTR) void k_mz(const void* __restrict__ P2, const float* __restrict__ c,
+                                            const uint4* __restrict__ hf, const float* __restrict__ hsc, int B,
+                                            int F, int r, float tau, int n_hot, uint64_t* __restrict__ mask,
+                                            float* __restrict__ logits) {
+  constexpr int NH = 2, KC = 4;                        // two fp16 planes; 4 k blocks (a quad) per chunk
+  constexpr int XV = KC * NTT * NH * 64 / NTR;
+  static_assert(XV * NTR == KC * NTT * NH * 64, "fragment share");
+  __shared__ uint4 xl[2][KC * NTT * NH * 64];          // token fragments of two chunks
+  __shared__ uint32_t bits16[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * 64 + w * 16;
+  const int rl = row0 + (lane & 15);                   // this lane's A-operand row
+  const bool live = rl < F && rl >= n_hot;             // the prefix reads no row
+  const uint32_t row = (uint32_t)(live ? rl : 0);
+  const int jq = lane >> 4;
+  const int KB = (r + 31) >> 5, KQ = (KB + 3) >> 2;
+  const int nch = (KQ + 2) / 3 * 3;                    // chunks (one quad each), padded to rounds of three
+  const Buf bx(hf, (uint32_t)KQ * 4u * NTT * NH * 1024u);   // chunks past KQ read 0
+  const Buf bw(P2, (uint32_t)F * (uint32_t)r * 2u);
+  struct Set {
+    uint4 xv[XV];
+    uint4 wv[4];
+  };
+  auto load = [&](int g, Set& S) {
+#pragma unroll
+    for (int m = 0; m < XV; ++m)
+      S.xv[m] = bx.ld16(((uint32_t)g * 4u * NTT * NH * 64 + (uint32_t)(m * NTR) + threadIdx.x) * 16u);
+    const int kb = g * 4 + jq;                         // this lane's k block of the quad
+    const bool ok = g < KQ && kb < KB && live;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {                      // elements 8 q .. 8 q + 7 of the lane's k block
+      const int k = kb * 32 + q * 8;
+      S.wv[q] = bw.ld16(boff(ok && k < r, (row * (uint32_t)r + (uint32_t)k) * 2u));
+    }
+  };
+  auto store_x = [&](const Set& S, int buf) {
+#pragma unroll
+    for (int m = 0; m < XV; ++m) xl[buf][m * NTR + threadIdx.x] = S.xv[m];
+  };
+  f32x4 az[NTT];
+#pragma unroll
+  for (int t = 0; t < NTT; ++t) az[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Set& S, int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const half8 a = __builtin_bit_cast(half8, S.wv[q]);
+#pragma unroll
+      for (int t = 0; t < NTT; ++t) {
+        const int f = (q * NTT + t) * NH;
+        const half8 xh = __builtin_bit_cast(half8, xl[buf][f * 64 + lane]);
+        const half8 xo = __builtin_bit_cast(half8, xl[buf][(f + 1) * 64 + lane]);
+        az[t] = mfma16(a, xo, mfma16(a, xh, az[t]));
+      }
+    }
+  };
+  Set S0, S1, S2;
+  load(0, S0);
+  load(1, S1);
+  store_x(S0, 0);
+  __syncthreads();
+  for (int cc = 0; cc < nch; cc += 3) {                // nch is a multiple of 3
+    load(cc + 2, S2);
+    compute(S0, cc & 1);
+    store_x(S1, (cc + 1) & 1);
+    __syncthreads();
+    load(cc + 3, S0);
+    compute(S1, (cc + 1) & 1);
+    store_x(S2, cc & 1);
+    __syncthreads();
+    load(cc + 4, S1);
+    compute(S2, cc & 1);
+    store_x(S0, (cc + 1) & 1);
+    __syncthreads();
+  }
+  // lane l holds neurons row0 + 4 (l / 16) + i of token t * 16 + l % 16
+  const Buf bc(c ? (const void*)c : (const void*)P2, c ? (uint32_t)F * 4u : 0u);   // no bias: every load is 0
+  float cb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kk = row0 + (lane >> 4) * 4 + i;
+    cb[i] = bc.ldf(boff(kk < F && kk >= n_hot, (uint32_t)kk * 4u));
+  }
+  float sx[NTT];
+#pragma unroll
+  for (int t = 0; t < NTT; ++t) {
+    const int tok = t * 16 + (lane & 15);
+    sx[t] = tok < B ? hsc[tok] : 0.f;
+  }
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kk = row0 + (lane >> 4) * 4 + i;
+    bool any = false;
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+      const int tok = t * 16 + (lane & 15);
+      const float z = kk < n_hot ? INFINITY : fmaf(az[t][i], sx[t], cb[i]);
+      const bool valid = tok < B && kk < F;
+      if (valid && logits) logits[(size_t)tok * F + kk] = z;
+      any = any || (valid && z > tau);
+    }
+    const unsigned long long bal = __ballot(any);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      if ((bal >> (16 * g)) & 0xFFFFull) word |= 1u << (g * 4 + i);
+  }
+  if (lane == 0) bits16[w] = word;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    mask[blockIdx.x] = (uint64_t)bits16[0] | ((uint64_t)bits16[1] << 16) | ((uint64_t)bits16[2] << 32) |
+                       ((uint64_t)bits16[3] << 48);
+}
+
 template <int XPT, bool EXACT>
 hipError_t launch_split_x(const float* x, int x_norm, int B, int D, int NTT, uint4* xf, float* xs, hipStream_t st) {
   hipLaunchKernelGGL((k_split_x<XPT, EXACT>), dim3(NTT * 16), dim3(NTX), 0, st, x, x_norm, B, D, NTT, xf, xs);
@@ -594,7 +715,34 @@ hipError_t ur_act(int act, bool q4, const void* Wg, const void* Sg, const float*
 #undef UR
 }
 
+template <int NTT>
+hipError_t launch_mz(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, int n_hot,
+                     uint64_t* mask, float* logits, uint4* hf, float* hs, hipStream_t st) {
+  const int xpt = (r / 4 + NTX - 1) / NTX;
+  hipError_t e;
+  if (xpt <= 1) e = launch_split_x<1, true>(h, 0, B, r, NTT, hf, hs, st);
+  else return hipErrorInvalidValue;                    // r <= 1024
+  if (e != hipSuccess) return e;
+  SFFN_LAUNCH(1, k_mz<NTT>, dim3((F + 63) / 64), dim3(NTR), 0, st, P2, c, (const uint4*)hf, hs, B, F, r, tau, n_hot,
+              mask, logits);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// Predictor stage 2 for B tokens from h [B, r] (fp32) on the matrix cores: h split into token fragments in hf
+// (sffn_ur_xf_bytes(B, r, true) bytes) with its powers of two in hs, then z, threshold and the union mask.
+hipError_t sffn_launch_predict_mz(const void* P2, const float* c, const float* h, int B, int F, int r, float tau,
+                                  int n_hot, uint64_t* mask, float* logits, void* hf, float* hs, hipStream_t st) {
+  if (r % 8 || r > 1024) return hipErrorInvalidValue;
+  switch ((B + 15) / 16) {
+    case 1: return launch_mz<1>(P2, c, h, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
+    case 2: return launch_mz<2>(P2, c, h, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
+    case 3: return launch_mz<3>(P2, c, h, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
+    case 4: return launch_mz<4>(P2, c, h, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 // Bytes of the token fragments k_split_x writes for B tokens of D values (EXACT: two planes): whole quads of k blocks.
 size_t sffn_ur_xf_bytes(int B, int D, bool exact) {
