@@ -38,21 +38,10 @@ __device__ __forceinline__ f32x4 mfma16(const half8& a, const half8& b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-constexpr int NTD = 256;             // 4 waves
-constexpr int CTD = 256;             // columns per workgroup: 16 column tiles, 4 per wave
+constexpr int NTD = 512;             // 8 waves
+constexpr int CTD = 256;             // columns per workgroup: 16 column tiles, 2 per wave
 constexpr int KSTD = 64;             // union rows per step: 2 MFMA k chunks
 constexpr int UD_PAD = 7;            // steps of ids past a share: the ring reads up to 6 steps beyond its last
-
-// 8 nibbles (one byte each, low or high half of the block's bytes) as exact fp16 (q - 8)
-__device__ __forceinline__ void nib8_half(uint32_t px, uint32_t py, uint32_t sh, half2v (&o)[4]) {
-  const uint32_t w0 = (px >> sh) & 0x0F0F0F0Fu, w1 = (py >> sh) & 0x0F0F0F0Fu;
-  const uint32_t e = 0x64646464u;   // v_perm_b32: selector 0..3 = second source's bytes, 4..7 = first source's
-  const half2v off = {(_Float16)1032.f, (_Float16)1032.f};
-  o[0] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(w0, e, 0x00050004u)) - off;
-  o[1] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(w0, e, 0x00070006u)) - off;
-  o[2] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(w1, e, 0x00050004u)) - off;
-  o[3] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(w1, e, 0x00070006u)) - off;
-}
 
 template <int NTT, bool Q4, bool EXACT>
 __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const void* __restrict__ Sd,
@@ -67,7 +56,8 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
   extern __shared__ __align__(16) int ids[];           // [(M + UD_PAD) * KSTD] ids of this share's union rows
   __shared__ uint4 Bl[2][2][16][64];                   // weight fragments [buffer][k chunk][column tile][slot]
   __shared__ uint4 Al[2][2][NTT][NHA][64];             // activation fragments [buffer][k chunk][token tile][plane]
-  __shared__ float smx[4][64];
+  __shared__ uint2 junk[NHA][NTD];                     // landing slots of the activation pieces a thread lacks
+  __shared__ float smx[NTD / 64][64];
   __shared__ float inv_s[64];                          // per token: 2^(15 - e), max |a| < 2^e over this share
   __shared__ float scl[64];                            // and its inverse 2^(e - 15)
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -86,16 +76,16 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
     const int tok = threadIdx.x & 63, sub = threadIdx.x >> 6;
     const int ne = Mn << (6 - rbs);                    // table entries (row tiles of 2^rbs rows) of this share
     float m = 0.f;
-    for (int b0 = 0; b0 < ne; b0 += 32) {
+    for (int b0 = 0; b0 < ne; b0 += 8 * (NTD / 64)) {
       float v[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int b = b0 + sub + 4 * k;
+        const int b = b0 + sub + (NTD / 64) * k;
         v[k] = bm.ldf(boff(b < ne && tok < B, ((uint32_t)(ks * ne + b) * (uint32_t)B + (uint32_t)tok) * 4u));
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int b = b0 + sub + 4 * k;
+        const int b = b0 + sub + (NTD / 64) * k;
         if (ibase + (b << rbs) < n) m = fmaxf(m, v[k]);   // row tiles past n hold stale maxima
       }
     }
@@ -118,7 +108,9 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
   __syncthreads();
   if (threadIdx.x < 64) {
     const int t = threadIdx.x;
-    const float mx = fmaxf(fmaxf(smx[0][t], smx[1][t]), fmaxf(smx[2][t], smx[3][t]));
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < NTD / 64; ++i) mx = fmaxf(mx, smx[i][t]);
     int ex = 0;
     if (mx > 0.f) (void)frexpf(mx, &ex);
     const int p = min(15 - ex, 126);
@@ -129,11 +121,13 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
   const int nst = (max(0, min(total, n - ibase)) + KSTD - 1) / KSTD;   // steps with rows
   const int nst4 = (nst + 3) / 4 * 4;                  // padded to rounds of four
 
-  // weight roles: neuron quad nq = t / 16 (neurons 4 nq .. + 3 of the step), column unit cu = t % 16: 32-column
-  // block wb = cu / 2, offset wo = 8 (cu % 2): columns 32 wb + wo + (0..7) and 32 wb + 16 + wo + (0..7), which Q4_0
-  // holds in the low and high nibbles of the same 8 bytes
-  const int nq = threadIdx.x >> 4, cu = threadIdx.x & 15;
-  const int wb = cu >> 1, wo = (cu & 1) * 8;
+  // weight roles (wave w, lane l): neuron quad nq = 2 w + l % 2 (neurons 4 nq .. + 3 of the step), column unit
+  // cu = (l / 2) % 16 and half hb = l / 32: 32-column block wb = cu / 2, offset wo = 8 (cu % 2) + 4 hb: columns
+  // 32 wb + wo + (0..3) and 32 wb + 16 + wo + (0..3), which Q4_0 holds in the low and high nibbles of the same 4
+  // bytes. A half-wave then holds both quads of a lane group at 16 distinct columns, so its fragment writes fall
+  // in distinct banks.
+  const int nq = 2 * w + (lane & 1), cu = (lane >> 1) & 15;
+  const int wb = cu >> 1, wo = (cu & 1) * 8 + (lane >> 5) * 4;
   const int kcw = nq >> 3, lgw = (nq >> 1) & 3, hfw = nq & 1;   // fragment k chunk, lane group, 8-byte half
   const uint32_t nbytes = Q4 ? (uint32_t)F * (uint32_t)(D >> 1) : (uint32_t)F * (uint32_t)D * 2u;
   const Buf bw(Wd, nbytes);
@@ -145,29 +139,43 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
   const uint32_t cb0 = Q4 ? (jb < nblk ? (uint32_t)jb * 16u + (uint32_t)wo : OOB) : (cl < D ? (uint32_t)cl * 2u : OOB);
   const uint32_t cb1 = Q4 ? 0u : (cl + 16 < D ? (uint32_t)(cl + 16) * 2u : OOB);
   const uint32_t cbs = jb < nblk ? (uint32_t)jb * 2u : OOB;
-  // activation roles: piece j (of NTT) is 16 bytes g = 256 j + t of the step's block: octet g / (2 BP), token
-  // (g / 2) % BP, half g % 2 (rows 4 (g % 2) .. + 3 of the octet)
+  // activation roles: the step's block has 256 NTT pieces of 16 bytes; piece g = NTD j + t (j < AP) is octet
+  // g / (2 BP), token (g / 2) % BP, half g % 2 (rows 4 (g % 2) .. + 3 of the octet). A thread past the last piece
+  // reads nothing (out-of-range offset) and writes its zeros to its own junk slot.
+  constexpr int AP = (256 * NTT + NTD - 1) / NTD;
   const int nr = min(((n + 63) >> 6) << 6, ((F + 63) >> 6) << 6);
   const Buf ba(abuf, (uint32_t)nr * (uint32_t)BP * 4u);   // rows past the union's last 64-row block read 0
-  uint32_t aoff[NTT];
-  float asc[NTT];
-  int aslot[NTT];                                      // Al slot offset in uint2 units within [buffer][plane 0]
+  uint32_t aoff[AP];
+  float asc[AP];
+  int aslot[AP];                                       // Al slot in uint2 units within [buffer][plane 0]; -1: none
 #pragma unroll
-  for (int j = 0; j < NTT; ++j) {
-    const int g = 256 * j + (int)threadIdx.x;
+  for (int j = 0; j < AP; ++j) {
+    const int g = NTD * j + (int)threadIdx.x;
+    const bool real = g < 256 * NTT;
     const int oc = g / (2 * BP), tk = (g >> 1) % BP, h = g & 1;
-    aoff[j] = ((uint32_t)((ibase >> 3) + oc) * (uint32_t)BP + (uint32_t)tk) * 32u + (uint32_t)h * 16u;
-    asc[j] = inv_s[tk];
+    aoff[j] = real ? ((uint32_t)((ibase >> 3) + oc) * (uint32_t)BP + (uint32_t)tk) * 32u + (uint32_t)h * 16u : OOB;
+    asc[j] = real ? inv_s[tk] : 0.f;
     const int kc = oc >> 2, lg = oc & 3;
-    aslot[j] = ((((kc * NTT + (tk >> 4)) * NHA) * 64) + (tk & 15) + 16 * lg) * 2 + h;
+    aslot[j] = real ? ((((kc * NTT + (tk >> 4)) * NHA) * 64) + (tk & 15) + 16 * lg) * 2 + h : -1;
   }
   const uint32_t astep = (uint32_t)KSTD * (uint32_t)BP * 4u;   // bytes of one step's activations
 
   struct Set {
-    uint2 q[Q4 ? 4 : 1];                               // Q4_0: 8 nibble bytes per neuron
+    uint32_t q[Q4 ? 4 : 1];                            // Q4_0: 4 nibble bytes per neuron
     uint32_t s[Q4 ? 4 : 1];                            // Q4_0: the block scale's fp16 bits
-    uint4 h[Q4 ? 1 : 4][2];                            // fp16: 8 + 8 columns per neuron
-    float4 a[NTT];
+    uint2 h[Q4 ? 1 : 4][2];                            // fp16: 4 + 4 columns per neuron
+    float4 a[AP];
+  };
+  // The set's registers are first read in stage, after the previous phase's barrier: the empty asm keeps the
+  // compiler from hoisting their conversion next to the loads, which would wait for loads issued one phase ago.
+  auto pin = [](Set& S) {
+#pragma unroll
+    for (int e = 0; e < (Q4 ? 4 : 1); ++e) asm volatile("" : "+v"(S.q[e]), "+v"(S.s[e]));
+#pragma unroll
+    for (int e = 0; e < (Q4 ? 1 : 4); ++e)
+      asm volatile("" : "+v"(S.h[e][0].x), "+v"(S.h[e][0].y), "+v"(S.h[e][1].x), "+v"(S.h[e][1].y));
+#pragma unroll
+    for (int j = 0; j < AP; ++j) asm volatile("" : "+v"(S.a[j].x), "+v"(S.a[j].y), "+v"(S.a[j].z), "+v"(S.a[j].w));
   };
   auto load = [&](int st, Set& S) {
     const int4 id4 = *reinterpret_cast<const int4*>(&ids[st * KSTD + 4 * nq]);
@@ -175,49 +183,51 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (Q4) {
-        S.q[e] = bw.ld8(id[e] * rowb + cb0);
+        S.q[e] = bw.ldu(id[e] * rowb + cb0);
         S.s[e] = bs.ldu16(id[e] * (uint32_t)nblk * 2u + cbs);
       } else {
-        S.h[e][0] = bw.ld16(id[e] * rowb + cb0);
-        S.h[e][1] = bw.ld16(id[e] * rowb + cb1);
+        S.h[e][0] = bw.ld8(id[e] * rowb + cb0);
+        S.h[e][1] = bw.ld8(id[e] * rowb + cb1);
       }
     }
     const uint32_t ast = st < nst ? (uint32_t)st * astep : OOB;   // steps past the share's rows read zeros
 #pragma unroll
-    for (int j = 0; j < NTT; ++j) S.a[j] = ba.ldf4(aoff[j] + ast);
+    for (int j = 0; j < AP; ++j) S.a[j] = ba.ldf4(aoff[j] + ast);
   };
   // fragment slots: a column tile's 64 slots hold (lane group g, column c) at 16 g + (c ^ (tile / 2 % 8)), so
-  // the staging writes of a half-wave (16 columns x 2 halves) fall in distinct banks; a 16-lane read stays a
-  // permutation of one 256-byte row
-  auto stage = [&](const Set& S, int buf) {
-    half2v lo[4][4], hi[4][4];                         // [neuron][column pair]: columns wo.., 16 + wo..
+  // a 16-lane read stays a permutation of one 256-byte row
+  auto stage = [&](Set& S, int buf) {
+    pin(S);
+    half2v lo[4][2], hi[4][2];                         // [neuron][column pair]: columns wo.., 16 + wo..
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (Q4) {
-        nib8_half(S.q[e].x, S.q[e].y, 0u, lo[e]);
-        nib8_half(S.q[e].x, S.q[e].y, 4u, hi[e]);
+        const uint32_t l4 = S.q[e] & 0x0F0F0F0Fu, h4 = (S.q[e] >> 4) & 0x0F0F0F0Fu;
+        const uint32_t ex = 0x64646464u;               // v_perm_b32 pool: 0..3 second source, 4..7 first
+        const half2v off = {(_Float16)1032.f, (_Float16)1032.f};
         const half2v s2 = __builtin_bit_cast(half2v, S.s[e] * 0x10001u);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) { lo[e][p] = lo[e][p] * s2; hi[e][p] = hi[e][p] * s2; }
+        lo[e][0] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(l4, ex, 0x00050004u)) - off) * s2;
+        lo[e][1] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(l4, ex, 0x00070006u)) - off) * s2;
+        hi[e][0] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(h4, ex, 0x00050004u)) - off) * s2;
+        hi[e][1] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(h4, ex, 0x00070006u)) - off) * s2;
       } else {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < 2; ++p) {
           lo[e][p] = __builtin_bit_cast(half2v, (&S.h[e][0].x)[p]);
           hi[e][p] = __builtin_bit_cast(half2v, (&S.h[e][1].x)[p]);
         }
       }
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < 4; ++c) {
       const int ln = 16 * lgw + ((wo + c) ^ wb);
       const half4 vlo = {lo[0][c >> 1][c & 1], lo[1][c >> 1][c & 1], lo[2][c >> 1][c & 1], lo[3][c >> 1][c & 1]};
       const half4 vhi = {hi[0][c >> 1][c & 1], hi[1][c >> 1][c & 1], hi[2][c >> 1][c & 1], hi[3][c >> 1][c & 1]};
       reinterpret_cast<uint2*>(&Bl[buf][kcw][2 * wb][ln])[hfw] = __builtin_bit_cast(uint2, vlo);
       reinterpret_cast<uint2*>(&Bl[buf][kcw][2 * wb + 1][ln])[hfw] = __builtin_bit_cast(uint2, vhi);
     }
-    uint2* al = reinterpret_cast<uint2*>(&Al[buf][0][0][0][0]);
 #pragma unroll
-    for (int j = 0; j < NTT; ++j) {
+    for (int j = 0; j < AP; ++j) {
       const float v[4] = {S.a[j].x * asc[j], S.a[j].y * asc[j], S.a[j].z * asc[j], S.a[j].w * asc[j]};
       half4 vh, vl;
 #pragma unroll
@@ -225,33 +235,40 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
         vh[e] = (_Float16)v[e];
         vl[e] = (_Float16)(v[e] - (float)vh[e]);
       }
-      al[aslot[j]] = __builtin_bit_cast(uint2, vh);
-      if (EXACT) al[aslot[j] + 128] = __builtin_bit_cast(uint2, vl);   // the lo plane: 64 slots further
+      const bool real = 256 * NTT % NTD == 0 || aslot[j] >= 0;
+      uint2* al = reinterpret_cast<uint2*>(&Al[buf][0][0][0][0]);
+      uint2* dh = real ? &al[aslot[j]] : &junk[0][threadIdx.x];
+      *dh = __builtin_bit_cast(uint2, vh);
+      if (EXACT) {
+        uint2* dl = real ? &al[aslot[j] + 128] : &junk[NHA - 1][threadIdx.x];   // the lo plane: 64 slots further
+        *dl = __builtin_bit_cast(uint2, vl);
+      }
     }
   };
-  f32x4 acc[NTT][4];
+  constexpr int CPW = 16 / (NTD / 64);                 // column tiles per wave
+  f32x4 acc[NTT][CPW];
 #pragma unroll
   for (int t = 0; t < NTT; ++t)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CPW; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int buf) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      half8 bop[4];
+      half8 bop[CPW];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int tile = 4 * w + c;
+      for (int c = 0; c < CPW; ++c) {
+        const int tile = CPW * w + c;
         bop[c] = __builtin_bit_cast(half8, Bl[buf][kc][tile][(lane & 48) | ((lane & 15) ^ ((tile >> 1) & 7))]);
       }
 #pragma unroll
       for (int t = 0; t < NTT; ++t) {
         const half8 ah = __builtin_bit_cast(half8, Al[buf][kc][t][0][lane]);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[t][c] = mfma16(ah, bop[c], acc[t][c]);
+        for (int c = 0; c < CPW; ++c) acc[t][c] = mfma16(ah, bop[c], acc[t][c]);
         if constexpr (EXACT) {
           const half8 al = __builtin_bit_cast(half8, Al[buf][kc][t][NHA - 1][lane]);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) acc[t][c] = mfma16(al, bop[c], acc[t][c]);
+          for (int c = 0; c < CPW; ++c) acc[t][c] = mfma16(al, bop[c], acc[t][c]);
         }
       }
     }
@@ -282,7 +299,7 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
     __syncthreads();
   }
   // partial sums with the tokens' powers of two undone: lane l holds tokens 4 (l / 16) + i of column l % 16 of
-  // column tile 4 w + c
+  // column tile CPW w + c
 #pragma unroll
   for (int t = 0; t < NTT; ++t)
 #pragma unroll
@@ -291,8 +308,8 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
       if (tok >= B) continue;
       const float sc = scl[tok];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int col = c0 + 64 * w + 16 * c + (lane & 15);
+      for (int c = 0; c < CPW; ++c) {
+        const int col = c0 + 16 * CPW * w + 16 * c + (lane & 15);
         if (col < D) part[((size_t)ks * B + tok) * D + col] = acc[t][c][i] * sc;
       }
     }
