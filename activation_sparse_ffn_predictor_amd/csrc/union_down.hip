@@ -10,14 +10,15 @@
 // one token) is then 32 contiguous bytes, and a step's 64 rows x BP tokens one contiguous block.
 // The weights are stored neuron-major (a neuron's row runs along D) while a B-operand lane needs 8 neurons at one
 // column, so every tile is transposed once on its way through LDS.
-// k_ud (workgroups of 4 waves, 256 columns x every token tile, KS workgroups over the union rows, split by the
+// k_ud (workgroups of 4 or 8 waves, 256 columns x every token tile, KS workgroups over the union rows, split by the
 // device-side union size): the workgroup stages the ids of its share of union rows in LDS, then walks them in steps
-// of 64. Per step each thread loads a 4-neuron x 16-column piece of W_downT (Q4_0: 8 nibble bytes and the block
-// scale per neuron; fp16: two 16-byte loads per neuron) and NTT 16-byte pieces of the activations, and writes them,
-// converted to fp16, as operand fragments into LDS (8 bytes per column and 4 neurons; 8 bytes per token and 4 rows).
-// Loads run three steps ahead of the matrix-core work in four register sets, with no branch in the loop: rows past
-// the union and steps past the share read neuron 0's weights against zero activations. The fragment
-// buffers are double-buffered with one barrier per step. Each wave multiplies its 64 columns by every token tile.
+// of 64. Per step each thread loads a piece of W_downT of 4 neurons x 16 (4 waves) or 8 (8 waves) columns (Q4_0:
+// 8 or 4 nibble bytes and the block scale per neuron; fp16: two 16- or 8-byte loads per neuron) and its share of
+// 16-byte pieces of the activations, and writes them, converted to fp16, as operand fragments into LDS (8 bytes
+// per column and 4 neurons; 8 bytes per token and 4 rows). Loads run three steps ahead of the matrix-core work in four register sets, with no branch in the loop:
+// rows past the union and steps past the share read neuron 0's weights against zero activations. The fragment
+// buffers are double-buffered with one barrier per step. Each wave multiplies its 64 or 32 columns by every token
+// tile; with 8 waves two share a SIMD, so one's LDS and barrier waits overlap the other's matrix-core work.
 // Activations enter multiplied by a per-token power of two 2^(15 - e), with 2^e above their largest magnitude over
 // the workgroup's share of rows (from the per-64-row maxima the row kernels write), so every value lies inside
 // fp16's range with its full precision; the partial sums are scaled back before they are written. Q4_0 weights
@@ -38,19 +39,21 @@ __device__ __forceinline__ f32x4 mfma16(const half8& a, const half8& b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-constexpr int NTD = 512;             // 8 waves
-constexpr int CTD = 256;             // columns per workgroup: 16 column tiles, 2 per wave
+constexpr int CTD = 256;             // columns per workgroup: 16 column tiles
 constexpr int KSTD = 64;             // union rows per step: 2 MFMA k chunks
 constexpr int UD_PAD = 7;            // steps of ids past a share: the ring reads up to 6 steps beyond its last
 
-template <int NTT, bool Q4, bool EXACT>
-__global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const void* __restrict__ Sd,
+template <int NW, int NTT, bool Q4, bool EXACT>
+__global__ __launch_bounds__(64 * NW) void k_ud(const void* __restrict__ Wd, const void* __restrict__ Sd,
                                             const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
                                             const float* __restrict__ abuf, const float* __restrict__ bmax,
                                             int rbs, int B, int D, int F, int M, float* __restrict__ part) {
   // M: the most 64-row steps one share can hold (sizes the ids in LDS, with UD_PAD steps of padding); bmax holds
   // the largest |a| per token of every row tile of 2^rbs rows (rbs = 4 or 6)
   static_assert(!(Q4 && EXACT), "Q4_0 weights take fp16 activations");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int NTD = 64 * NW;
+  constexpr int CW = 32 / NW;                          // columns per staging unit and half block
   constexpr int NHA = EXACT ? 2 : 1;                   // activation planes (hi, lo)
   constexpr int BP = NTT * 16;                         // token stride of the activations
   extern __shared__ __align__(16) int ids[];           // [(M + UD_PAD) * KSTD] ids of this share's union rows
@@ -121,13 +124,15 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
   const int nst = (max(0, min(total, n - ibase)) + KSTD - 1) / KSTD;   // steps with rows
   const int nst4 = (nst + 3) / 4 * 4;                  // padded to rounds of four
 
-  // weight roles (wave w, lane l): neuron quad nq = 2 w + l % 2 (neurons 4 nq .. + 3 of the step), column unit
-  // cu = (l / 2) % 16 and half hb = l / 32: 32-column block wb = cu / 2, offset wo = 8 (cu % 2) + 4 hb: columns
-  // 32 wb + wo + (0..3) and 32 wb + 16 + wo + (0..3), which Q4_0 holds in the low and high nibbles of the same 4
-  // bytes. A half-wave then holds both quads of a lane group at 16 distinct columns, so its fragment writes fall
-  // in distinct banks.
-  const int nq = 2 * w + (lane & 1), cu = (lane >> 1) & 15;
-  const int wb = cu >> 1, wo = (cu & 1) * 8 + (lane >> 5) * 4;
+  // weight roles: a thread stages 4 neurons (quad nq: neurons 4 nq .. + 3 of the step) at CW columns: column
+  // unit cu, 32-column block wb = cu / 2, offset wo: columns 32 wb + wo + (0..CW-1) and 32 wb + 16 + wo + (0..CW-1),
+  // which Q4_0 holds in the low and high nibbles of the same CW bytes. 4 waves: nq = t / 16, cu = t % 16,
+  // wo = 8 (cu % 2). 8 waves (wave w, lane l): nq = 2 w + l % 2, cu = (l / 2) % 16, wo = 8 (cu % 2) + 4 (l / 32).
+  // Either way a half-wave holds both quads of a lane group at 16 distinct columns, so its fragment writes fall in
+  // distinct banks.
+  const int nq = NW == 4 ? (int)threadIdx.x >> 4 : 2 * w + (lane & 1);
+  const int cu = NW == 4 ? lane & 15 : (lane >> 1) & 15;
+  const int wb = cu >> 1, wo = (cu & 1) * 8 + (NW == 4 ? 0 : (lane >> 5) * 4);
   const int kcw = nq >> 3, lgw = (nq >> 1) & 3, hfw = nq & 1;   // fragment k chunk, lane group, 8-byte half
   const uint32_t nbytes = Q4 ? (uint32_t)F * (uint32_t)(D >> 1) : (uint32_t)F * (uint32_t)D * 2u;
   const Buf bw(Wd, nbytes);
@@ -160,20 +165,27 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
   }
   const uint32_t astep = (uint32_t)KSTD * (uint32_t)BP * 4u;   // bytes of one step's activations
 
+  constexpr int QW = CW / 4;                           // Q4_0: 32-bit words of nibble bytes per neuron
+  constexpr int HW = CW / 2;                           // fp16: 32-bit words per neuron and half block
   struct Set {
-    uint32_t q[Q4 ? 4 : 1];                            // Q4_0: 4 nibble bytes per neuron
+    uint32_t q[Q4 ? 4 : 1][QW];                        // Q4_0: CW nibble bytes per neuron
     uint32_t s[Q4 ? 4 : 1];                            // Q4_0: the block scale's fp16 bits
-    uint2 h[Q4 ? 1 : 4][2];                            // fp16: 4 + 4 columns per neuron
+    uint32_t h[Q4 ? 1 : 4][2][HW];                     // fp16: CW + CW columns per neuron
     float4 a[AP];
   };
   // The set's registers are first read in stage, after the previous phase's barrier: the empty asm keeps the
   // compiler from hoisting their conversion next to the loads, which would wait for loads issued one phase ago.
   auto pin = [](Set& S) {
 #pragma unroll
-    for (int e = 0; e < (Q4 ? 4 : 1); ++e) asm volatile("" : "+v"(S.q[e]), "+v"(S.s[e]));
+    for (int e = 0; e < (Q4 ? 4 : 1); ++e) {
+      asm volatile("" : "+v"(S.s[e]));
+#pragma unroll
+      for (int k = 0; k < QW; ++k) asm volatile("" : "+v"(S.q[e][k]));
+    }
 #pragma unroll
     for (int e = 0; e < (Q4 ? 1 : 4); ++e)
-      asm volatile("" : "+v"(S.h[e][0].x), "+v"(S.h[e][0].y), "+v"(S.h[e][1].x), "+v"(S.h[e][1].y));
+#pragma unroll
+      for (int k = 0; k < HW; ++k) asm volatile("" : "+v"(S.h[e][0][k]), "+v"(S.h[e][1][k]));
 #pragma unroll
     for (int j = 0; j < AP; ++j) asm volatile("" : "+v"(S.a[j].x), "+v"(S.a[j].y), "+v"(S.a[j].z), "+v"(S.a[j].w));
   };
@@ -183,11 +195,26 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (Q4) {
-        S.q[e] = bw.ldu(id[e] * rowb + cb0);
+        if constexpr (QW == 2) {
+          const uint2 v = bw.ld8(id[e] * rowb + cb0);
+          S.q[e][0] = v.x;
+          S.q[e][QW - 1] = v.y;
+        } else {
+          S.q[e][0] = bw.ldu(id[e] * rowb + cb0);
+        }
         S.s[e] = bs.ldu16(id[e] * (uint32_t)nblk * 2u + cbs);
       } else {
-        S.h[e][0] = bw.ld8(id[e] * rowb + cb0);
-        S.h[e][1] = bw.ld8(id[e] * rowb + cb1);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t o = id[e] * rowb + (hh ? cb1 : cb0);
+          if constexpr (HW == 4) {
+            const uint4 v = bw.ld16(o);
+            S.h[e][hh][0] = v.x; S.h[e][hh][1] = v.y; S.h[e][hh][HW - 2] = v.z; S.h[e][hh][HW - 1] = v.w;
+          } else {
+            const uint2 v = bw.ld8(o);
+            S.h[e][hh][0] = v.x; S.h[e][hh][HW - 1] = v.y;
+          }
+        }
       }
     }
     const uint32_t ast = st < nst ? (uint32_t)st * astep : OOB;   // steps past the share's rows read zeros
@@ -198,28 +225,31 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
   // a 16-lane read stays a permutation of one 256-byte row
   auto stage = [&](Set& S, int buf) {
     pin(S);
-    half2v lo[4][2], hi[4][2];                         // [neuron][column pair]: columns wo.., 16 + wo..
+    half2v lo[4][HW], hi[4][HW];                       // [neuron][column pair]: columns wo.., 16 + wo..
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (Q4) {
-        const uint32_t l4 = S.q[e] & 0x0F0F0F0Fu, h4 = (S.q[e] >> 4) & 0x0F0F0F0Fu;
         const uint32_t ex = 0x64646464u;               // v_perm_b32 pool: 0..3 second source, 4..7 first
         const half2v off = {(_Float16)1032.f, (_Float16)1032.f};
         const half2v s2 = __builtin_bit_cast(half2v, S.s[e] * 0x10001u);
-        lo[e][0] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(l4, ex, 0x00050004u)) - off) * s2;
-        lo[e][1] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(l4, ex, 0x00070006u)) - off) * s2;
-        hi[e][0] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(h4, ex, 0x00050004u)) - off) * s2;
-        hi[e][1] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(h4, ex, 0x00070006u)) - off) * s2;
+#pragma unroll
+        for (int k = 0; k < QW; ++k) {
+          const uint32_t l4 = S.q[e][k] & 0x0F0F0F0Fu, h4 = (S.q[e][k] >> 4) & 0x0F0F0F0Fu;
+          lo[e][2 * k] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(l4, ex, 0x00050004u)) - off) * s2;
+          lo[e][2 * k + 1] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(l4, ex, 0x00070006u)) - off) * s2;
+          hi[e][2 * k] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(h4, ex, 0x00050004u)) - off) * s2;
+          hi[e][2 * k + 1] = (__builtin_bit_cast(half2v, __builtin_amdgcn_perm(h4, ex, 0x00070006u)) - off) * s2;
+        }
       } else {
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          lo[e][p] = __builtin_bit_cast(half2v, (&S.h[e][0].x)[p]);
-          hi[e][p] = __builtin_bit_cast(half2v, (&S.h[e][1].x)[p]);
+        for (int p = 0; p < HW; ++p) {
+          lo[e][p] = __builtin_bit_cast(half2v, S.h[e][0][p]);
+          hi[e][p] = __builtin_bit_cast(half2v, S.h[e][1][p]);
         }
       }
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < CW; ++c) {
       const int ln = 16 * lgw + ((wo + c) ^ wb);
       const half4 vlo = {lo[0][c >> 1][c & 1], lo[1][c >> 1][c & 1], lo[2][c >> 1][c & 1], lo[3][c >> 1][c & 1]};
       const half4 vhi = {hi[0][c >> 1][c & 1], hi[1][c >> 1][c & 1], hi[2][c >> 1][c & 1], hi[3][c >> 1][c & 1]};
@@ -245,7 +275,7 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
       }
     }
   };
-  constexpr int CPW = 16 / (NTD / 64);                 // column tiles per wave
+  constexpr int CPW = 16 / NW;                         // column tiles per wave
   f32x4 acc[NTT][CPW];
 #pragma unroll
   for (int t = 0; t < NTT; ++t)
@@ -315,7 +345,7 @@ __global__ __launch_bounds__(NTD) void k_ud(const void* __restrict__ Wd, const v
     }
 }
 
-template <int NTT, bool Q4, bool EXACT>
+template <int NW, int NTT, bool Q4, bool EXACT>
 hipError_t launch_ud(const void* Wd, const void* Sd, const int32_t* active, const int32_t* n_active,
                      const float* abuf, const float* bmax, int rbs, int B, int D, int F, float* part, int KS, float* y,
                      hipStream_t st) {
@@ -323,23 +353,27 @@ hipError_t launch_ud(const void* Wd, const void* Sd, const int32_t* active, cons
   const size_t lds = (size_t)(M + UD_PAD) * KSTD * sizeof(int);
   static LdsLimit lds_limit;   // per kernel, set once per device
   size_t avail = 0;
-  hipError_t ea = lds_limit.get((const void*)k_ud<NTT, Q4, EXACT>, &avail);
+  hipError_t ea = lds_limit.get((const void*)k_ud<NW, NTT, Q4, EXACT>, &avail);
   if (ea != hipSuccess) return ea;
   if (lds > avail) return hipErrorInvalidValue;
-  SFFN_LAUNCH(3, (k_ud<NTT, Q4, EXACT>), dim3((D + CTD - 1) / CTD, KS), dim3(NTD), lds, st, Wd, Sd, active, n_active,
+  SFFN_LAUNCH(3, (k_ud<NW, NTT, Q4, EXACT>), dim3((D + CTD - 1) / CTD, KS), dim3(64 * NW), lds, st, Wd, Sd, active, n_active,
               abuf, bmax, rbs, B, D, F, M, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return sffn_launch_sum_parts(part, KS, B * D, y, st);
 }
 
+// Waves per k_ud workgroup by token tiles. Measured at the 13B shape: 64 tokens 74 -> 57 us per layer with 8 waves,
+// 32 tokens 36.4 -> 34.4 us; at 4 to 16 tokens (one tile) 8 waves are slower (8 tokens 18.9 -> 23.3 us).
+constexpr int ud_waves(int ntt) { return ntt >= 2 ? 8 : 4; }
+
 template <int NTT>
 hipError_t ud_q(bool q4, bool exact, const void* Wd, const void* Sd, const int32_t* active, const int32_t* n_active,
                 const float* abuf, const float* bmax, int rbs, int B, int D, int F, float* part, int KS, float* y,
                 hipStream_t st) {
-  if (q4) return launch_ud<NTT, true, false>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
-  if (exact) return launch_ud<NTT, false, true>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
-  return launch_ud<NTT, false, false>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
+  if (q4) return launch_ud<ud_waves(NTT), NTT, true, false>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
+  if (exact) return launch_ud<ud_waves(NTT), NTT, false, true>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
+  return launch_ud<ud_waves(NTT), NTT, false, false>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
 }
 
 }  // namespace

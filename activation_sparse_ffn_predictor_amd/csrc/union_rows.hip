@@ -18,18 +18,19 @@
 // bytes, so a wave reads one as a contiguous kilobyte. EXACT adds a plane of fp16 residuals (x = hi + lo, the
 // single-token kernels' fp32 to within 2^-22); without it the operand is fp16(x).
 //
-// k_ur (workgroups of 4 waves, 64 dense indices each, one 16-row tile per wave, every token tile; KS workgroups
-// per 64 rows split the quads): the workgroup's union rows come from the mask (block scan of the words' popcounts,
-// then a search per row). Quads are walked in chunks; per chunk each thread loads a share of the chunk's token
-// fragments (into registers, then LDS, double-buffered: all four waves read them) and its row's k blocks of
-// weights (Q4_0 nibbles and block scales, or fp16); loads run two chunks ahead of the matrix-core work in a ring
-// of three register sets. The chunk count is padded to a multiple of three (the padding reads nothing:
+// k_ur (workgroups of 4 or 8 waves, 64 dense indices each, one 16-row tile per wave and, with 8 waves, one k half
+// of every chunk per wave; every token tile; KS workgroups per 64 rows split the quads): the workgroup's union rows
+// come from the mask (block scan of the words' popcounts, then a search per row). Quads are walked in chunks; per
+// chunk each thread loads a share of the next chunk's token fragments (into registers, then LDS, double-buffered:
+// all waves read them) and its row's k blocks of weights two chunks ahead (Q4_0 nibbles and block scales, or fp16)
+// in a ring of three register sets. The chunk count is padded to a multiple of three (the padding reads nothing:
 // out-of-range buffer loads return 0). Q4_0 weights become exact fp16 (q - 8) through the exponent trick (0x64qq
 // is 1024 + q in fp16), times the block scale in fp16 (one rounding per weight; the whole block's scale is one
 // lane's, so no per-block fp32 step is needed). fp16 weights enter as they are; with EXACT each token operand is
-// two fp16 halves and every product is exact. The epilogue undoes the token's power of two and, with one
-// share, adds the bias and applies the activation; with KS shares each writes its partial pre-activations and
-// k_act_combine (union.hip) adds them in share order.
+// two fp16 halves and every product is exact. With two k halves the second half's sums meet the first's in LDS,
+// always added in that order. The epilogue undoes the token's power of two and, with one share, adds the bias and
+// applies the activation; with KS shares each writes its partial pre-activations and k_act_combine (union.hip)
+// adds them in share order.
 #include "common.h"
 
 using namespace sffn;
@@ -148,8 +149,9 @@ constexpr int WMAXR = 2;             // mask words per thread kept in LDS (F <= 
 // k blocks per chunk: 8 for Q4_0 (two quads: 32 bytes of a row per lane and matrix), 4 for fp16 (a quad: 64 bytes)
 template <bool Q4> struct URChunk { static constexpr int KC = Q4 ? 8 : 4; };
 
-template <int NTT, int ACT, bool Q4, bool EXACT>
-__global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
+// k_ur: NW = 4 or 8 waves; wave w takes row tile w % 4 and, with 8 waves, k half w / 4 of every chunk
+template <int NW, int NTT, int ACT, bool Q4, bool EXACT>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2))) void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
                                             const float* __restrict__ bg, const void* __restrict__ Wu,
                                             const void* __restrict__ Su, const float* __restrict__ bu,
                                             const uint4* __restrict__ xf, const float* __restrict__ xsc, int B,
@@ -158,22 +160,31 @@ __global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const v
                                             float* __restrict__ abuf, float* __restrict__ bmax,
                                             float* __restrict__ pre, int KS) {
   static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int NTU = 64 * NW;
+  constexpr int KH = NW / 4;                           // k halves
   constexpr bool GT = ACT == 1;                        // ReGLU: a gate row per neuron
   constexpr int NH = EXACT ? 2 : 1;                    // token fragment planes (hi, lo)
   constexpr int KC = URChunk<Q4>::KC;
   constexpr int QC = KC / 4;                           // quads per chunk
-  constexpr int XV = KC * NTT * NH * 64 / NTR;         // uint4 of token fragments per thread per chunk
-  static_assert(XV * NTR == KC * NTT * NH * 64, "fragment share");
-  constexpr int WV = Q4 ? QC : 4 * QC;                 // uint4 of weights per lane and matrix per chunk
-  __shared__ uint64_t wl[WMAXR * NTR];                 // mask words
-  __shared__ int roff[NTR];
-  __shared__ int tmp[NTR / 64 + 4];
+  constexpr int XT = KC * NTT * NH * 64;               // uint4 of token fragments per chunk
+  constexpr int XV = (XT + NTU - 1) / NTU;             // per thread
+  // a wave's part of a chunk: Q4_0 GQW of the chunk's two quads (per quad a lane's whole k block, one 16-byte
+  // load), fp16 QW of the quad's four 8-element groups
+  constexpr int GQW = Q4 ? QC / KH : 1;
+  constexpr int QW = Q4 ? 4 : 4 / KH;
+  constexpr int WV = Q4 ? GQW : QW;                    // uint4 of weights per lane and matrix per chunk
+  __shared__ uint64_t wl[WMAXR * NTU];                 // mask words
+  __shared__ int roff[NTU];
+  __shared__ int tmp[NTU / 64 + 4];
   __shared__ int ids[RTB];
-  __shared__ uint4 xl[2][KC * NTT * NH * 64];          // token fragments of two chunks
+  __shared__ uint4 xl[2][XT];                          // token fragments of two chunks
+  __shared__ uint4 xjunk[XT % NTU ? NTU : 1];          // landing slots of the fragment pieces a thread lacks
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rt = w & 3, kh = w >> 2;                   // row tile, k half
   const int nw = (F + 63) >> 6;
-  const int wpt = (nw + NTR - 1) / NTR;
-  const int n = mask_prefix<NTR, WMAXR>(mask, nw, F, wpt, wl, roff, tmp);
+  const int wpt = (nw + NTU - 1) / NTU;
+  const int n = mask_prefix<NTU, WMAXR>(mask, nw, F, wpt, wl, roff, tmp);
   if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
   const int ks = blockIdx.x % KS;                      // the shares of 64 rows are neighbours in dispatch order
   const int i0 = (blockIdx.x / KS) * RTB;
@@ -182,7 +193,7 @@ __global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const v
     const int i = i0 + threadIdx.x;
     int id = -1;
     if (i < n) {                                       // the (i - roff)-th set bit after word range T * wpt
-      int lo = 0, hi = NTR - 1;
+      int lo = 0, hi = NTU - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (roff[mid] <= i) lo = mid; else hi = mid - 1;
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const v
     ids[threadIdx.x] = id;
   }
   __syncthreads();
-  const int idl = ids[w * 16 + (lane & 15)];           // this lane's A-operand row (-1: none)
+  const int idl = ids[rt * 16 + (lane & 15)];          // this lane's A-operand row (-1: none)
   const int jq = lane >> 4;                            // lane group: the k block of a quad this lane holds
   const int KB = (D + 31) >> 5, nblk = D >> 5;
   const int KQ = (KB + 3) >> 2;                        // quads
@@ -211,149 +222,188 @@ __global__ __launch_bounds__(NTR) void k_ur(const void* __restrict__ Wg, const v
   const Buf bwu(Wu, wbytes), bwg(GT ? Wg : Wu, GT ? wbytes : 0u);
   const Buf bsu(Q4 ? Su : Wu, sbytes), bsg(Q4 && GT ? Sg : Wu, GT ? sbytes : 0u);
   const uint32_t row = (uint32_t)(idl >= 0 ? idl : 0);
+  const int gqh = Q4 ? kh * GQW : 0;                   // the wave's first quad within the chunk
+  const int qh = Q4 ? 0 : kh * QW;                     // fp16: the wave's first 8-element group
 
   struct Set {
-    uint4 xv[XV];
     uint4 wu[WV], wg[WV];
-    uint32_t su[Q4 ? QC : 1], sg[Q4 ? QC : 1];         // block scales' fp16 bits (32-bit: kept in registers)
+    uint32_t su[GQW], sg[GQW];                         // block scales' fp16 bits (32-bit: kept in registers)
   };
-  auto load = [&](int c, Set& S) {
+  uint4 xv[XV];                                        // this thread's share of the next chunk's token fragments
+  auto load_x = [&](int c) {
     const int g0 = q0 + c * QC;                        // first quad of the chunk
 #pragma unroll
-    for (int m = 0; m < XV; ++m)
-      S.xv[m] = bx.ld16(((uint32_t)g0 * 4u * NTT * NH * 64 + (uint32_t)(m * NTR) + threadIdx.x) * 16u);
-#pragma unroll
-    for (int gq = 0; gq < QC; ++gq) {
-      const int kb = (g0 + gq) * 4 + jq;               // this lane's k block of the quad
-      const bool ok = g0 + gq < q1 && kb < KB && idl >= 0;
-      if constexpr (Q4) {
-        const uint32_t o = row * (uint32_t)(D >> 1) + (uint32_t)kb * 16u;
-        S.wu[gq] = bwu.ld16(boff(ok, o));
-        if (GT) S.wg[gq] = bwg.ld16(boff(ok, o));
-        const uint32_t so = (row * nblk + kb) * 2u;
-        S.su[gq] = bsu.ldu16(boff(ok, so));
-        if (GT) S.sg[gq] = bsg.ldu16(boff(ok, so));
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {                  // elements 8 q .. 8 q + 7 of the lane's k block
-          const int k = kb * 32 + q * 8;
-          const uint32_t o = (row * (uint32_t)D + (uint32_t)k) * 2u;
-          S.wu[gq * 4 + q] = bwu.ld16(boff(ok && k < D, o));
-          if (GT) S.wg[gq * 4 + q] = bwg.ld16(boff(ok && k < D, o));
-        }
-      }
+    for (int m = 0; m < XV; ++m) {
+      const int p = m * NTU + (int)threadIdx.x;
+      xv[m] = bx.ld16(boff(XT % NTU == 0 || p < XT, ((uint32_t)g0 * 4u * NTT * NH * 64 + (uint32_t)p) * 16u));
     }
   };
-  auto store_x = [&](const Set& S, int buf) {
+  auto load_w = [&](int c, Set& S) {
 #pragma unroll
-    for (int m = 0; m < XV; ++m) xl[buf][m * NTR + threadIdx.x] = S.xv[m];
+    for (int i = 0; i < GQW; ++i) {
+    const int g = q0 + c * QC + gqh + i;
+    const int kb = g * 4 + jq;                         // this lane's k block of the quad
+    const bool ok = g < q1 && kb < KB && idl >= 0;
+    if constexpr (Q4) {
+      const uint32_t o = row * (uint32_t)(D >> 1) + (uint32_t)kb * 16u;
+      S.wu[i] = bwu.ld16(boff(ok, o));
+      if (GT) S.wg[i] = bwg.ld16(boff(ok, o));
+      const uint32_t so = (row * nblk + kb) * 2u;
+      S.su[i] = bsu.ldu16(boff(ok, so));
+      if (GT) S.sg[i] = bsg.ldu16(boff(ok, so));
+    } else {
+#pragma unroll
+      for (int j = 0; j < WV; ++j) {                   // elements 8 q .. 8 q + 7 of the lane's k block
+        const int k = kb * 32 + (qh + j) * 8;
+        const uint32_t o = (row * (uint32_t)D + (uint32_t)k) * 2u;
+        S.wu[j] = bwu.ld16(boff(ok && k < D, o));
+        if (GT) S.wg[j] = bwg.ld16(boff(ok && k < D, o));
+      }
+    }
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < XV; ++m) {
+      const int p = m * NTU + (int)threadIdx.x;
+      uint4* d = (XT % NTU == 0 || p < XT) ? &xl[buf][p] : &xjunk[threadIdx.x];
+      *d = xv[m];
+    }
   };
   f32x4 au[NTT], ag[NTT];
 #pragma unroll
   for (int t = 0; t < NTT; ++t) { au[t] = f32x4{0.f, 0.f, 0.f, 0.f}; ag[t] = au[t]; }
   auto compute = [&](const Set& S, int buf) {
 #pragma unroll
-    for (int gq = 0; gq < QC; ++gq) {
+    for (int i = 0; i < GQW; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        half8 a_u, a_g;
-        if constexpr (Q4) {                            // fp16((q - 8) s): one rounding per weight
-          a_u = q4_half8(S.wu[gq], q) * splat8(S.su[gq]);
-          if (GT) a_g = q4_half8(S.wg[gq], q) * splat8(S.sg[gq]);
+    for (int j = 0; j < QW; ++j) {
+      const int q = qh + j;
+      half8 a_u, a_g;
+      if constexpr (Q4) {                              // fp16((q - 8) s): one rounding per weight
+        a_u = q4_half8(S.wu[i], q) * splat8(S.su[i]);
+        if (GT) a_g = q4_half8(S.wg[i], q) * splat8(S.sg[i]);
+      } else {
+        a_u = __builtin_bit_cast(half8, S.wu[j]);
+        if (GT) a_g = __builtin_bit_cast(half8, S.wg[j]);
+      }
+#pragma unroll
+      for (int t = 0; t < NTT; ++t) {
+        const int f = (((gqh + i) * 4 + q) * NTT + t) * NH;
+        const half8 xh = __builtin_bit_cast(half8, xl[buf][f * 64 + lane]);
+        if constexpr (EXACT) {
+          const half8 xo = __builtin_bit_cast(half8, xl[buf][(f + 1) * 64 + lane]);
+          au[t] = mfma16(a_u, xo, mfma16(a_u, xh, au[t]));
+          if (GT) ag[t] = mfma16(a_g, xo, mfma16(a_g, xh, ag[t]));
         } else {
-          a_u = __builtin_bit_cast(half8, S.wu[gq * 4 + q]);
-          if (GT) a_g = __builtin_bit_cast(half8, S.wg[gq * 4 + q]);
-        }
-#pragma unroll
-        for (int t = 0; t < NTT; ++t) {
-          const int f = ((gq * 4 + q) * NTT + t) * NH;
-          const half8 xh = __builtin_bit_cast(half8, xl[buf][f * 64 + lane]);
-          if constexpr (EXACT) {
-            const half8 xo = __builtin_bit_cast(half8, xl[buf][(f + 1) * 64 + lane]);
-            au[t] = mfma16(a_u, xo, mfma16(a_u, xh, au[t]));
-            if (GT) ag[t] = mfma16(a_g, xo, mfma16(a_g, xh, ag[t]));
-          } else {
-            au[t] = mfma16(a_u, xh, au[t]);
-            if (GT) ag[t] = mfma16(a_g, xh, ag[t]);
-          }
+          au[t] = mfma16(a_u, xh, au[t]);
+          if (GT) ag[t] = mfma16(a_g, xh, ag[t]);
         }
       }
     }
   };
-  // three register sets in turn: step c loads chunk c + 2, computes chunk c (its tokens in LDS buffer c % 2) and
-  // stages chunk c + 1's tokens into the other buffer
+  // weights two chunks ahead in three register sets, tokens one chunk ahead (from L2): step c loads chunk c + 1's
+  // tokens and chunk c + 2's weights, computes chunk c (its tokens in LDS buffer c % 2) and stages chunk c + 1's
+  // tokens into the other buffer
   Set S0, S1, S2;
-  load(0, S0);
-  load(1, S1);
-  store_x(S0, 0);
+  load_x(0);
+  load_w(0, S0);
+  load_w(1, S1);
+  store_x(0);
   __syncthreads();
   for (int c = 0; c < nch; c += 3) {                   // nch is a multiple of 3
-    load(c + 2, S2);
+    load_x(c + 1);
+    load_w(c + 2, S2);
     compute(S0, c & 1);
-    store_x(S1, (c + 1) & 1);
+    store_x((c + 1) & 1);
     __syncthreads();
-    load(c + 3, S0);
+    load_x(c + 2);
+    load_w(c + 3, S0);
     compute(S1, (c + 1) & 1);
-    store_x(S2, c & 1);
+    store_x(c & 1);
     __syncthreads();
-    load(c + 4, S1);
+    load_x(c + 3);
+    load_w(c + 4, S1);
     compute(S2, c & 1);
-    store_x(S0, (c + 1) & 1);
+    store_x((c + 1) & 1);
     __syncthreads();
   }
-  // epilogue: the token's power of two back; one share: bias and activation, else the partial pre-activations
-  int idr[4];                                          // the rows of this lane's 4 outputs (D layout)
+  // the k halves meet: the second half's sums go through LDS (xl is free: every wave is past its last chunk) and
+  // the first half adds them, always in this order
+  f32x4* red = reinterpret_cast<f32x4*>(&xl[0][0]);   // [row tile][token tile][up, gate][64 lanes]
+  if (KH == 2 && kh == 1) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) idr[i] = ids[w * 16 + (lane >> 4) * 4 + i];
-  const float* bp = GT ? bg : bu;
-  float bias[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) bias[i] = (bp && idr[i] >= 0) ? bp[idr[i]] : 0.f;
-  const size_t FB = (size_t)F * B;
-  float amx[NTT];                                      // largest |a| of this lane's rows, per token tile
-#pragma unroll
-  for (int t = 0; t < NTT; ++t) {
-    amx[t] = 0.f;
-    const int tok = t * 16 + (lane & 15);
-    const int r0 = i0 + w * 16 + (lane >> 4) * 4;      // this lane's 4 rows: half an octet
-    const float sx = tok < B ? xsc[tok] : 0.f;
-    float a4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ii = r0 + i;
-      const float u = au[t][i] * sx, g = ag[t][i] * sx;
-      float a = 0.f;
-      if (KS > 1) {
-        if (tok < B && ii < n) {
-          const size_t e = (size_t)ii * B + tok;
-          pre[(size_t)(2 * ks) * FB + e] = u;
-          if (GT) pre[(size_t)(2 * ks + 1) * FB + e] = g;
-        }
-        continue;
-      }
-      if (GT) {
-        a = fmaxf(g + bias[i], 0.f) * u;
-      } else {
-        a = fmaxf(u + bias[i], 0.f);
-        if (ACT == 2) a *= a;
-      }
-      a4[i] = (tok < B && ii < n) ? a : 0.f;           // the 64-row tile is written whole: zeros past n and B
-      amx[t] = fmaxf(amx[t], fabsf(a4[i]));
+    for (int t = 0; t < NTT; ++t) {
+      red[((rt * NTT + t) * 2) * 64 + lane] = au[t];
+      if (GT) red[((rt * NTT + t) * 2 + 1) * 64 + lane] = ag[t];
     }
-    if (KS == 1)   // octet order: ((row / 8) * 16 NTT + token) * 8 + row % 8
-      *reinterpret_cast<float4*>(&abuf[((size_t)(r0 >> 3) * (NTT * 16) + tok) * 8 + (r0 & 7)]) =
-          make_float4(a4[0], a4[1], a4[2], a4[3]);
+  }
+  if (KH == 2) __syncthreads();
+  if (KH == 2 && kh == 0) {
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+      au[t] += red[((rt * NTT + t) * 2) * 64 + lane];
+      if (GT) ag[t] += red[((rt * NTT + t) * 2 + 1) * 64 + lane];
+    }
+  }
+  // epilogue (first half): the token's power of two back; one share: bias and activation, else the partial
+  // pre-activations
+  float amx[NTT];                                      // largest |a| of this lane's rows, per token tile
+  if (kh == 0) {
+    int idr[4];                                        // the rows of this lane's 4 outputs (D layout)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) idr[i] = ids[rt * 16 + (lane >> 4) * 4 + i];
+    const float* bp = GT ? bg : bu;
+    float bias[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias[i] = (bp && idr[i] >= 0) ? bp[idr[i]] : 0.f;
+    const size_t FB = (size_t)F * B;
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+      amx[t] = 0.f;
+      const int tok = t * 16 + (lane & 15);
+      const int r0 = i0 + rt * 16 + (lane >> 4) * 4;   // this lane's 4 rows: half an octet
+      const float sx = tok < B ? xsc[tok] : 0.f;
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ii = r0 + i;
+        const float u = au[t][i] * sx, g = ag[t][i] * sx;
+        float a = 0.f;
+        if (KS > 1) {
+          if (tok < B && ii < n) {
+            const size_t e = (size_t)ii * B + tok;
+            pre[(size_t)(2 * ks) * FB + e] = u;
+            if (GT) pre[(size_t)(2 * ks + 1) * FB + e] = g;
+          }
+          continue;
+        }
+        if (GT) {
+          a = fmaxf(g + bias[i], 0.f) * u;
+        } else {
+          a = fmaxf(u + bias[i], 0.f);
+          if (ACT == 2) a *= a;
+        }
+        a4[i] = (tok < B && ii < n) ? a : 0.f;         // the 64-row tile is written whole: zeros past n and B
+        amx[t] = fmaxf(amx[t], fabsf(a4[i]));
+      }
+      if (KS == 1)   // octet order: ((row / 8) * 16 NTT + token) * 8 + row % 8
+        *reinterpret_cast<float4*>(&abuf[((size_t)(r0 >> 3) * (NTT * 16) + tok) * 8 + (r0 & 7)]) =
+            make_float4(a4[0], a4[1], a4[2], a4[3]);
+    }
   }
   if (KS > 1) return;                                  // k_act_combine writes the maxima
-  // the workgroup's largest |a| per token: over the lane groups (rows), then over the waves
-  __syncthreads();                                     // xl is free: every wave is past its last chunk
-  float* smx = reinterpret_cast<float*>(&xl[0][0]);    // [4 waves][64 tokens]
+  // the workgroup's largest |a| per token: over the lane groups (rows), then over the row tiles
+  __syncthreads();                                     // every read of red is done
+  float* smx = reinterpret_cast<float*>(&xl[0][0]);    // [4 row tiles][64 tokens]
+  if (kh == 0) {
 #pragma unroll
-  for (int t = 0; t < NTT; ++t) {
-    float m = amx[t];
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    if (lane < 16) smx[w * 64 + t * 16 + lane] = m;
+    for (int t = 0; t < NTT; ++t) {
+      float m = amx[t];
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (lane < 16) smx[rt * 64 + t * 16 + lane] = m;
+    }
   }
   __syncthreads();
   if ((int)threadIdx.x < B) {
@@ -671,6 +721,10 @@ hipError_t launch_split_x(const float* x, int x_norm, int B, int D, int NTT, uin
   return hipGetLastError();
 }
 
+// Waves per k_ur workgroup by token tiles. Measured at the 13B shape: 64 tokens 101 -> 85 us per layer with 8
+// waves (two k halves per row tile); 32 tokens (2 tiles) the same either way; 8 and 16 tokens the same.
+constexpr int ur_waves(int ntt) { return ntt >= 4 ? 8 : 4; }
+
 template <int NTT, int ACT, bool Q4, bool EXACT>
 hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void* Wu, const void* Su, const float* bu,
                      const float* x, int x_norm, int B, int D, int F, const uint64_t* mask, int32_t* active,
@@ -692,7 +746,8 @@ hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void
                 (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax);
     return hipGetLastError();
   }
-  SFFN_LAUNCH(2, (k_ur<NTT, ACT, Q4, EXACT>), dim3((F + RTB - 1) / RTB * KS), dim3(NTR), 0, st, Wg, Sg, bg, Wu, Su, bu,
+  constexpr int NW = ur_waves(NTT);
+  SFFN_LAUNCH(2, (k_ur<NW, NTT, ACT, Q4, EXACT>), dim3((F + RTB - 1) / RTB * KS), dim3(64 * NW), 0, st, Wg, Sg, bg, Wu, Su, bu,
               (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
   e = hipGetLastError();
   if (e != hipSuccess || KS == 1) return e;
