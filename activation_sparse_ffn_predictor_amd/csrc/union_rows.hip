@@ -174,12 +174,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2)
   constexpr int GQW = Q4 ? QC / KH : 1;
   constexpr int QW = Q4 ? 4 : 4 / KH;
   constexpr int WV = Q4 ? GQW : QW;                    // uint4 of weights per lane and matrix per chunk
-  __shared__ uint64_t wl[WMAXR * NTU];                 // mask words
+  constexpr int NM = GT ? 2 : 1;                       // weight matrices (up, gate)
   __shared__ int roff[NTU];
   __shared__ int tmp[NTU / 64 + 4];
   __shared__ int ids[RTB];
   __shared__ uint4 xl[2][XT];                          // token fragments of two chunks
   __shared__ uint4 xjunk[XT % NTU ? NTU : 1];          // landing slots of the fragment pieces a thread lacks
+  // Q4_0 block scales of two chunks: [buffer][matrix][row][the chunk's 8 blocks], loaded 16 bytes per row by the
+  // first NM waves with the token fragments (per lane and quad they would be 2-byte loads from 16 rows)
+  __shared__ uint4 sl[Q4 ? 2 : 1][NM][Q4 ? RTB : 1];
+  // the mask words are needed only before the first chunk: they share the token fragments' space
+  static_assert(sizeof(xl) >= WMAXR * NTU * sizeof(uint64_t), "mask words fit in the fragment buffers");
+  uint64_t* wl = reinterpret_cast<uint64_t*>(&xl[0][0]);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int rt = w & 3, kh = w >> 2;                   // row tile, k half
   const int nw = (F + 63) >> 6;
@@ -227,15 +233,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2)
 
   struct Set {
     uint4 wu[WV], wg[WV];
-    uint32_t su[GQW], sg[GQW];                         // block scales' fp16 bits (32-bit: kept in registers)
   };
   uint4 xv[XV];                                        // this thread's share of the next chunk's token fragments
+  uint4 sv;                                            // Q4_0, first NM waves: the next chunk's scales of one row
+  const int wu0 = __builtin_amdgcn_readfirstlane(w);   // wave index in a scalar register (selects the matrix)
+  const int srow = ids[lane];                          // the row whose scales this lane stages
   auto load_x = [&](int c) {
     const int g0 = q0 + c * QC;                        // first quad of the chunk
 #pragma unroll
     for (int m = 0; m < XV; ++m) {
       const int p = m * NTU + (int)threadIdx.x;
       xv[m] = bx.ld16(boff(XT % NTU == 0 || p < XT, ((uint32_t)g0 * 4u * NTT * NH * 64 + (uint32_t)p) * 16u));
+    }
+    if constexpr (Q4) {
+      // the chunk's 8 blocks: 16 bytes of the row's scales (past the row's last block they belong to the next
+      // row, harmless: there the tokens are zero; past the tensor they read 0)
+      const uint32_t so = ((uint32_t)(srow >= 0 ? srow : 0) * nblk + (uint32_t)g0 * 4u) * 2u;
+      const bool ok = srow >= 0 && g0 < q1 && wu0 < NM;
+      sv = (wu0 == 1 ? bsg : bsu).ld16(boff(ok, so));
     }
   };
   auto load_w = [&](int c, Set& S) {
@@ -248,9 +263,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2)
       const uint32_t o = row * (uint32_t)(D >> 1) + (uint32_t)kb * 16u;
       S.wu[i] = bwu.ld16(boff(ok, o));
       if (GT) S.wg[i] = bwg.ld16(boff(ok, o));
-      const uint32_t so = (row * nblk + kb) * 2u;
-      S.su[i] = bsu.ldu16(boff(ok, so));
-      if (GT) S.sg[i] = bsg.ldu16(boff(ok, so));
     } else {
 #pragma unroll
       for (int j = 0; j < WV; ++j) {                   // elements 8 q .. 8 q + 7 of the lane's k block
@@ -269,6 +281,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2)
       uint4* d = (XT % NTU == 0 || p < XT) ? &xl[buf][p] : &xjunk[threadIdx.x];
       *d = xv[m];
     }
+    if (Q4 && wu0 < NM) sl[Q4 ? buf : 0][wu0 < NM ? wu0 : 0][Q4 ? lane : 0] = sv;
   };
   f32x4 au[NTT], ag[NTT];
 #pragma unroll
@@ -281,8 +294,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2)
       const int q = qh + j;
       half8 a_u, a_g;
       if constexpr (Q4) {                              // fp16((q - 8) s): one rounding per weight
-        a_u = q4_half8(S.wu[i], q) * splat8(S.su[i]);
-        if (GT) a_g = q4_half8(S.wg[i], q) * splat8(S.sg[i]);
+        const int blk = 4 * (gqh + i) + jq;            // this lane's block within the chunk
+        const int srw = rt * 16 + (lane & 15);
+        const uint32_t su = reinterpret_cast<const uint16_t*>(&sl[Q4 ? buf : 0][0][Q4 ? srw : 0])[blk];
+        a_u = q4_half8(S.wu[i], q) * splat8(su);
+        if (GT) {
+          const uint32_t sg = reinterpret_cast<const uint16_t*>(&sl[Q4 ? buf : 0][NM - 1][Q4 ? srw : 0])[blk];
+          a_g = q4_half8(S.wg[i], q) * splat8(sg);
+        }
       } else {
         a_u = __builtin_bit_cast(half8, S.wu[j]);
         if (GT) a_g = __builtin_bit_cast(half8, S.wg[j]);
