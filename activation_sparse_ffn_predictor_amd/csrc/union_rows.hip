@@ -7,10 +7,11 @@
 // tokens, lane l: token l % 16, the same 8 k values; D: lane l holds rows 4 (l / 16) + i of token l % 16).
 //
 // k order. A dot product may take its k terms in any order, so the MFMA k slots are assigned to suit the loads:
-// k blocks of 32 go in quads; in MFMA q (0..3) of quad g, lane group j takes elements 8 q .. 8 q + 7 of k block
-// 4 g + j. A lane therefore holds one whole k block of its row per quad: one 16-byte load of Q4_0 nibbles (or four
-// of fp16), and the four lanes of a row read 64 (256) contiguous bytes of it. The token fragments are written in
-// the same order.
+// k blocks of 32 go in quads. Q4_0: in MFMA q (0..3) of quad g, lane group j takes elements 8 q .. 8 q + 7 of k
+// block 4 g + j, so a lane holds one whole block of its row per quad (one 16-byte load of nibbles) and the four
+// lanes of a row read 64 contiguous bytes. fp16 ("block-major"): in MFMA q of quad g, lane group j takes elements
+// 8 j .. 8 j + 7 of k block 4 g + q, so each of the quad's four 16-byte loads reads one block, 64 contiguous bytes
+// per row. The token fragments are written in the matching order.
 //
 // k_split_x (one workgroup per token slot): normalises the token (optional, as every entry point's x_norm),
 // scales it by a power of two 2^-e with 2^e the smallest power above max |x| (exact, and it keeps every value
@@ -78,7 +79,7 @@ constexpr int NTX = 256;
 
 // One workgroup per token slot tok < NTT * 16 (slots >= B are zero). xf: [KB][NTT][NH][64] uint4, NH = 2 with EXACT
 // (hi, lo). xs[tok] = 2^e, the power of two the fragments are divided by.
-template <int XPT, bool EXACT>
+template <int XPT, bool EXACT, bool PERM>
 __global__ __launch_bounds__(NTX) void k_split_x(const float* __restrict__ x, int x_norm, int B, int D, int NTT,
                                                  uint4* __restrict__ xf, float* __restrict__ xs) {
   constexpr int NH = EXACT ? 2 : 1;
@@ -107,10 +108,12 @@ __global__ __launch_bounds__(NTX) void k_split_x(const float* __restrict__ x, in
   const float inv = ldexpf(1.f, -ex);
   if (threadIdx.x == 0) xs[tok] = ldexpf(1.f, ex);
   const int t = tok >> 4, tl = tok & 15;
-  // element e: k block kb = e / 32 (quad kb / 4, lane group kb % 4), fragment q = (e % 32) / 8; float4 i holds
-  // elements 4 i .. 4 i + 3, half i % 2 of an 8-element group
+  // element e: k block kb = e / 32, 8-element group q = (e % 32) / 8. Q4_0 order: fragment 4 (kb / 4) + q (quad
+  // kb / 4, MFMA q), lane group kb % 4; block-major (PERM): fragment kb (quad kb / 4, MFMA kb % 4), lane group q.
+  // float4 i holds elements 4 i .. 4 i + 3, half i % 2 of an 8-element group
   auto slot = [&](int kb, int q, int h) {
-    return (((size_t)((kb >> 2) * 4 + q) * NTT + t) * NH + h) * 64 + (size_t)((kb & 3) * 16 + tl);
+    const int f = PERM ? kb : (kb >> 2) * 4 + q, lg = PERM ? q : kb & 3;
+    return (((size_t)f * NTT + t) * NH + h) * 64 + (size_t)(lg * 16 + tl);
   };
 #pragma unroll
   for (int k = 0; k < XPT; ++k) {
@@ -148,6 +151,11 @@ constexpr int WMAXR = 2;             // mask words per thread kept in LDS (F <= 
 
 // k blocks per chunk: 8 for Q4_0 (two quads: 32 bytes of a row per lane and matrix), 4 for fp16 (a quad: 64 bytes)
 template <bool Q4> struct URChunk { static constexpr int KC = Q4 ? 8 : 4; };
+
+// fp16 token fragments and weight loads of k_ur with NW waves in block-major k order (see the k order note above).
+// Measured at the 13B shape: with 4 waves 8 tokens 33.9 -> 30.6 us, 32 tokens 79.2 -> 69.3 us per layer; with 8
+// waves (64 tokens) 85.3 -> 90.7 us, so those keep the Q4_0 order.
+constexpr bool ur_block_major(bool q4, int nw) { return !q4 && nw == 4; }
 
 // k_ur: NW = 4 or 8 waves; wave w takes row tile w % 4 and, with 8 waves, k half w / 4 of every chunk
 template <int NW, int NTT, int ACT, bool Q4, bool EXACT>
@@ -257,19 +265,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2)
 #pragma unroll
     for (int i = 0; i < GQW; ++i) {
     const int g = q0 + c * QC + gqh + i;
-    const int kb = g * 4 + jq;                         // this lane's k block of the quad
+    const int kb = g * 4 + jq;                         // Q4_0: this lane's k block of the quad
     const bool ok = g < q1 && kb < KB && idl >= 0;
+    const bool okh = g < q1 && idl >= 0;               // fp16: the element bound is checked per load
     if constexpr (Q4) {
       const uint32_t o = row * (uint32_t)(D >> 1) + (uint32_t)kb * 16u;
       S.wu[i] = bwu.ld16(boff(ok, o));
       if (GT) S.wg[i] = bwg.ld16(boff(ok, o));
     } else {
 #pragma unroll
-      for (int j = 0; j < WV; ++j) {                   // elements 8 q .. 8 q + 7 of the lane's k block
-        const int k = kb * 32 + (qh + j) * 8;
+      for (int j = 0; j < WV; ++j) {                   // block-major: elements 8 jq .. 8 jq + 7 of block 4 g + q,
+        constexpr bool BM = ur_block_major(Q4, NW);    // else elements 8 q .. 8 q + 7 of block kb
+        const int k = BM ? (g * 4 + qh + j) * 32 + jq * 8 : kb * 32 + (qh + j) * 8;
+        const bool v = BM ? okh && k < D : ok && k < D;
         const uint32_t o = (row * (uint32_t)D + (uint32_t)k) * 2u;
-        S.wu[j] = bwu.ld16(boff(ok && k < D, o));
-        if (GT) S.wg[j] = bwg.ld16(boff(ok && k < D, o));
+        S.wu[j] = bwu.ld16(boff(v, o));
+        if (GT) S.wg[j] = bwg.ld16(boff(v, o));
       }
     }
     }
@@ -514,8 +525,9 @@ __global__ __launch_bounds__(NTR) void k_ur16(const void* __restrict__ Wg, const
     uint4 xv[4][NH];
   };
   auto load = [&](int g, Set& S) {                     // quad g of the wave's range (past q1: nothing)
-    const int kb = g * 4 + jq;
+    const int kb = g * 4 + jq;                         // Q4_0: this lane's k block of the quad
     const bool ok = g < q1 && kb < KB && idl >= 0;
+    const bool okh = g < q1 && idl >= 0;               // fp16: the element bound is checked per load
     if constexpr (Q4) {
       const uint32_t o = row * (uint32_t)(D >> 1) + (uint32_t)kb * 16u;
       S.wu[0] = bwu.ld16(boff(ok, o));
@@ -525,11 +537,11 @@ __global__ __launch_bounds__(NTR) void k_ur16(const void* __restrict__ Wg, const
       if (GT) S.sg = bsg.ldu16(boff(ok, so));
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {                    // elements 8 q .. 8 q + 7 of the lane's k block
-        const int k = kb * 32 + q * 8;
+      for (int q = 0; q < 4; ++q) {                    // block-major: elements 8 jq .. 8 jq + 7 of block 4 g + q
+        const int k = (g * 4 + q) * 32 + jq * 8;
         const uint32_t o = (row * (uint32_t)D + (uint32_t)k) * 2u;
-        S.wu[q] = bwu.ld16(boff(ok && k < D, o));
-        if (GT) S.wg[q] = bwg.ld16(boff(ok && k < D, o));
+        S.wu[q] = bwu.ld16(boff(okh && k < D, o));
+        if (GT) S.wg[q] = bwg.ld16(boff(okh && k < D, o));
       }
     }
 #pragma unroll
@@ -648,11 +660,10 @@ __global__ __launch_bounds__(NTR) void k_mz(const void* __restrict__ P2, const f
 #pragma unroll
     for (int m = 0; m < XV; ++m)
       S.xv[m] = bx.ld16(((uint32_t)g * 4u * NTT * NH * 64 + (uint32_t)(m * NTR) + threadIdx.x) * 16u);
-    const int kb = g * 4 + jq;                         // this lane's k block of the quad
-    const bool ok = g < KQ && kb < KB && live;
+    const bool ok = g < KQ && live;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {                      // elements 8 q .. 8 q + 7 of the lane's k block
-      const int k = kb * 32 + q * 8;
+    for (int q = 0; q < 4; ++q) {                      // block-major: elements 8 jq .. 8 jq + 7 of block 4 g + q
+      const int k = (g * 4 + q) * 32 + jq * 8;
       S.wv[q] = bw.ld16(boff(ok && k < r, (row * (uint32_t)r + (uint32_t)k) * 2u));
     }
   };
@@ -734,10 +745,21 @@ __global__ __launch_bounds__(NTR) void k_mz(const void* __restrict__ P2, const f
                        ((uint64_t)bits16[3] << 48);
 }
 
-template <int XPT, bool EXACT>
+template <int XPT, bool EXACT, bool PERM>
 hipError_t launch_split_x(const float* x, int x_norm, int B, int D, int NTT, uint4* xf, float* xs, hipStream_t st) {
-  hipLaunchKernelGGL((k_split_x<XPT, EXACT>), dim3(NTT * 16), dim3(NTX), 0, st, x, x_norm, B, D, NTT, xf, xs);
+  hipLaunchKernelGGL((k_split_x<XPT, EXACT, PERM>), dim3(NTT * 16), dim3(NTX), 0, st, x, x_norm, B, D, NTT, xf, xs);
   return hipGetLastError();
+}
+
+template <bool EXACT, bool PERM>
+hipError_t split_x_xpt(int xpt, const float* x, int x_norm, int B, int D, int NTT, uint4* xf, float* xs,
+                       hipStream_t st) {
+  if (xpt <= 1) return launch_split_x<1, EXACT, PERM>(x, x_norm, B, D, NTT, xf, xs, st);
+  if (xpt <= 2) return launch_split_x<2, EXACT, PERM>(x, x_norm, B, D, NTT, xf, xs, st);
+  if (xpt <= 4) return launch_split_x<4, EXACT, PERM>(x, x_norm, B, D, NTT, xf, xs, st);
+  if (xpt <= 8) return launch_split_x<8, EXACT, PERM>(x, x_norm, B, D, NTT, xf, xs, st);
+  if (xpt <= 16) return launch_split_x<16, EXACT, PERM>(x, x_norm, B, D, NTT, xf, xs, st);
+  return hipErrorInvalidValue;
 }
 
 // Waves per k_ur workgroup by token tiles. Measured at the 13B shape: 64 tokens 101 -> 85 us per layer with 8
@@ -752,12 +774,10 @@ hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void
   const int xpt = (D / 4 + NTX - 1) / NTX;
   hipError_t e;
   static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
-  if (xpt <= 1) e = launch_split_x<1, EXACT>(x, x_norm, B, D, NTT, xf, xs, st);
-  else if (xpt <= 2) e = launch_split_x<2, EXACT>(x, x_norm, B, D, NTT, xf, xs, st);
-  else if (xpt <= 4) e = launch_split_x<4, EXACT>(x, x_norm, B, D, NTT, xf, xs, st);
-  else if (xpt <= 8) e = launch_split_x<8, EXACT>(x, x_norm, B, D, NTT, xf, xs, st);
-  else if (xpt <= 16) e = launch_split_x<16, EXACT>(x, x_norm, B, D, NTT, xf, xs, st);
-  else return hipErrorInvalidValue;
+  // the fragment order of the row kernel that runs (k_ur16, up to UR16_MAX_B tokens: fp16 block-major)
+  constexpr bool BMUR = ur_block_major(Q4, ur_waves(NTT));
+  e = (NTT == 1 && B <= UR16_MAX_B ? !Q4 : BMUR) ? split_x_xpt<EXACT, true>(xpt, x, x_norm, B, D, NTT, xf, xs, st)
+                                                : split_x_xpt<EXACT, false>(xpt, x, x_norm, B, D, NTT, xf, xs, st);
   if (e != hipSuccess) return e;
   if ((F + 63) / 64 > WMAXR * NTR || KS < 1 || (KS > 1 && !pre)) return hipErrorInvalidValue;
   if (NTT == 1 && B <= UR16_MAX_B) {                   // 16-row workgroups, k split over the waves
@@ -794,7 +814,7 @@ hipError_t launch_mz(const void* P2, const float* c, const float* h, int B, int 
                      uint64_t* mask, float* logits, uint4* hf, float* hs, hipStream_t st) {
   const int xpt = (r / 4 + NTX - 1) / NTX;
   hipError_t e;
-  if (xpt <= 1) e = launch_split_x<1, true>(h, 0, B, r, NTT, hf, hs, st);
+  if (xpt <= 1) e = launch_split_x<1, true, true>(h, 0, B, r, NTT, hf, hs, st);
   else return hipErrorInvalidValue;                    // r <= 1024
   if (e != hipSuccess) return e;
   SFFN_LAUNCH(1, k_mz<NTT>, dim3((F + 63) / 64), dim3(NTR), 0, st, P2, c, (const uint4*)hf, hs, B, F, r, tau, n_hot,
