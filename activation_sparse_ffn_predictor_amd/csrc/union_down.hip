@@ -12,13 +12,14 @@
 // column, so every tile is transposed once on its way through LDS.
 // k_ud (workgroups of 4 or 8 waves, 256 columns x every token tile, KS workgroups over the union rows, split by the
 // device-side union size): the workgroup stages the ids of its share of union rows in LDS, then walks them in steps
-// of 64. Per step each thread loads a piece of W_downT of 4 neurons x 16 (4 waves) or 8 (8 waves) columns (Q4_0:
-// 8 or 4 nibble bytes and the block scale per neuron; fp16: two 16- or 8-byte loads per neuron) and its share of
-// 16-byte pieces of the activations, and writes them, converted to fp16, as operand fragments into LDS (8 bytes
-// per column and 4 neurons; 8 bytes per token and 4 rows). Loads run three steps ahead of the matrix-core work in four register sets, with no branch in the loop:
-// rows past the union and steps past the share read neuron 0's weights against zero activations. The fragment
-// buffers are double-buffered with one barrier per step. Each wave multiplies its 64 or 32 columns by every token
-// tile; with 8 waves two share a SIMD, so one's LDS and barrier waits overlap the other's matrix-core work.
+// of 64 or 32 rows (two or one MFMA k chunks). Per step each thread loads a piece of W_downT of 4 neurons x 16 or 8
+// columns (Q4_0: 8 or 4 nibble bytes and the block scale per neuron; fp16: two 16- or 8-byte loads per neuron) and
+// its share of 16-byte pieces of the activations, and writes them, converted to fp16, as operand fragments into LDS
+// (8 bytes per column and 4 neurons; 8 bytes per token and 4 rows). Loads run three steps ahead of the matrix-core
+// work in four register sets, with no branch in the loop: rows past the union and steps past the share read neuron
+// 0's weights against zero activations. The fragment buffers are double-buffered with one barrier per step. Each
+// wave multiplies its 64 or 32 columns by every token tile; with 8 waves two share a SIMD, so one's LDS and barrier
+// waits overlap the other's matrix-core work.
 // Activations enter multiplied by a per-token power of two 2^(15 - e), with 2^e above their largest magnitude over
 // the workgroup's share of rows (from the per-64-row maxima the row kernels write), so every value lies inside
 // fp16's range with its full precision; the partial sums are scaled back before they are written. Q4_0 weights
@@ -40,26 +41,31 @@ __device__ __forceinline__ f32x4 mfma16(const half8& a, const half8& b, const f3
 }
 
 constexpr int CTD = 256;             // columns per workgroup: 16 column tiles
-constexpr int KSTD = 64;             // union rows per step: 2 MFMA k chunks
 constexpr int UD_PAD = 7;            // steps of ids past a share: the ring reads up to 6 steps beyond its last
 
-template <int NW, int NTT, bool Q4, bool EXACT>
+template <int NW, int KR, int NTT, bool Q4, bool EXACT>
 __global__ __launch_bounds__(64 * NW) void k_ud(const void* __restrict__ Wd, const void* __restrict__ Sd,
                                             const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
                                             const float* __restrict__ abuf, const float* __restrict__ bmax,
                                             int rbs, int B, int D, int F, int M, float* __restrict__ part) {
-  // M: the most 64-row steps one share can hold (sizes the ids in LDS, with UD_PAD steps of padding); bmax holds
-  // the largest |a| per token of every row tile of 2^rbs rows (rbs = 4 or 6)
+  // KR union rows per step (64 or 32: 2 or 1 MFMA k chunks). M: the most 64-row blocks one share can hold (sizes
+  // the ids in LDS, with UD_PAD steps of padding); bmax holds the largest |a| per token of every row tile of 2^rbs
+  // rows (rbs = 4 or 6)
   static_assert(!(Q4 && EXACT), "Q4_0 weights take fp16 activations");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(KR == 64 || KR == 32, "64 or 32 rows per step");
   constexpr int NTD = 64 * NW;
-  constexpr int CW = 32 / NW;                          // columns per staging unit and half block
+  constexpr int KC = KR / 32;                          // MFMA k chunks per step
+  constexpr int UPQ = NTD / (KR / 4);                  // staging units per neuron quad
+  static_assert(UPQ == 16 || UPQ == 32, "16 or 32 units per quad");
+  constexpr int CW = 128 / UPQ;                        // columns per staging unit and half block
   constexpr int NHA = EXACT ? 2 : 1;                   // activation planes (hi, lo)
   constexpr int BP = NTT * 16;                         // token stride of the activations
-  extern __shared__ __align__(16) int ids[];           // [(M + UD_PAD) * KSTD] ids of this share's union rows
-  __shared__ uint4 Bl[2][2][16][64];                   // weight fragments [buffer][k chunk][column tile][slot]
-  __shared__ uint4 Al[2][2][NTT][NHA][64];             // activation fragments [buffer][k chunk][token tile][plane]
-  __shared__ uint2 junk[NHA][NTD];                     // landing slots of the activation pieces a thread lacks
+  constexpr int NPC = KR * NTT * 4;                    // 16-byte activation pieces per step
+  extern __shared__ __align__(16) int ids[];           // [64 M + UD_PAD KR] ids of this share's union rows
+  __shared__ uint4 Bl[2][KC][16][64];                  // weight fragments [buffer][k chunk][column tile][slot]
+  __shared__ uint4 Al[2][KC][NTT][NHA][64];            // activation fragments [buffer][k chunk][token tile][plane]
+  __shared__ uint2 junk[NPC % NTD ? NHA : 1][NPC % NTD ? NTD : 1];   // landing slots of pieces a thread lacks
   __shared__ float smx[NTD / 64][64];
   __shared__ float inv_s[64];                          // per token: 2^(15 - e), max |a| < 2^e over this share
   __shared__ float scl[64];                            // and its inverse 2^(e - 15)
@@ -70,7 +76,7 @@ __global__ __launch_bounds__(64 * NW) void k_ud(const void* __restrict__ Wd, con
   // the union rows in KS shares of whole 64-row blocks
   const int n = min(max((int)Buf(n_active, 4u).ldu(0u), 0), F);
   const int Mn = min(((n + 63) / 64 + KS - 1) / KS, M);
-  const int total = Mn * KSTD;
+  const int total = Mn * 64;
   const int ibase = ks * total;                        // dense index of this workgroup's first row
   // the row-block maxima of this share and the ids (0 past the union and past the share) in one round trip
   {
@@ -93,7 +99,7 @@ __global__ __launch_bounds__(64 * NW) void k_ud(const void* __restrict__ Wd, con
       }
     }
     smx[sub][tok] = m;
-    const int tot_p = total + UD_PAD * KSTD;
+    const int tot_p = total + UD_PAD * KR;
     for (int e0 = 0; e0 < tot_p; e0 += 8 * NTD) {
       int v[8];
 #pragma unroll
@@ -121,18 +127,18 @@ __global__ __launch_bounds__(64 * NW) void k_ud(const void* __restrict__ Wd, con
     scl[t] = ldexpf(1.f, -p);
   }
   __syncthreads();
-  const int nst = (max(0, min(total, n - ibase)) + KSTD - 1) / KSTD;   // steps with rows
+  const int nst = (max(0, min(total, n - ibase)) + KR - 1) / KR;       // steps with rows
   const int nst4 = (nst + 3) / 4 * 4;                  // padded to rounds of four
 
   // weight roles: a thread stages 4 neurons (quad nq: neurons 4 nq .. + 3 of the step) at CW columns: column
   // unit cu, 32-column block wb = cu / 2, offset wo: columns 32 wb + wo + (0..CW-1) and 32 wb + 16 + wo + (0..CW-1),
-  // which Q4_0 holds in the low and high nibbles of the same CW bytes. 4 waves: nq = t / 16, cu = t % 16,
-  // wo = 8 (cu % 2). 8 waves (wave w, lane l): nq = 2 w + l % 2, cu = (l / 2) % 16, wo = 8 (cu % 2) + 4 (l / 32).
-  // Either way a half-wave holds both quads of a lane group at 16 distinct columns, so its fragment writes fall in
-  // distinct banks.
-  const int nq = NW == 4 ? (int)threadIdx.x >> 4 : 2 * w + (lane & 1);
-  const int cu = NW == 4 ? lane & 15 : (lane >> 1) & 15;
-  const int wb = cu >> 1, wo = (cu & 1) * 8 + (NW == 4 ? 0 : (lane >> 5) * 4);
+  // which Q4_0 holds in the low and high nibbles of the same CW bytes. 16 units per quad (CW = 8): nq = t / 16,
+  // cu = t % 16, wo = 8 (cu % 2). 32 units per quad (CW = 4; wave w, lane l): nq = 2 w + l % 2, cu = (l / 2) % 16,
+  // wo = 8 (cu % 2) + 4 (l / 32). Either way a half-wave holds both quads of a lane group at 16 distinct columns,
+  // so its fragment writes fall in distinct banks.
+  const int nq = UPQ == 16 ? (int)threadIdx.x >> 4 : 2 * w + (lane & 1);
+  const int cu = UPQ == 16 ? lane & 15 : (lane >> 1) & 15;
+  const int wb = cu >> 1, wo = (cu & 1) * 8 + (UPQ == 16 ? 0 : (lane >> 5) * 4);
   const int kcw = nq >> 3, lgw = (nq >> 1) & 3, hfw = nq & 1;   // fragment k chunk, lane group, 8-byte half
   const uint32_t nbytes = Q4 ? (uint32_t)F * (uint32_t)(D >> 1) : (uint32_t)F * (uint32_t)D * 2u;
   const Buf bw(Wd, nbytes);
@@ -144,10 +150,10 @@ __global__ __launch_bounds__(64 * NW) void k_ud(const void* __restrict__ Wd, con
   const uint32_t cb0 = Q4 ? (jb < nblk ? (uint32_t)jb * 16u + (uint32_t)wo : OOB) : (cl < D ? (uint32_t)cl * 2u : OOB);
   const uint32_t cb1 = Q4 ? 0u : (cl + 16 < D ? (uint32_t)(cl + 16) * 2u : OOB);
   const uint32_t cbs = jb < nblk ? (uint32_t)jb * 2u : OOB;
-  // activation roles: the step's block has 256 NTT pieces of 16 bytes; piece g = NTD j + t (j < AP) is octet
+  // activation roles: the step's block has NPC pieces of 16 bytes; piece g = NTD j + t (j < AP) is octet
   // g / (2 BP), token (g / 2) % BP, half g % 2 (rows 4 (g % 2) .. + 3 of the octet). A thread past the last piece
   // reads nothing (out-of-range offset) and writes its zeros to its own junk slot.
-  constexpr int AP = (256 * NTT + NTD - 1) / NTD;
+  constexpr int AP = (NPC + NTD - 1) / NTD;
   const int nr = min(((n + 63) >> 6) << 6, ((F + 63) >> 6) << 6);
   const Buf ba(abuf, (uint32_t)nr * (uint32_t)BP * 4u);   // rows past the union's last 64-row block read 0
   uint32_t aoff[AP];
@@ -156,14 +162,14 @@ __global__ __launch_bounds__(64 * NW) void k_ud(const void* __restrict__ Wd, con
 #pragma unroll
   for (int j = 0; j < AP; ++j) {
     const int g = NTD * j + (int)threadIdx.x;
-    const bool real = g < 256 * NTT;
+    const bool real = g < NPC;
     const int oc = g / (2 * BP), tk = (g >> 1) % BP, h = g & 1;
     aoff[j] = real ? ((uint32_t)((ibase >> 3) + oc) * (uint32_t)BP + (uint32_t)tk) * 32u + (uint32_t)h * 16u : OOB;
     asc[j] = real ? inv_s[tk] : 0.f;
     const int kc = oc >> 2, lg = oc & 3;
     aslot[j] = real ? ((((kc * NTT + (tk >> 4)) * NHA) * 64) + (tk & 15) + 16 * lg) * 2 + h : -1;
   }
-  const uint32_t astep = (uint32_t)KSTD * (uint32_t)BP * 4u;   // bytes of one step's activations
+  const uint32_t astep = (uint32_t)KR * (uint32_t)BP * 4u;     // bytes of one step's activations
 
   constexpr int QW = CW / 4;                           // Q4_0: 32-bit words of nibble bytes per neuron
   constexpr int HW = CW / 2;                           // fp16: 32-bit words per neuron and half block
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(64 * NW) void k_ud(const void* __restrict__ Wd, con
     for (int j = 0; j < AP; ++j) asm volatile("" : "+v"(S.a[j].x), "+v"(S.a[j].y), "+v"(S.a[j].z), "+v"(S.a[j].w));
   };
   auto load = [&](int st, Set& S) {
-    const int4 id4 = *reinterpret_cast<const int4*>(&ids[st * KSTD + 4 * nq]);
+    const int4 id4 = *reinterpret_cast<const int4*>(&ids[st * KR + 4 * nq]);
     const uint32_t id[4] = {(uint32_t)id4.x, (uint32_t)id4.y, (uint32_t)id4.z, (uint32_t)id4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -265,12 +271,12 @@ __global__ __launch_bounds__(64 * NW) void k_ud(const void* __restrict__ Wd, con
         vh[e] = (_Float16)v[e];
         vl[e] = (_Float16)(v[e] - (float)vh[e]);
       }
-      const bool real = 256 * NTT % NTD == 0 || aslot[j] >= 0;
+      const bool real = NPC % NTD == 0 || aslot[j] >= 0;
       uint2* al = reinterpret_cast<uint2*>(&Al[buf][0][0][0][0]);
-      uint2* dh = real ? &al[aslot[j]] : &junk[0][threadIdx.x];
+      uint2* dh = real ? &al[aslot[j]] : &junk[0][NPC % NTD ? threadIdx.x : 0];
       *dh = __builtin_bit_cast(uint2, vh);
       if (EXACT) {
-        uint2* dl = real ? &al[aslot[j] + 128] : &junk[NHA - 1][threadIdx.x];   // the lo plane: 64 slots further
+        uint2* dl = real ? &al[aslot[j] + 128] : &junk[NPC % NTD ? NHA - 1 : 0][NPC % NTD ? threadIdx.x : 0];
         *dl = __builtin_bit_cast(uint2, vl);
       }
     }
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(64 * NW) void k_ud(const void* __restrict__ Wd, con
     for (int c = 0; c < CPW; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int buf) {
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < KC; ++kc) {
       half8 bop[CPW];
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
@@ -345,35 +351,45 @@ __global__ __launch_bounds__(64 * NW) void k_ud(const void* __restrict__ Wd, con
     }
 }
 
-template <int NW, int NTT, bool Q4, bool EXACT>
+template <int NW, int KR, int NTT, bool Q4, bool EXACT>
 hipError_t launch_ud(const void* Wd, const void* Sd, const int32_t* active, const int32_t* n_active,
                      const float* abuf, const float* bmax, int rbs, int B, int D, int F, float* part, int KS, float* y,
                      hipStream_t st) {
-  const int M = (F + KSTD * KS - 1) / (KSTD * KS);     // steps per workgroup at most
-  const size_t lds = (size_t)(M + UD_PAD) * KSTD * sizeof(int);
+  const int M = (F + 64 * KS - 1) / (64 * KS);         // 64-row blocks per workgroup at most
+  const size_t lds = ((size_t)M * 64 + (size_t)UD_PAD * KR) * sizeof(int);
   static LdsLimit lds_limit;   // per kernel, set once per device
   size_t avail = 0;
-  hipError_t ea = lds_limit.get((const void*)k_ud<NW, NTT, Q4, EXACT>, &avail);
+  hipError_t ea = lds_limit.get((const void*)k_ud<NW, KR, NTT, Q4, EXACT>, &avail);
   if (ea != hipSuccess) return ea;
   if (lds > avail) return hipErrorInvalidValue;
-  SFFN_LAUNCH(3, (k_ud<NW, NTT, Q4, EXACT>), dim3((D + CTD - 1) / CTD, KS), dim3(64 * NW), lds, st, Wd, Sd, active, n_active,
-              abuf, bmax, rbs, B, D, F, M, part);
+  SFFN_LAUNCH(3, (k_ud<NW, KR, NTT, Q4, EXACT>), dim3((D + CTD - 1) / CTD, KS), dim3(64 * NW), lds, st, Wd, Sd,
+              active, n_active, abuf, bmax, rbs, B, D, F, M, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return sffn_launch_sum_parts(part, KS, B * D, y, st);
 }
 
-// Waves per k_ud workgroup by token tiles. Measured at the 13B shape: 64 tokens 74 -> 57 us per layer with 8 waves,
-// 32 tokens 36.4 -> 34.4 us; at 4 to 16 tokens (one tile) 8 waves are slower (8 tokens 18.9 -> 23.3 us).
-constexpr int ud_waves(int ntt) { return ntt >= 2 ? 8 : 4; }
+// Waves and rows per step of k_ud by weight format and token tiles. fp16: 4 waves with 32-row steps (half the LDS
+// of 64-row steps, so two or three workgroups share a CU) up to 3 token tiles, 8 waves with 64-row steps at 4.
+// Q4_0: 64-row steps, 8 waves from 2 token tiles. Same box, one 13B or 70B layer per launch: fp16 4 tokens 13.8 ->
+// 12.6 us, 8 tokens 19.7 -> 18.4, 32 tokens 35.4 -> 29.7 (against 8 waves), 40 tokens 44.0 -> 35.0, 64 tokens
+// 46.0 -> 46.8; Q4_0 8 tokens 32.6 -> 38.1, 32 tokens 60.4 -> 63.2, 64 tokens 64.2 -> 80.0 (there the 4-wave
+// kernel needs 262 registers).
+constexpr int ud_waves(bool q4, int ntt) { return ntt >= 4 || (q4 && ntt >= 2) ? 8 : 4; }
+constexpr int ud_rows(bool q4, int ntt) { return q4 || ntt >= 4 ? 64 : 32; }
 
 template <int NTT>
 hipError_t ud_q(bool q4, bool exact, const void* Wd, const void* Sd, const int32_t* active, const int32_t* n_active,
                 const float* abuf, const float* bmax, int rbs, int B, int D, int F, float* part, int KS, float* y,
                 hipStream_t st) {
-  if (q4) return launch_ud<ud_waves(NTT), NTT, true, false>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
-  if (exact) return launch_ud<ud_waves(NTT), NTT, false, true>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
-  return launch_ud<ud_waves(NTT), NTT, false, false>(Wd, Sd, active, n_active, abuf, bmax, rbs, B, D, F, part, KS, y, st);
+  if (q4)
+    return launch_ud<ud_waves(true, NTT), ud_rows(true, NTT), NTT, true, false>(Wd, Sd, active, n_active, abuf, bmax,
+                                                                                 rbs, B, D, F, part, KS, y, st);
+  if (exact)
+    return launch_ud<ud_waves(false, NTT), ud_rows(false, NTT), NTT, false, true>(Wd, Sd, active, n_active, abuf, bmax,
+                                                                                   rbs, B, D, F, part, KS, y, st);
+  return launch_ud<ud_waves(false, NTT), ud_rows(false, NTT), NTT, false, false>(Wd, Sd, active, n_active, abuf, bmax,
+                                                                                  rbs, B, D, F, part, KS, y, st);
 }
 
 }  // namespace

@@ -159,14 +159,15 @@ constexpr bool ur_block_major(bool q4, int nw) { return !q4 && nw == 4; }
 
 // k_ur: NW = 4 or 8 waves; wave w takes row tile w % 4 and, with 8 waves, k half w / 4 of every chunk
 template <int NW, int NTT, int ACT, bool Q4, bool EXACT>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2))) void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
-                                            const float* __restrict__ bg, const void* __restrict__ Wu,
-                                            const void* __restrict__ Su, const float* __restrict__ bu,
-                                            const uint4* __restrict__ xf, const float* __restrict__ xsc, int B,
-                                            int D, int F, const uint64_t* __restrict__ mask,
-                                            int32_t* __restrict__ active, int32_t* __restrict__ n_active,
-                                            float* __restrict__ abuf, float* __restrict__ bmax,
-                                            float* __restrict__ pre, int KS) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2)))
+void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
+          const float* __restrict__ bg, const void* __restrict__ Wu,
+          const void* __restrict__ Su, const float* __restrict__ bu,
+          const uint4* __restrict__ xf, const float* __restrict__ xsc, int B,
+          int D, int F, const uint64_t* __restrict__ mask,
+          int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+          float* __restrict__ abuf, float* __restrict__ bmax,
+          float* __restrict__ pre, int KS) {
   static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int NTU = 64 * NW;
@@ -786,8 +787,8 @@ hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void
     return hipGetLastError();
   }
   constexpr int NW = ur_waves(NTT);
-  SFFN_LAUNCH(2, (k_ur<NW, NTT, ACT, Q4, EXACT>), dim3((F + RTB - 1) / RTB * KS), dim3(64 * NW), 0, st, Wg, Sg, bg, Wu, Su, bu,
-              (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
+  SFFN_LAUNCH(2, (k_ur<NW, NTT, ACT, Q4, EXACT>), dim3((F + RTB - 1) / RTB * KS), dim3(64 * NW), 0, st, Wg, Sg, bg,
+              Wu, Su, bu, (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
   e = hipGetLastError();
   if (e != hipSuccess || KS == 1) return e;
   return sffn_launch_act_combine(ACT, pre, KS, active, n_active, GT_BIAS(ACT, bg, bu), B, F, abuf, bmax, st);
