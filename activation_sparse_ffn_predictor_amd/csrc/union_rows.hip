@@ -146,20 +146,20 @@ __global__ __launch_bounds__(NTX) void k_split_x(const float* __restrict__ x, in
 }
 
 constexpr int NTR = 256;             // 4 waves
-constexpr int RTB = 64;              // union rows per workgroup (a 16-row tile per wave)
 constexpr int WMAXR = 2;             // mask words per thread kept in LDS (F <= 32768)
 
 // k blocks per chunk: 8 for Q4_0 (two quads: 32 bytes of a row per lane and matrix), 4 for fp16 (a quad: 64 bytes)
 template <bool Q4> struct URChunk { static constexpr int KC = Q4 ? 8 : 4; };
 
-// fp16 token fragments and weight loads of k_ur with NW waves in block-major k order (see the k order note above).
-// Measured at the 13B shape: with 4 waves 8 tokens 33.9 -> 30.6 us, 32 tokens 79.2 -> 69.3 us per layer; with 8
-// waves (64 tokens) 85.3 -> 90.7 us, so those keep the Q4_0 order.
-constexpr bool ur_block_major(bool q4, int nw) { return !q4 && nw == 4; }
+// fp16 token fragments and weight loads of k_ur with KH k halves in block-major k order (see the k order note
+// above). Measured at the 13B shape: with one k half 8 tokens 33.9 -> 30.6 us, 32 tokens 79.2 -> 69.3 us per
+// layer; with two (64 tokens) 85.3 -> 90.7 us, so those keep the Q4_0 order.
+constexpr bool ur_block_major(bool q4, int kh) { return !q4 && kh == 1; }
 
-// k_ur: NW = 4 or 8 waves; wave w takes row tile w % 4 and, with 8 waves, k half w / 4 of every chunk
-template <int NW, int NTT, int ACT, bool Q4, bool EXACT>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 2)))
+// k_ur: RT row tiles of 16 rows (4 or 8) and KH k halves (1 or 2); NW = RT KH waves, wave w takes row tile w % RT
+// and k half w / RT of every chunk
+template <int RT, int KH, int NTT, int ACT, bool Q4, bool EXACT>
+__global__ __launch_bounds__(64 * RT * KH) __attribute__((amdgpu_waves_per_eu(RT * KH >= 8 ? 4 : 2)))
 void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
           const float* __restrict__ bg, const void* __restrict__ Wu,
           const void* __restrict__ Su, const float* __restrict__ bu,
@@ -169,9 +169,10 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
           float* __restrict__ abuf, float* __restrict__ bmax,
           float* __restrict__ pre, int KS) {
   static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
-  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert((RT == 4 || RT == 8) && (KH == 1 || KH == 2), "4 or 8 row tiles, 1 or 2 k halves");
+  constexpr int NW = RT * KH;
   constexpr int NTU = 64 * NW;
-  constexpr int KH = NW / 4;                           // k halves
+  constexpr int RB = 16 * RT;                          // union rows per workgroup
   constexpr bool GT = ACT == 1;                        // ReGLU: a gate row per neuron
   constexpr int NH = EXACT ? 2 : 1;                    // token fragment planes (hi, lo)
   constexpr int KC = URChunk<Q4>::KC;
@@ -186,25 +187,28 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
   constexpr int NM = GT ? 2 : 1;                       // weight matrices (up, gate)
   __shared__ int roff[NTU];
   __shared__ int tmp[NTU / 64 + 4];
-  __shared__ int ids[RTB];
-  __shared__ uint4 xl[2][XT];                          // token fragments of two chunks
+  __shared__ int ids[RB];
+  // token fragments of two chunks; after the last chunk the k halves' sums [row tile][token tile][up, gate][lane]
+  constexpr int XLN = 2 * XT > RT * NTT * 2 * 64 ? 2 * XT : RT * NTT * 2 * 64;
+  __shared__ uint4 xlraw[XLN];
+  uint4 (*xl)[XT] = reinterpret_cast<uint4 (*)[XT]>(xlraw);
   __shared__ uint4 xjunk[XT % NTU ? NTU : 1];          // landing slots of the fragment pieces a thread lacks
   // Q4_0 block scales of two chunks: [buffer][matrix][row][the chunk's 8 blocks], loaded 16 bytes per row by the
-  // first NM waves with the token fragments (per lane and quad they would be 2-byte loads from 16 rows)
-  __shared__ uint4 sl[Q4 ? 2 : 1][NM][Q4 ? RTB : 1];
+  // first NM RB / 64 waves with the token fragments (per lane and quad they would be 2-byte loads from 16 rows)
+  __shared__ uint4 sl[Q4 ? 2 : 1][NM][Q4 ? RB : 1];
   // the mask words are needed only before the first chunk: they share the token fragments' space
-  static_assert(sizeof(xl) >= WMAXR * NTU * sizeof(uint64_t), "mask words fit in the fragment buffers");
+  static_assert(sizeof(xlraw) >= WMAXR * NTU * sizeof(uint64_t), "mask words fit in the fragment buffers");
   uint64_t* wl = reinterpret_cast<uint64_t*>(&xl[0][0]);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int rt = w & 3, kh = w >> 2;                   // row tile, k half
+  const int rt = w % RT, kh = w / RT;                  // row tile, k half
   const int nw = (F + 63) >> 6;
   const int wpt = (nw + NTU - 1) / NTU;
   const int n = mask_prefix<NTU, WMAXR>(mask, nw, F, wpt, wl, roff, tmp);
   if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
   const int ks = blockIdx.x % KS;                      // the shares of 64 rows are neighbours in dispatch order
-  const int i0 = (blockIdx.x / KS) * RTB;
+  const int i0 = (blockIdx.x / KS) * RB;
   if (i0 >= n) return;                                 // block-uniform
-  if (threadIdx.x < RTB) {
+  if (threadIdx.x < RB) {
     const int i = i0 + threadIdx.x;
     int id = -1;
     if (i < n) {                                       // the (i - roff)-th set bit after word range T * wpt
@@ -246,7 +250,8 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
   uint4 xv[XV];                                        // this thread's share of the next chunk's token fragments
   uint4 sv;                                            // Q4_0, first NM waves: the next chunk's scales of one row
   const int wu0 = __builtin_amdgcn_readfirstlane(w);   // wave index in a scalar register (selects the matrix)
-  const int srow = ids[lane];                          // the row whose scales this lane stages
+  const int smat = wu0 % NM, sblk = wu0 / NM;          // staging waves: matrix, 64-row block
+  const int srow = ids[(sblk < RB / 64 ? sblk : 0) * 64 + lane];   // the row whose scales this lane stages
   auto load_x = [&](int c) {
     const int g0 = q0 + c * QC;                        // first quad of the chunk
 #pragma unroll
@@ -258,8 +263,8 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
       // the chunk's 8 blocks: 16 bytes of the row's scales (past the row's last block they belong to the next
       // row, harmless: there the tokens are zero; past the tensor they read 0)
       const uint32_t so = ((uint32_t)(srow >= 0 ? srow : 0) * nblk + (uint32_t)g0 * 4u) * 2u;
-      const bool ok = srow >= 0 && g0 < q1 && wu0 < NM;
-      sv = (wu0 == 1 ? bsg : bsu).ld16(boff(ok, so));
+      const bool ok = srow >= 0 && g0 < q1 && sblk < RB / 64;
+      sv = (smat == 1 ? bsg : bsu).ld16(boff(ok, so));
     }
   };
   auto load_w = [&](int c, Set& S) {
@@ -276,7 +281,7 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
     } else {
 #pragma unroll
       for (int j = 0; j < WV; ++j) {                   // block-major: elements 8 jq .. 8 jq + 7 of block 4 g + q,
-        constexpr bool BM = ur_block_major(Q4, NW);    // else elements 8 q .. 8 q + 7 of block kb
+        constexpr bool BM = ur_block_major(Q4, KH);    // else elements 8 q .. 8 q + 7 of block kb
         const int k = BM ? (g * 4 + qh + j) * 32 + jq * 8 : kb * 32 + (qh + j) * 8;
         const bool v = BM ? okh && k < D : ok && k < D;
         const uint32_t o = (row * (uint32_t)D + (uint32_t)k) * 2u;
@@ -293,7 +298,7 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
       uint4* d = (XT % NTU == 0 || p < XT) ? &xl[buf][p] : &xjunk[threadIdx.x];
       *d = xv[m];
     }
-    if (Q4 && wu0 < NM) sl[Q4 ? buf : 0][wu0 < NM ? wu0 : 0][Q4 ? lane : 0] = sv;
+    if (Q4 && sblk < RB / 64) sl[Q4 ? buf : 0][smat][Q4 ? (sblk < RB / 64 ? sblk : 0) * 64 + lane : 0] = sv;
   };
   f32x4 au[NTT], ag[NTT];
 #pragma unroll
@@ -426,7 +431,7 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
   if (KS > 1) return;                                  // k_act_combine writes the maxima
   // the workgroup's largest |a| per token: over the lane groups (rows), then over the row tiles
   __syncthreads();                                     // every read of red is done
-  float* smx = reinterpret_cast<float*>(&xl[0][0]);    // [4 row tiles][64 tokens]
+  float* smx = reinterpret_cast<float*>(&xl[0][0]);    // [RT row tiles][64 tokens]
   if (kh == 0) {
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
@@ -437,9 +442,10 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
     }
   }
   __syncthreads();
-  if ((int)threadIdx.x < B) {
-    const int t = threadIdx.x;
-    bmax[(size_t)(i0 / RTB) * B + t] = fmaxf(fmaxf(smx[t], smx[64 + t]), fmaxf(smx[128 + t], smx[192 + t]));
+  if ((int)threadIdx.x < B * (RB / 64)) {             // one entry per 64-row block and token
+    const int t = threadIdx.x % B, b = threadIdx.x / B;
+    const float* sm = smx + b * 256;
+    bmax[(size_t)(i0 / 64 + b) * B + t] = fmaxf(fmaxf(sm[t], sm[64 + t]), fmaxf(sm[128 + t], sm[192 + t]));
   }
 }
 
@@ -763,9 +769,12 @@ hipError_t split_x_xpt(int xpt, const float* x, int x_norm, int B, int D, int NT
   return hipErrorInvalidValue;
 }
 
-// Waves per k_ur workgroup by token tiles. Measured at the 13B shape: 64 tokens 101 -> 85 us per layer with 8
-// waves (two k halves per row tile); 32 tokens (2 tiles) the same either way; 8 and 16 tokens the same.
-constexpr int ur_waves(int ntt) { return ntt >= 4 ? 8 : 4; }
+// k halves of k_ur by token tiles. Measured at the 13B shape: 64 tokens 101 -> 85 us per layer with two (8 waves);
+// 32 tokens (2 tiles) the same either way; 8 and 16 tokens the same.
+constexpr int ur_halves(int ntt) { return ntt >= 4 ? 2 : 1; }
+// Row tiles of k_ur (16 rows each): 8 where a union of up to F rows would give more than 1.5 workgroups of 64 rows
+// per CU (UR_WIDE_ROWS), with two k halves: every token fragment loaded then serves 128 rows instead of 64.
+constexpr int UR_WIDE_ROWS = 384 * 64;
 
 template <int NTT, int ACT, bool Q4, bool EXACT>
 hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void* Wu, const void* Su, const float* bu,
@@ -776,7 +785,7 @@ hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void
   hipError_t e;
   static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
   // the fragment order of the row kernel that runs (k_ur16, up to UR16_MAX_B tokens: fp16 block-major)
-  constexpr bool BMUR = ur_block_major(Q4, ur_waves(NTT));
+  constexpr bool BMUR = ur_block_major(Q4, ur_halves(NTT));
   e = (NTT == 1 && B <= UR16_MAX_B ? !Q4 : BMUR) ? split_x_xpt<EXACT, true>(xpt, x, x_norm, B, D, NTT, xf, xs, st)
                                                 : split_x_xpt<EXACT, false>(xpt, x, x_norm, B, D, NTT, xf, xs, st);
   if (e != hipSuccess) return e;
@@ -786,9 +795,20 @@ hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void
                 (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax);
     return hipGetLastError();
   }
-  constexpr int NW = ur_waves(NTT);
-  SFFN_LAUNCH(2, (k_ur<NW, NTT, ACT, Q4, EXACT>), dim3((F + RTB - 1) / RTB * KS), dim3(64 * NW), 0, st, Wg, Sg, bg,
-              Wu, Su, bu, (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
+  constexpr int KH = ur_halves(NTT);
+  if constexpr (KH == 2) {
+    if (F > UR_WIDE_ROWS) {
+      SFFN_LAUNCH(2, (k_ur<8, KH, NTT, ACT, Q4, EXACT>), dim3((F + 127) / 128 * KS), dim3(64 * 8 * KH), 0, st, Wg,
+                  Sg, bg, Wu, Su, bu, (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
+      e = hipGetLastError();
+      if (e != hipSuccess || KS == 1) return e;
+      return sffn_launch_act_combine(ACT, pre, KS, active, n_active, GT_BIAS(ACT, bg, bu), B, F, abuf, bmax, st);
+    }
+  }
+  {
+    SFFN_LAUNCH(2, (k_ur<4, KH, NTT, ACT, Q4, EXACT>), dim3((F + 63) / 64 * KS), dim3(64 * 4 * KH), 0, st, Wg, Sg,
+                bg, Wu, Su, bu, (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
+  }
   e = hipGetLastError();
   if (e != hipSuccess || KS == 1) return e;
   return sffn_launch_act_combine(ACT, pre, KS, active, n_active, GT_BIAS(ACT, bg, bu), B, F, abuf, bmax, st);
