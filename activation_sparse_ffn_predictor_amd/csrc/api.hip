@@ -33,7 +33,7 @@ constexpr int MAX_B = 64, MAX_D = 16384, MAX_F = 1 << 22, MAX_R = 1024, MAX_BR =
 #endif
 constexpr int MAX_BD_VALU = SFFN_MAX_BD_VALU;   // decode-batch kernels (B in {2, 4, 8}): B * D <= this
 constexpr int MAX_F_UNION = 32768;   // union kernels compact the whole mask in one block
-constexpr int KS_MAX = 8;            // k shares of the multi-token predictor's first stage
+constexpr int KS_MAX = 16;           // k shares of the multi-token predictor's first stage
 constexpr int UD_KS_MAX = 16;        // row shares of the union down projection
 constexpr int MZ_MIN_B = 17;         // tokens from which the predictor's stage 2 runs on pre-split h fragments
 constexpr int G_FUSED = 256;         // blocks (= partial sums of y) of the fused single-token forward
@@ -288,8 +288,10 @@ static int predict_impl(const void* P1, const void* P2, const float* c, const fl
       xin = ws_xn(ws, B, F);
     }
     // shares of d for the union predictor's first stage; their partial sums use the partials region
-    // (KS_MAX * B * D floats >= ksh * B * r)
-    const int ksh = std::max(1, std::min({KS_MAX, D / 32 > 0 ? D / 32 : 1, (KS_MAX * D) / r}));
+    // (KS_MAX * B * D floats >= ksh * B * r): 16 shares with the two-row-tile blocks from 17 tokens on, 8 below
+    // (about 256 blocks either way at r = 512)
+    const int ksm = B > 16 ? KS_MAX : KS_MAX / 2;
+    const int ksh = std::max(1, std::min({ksm, D / 32 > 0 ? D / 32 : 1, (ksm * D) / r}));
     // stage 2 on pre-split h fragments (in the union row kernel's token-fragment region, free until the forward
     // call) from 17 tokens; below, its split launch costs more than the fragments save
     const bool mz = B > MZ_MIN_B - 1 && sffn_ur_xf_bytes(B, r, true) <= sffn_ur_xf_bytes(B, D, true);

@@ -84,13 +84,18 @@ constexpr int NTK = 512;            // 8 waves split the k dimension
 constexpr int KW = NTK / 64;
 
 // Partial h over one of gridDim.y shares of d: hp[ks][b][j] = sum_{d in share ks} P1[j, d] x[b, d]; block = 16
-// rows of P1 and one share of the k range, split again over the 8 waves.
+// mh_tiles(NTT) rows of P1 and one share of the k range, split again over the 8 waves. Every lane's tokens (loaded
+// and split once per k block) serve the block's row tiles, so two row tiles per block halve the reads of x, which
+// outweigh P1's from 2 token tiles on (70B, 64 tokens: 14.3 -> 11.0 us; 13B, 16 tokens: 6.4 -> 6.6 us).
+constexpr int mh_tiles(int ntt) { return ntt >= 2 ? 2 : 1; }
+
 template <int NTT>
 __global__ __launch_bounds__(NTK) void k_mt_h(const uint4* __restrict__ P1, const float* __restrict__ x, int B, int D,
                                               int r, float* __restrict__ hp) {
-  __shared__ f32x4 part[KW][NTT][64];
+  constexpr int RT = mh_tiles(NTT);
+  __shared__ f32x4 part[KW][RT][NTT][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int j0 = blockIdx.x * 16;
+  const int j0 = blockIdx.x * 16 * RT;
   const int KB = (D + 31) / 32;
   const int KSH = gridDim.y, ks = blockIdx.y;
   const int kps = (KB + KSH - 1) / KSH;                  // k blocks of this share
@@ -98,46 +103,57 @@ __global__ __launch_bounds__(NTK) void k_mt_h(const uint4* __restrict__ P1, cons
   const int kpw = (kps + KW - 1) / KW;
   const int kb0 = ks0 + w * kpw, kb1 = min(ks1, kb0 + kpw);
   const Buf bp(P1, (uint32_t)r * D * 2u), bx(x, (uint32_t)B * D * 4u);
-  const int row = j0 + (lane & 15);
-  f32x4 acc[NTT];
+  f32x4 acc[RT][NTT];
 #pragma unroll
-  for (int t = 0; t < NTT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int CH = KChunk<NTT>::CH;
   for (int c0 = kb0; c0 < kb1; c0 += CH) {
-    uint4 av[CH];
+    uint4 av[CH][RT];
     XRaw xr[CH][NTT];
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       const int kb = c0 + q;
       const int k = kb * 32 + (lane >> 4) * 8;
-      av[q] = bp.ld16(boff(kb < kb1 && row < r && k < D, ((uint32_t)row * D + k) * 2u));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int row = j0 + 16 * rt + (lane & 15);
+        av[q][rt] = bp.ld16(boff(kb < kb1 && row < r && k < D, ((uint32_t)row * D + k) * 2u));
+      }
 #pragma unroll
       for (int t = 0; t < NTT; ++t) xr[q][t] = load_xraw(bx, B, kb < kb1 ? D : 0, t, kb);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
-      const half8 a = __builtin_bit_cast(half8, av[q]);
 #pragma unroll
       for (int t = 0; t < NTT; ++t) {
         half8 xh, xl;
         split_xraw(xr[q][t], xh, xl);
-        acc[t] = mfma16(a, xl, mfma16(a, xh, acc[t]));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const half8 a = __builtin_bit_cast(half8, av[q][rt]);
+          acc[rt][t] = mfma16(a, xl, mfma16(a, xh, acc[rt][t]));
+        }
       }
     }
   }
 #pragma unroll
-  for (int t = 0; t < NTT; ++t) part[w][t][lane] = acc[t];
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) part[w][rt][t][lane] = acc[rt][t];
   __syncthreads();
-  if (w == 0) {
+  if (w < RT) {                                        // wave rt adds row tile rt's partials in wave order
+    const int rt = w;
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
-      f32x4 s = part[0][t][lane];
-      for (int ww = 1; ww < KW; ++ww) s += part[ww][t][lane];
+      f32x4 s = part[0][rt][t][lane];
+      for (int ww = 1; ww < KW; ++ww) s += part[ww][rt][t][lane];
       const int tok = t * 16 + (lane & 15);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = j0 + (lane >> 4) * 4 + i;
+        const int j = j0 + 16 * rt + (lane >> 4) * 4 + i;
         if (tok < B && j < r) hp[((size_t)ks * B + tok) * r + j] = s[i];
       }
     }
@@ -286,7 +302,8 @@ hipError_t predict_mt(const void* P1, const void* P2, const float* c, const floa
                       void* hf, float* hs, hipStream_t st) {
   hipError_t e;
   if (KSH > 0) {                                       // else hbuf holds h already
-    SFFN_LAUNCH(0, k_mt_h<NTT>, dim3((r + 15) / 16, KSH), dim3(NTK), 0, st, (const uint4*)P1, x, B, D, r, hpart);
+    SFFN_LAUNCH(0, k_mt_h<NTT>, dim3((r + 16 * mh_tiles(NTT) - 1) / (16 * mh_tiles(NTT)), KSH), dim3(NTK), 0, st,
+                (const uint4*)P1, x, B, D, r, hpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nh = B * r;
