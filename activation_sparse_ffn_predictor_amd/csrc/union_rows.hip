@@ -639,18 +639,20 @@ __global__ __launch_bounds__(NTR) void k_ur16(const void* __restrict__ Wg, const
 // ahead in three register sets, the chunk's fragments shared through LDS) and takes exact products into fp32 sums.
 // Epilogue: z = sum * 2^e + c (the always-active prefix: +inf, its row never read), optional logits[token][neuron],
 // and the OR over tokens by ballot into the block's mask word.
-template <int NTT>
-__global__ __launch_bounds__(NTR) void k_mz(const void* __restrict__ P2, const float* __restrict__ c,
-                                            const uint4* __restrict__ hf, const float* __restrict__ hsc, int B,
-                                            int F, int r, float tau, int n_hot, uint64_t* __restrict__ mask,
-                                            float* __restrict__ logits) {
+template <int RT, int NTT>
+__global__ __launch_bounds__(64 * RT) void k_mz(const void* __restrict__ P2, const float* __restrict__ c,
+                                                const uint4* __restrict__ hf, const float* __restrict__ hsc, int B,
+                                                int F, int r, float tau, int n_hot, uint64_t* __restrict__ mask,
+                                                float* __restrict__ logits) {
+  // RT waves of 16 neurons each (4 or 8): every chunk of h fragments staged serves 16 RT neurons
+  constexpr int NT = 64 * RT;
   constexpr int NH = 2, KC = 4;                        // two fp16 planes; 4 k blocks (a quad) per chunk
-  constexpr int XV = KC * NTT * NH * 64 / NTR;
-  static_assert(XV * NTR == KC * NTT * NH * 64, "fragment share");
+  constexpr int XV = KC * NTT * NH * 64 / NT;
+  static_assert(XV * NT == KC * NTT * NH * 64, "fragment share");
   __shared__ uint4 xl[2][KC * NTT * NH * 64];          // token fragments of two chunks
-  __shared__ uint32_t bits16[4];
+  __shared__ uint32_t bits16[RT];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row0 = blockIdx.x * 64 + w * 16;
+  const int row0 = blockIdx.x * 16 * RT + w * 16;
   const int rl = row0 + (lane & 15);                   // this lane's A-operand row
   const bool live = rl < F && rl >= n_hot;             // the prefix reads no row
   const uint32_t row = (uint32_t)(live ? rl : 0);
@@ -666,7 +668,7 @@ __global__ __launch_bounds__(NTR) void k_mz(const void* __restrict__ P2, const f
   auto load = [&](int g, Set& S) {
 #pragma unroll
     for (int m = 0; m < XV; ++m)
-      S.xv[m] = bx.ld16(((uint32_t)g * 4u * NTT * NH * 64 + (uint32_t)(m * NTR) + threadIdx.x) * 16u);
+      S.xv[m] = bx.ld16(((uint32_t)g * 4u * NTT * NH * 64 + (uint32_t)(m * NT) + threadIdx.x) * 16u);
     const bool ok = g < KQ && live;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {                      // block-major: elements 8 jq .. 8 jq + 7 of block 4 g + q
@@ -676,7 +678,7 @@ __global__ __launch_bounds__(NTR) void k_mz(const void* __restrict__ P2, const f
   };
   auto store_x = [&](const Set& S, int buf) {
 #pragma unroll
-    for (int m = 0; m < XV; ++m) xl[buf][m * NTR + threadIdx.x] = S.xv[m];
+    for (int m = 0; m < XV; ++m) xl[buf][m * NT + threadIdx.x] = S.xv[m];
   };
   f32x4 az[NTT];
 #pragma unroll
@@ -747,9 +749,12 @@ __global__ __launch_bounds__(NTR) void k_mz(const void* __restrict__ P2, const f
   }
   if (lane == 0) bits16[w] = word;
   __syncthreads();
-  if (threadIdx.x == 0)
-    mask[blockIdx.x] = (uint64_t)bits16[0] | ((uint64_t)bits16[1] << 16) | ((uint64_t)bits16[2] << 32) |
-                       ((uint64_t)bits16[3] << 48);
+  const int wi = blockIdx.x * (RT / 4) + (int)threadIdx.x;   // one mask word per 64 neurons (those below F)
+  if ((int)threadIdx.x < RT / 4 && wi < (F + 63) / 64) {
+    const int h = threadIdx.x;
+    mask[wi] = (uint64_t)bits16[4 * h] | ((uint64_t)bits16[4 * h + 1] << 16) | ((uint64_t)bits16[4 * h + 2] << 32) |
+               ((uint64_t)bits16[4 * h + 3] << 48);
+  }
 }
 
 template <int XPT, bool EXACT, bool PERM>
@@ -838,8 +843,13 @@ hipError_t launch_mz(const void* P2, const float* c, const float* h, int B, int 
   if (xpt <= 1) e = launch_split_x<1, true, true>(h, 0, B, r, NTT, hf, hs, st);
   else return hipErrorInvalidValue;                    // r <= 1024
   if (e != hipSuccess) return e;
-  SFFN_LAUNCH(1, k_mz<NTT>, dim3((F + 63) / 64), dim3(NTR), 0, st, P2, c, (const uint4*)hf, hs, B, F, r, tau, n_hot,
-              mask, logits);
+  if (F > UR_WIDE_ROWS) {                              // large layers: 128 neurons per workgroup (as k_ur)
+    SFFN_LAUNCH(1, (k_mz<8, NTT>), dim3((F + 127) / 128), dim3(512), 0, st, P2, c, (const uint4*)hf, hs, B, F, r, tau,
+                n_hot, mask, logits);
+  } else {
+    SFFN_LAUNCH(1, (k_mz<4, NTT>), dim3((F + 63) / 64), dim3(256), 0, st, P2, c, (const uint4*)hf, hs, B, F, r, tau,
+                n_hot, mask, logits);
+  }
   return hipGetLastError();
 }
 
