@@ -452,9 +452,11 @@ hipError_t sffn_launch_rows_ur(int act, bool q4, bool exact, const void* Wg, con
                                const void* Wu, const void* Su, const float* bu, const float* x, int x_norm, int B,
                                int D, int F, const uint64_t* mask, int32_t* active, int32_t* n_active, float* abuf,
                                float* bmax, void* xf, float* xs, float* pre, hipStream_t st);
-// multi-token predictor stage 2 from h [B, r]: h split into fragments in hf (sffn_ur_xf_bytes(B, r, true)) and hs
-hipError_t sffn_launch_predict_mz(const void* P2, const float* c, const float* h, int B, int F, int r, float tau,
-                                  int n_hot, uint64_t* mask, float* logits, void* hf, float* hs, hipStream_t st);
+// multi-token predictor stage 2 from h [B, r] (hparts > 0, at most 16: the sum of hparts partials [hparts][B][r]): h
+// split into fragments in hf (sffn_ur_xf_bytes(B, r, true)) and hs
+hipError_t sffn_launch_predict_mz(const void* P2, const float* c, const float* h, int hparts, int B, int F, int r,
+                                  float tau, int n_hot, uint64_t* mask, float* logits, void* hf, float* hs,
+                                  hipStream_t st);
 // activations (octet order, 64-row tiles written whole) from the k shares' partial pre-activations, and the
 // largest |a| per 64 rows and token into bmax
 hipError_t sffn_launch_act_combine(int act, const float* pre, int KSP, const int32_t* active, const int32_t* n_active,

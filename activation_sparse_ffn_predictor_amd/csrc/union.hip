@@ -306,13 +306,15 @@ hipError_t predict_mt(const void* P1, const void* P2, const float* c, const floa
                 (const uint4*)P1, x, B, D, r, hpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (hf)                                            // the split adds the partials itself (one launch fewer)
+      return sffn_launch_predict_mz(P2, c, hpart, KSH, B, F, r, tau, n_hot, mask, logits, hf, hs, st);
     const int nh = B * r;
     hipLaunchKernelGGL(k_sum_parts, dim3((nh + 255) / 256), dim3(256), 0, st, hpart, KSH, nh, hbuf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (hf)                                              // h split once, P2 streamed on the 64-row tiling
-    return sffn_launch_predict_mz(P2, c, hbuf, B, F, r, tau, n_hot, mask, logits, hf, hs, st);
+    return sffn_launch_predict_mz(P2, c, hbuf, 0, B, F, r, tau, n_hot, mask, logits, hf, hs, st);
   SFFN_LAUNCH(1, k_mt_z<NTT>, dim3((F + 63) / 64), dim3(256), 0, st, (const uint4*)P2, c, hbuf, B, F, r, tau, n_hot,
               mask, logits);
   return hipGetLastError();

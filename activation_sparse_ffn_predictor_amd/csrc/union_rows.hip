@@ -78,10 +78,12 @@ __device__ __forceinline__ half8 splat8(uint32_t s) {
 constexpr int NTX = 256;
 
 // One workgroup per token slot tok < NTT * 16 (slots >= B are zero). xf: [KB][NTT][NH][64] uint4, NH = 2 with EXACT
-// (hi, lo). xs[tok] = 2^e, the power of two the fragments are divided by.
+// (hi, lo). xs[tok] = 2^e, the power of two the fragments are divided by. With nparts > 0 (XPT = 1) the values are
+// the sum of nparts partials x[p][B][D], added in share order (as k_sum_parts adds them).
+constexpr int SPLIT_PARTS_MAX = 16;
 template <int XPT, bool EXACT, bool PERM>
 __global__ __launch_bounds__(NTX) void k_split_x(const float* __restrict__ x, int x_norm, int B, int D, int NTT,
-                                                 uint4* __restrict__ xf, float* __restrict__ xs) {
+                                                 uint4* __restrict__ xf, float* __restrict__ xs, int nparts) {
   constexpr int NH = EXACT ? 2 : 1;
   __shared__ float red[2 * (NTX / 64) + 4];
   const int tok = blockIdx.x;
@@ -89,7 +91,25 @@ __global__ __launch_bounds__(NTX) void k_split_x(const float* __restrict__ x, in
   const int n4 = real ? D >> 2 : 0;                    // padding slots load nothing (all zero)
   const float* xb = x + (size_t)(real ? tok : 0) * D;
   float4 v[XPT];
-  stage_load<NTX, XPT>(xb, n4, v);
+  if constexpr (XPT == 1) {
+    if (nparts > 0) {                                  // every share's load issued before the first add
+      const Buf bp(x, (uint32_t)nparts * (uint32_t)B * (uint32_t)D * 4u);
+      const bool ok = (int)threadIdx.x < n4;
+      float4 u[SPLIT_PARTS_MAX];
+#pragma unroll
+      for (int k = 0; k < SPLIT_PARTS_MAX; ++k)
+        u[k] = bp.ldf4(boff(ok && k < nparts, ((uint32_t)(k * B + tok) * (uint32_t)D + 4u * threadIdx.x) * 4u));
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < SPLIT_PARTS_MAX; ++k)
+        if (k < nparts) { acc.x += u[k].x; acc.y += u[k].y; acc.z += u[k].z; acc.w += u[k].w; }
+      v[0] = acc;
+    } else {
+      stage_load<NTX, XPT>(xb, n4, v);
+    }
+  } else {
+    stage_load<NTX, XPT>(xb, n4, v);
+  }
   if (real && x_norm) block_norm_regs<NTX, XPT>(v, n4, xb[0], red);
   float m = 0.f;
 #pragma unroll
@@ -758,8 +778,10 @@ __global__ __launch_bounds__(64 * RT) void k_mz(const void* __restrict__ P2, con
 }
 
 template <int XPT, bool EXACT, bool PERM>
-hipError_t launch_split_x(const float* x, int x_norm, int B, int D, int NTT, uint4* xf, float* xs, hipStream_t st) {
-  hipLaunchKernelGGL((k_split_x<XPT, EXACT, PERM>), dim3(NTT * 16), dim3(NTX), 0, st, x, x_norm, B, D, NTT, xf, xs);
+hipError_t launch_split_x(const float* x, int x_norm, int B, int D, int NTT, uint4* xf, float* xs, hipStream_t st,
+                          int nparts = 0) {
+  hipLaunchKernelGGL((k_split_x<XPT, EXACT, PERM>), dim3(NTT * 16), dim3(NTX), 0, st, x, x_norm, B, D, NTT, xf, xs,
+                     nparts);
   return hipGetLastError();
 }
 
@@ -836,11 +858,12 @@ hipError_t ur_act(int act, bool q4, const void* Wg, const void* Sg, const float*
 }
 
 template <int NTT>
-hipError_t launch_mz(const void* P2, const float* c, const float* h, int B, int F, int r, float tau, int n_hot,
-                     uint64_t* mask, float* logits, uint4* hf, float* hs, hipStream_t st) {
+hipError_t launch_mz(const void* P2, const float* c, const float* h, int hparts, int B, int F, int r, float tau,
+                     int n_hot, uint64_t* mask, float* logits, uint4* hf, float* hs, hipStream_t st) {
   const int xpt = (r / 4 + NTX - 1) / NTX;
   hipError_t e;
-  if (xpt <= 1) e = launch_split_x<1, true, true>(h, 0, B, r, NTT, hf, hs, st);
+  if (hparts > SPLIT_PARTS_MAX) return hipErrorInvalidValue;
+  if (xpt <= 1) e = launch_split_x<1, true, true>(h, 0, B, r, NTT, hf, hs, st, hparts);
   else return hipErrorInvalidValue;                    // r <= 1024
   if (e != hipSuccess) return e;
   if (F > UR_WIDE_ROWS) {                              // large layers: 128 neurons per workgroup (as k_ur)
@@ -855,16 +878,18 @@ hipError_t launch_mz(const void* P2, const float* c, const float* h, int B, int 
 
 }  // namespace
 
-// Predictor stage 2 for B tokens from h [B, r] (fp32) on the matrix cores: h split into token fragments in hf
-// (sffn_ur_xf_bytes(B, r, true) bytes) with its powers of two in hs, then z, threshold and the union mask.
-hipError_t sffn_launch_predict_mz(const void* P2, const float* c, const float* h, int B, int F, int r, float tau,
-                                  int n_hot, uint64_t* mask, float* logits, void* hf, float* hs, hipStream_t st) {
+// Predictor stage 2 for B tokens from h [B, r] (fp32; hparts > 0: the sum of hparts partials [hparts][B][r]) on the
+// matrix cores: h split into token fragments in hf (sffn_ur_xf_bytes(B, r, true) bytes) with its powers of two in
+// hs, then z, threshold and the union mask.
+hipError_t sffn_launch_predict_mz(const void* P2, const float* c, const float* h, int hparts, int B, int F, int r,
+                                  float tau, int n_hot, uint64_t* mask, float* logits, void* hf, float* hs,
+                                  hipStream_t st) {
   if (r % 8 || r > 1024) return hipErrorInvalidValue;
   switch ((B + 15) / 16) {
-    case 1: return launch_mz<1>(P2, c, h, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
-    case 2: return launch_mz<2>(P2, c, h, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
-    case 3: return launch_mz<3>(P2, c, h, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
-    case 4: return launch_mz<4>(P2, c, h, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
+    case 1: return launch_mz<1>(P2, c, h, hparts, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
+    case 2: return launch_mz<2>(P2, c, h, hparts, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
+    case 3: return launch_mz<3>(P2, c, h, hparts, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
+    case 4: return launch_mz<4>(P2, c, h, hparts, B, F, r, tau, n_hot, mask, logits, (uint4*)hf, hs, st);
     default: return hipErrorInvalidValue;
   }
 }
