@@ -50,14 +50,16 @@ def test_normalised_input_and_no_predictor_bias(gpu_ready, name, wl):
 
 
 @pytest.mark.parametrize("name,wl", SMALL, ids=[s[0] for s in SMALL])
-@pytest.mark.parametrize("B", [2, 5, 33])
+@pytest.mark.parametrize("B", [2, 5, 17, 33, 64])
 def test_union_normalised_input(gpu_ready, name, wl, B):
+    # from 17 tokens the normalisation is folded into the predictor (partials of P1 (x - x[0]) and row sums of P1)
     case = make_case(wl, 0, gpu_ready)
     x = 2.5 * _x(wl, B, 6) + 0.75            # un-normalised tokens; normalised per token on load
     say(f"[{name}] union B={B} x_norm")
     res = run_gpu(case, torch.from_numpy(x).to(gpu_ready), x_norm=True)
     st = check(case, x, res, x_norm=True)
     say("   ", st)
+    assert st["logit_err"] < 1e-4
 
 
 @pytest.mark.parametrize("name,wl", SMALL, ids=[s[0] for s in SMALL])
@@ -237,17 +239,21 @@ def test_full_size_layer(gpu_ready, name):
 
 # full-size union batches: the decode batches of the 13B shape that exceed the decode kernels, the Falcon shape at
 # B = 4, and the 70B Q4 prompt of 64 tokens
-UNION_FULL = [("c3", 4, sg.TAG_X_DECODE), ("c3", 8, sg.TAG_X_DECODE), ("c4", 4, sg.TAG_X_DECODE),
-              ("c5", 64, sg.TAG_X_PROMPT)]
+UNION_FULL = [("c3", 4, sg.TAG_X_DECODE, False), ("c3", 8, sg.TAG_X_DECODE, False),
+              ("c4", 4, sg.TAG_X_DECODE, False), ("c5", 64, sg.TAG_X_PROMPT, False),
+              ("c5", 64, sg.TAG_X_PROMPT, True)]
 
 
-@pytest.mark.parametrize("name,B,tag", UNION_FULL, ids=[f"{n}-B{b}" for n, b, _ in UNION_FULL])
-def test_full_size_union(gpu_ready, name, B, tag):
+@pytest.mark.parametrize("name,B,tag,xn", UNION_FULL, ids=[f"{n}-B{b}{'-xnorm' if xn else ''}"
+                                                          for n, b, _, xn in UNION_FULL])
+def test_full_size_union(gpu_ready, name, B, tag, xn):
     wl = sg.workload(name)
     layer = 0 if wl.L == 1 else 2
-    say(f"[full union {name} B={B}] generating layer {layer}")
+    say(f"[full union {name} B={B} x_norm={xn}] generating layer {layer}")
     case = make_case(wl, layer, gpu_ready)
     x = _x(wl, B, 0, tag=tag)
-    res = run_gpu(case, torch.from_numpy(x).to(gpu_ready))
-    st = check(case, x, res)
-    say(f"[full union {name} B={B}]: {st}")
+    if xn:                                    # tokens off unit scale and centre, normalised by the library
+        x = 1.9 * x - 0.4
+    res = run_gpu(case, torch.from_numpy(x).to(gpu_ready), x_norm=xn)
+    st = check(case, x, res, x_norm=xn)
+    say(f"[full union {name} B={B} x_norm={xn}]: {st}")
