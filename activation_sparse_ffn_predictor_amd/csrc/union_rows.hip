@@ -80,13 +80,17 @@ constexpr int NTX = 256;
 // One workgroup per token slot tok < NTT * 16 (slots >= B are zero). xf: [KB][NTT][NH][64] uint4, NH = 2 with EXACT
 // (hi, lo). xs[tok] = 2^e, the power of two the fragments are divided by. With nparts > 0 (XPT = 1) the values are
 // the sum of nparts partials x[p][B][D], added in share order (as k_sum_parts adds them).
+// PACK (EXACT, NTT = 1, B <= 8): one plane whose lane columns 0..7 hold the tokens' hi halves and 8..15 their lo
+// halves, so that one matrix-core product takes both (slots 8..15 write nothing).
 constexpr int SPLIT_PARTS_MAX = 16;
-template <int XPT, bool EXACT, bool PERM>
+template <int XPT, bool EXACT, bool PERM, bool PACK = false>
 __global__ __launch_bounds__(NTX) void k_split_x(const float* __restrict__ x, int x_norm, int B, int D, int NTT,
                                                  uint4* __restrict__ xf, float* __restrict__ xs, int nparts) {
-  constexpr int NH = EXACT ? 2 : 1;
+  static_assert(!PACK || EXACT, "packed planes are the hi and lo halves");
+  constexpr int NH = EXACT && !PACK ? 2 : 1;
   __shared__ float red[2 * (NTX / 64) + 4];
   const int tok = blockIdx.x;
+  if (PACK && tok >= 8) return;                        // block-uniform
   const bool real = tok < B;
   const int n4 = real ? D >> 2 : 0;                    // padding slots load nothing (all zero)
   const float* xb = x + (size_t)(real ? tok : 0) * D;
@@ -133,6 +137,7 @@ __global__ __launch_bounds__(NTX) void k_split_x(const float* __restrict__ x, in
   // float4 i holds elements 4 i .. 4 i + 3, half i % 2 of an 8-element group
   auto slot = [&](int kb, int q, int h) {
     const int f = PERM ? kb : (kb >> 2) * 4 + q, lg = PERM ? q : kb & 3;
+    if constexpr (PACK) return ((size_t)f * NTT + t) * 64 + (size_t)(lg * 16 + tl + 8 * h);
     return (((size_t)f * NTT + t) * NH + h) * 64 + (size_t)(lg * 16 + tl);
   };
 #pragma unroll
@@ -483,7 +488,7 @@ constexpr int R16 = 16;
 constexpr int UR16_MAX_B = 4;
 
 
-template <int ACT, bool Q4, bool EXACT>
+template <int ACT, bool Q4, bool EXACT, bool PACK>
 __global__ __launch_bounds__(NTR) void k_ur16(const void* __restrict__ Wg, const void* __restrict__ Sg,
                                               const float* __restrict__ bg, const void* __restrict__ Wu,
                                               const void* __restrict__ Su, const float* __restrict__ bu,
@@ -492,8 +497,9 @@ __global__ __launch_bounds__(NTR) void k_ur16(const void* __restrict__ Wg, const
                                               int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                               float* __restrict__ abuf, float* __restrict__ bmax) {
   static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
+  static_assert(!PACK || EXACT, "packed planes are the hi and lo halves");
   constexpr bool GT = ACT == 1;                        // ReGLU: a gate row per neuron
-  constexpr int NH = EXACT ? 2 : 1;                    // token fragment planes (hi, lo)
+  constexpr int NH = EXACT && !PACK ? 2 : 1;           // token fragment planes (hi, lo; PACK: both in one)
   constexpr int WV = Q4 ? 1 : 4;                       // uint4 of weights per lane and matrix per quad
   __shared__ uint64_t wl[WMAXR * NTR];                 // mask words
   __shared__ int roff[NTR];
@@ -590,7 +596,7 @@ __global__ __launch_bounds__(NTR) void k_ur16(const void* __restrict__ Wg, const
         if (GT) a_g = __builtin_bit_cast(half8, S.wg[q]);
       }
       const half8 xh = __builtin_bit_cast(half8, S.xv[q][0]);
-      if constexpr (EXACT) {
+      if constexpr (EXACT && !PACK) {
         const half8 xo = __builtin_bit_cast(half8, S.xv[q][NH - 1]);
         au = mfma16(a_u, xo, mfma16(a_u, xh, au));
         if (GT) ag = mfma16(a_g, xo, mfma16(a_g, xh, ag));
@@ -624,6 +630,13 @@ __global__ __launch_bounds__(NTR) void k_ur16(const void* __restrict__ Wg, const
     if (GT) ag += red[k][1][lane];
   }
   // epilogue: lane l holds rows 4 (l / 16) + i of token l % 16; the token's power of two back, bias, activation
+  if constexpr (PACK) {                                // column t + 8 holds the lo half's sums of token t < 8
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      au[i] += __shfl_xor(au[i], 8, 64);
+      if (GT) ag[i] += __shfl_xor(ag[i], 8, 64);
+    }
+  }
   const int tok = lane & 15;
   const int r0 = i0 + (lane >> 4) * 4;                 // this lane's 4 rows: half an octet
   const float sx = tok < B ? xsc[tok] : 0.f;
@@ -777,22 +790,23 @@ __global__ __launch_bounds__(64 * RT) void k_mz(const void* __restrict__ P2, con
   }
 }
 
-template <int XPT, bool EXACT, bool PERM>
+template <int XPT, bool EXACT, bool PERM, bool PACK = false>
 hipError_t launch_split_x(const float* x, int x_norm, int B, int D, int NTT, uint4* xf, float* xs, hipStream_t st,
                           int nparts = 0) {
-  hipLaunchKernelGGL((k_split_x<XPT, EXACT, PERM>), dim3(NTT * 16), dim3(NTX), 0, st, x, x_norm, B, D, NTT, xf, xs,
-                     nparts);
+  if (PACK && (NTT != 1 || B > 8)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_split_x<XPT, EXACT, PERM, PACK>), dim3(PACK ? 8 : NTT * 16), dim3(NTX), 0, st, x, x_norm, B,
+                     D, NTT, xf, xs, nparts);
   return hipGetLastError();
 }
 
-template <bool EXACT, bool PERM>
+template <bool EXACT, bool PERM, bool PACK = false>
 hipError_t split_x_xpt(int xpt, const float* x, int x_norm, int B, int D, int NTT, uint4* xf, float* xs,
                        hipStream_t st) {
-  if (xpt <= 1) return launch_split_x<1, EXACT, PERM>(x, x_norm, B, D, NTT, xf, xs, st);
-  if (xpt <= 2) return launch_split_x<2, EXACT, PERM>(x, x_norm, B, D, NTT, xf, xs, st);
-  if (xpt <= 4) return launch_split_x<4, EXACT, PERM>(x, x_norm, B, D, NTT, xf, xs, st);
-  if (xpt <= 8) return launch_split_x<8, EXACT, PERM>(x, x_norm, B, D, NTT, xf, xs, st);
-  if (xpt <= 16) return launch_split_x<16, EXACT, PERM>(x, x_norm, B, D, NTT, xf, xs, st);
+  if (xpt <= 1) return launch_split_x<1, EXACT, PERM, PACK>(x, x_norm, B, D, NTT, xf, xs, st);
+  if (xpt <= 2) return launch_split_x<2, EXACT, PERM, PACK>(x, x_norm, B, D, NTT, xf, xs, st);
+  if (xpt <= 4) return launch_split_x<4, EXACT, PERM, PACK>(x, x_norm, B, D, NTT, xf, xs, st);
+  if (xpt <= 8) return launch_split_x<8, EXACT, PERM, PACK>(x, x_norm, B, D, NTT, xf, xs, st);
+  if (xpt <= 16) return launch_split_x<16, EXACT, PERM, PACK>(x, x_norm, B, D, NTT, xf, xs, st);
   return hipErrorInvalidValue;
 }
 
@@ -813,12 +827,19 @@ hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void
   static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
   // the fragment order of the row kernel that runs (k_ur16, up to UR16_MAX_B tokens: fp16 block-major)
   constexpr bool BMUR = ur_block_major(Q4, ur_halves(NTT));
-  e = (NTT == 1 && B <= UR16_MAX_B ? !Q4 : BMUR) ? split_x_xpt<EXACT, true>(xpt, x, x_norm, B, D, NTT, xf, xs, st)
-                                                : split_x_xpt<EXACT, false>(xpt, x, x_norm, B, D, NTT, xf, xs, st);
+  // up to UR16_MAX_B tokens with fp16 rows and exact tokens: hi and lo packed in one plane (k_ur16)
+  constexpr bool PACK16 = NTT == 1 && !Q4 && EXACT;
+  static_assert(UR16_MAX_B <= 8, "packed planes hold up to 8 tokens");
+  const bool ur16 = NTT == 1 && B <= UR16_MAX_B;
+  if (PACK16 && ur16)
+    e = split_x_xpt<EXACT, true, PACK16>(xpt, x, x_norm, B, D, NTT, xf, xs, st);
+  else
+    e = (ur16 ? !Q4 : BMUR) ? split_x_xpt<EXACT, true>(xpt, x, x_norm, B, D, NTT, xf, xs, st)
+                            : split_x_xpt<EXACT, false>(xpt, x, x_norm, B, D, NTT, xf, xs, st);
   if (e != hipSuccess) return e;
   if ((F + 63) / 64 > WMAXR * NTR || KS < 1 || (KS > 1 && !pre)) return hipErrorInvalidValue;
-  if (NTT == 1 && B <= UR16_MAX_B) {                   // 16-row workgroups, k split over the waves
-    SFFN_LAUNCH(2, (k_ur16<ACT, Q4, EXACT>), dim3((F + R16 - 1) / R16), dim3(NTR), 0, st, Wg, Sg, bg, Wu, Su, bu,
+  if (ur16) {                                          // 16-row workgroups, k split over the waves
+    SFFN_LAUNCH(2, (k_ur16<ACT, Q4, EXACT, PACK16>), dim3((F + R16 - 1) / R16), dim3(NTR), 0, st, Wg, Sg, bg, Wu, Su, bu,
                 (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax);
     return hipGetLastError();
   }
