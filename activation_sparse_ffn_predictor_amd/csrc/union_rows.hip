@@ -482,10 +482,11 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
 // activation, and writes the tile (octet order, zeros past n and B) and its largest |a| per token
 // (bmax[(i0 / 16) * B + token]). Workgroups past the union but inside its last 64-row block write a zero tile.
 constexpr int R16 = 16;
-// Up to 4 tokens the 16-row kernel (k split over the waves of a workgroup) runs; from 5 tokens its token fragments,
-// read again by every 16-row workgroup, cost more than the k-share combine of the 64-row kernel. Measured at the
-// 13B shape: 4 tokens 1616 -> 1689 tokens/s with the 16-row kernel, 8 tokens 2552 -> 2398.
-constexpr int UR16_MAX_B = 4;
+// Up to 6 tokens the 16-row kernel (k split over the waves of a workgroup) runs; beyond, its token fragments, read
+// again by every 16-row workgroup, cost more than the k-share combine of the 64-row kernel. Measured at the 13B
+// shape with the packed fragments (same box): 5 tokens 1967 -> 2114 tokens/s with the 16-row kernel, 6 tokens
+// 2252 -> 2321, 8 tokens 2692 -> 2654 (falcon 40B 2078 -> 2067, 7B 3773 -> 3905).
+constexpr int UR16_MAX_B = 6;
 
 
 template <int ACT, bool Q4, bool EXACT, bool PACK>
