@@ -183,7 +183,7 @@ constexpr bool ur_block_major(bool q4, int kh) { return !q4 && kh == 1; }
 
 // k_ur: RT row tiles of 16 rows (4 or 8) and KH k halves (1 or 2); NW = RT KH waves, wave w takes row tile w % RT
 // and k half w / RT of every chunk
-template <int RT, int KH, int NTT, int ACT, bool Q4, bool EXACT>
+template <int RT, int KH, int NTT, int ACT, bool Q4, bool EXACT, bool PACK>
 __global__ __launch_bounds__(64 * RT * KH) __attribute__((amdgpu_waves_per_eu(RT * KH >= 8 ? 4 : 2)))
 void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
           const float* __restrict__ bg, const void* __restrict__ Wu,
@@ -195,11 +195,12 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
           float* __restrict__ pre, int KS) {
   static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
   static_assert((RT == 4 || RT == 8) && (KH == 1 || KH == 2), "4 or 8 row tiles, 1 or 2 k halves");
+  static_assert(!PACK || (EXACT && NTT == 1), "packed planes: exact tokens of one tile");
   constexpr int NW = RT * KH;
   constexpr int NTU = 64 * NW;
   constexpr int RB = 16 * RT;                          // union rows per workgroup
   constexpr bool GT = ACT == 1;                        // ReGLU: a gate row per neuron
-  constexpr int NH = EXACT ? 2 : 1;                    // token fragment planes (hi, lo)
+  constexpr int NH = EXACT && !PACK ? 2 : 1;           // token fragment planes (hi, lo; PACK: both in one)
   constexpr int KC = URChunk<Q4>::KC;
   constexpr int QC = KC / 4;                           // quads per chunk
   constexpr int XT = KC * NTT * NH * 64;               // uint4 of token fragments per chunk
@@ -352,7 +353,7 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
       for (int t = 0; t < NTT; ++t) {
         const int f = (((gqh + i) * 4 + q) * NTT + t) * NH;
         const half8 xh = __builtin_bit_cast(half8, xl[buf][f * 64 + lane]);
-        if constexpr (EXACT) {
+        if constexpr (EXACT && !PACK) {
           const half8 xo = __builtin_bit_cast(half8, xl[buf][(f + 1) * 64 + lane]);
           au[t] = mfma16(a_u, xo, mfma16(a_u, xh, au[t]));
           if (GT) ag[t] = mfma16(a_g, xo, mfma16(a_g, xh, ag[t]));
@@ -410,6 +411,13 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
   // epilogue (first half): the token's power of two back; one share: bias and activation, else the partial
   // pre-activations
   float amx[NTT];                                      // largest |a| of this lane's rows, per token tile
+  if (PACK && kh == 0) {                               // column t + 8 holds the lo half's sums of token t < 8
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      au[0][i] += __shfl_xor(au[0][i], 8, 64);
+      if (GT) ag[0][i] += __shfl_xor(ag[0][i], 8, 64);
+    }
+  }
   if (kh == 0) {
     int idr[4];                                        // the rows of this lane's 4 outputs (D layout)
 #pragma unroll
@@ -828,35 +836,40 @@ hipError_t launch_ur(const void* Wg, const void* Sg, const float* bg, const void
   static_assert(!(Q4 && EXACT), "Q4_0 rows take fp16 tokens");
   // the fragment order of the row kernel that runs (k_ur16, up to UR16_MAX_B tokens: fp16 block-major)
   constexpr bool BMUR = ur_block_major(Q4, ur_halves(NTT));
-  // up to UR16_MAX_B tokens with fp16 rows and exact tokens: hi and lo packed in one plane (k_ur16)
-  constexpr bool PACK16 = NTT == 1 && !Q4 && EXACT;
-  static_assert(UR16_MAX_B <= 8, "packed planes hold up to 8 tokens");
+  // up to 8 tokens with fp16 rows and exact tokens: hi and lo packed in one plane (block-major, as both row kernels
+  // read fp16 rows there)
+  constexpr bool PK = NTT == 1 && !Q4 && EXACT;
+  static_assert(UR16_MAX_B <= 8 && (!PK || BMUR), "packed planes hold up to 8 tokens");
   const bool ur16 = NTT == 1 && B <= UR16_MAX_B;
-  if (PACK16 && ur16)
-    e = split_x_xpt<EXACT, true, PACK16>(xpt, x, x_norm, B, D, NTT, xf, xs, st);
+  const bool pack = PK && B <= 8;
+  if (pack)
+    e = split_x_xpt<EXACT, true, PK>(xpt, x, x_norm, B, D, NTT, xf, xs, st);
   else
     e = (ur16 ? !Q4 : BMUR) ? split_x_xpt<EXACT, true>(xpt, x, x_norm, B, D, NTT, xf, xs, st)
                             : split_x_xpt<EXACT, false>(xpt, x, x_norm, B, D, NTT, xf, xs, st);
   if (e != hipSuccess) return e;
   if ((F + 63) / 64 > WMAXR * NTR || KS < 1 || (KS > 1 && !pre)) return hipErrorInvalidValue;
   if (ur16) {                                          // 16-row workgroups, k split over the waves
-    SFFN_LAUNCH(2, (k_ur16<ACT, Q4, EXACT, PACK16>), dim3((F + R16 - 1) / R16), dim3(NTR), 0, st, Wg, Sg, bg, Wu, Su, bu,
+    SFFN_LAUNCH(2, (k_ur16<ACT, Q4, EXACT, PK>), dim3((F + R16 - 1) / R16), dim3(NTR), 0, st, Wg, Sg, bg, Wu, Su, bu,
                 (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax);
     return hipGetLastError();
   }
   constexpr int KH = ur_halves(NTT);
   if constexpr (KH == 2) {
     if (F > UR_WIDE_ROWS) {
-      SFFN_LAUNCH(2, (k_ur<8, KH, NTT, ACT, Q4, EXACT>), dim3((F + 127) / 128 * KS), dim3(64 * 8 * KH), 0, st, Wg,
-                  Sg, bg, Wu, Su, bu, (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
+      SFFN_LAUNCH(2, (k_ur<8, KH, NTT, ACT, Q4, EXACT, false>), dim3((F + 127) / 128 * KS), dim3(64 * 8 * KH), 0, st,
+                  Wg, Sg, bg, Wu, Su, bu, (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
       e = hipGetLastError();
       if (e != hipSuccess || KS == 1) return e;
       return sffn_launch_act_combine(ACT, pre, KS, active, n_active, GT_BIAS(ACT, bg, bu), B, F, abuf, bmax, st);
     }
   }
-  {
-    SFFN_LAUNCH(2, (k_ur<4, KH, NTT, ACT, Q4, EXACT>), dim3((F + 63) / 64 * KS), dim3(64 * 4 * KH), 0, st, Wg, Sg,
-                bg, Wu, Su, bu, (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
+  if (pack) {
+    SFFN_LAUNCH(2, (k_ur<4, KH, NTT, ACT, Q4, EXACT, PK>), dim3((F + 63) / 64 * KS), dim3(64 * 4 * KH), 0, st, Wg,
+                Sg, bg, Wu, Su, bu, (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
+  } else {
+    SFFN_LAUNCH(2, (k_ur<4, KH, NTT, ACT, Q4, EXACT, false>), dim3((F + 63) / 64 * KS), dim3(64 * 4 * KH), 0, st, Wg,
+                Sg, bg, Wu, Su, bu, (const uint4*)xf, xs, B, D, F, mask, active, n_active, abuf, bmax, pre, KS);
   }
   e = hipGetLastError();
   if (e != hipSuccess || KS == 1) return e;
