@@ -37,10 +37,14 @@ constexpr int KS_MAX = 16;           // k shares of the multi-token predictor's 
 constexpr int UD_KS_MAX = 16;        // row shares of the union down projection
 constexpr int MZ_MIN_B = 17;         // tokens from which the predictor's stage 2 runs on pre-split h fragments
 constexpr int G_FUSED = 256;         // blocks (= partial sums of y) of the fused single-token forward
-#ifndef SFFN_UNION_EXACT
-#define SFFN_UNION_EXACT 1
+// fp16 weights in the union kernels: up to this many tokens the tokens and activations enter the matrix cores as
+// exact fp16 hi + lo halves (packed into one operand plane, at no measured cost); beyond, as one fp16 value each
+// (relative 2^-11, as with Q4_0 weights), which saves a second product per k block. Same box, 13B layer:
+// 16 tokens 4292 -> 4365, 32 tokens 5871 -> 6183, 64 tokens 9336 -> 9911 tokens/s.
+#ifndef SFFN_UNION_EXACT_MAX_B
+#define SFFN_UNION_EXACT_MAX_B 8
 #endif
-constexpr bool UNION_EXACT = SFFN_UNION_EXACT != 0;   // union row kernel: tokens as fp16 hi + lo, scales on fp32
+bool union_exact(int B) { return B <= SFFN_UNION_EXACT_MAX_B; }
 constexpr size_t MAX_TENSOR = (size_t)1 << 31;   // buffer loads address each tensor with 31-bit byte offsets
 #ifndef SFFN_NOALLOC_SCRATCH_BYTES
 #define SFFN_NOALLOC_SCRATCH_BYTES (16u << 20)   // device scratch of sffn_decode_noalloc, per GPU
@@ -171,11 +175,11 @@ namespace {
 hipError_t run_union(int act, bool q4, const void* Wg, const void* Sg, const float* bg, const void* Wu, const void* Su,
                      const float* bu, const void* Wd, const void* Sd, const float* x, int x_norm, int B, int D, int F,
                      const uint64_t* mask, int32_t* active, int32_t* n_active, float* y, void* ws, hipStream_t st) {
-  hipError_t e = sffn_launch_rows_ur(act, q4, UNION_EXACT, Wg, Sg, bg, Wu, Su, bu, x, x_norm, B, D, F, mask, active,
+  hipError_t e = sffn_launch_rows_ur(act, q4, union_exact(B), Wg, Sg, bg, Wu, Su, bu, x, x_norm, B, D, F, mask, active,
                                      n_active, ws_abuf(ws), ws_bmax(ws, B, D, F), ws_xf(ws, B, D, F),
                                      ws_xs(ws, B, D, F), ws_pre(ws, B, D, F), st);
   if (e != hipSuccess) return e;
-  return sffn_launch_down_ud(q4, UNION_EXACT, Wd, Sd, active, n_active, ws_abuf(ws), ws_bmax(ws, B, D, F),
+  return sffn_launch_down_ud(q4, union_exact(B), Wd, Sd, active, n_active, ws_abuf(ws), ws_bmax(ws, B, D, F),
                              sffn_ur_bmax_shift(B), B, D, F, ws_part(ws, B, D, F), sffn_ud_shares(D, UD_KS_MAX), y, st);
 }
 

@@ -52,9 +52,12 @@
  * B * D <= 16384 when F > 32768. Every other B > 1 runs the union kernels on
  * the matrix cores ("Neuron-aware operator": each active row is read once for
  * the whole batch); these compact the whole mask inside one workgroup and
- * take F <= 32768 in sffn_forward / sffn_forward_q4. fp32
- * inputs enter the matrix cores as two fp16 halves (x = hi + lo), so the
- * batch results match the decode kernels' to within fp32 rounding.
+ * take F <= 32768 in sffn_forward / sffn_forward_q4. With fp16 weights and
+ * up to 8 tokens the fp32 inputs and activations enter the matrix cores as
+ * two fp16 halves (x = hi + lo), so those results match the decode kernels'
+ * to within fp32 rounding; larger batches, and Q4_0 weights, take each as one
+ * fp16 value after a per-token power-of-two scaling (relative 2^-11 per
+ * value, inside the output tolerance the parity tests hold).
  *
  * Workspace (sffn_workspace_size bytes, 256-byte parts, caller-owned, no
  * state kept between calls): activations a [F, B] fp32 (for B == 1 at least
