@@ -27,7 +27,9 @@ SMALL = [
 
 
 @pytest.mark.parametrize("name,wl", SMALL, ids=[s[0] for s in SMALL])
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 8, 16, 17, 64])
+# 6 and 7 tokens: the last batch of the 16-row union kernel and the first of the 64-row one with the packed token
+# plane; 9 tokens: the first with one fp16 value per token element
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 6, 7, 8, 9, 16, 17, 64])
 def test_small_layers(gpu_ready, name, wl, B):
     case = make_case(wl, 0, gpu_ready)
     for step in range(3):
