@@ -17,7 +17,8 @@
 // scales it by a power of two 2^-e with 2^e the smallest power above max |x| (exact, and it keeps every value
 // inside fp16's range), and writes the B-operand fragments, fragment f = (quad, q, token tile) as 64 lanes x 16
 // bytes, so a wave reads one as a contiguous kilobyte. EXACT adds a plane of fp16 residuals (x = hi + lo, the
-// single-token kernels' fp32 to within 2^-22); without it the operand is fp16(x).
+// single-token kernels' fp32 to within 2^-22); without it the operand is fp16(x). PACK (EXACT, up to 8 tokens)
+// puts both halves in one plane: lane columns 0..7 the tokens' hi halves, 8..15 their lo halves.
 //
 // k_ur (workgroups of 4 or 8 waves, 64 dense indices each, one 16-row tile per wave and, with 8 waves, one k half
 // of every chunk per wave; every token tile; KS workgroups per 64 rows split the quads): the workgroup's union rows
@@ -28,7 +29,8 @@
 // out-of-range buffer loads return 0). Q4_0 weights become exact fp16 (q - 8) through the exponent trick (0x64qq
 // is 1024 + q in fp16), times the block scale in fp16 (one rounding per weight; the whole block's scale is one
 // lane's, so no per-block fp32 step is needed). fp16 weights enter as they are; with EXACT each token operand is
-// two fp16 halves and every product is exact. With two k halves the second half's sums meet the first's in LDS,
+// two fp16 halves and every product is exact (PACK: both halves in one operand, one product per k block, the
+// lo columns added to the hi ones in the epilogue). With two k halves the second half's sums meet the first's in LDS,
 // always added in that order. The epilogue undoes the token's power of two and, with one share, adds the bias and
 // applies the activation; with KS shares each writes its partial pre-activations and k_act_combine (union.hip)
 // adds them in share order.
