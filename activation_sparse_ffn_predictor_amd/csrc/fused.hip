@@ -5,8 +5,9 @@
 // trip, and the down projection is accumulated where the activation is computed, so the activations never go
 // through memory and the column gather needs no launch of its own.
 //
-// k_fused1 (G >= 64 blocks of 8 waves): round 1 loads x and the mask words; a block scan gives each thread the
-// set bits before its mask word. Dense index i goes to block i % G, so every block gets a near-equal share. A
+// k_fused1 (up to 256 blocks of 8 waves): round 1 loads x and the mask words; a block scan gives each thread the
+// set bits before its mask word and the active count n. G = max(64, ceil(n / 8)) of the blocks (at most all) take
+// rows, so that a block's rows fill one pass; dense index i goes to block i % G, a near-equal share each. A
 // block's rows are G apart in dense order, so a mask word holds at most one of them: each thread finds its word's
 // one by a rank select, and the block has the ids of all its rows in LDS at once. The gather (rowgather.h,
 // shared with the folded kernel of decode.hip): per pass of 8 rows, each wave
@@ -19,7 +20,7 @@
 // values without bank conflicts; each pair of nibbles becomes exact fp16 (q - 8) and meets its pair of x in a
 // packed dot product (v_dot2, exact products, fp32 sum). The pass's W_downT nibble rows are loaded straight into
 // LDS (buffer loads with the LDS destination) instead of registers.
-// k_sum_rows: y[d] = sum over blocks b < min(G, n) of part[b][d] in a fixed order (16 groups of blocks per
+// k_sum_rows: y[d] = sum over the blocks b < min(G, n) that took rows of part[b][d] in a fixed order (16 groups per
 // column, each summed in block order, then the groups in order); all of a thread's loads are issued together.
 // Every sum has a fixed order, so the results do not depend on timing.
 #include "common.h"
@@ -36,6 +37,19 @@ constexpr int WMAX_F = 1;            // mask words per thread kept in LDS (nw <=
 #define SFFN_Q4_FUSED_RPW 1          // Q4_0 rows per wave per pass (measured best at the 70B shape: 1, over 2 and 3)
 #endif
 
+// The blocks that take rows, out of the Gmax launched, for n active rows: just enough for one pass of `pass` rows
+// each (at least 64, so that a mask word holds at most one row of a block). Fuller blocks mean fewer partial sums
+// of y and fewer idle slots in a pass (same box, one pass per block: 13B 1011 -> 1040, 40B 493 -> 499 tokens/s
+// against all 256). k_sum_rows takes the same count from n.
+__device__ __forceinline__ int fused_blocks(int n, int Gmax, int pass) {
+  return min(Gmax, max(64, (n + pass - 1) / pass));
+}
+// The most rows a block can take (the length of its row-id list in LDS): one pass while n <= pass * Gmax, else
+// ceil(n / Gmax) <= ceil(F / Gmax).
+__host__ __device__ __forceinline__ int fused_max_rows(int F, int Gmax, int pass) {
+  return max(pass, (F + Gmax - 1) / Gmax);
+}
+
 template <int ACT, int NCH, int DCH>
 __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, const float* __restrict__ bg,
                                                  const uint4* __restrict__ Wu, const float* __restrict__ bu,
@@ -51,7 +65,7 @@ __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, c
   float* av = reinterpret_cast<float*>(tmp + NT_F / 64 + 4);             // [FW] activations of the pass
   float* red = av + FW;                                                  // [2 * FW] normalisation scratch
   float* xs = red + 2 * FW + 4;                                          // [D] x (16-byte aligned)
-  int* bids = reinterpret_cast<int*>(xs + D);                            // [ceil(F / G)] the block's row ids
+  int* bids = reinterpret_cast<int*>(xs + D);                            // [fused_max_rows] the block's row ids
   const int n4 = D >> 2;
   constexpr int XPT = (128 * NCH + NT_F - 1) / NT_F;   // float4 of x per thread: D / 4 <= 128 * NCH
 
@@ -61,8 +75,8 @@ __global__ __launch_bounds__(NT_F) void k_fused1(const uint4* __restrict__ Wg, c
   const float x0 = x[0];                               // shift for the single-pass statistics
   const int n = mask_prefix<NT_F, WMAX_F>(mask, nw, F, 1, wl, roff, tmp);
   if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
-  const int G = gridDim.x;
-  if ((int)blockIdx.x >= n) return;                    // block-uniform: no row here; its partial is never read
+  const int G = fused_blocks(n, gridDim.x, FW);
+  if ((int)blockIdx.x >= min(G, n)) return;           // block-uniform: no row here; its partial is never read
   // the block's rows: dense indices blk + G * k, k < nrow, their ids in LDS (one rank select per mask word)
   const int blk = blockIdx.x;
   const int nrow = (n - blk + G - 1) / G;
@@ -123,10 +137,10 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
   float* av = reinterpret_cast<float*>(tmp + NT_F / 64 + 4);             // [NS] activations of the pass
   float* red = av + NS;                                                  // [3 * FW] normalisation / max scratch
   uint2* xt = reinterpret_cast<uint2*>(red + 3 * FW + 4);                // [8][D / 32] x as fp16 pieces (16-B aligned)
-  int* bids = reinterpret_cast<int*>(xt + 8 * nblk);                    // [ceil(F / G)] the block's row ids
+  int* bids = reinterpret_cast<int*>(xt + 8 * nblk);                    // [fused_max_rows] the block's row ids
   const uint32_t rstride = (uint32_t)NQ * 1024u;       // 1 kB pieces (64 lanes x 16 bytes) of a nibble row
   uint8_t* sdn = reinterpret_cast<uint8_t*>(lds64) +   // [NS][rstride] the pass's W_downT nibble rows
-                 ((reinterpret_cast<uintptr_t>(bids + (F + gridDim.x - 1) / gridDim.x) -
+                 ((reinterpret_cast<uintptr_t>(bids + fused_max_rows(F, gridDim.x, FW * RPW)) -
                    reinterpret_cast<uintptr_t>(lds64) + 15) & ~(uintptr_t)15);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n4 = D >> 2;
@@ -137,8 +151,8 @@ __global__ __launch_bounds__(NT_F) void k_fused1_q4(const uint4* __restrict__ qg
   const float x0 = x[0];
   const int n = mask_prefix<NT_F, WMAX_F>(mask, nw, F, 1, wl, roff, tmp);
   if (blockIdx.x == 0 && threadIdx.x == 0) *n_active = n;
-  const int G = gridDim.x;
-  if ((int)blockIdx.x >= n) return;                    // block-uniform: no row here; its partial is never read
+  const int G = fused_blocks(n, gridDim.x, FW * RPW);
+  if ((int)blockIdx.x >= min(G, n)) return;           // block-uniform: no row here; its partial is never read
   const uint32_t qbytes = (uint32_t)F * (uint32_t)nblk * 16u, sbytes = (uint32_t)F * (uint32_t)nblk * 2u;
   const Buf bqu(qu, qbytes), bsu(su, sbytes), bqd(qd, qbytes), bsd(sd, sbytes);
   const Buf bqg(ACT == 1 ? (const void*)qg : (const void*)qu, ACT == 1 ? qbytes : 0u);
@@ -341,7 +355,7 @@ constexpr int SG = NT_S / SC;
 constexpr int SPG = 16;              // partials per group: G <= SG * SPG = 256
 
 __global__ __launch_bounds__(NT_S) void k_sum_rows(const float* __restrict__ part, const int32_t* __restrict__ n_active,
-                                                   int G, int D, float* __restrict__ y) {
+                                                   int G, int pass, int D, float* __restrict__ y) {
   __shared__ float red[SG][SC];
   const int c = threadIdx.x % SC, g = threadIdx.x / SC;
   const int col = blockIdx.x * SC + c;
@@ -355,7 +369,8 @@ __global__ __launch_bounds__(NT_S) void k_sum_rows(const float* __restrict__ par
     const int b = g + SG * k;
     v[k] = bp.ldf(boff(b < G && col < D, ((uint32_t)b * D + col) * 4u));
   }
-  const int nb = min(G, max(*n_active, 0));            // blocks that wrote a partial
+  const int na = max(*n_active, 0);
+  const int nb = min(fused_blocks(na, G, pass), na);   // blocks that wrote a partial
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < SPG; ++k) s += (g + SG * k < nb) ? v[k] : 0.f;
@@ -376,7 +391,8 @@ hipError_t launch_fused(const void* Wg, const float* bg, const void* Wu, const f
   const int nw = (F + 63) / 64;
   if (G < 64) return hipErrorInvalidValue;            // one owned row per mask word at most
   const size_t lds = (size_t)((nw + 1) & ~1) * 8 + (NT_F + NT_F / 64 + 4) * sizeof(int) +
-                     (FW + 2 * FW + 4 + (size_t)D) * sizeof(float) + ((size_t)(F + G - 1) / G) * sizeof(int) + 16;
+                     (FW + 2 * FW + 4 + (size_t)D) * sizeof(float) + (size_t)fused_max_rows(F, G, FW) * sizeof(int) +
+                     16;
   static LdsLimit lds_limit;   // per kernel, set once per device
   size_t avail = 0;
   hipError_t ea = lds_limit.get((const void*)k_fused1<ACT, NCH, DCH>, &avail);
@@ -387,7 +403,7 @@ hipError_t launch_fused(const void* Wg, const float* bg, const void* Wu, const f
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (G > SG * SPG) return hipErrorInvalidValue;
-  SFFN_LAUNCH(3, k_sum_rows, dim3((D + SC - 1) / SC), dim3(NT_S), 0, st, part, n_active, G, D, y);
+  SFFN_LAUNCH(3, k_sum_rows, dim3((D + SC - 1) / SC), dim3(NT_S), 0, st, part, n_active, G, FW, D, y);
   return hipGetLastError();
 }
 
@@ -415,7 +431,8 @@ hipError_t launch_fused_q4(const uint8_t* qg, const void* sg, const float* bg, c
   constexpr int NS = FW * RPW;
   if (G < 64) return hipErrorInvalidValue;            // one owned row per mask word at most
   const size_t lds = (size_t)((nw + 1) & ~1) * 8 + (NT_F + NT_F / 64 + 4) * sizeof(int) +
-                     (NS + 3 * FW + 4 + (size_t)D / 2) * sizeof(float) + ((size_t)(F + G - 1) / G) * sizeof(int) +
+                     (NS + 3 * FW + 4 + (size_t)D / 2) * sizeof(float) +
+                     (size_t)fused_max_rows(F, G, NS) * sizeof(int) +
                      16 + (size_t)NS * NQ * 1024;   // + the pass's nibble rows (16-byte aligned)
   static LdsLimit lds_limit;   // per kernel, set once per device
   size_t avail = 0;
@@ -427,7 +444,7 @@ hipError_t launch_fused_q4(const uint8_t* qg, const void* sg, const float* bg, c
               n_active, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  SFFN_LAUNCH(3, k_sum_rows, dim3((D + SC - 1) / SC), dim3(NT_S), 0, st, part, n_active, G, D, y);
+  SFFN_LAUNCH(3, k_sum_rows, dim3((D + SC - 1) / SC), dim3(NT_S), 0, st, part, n_active, G, NS, D, y);
   return hipGetLastError();
 }
 
