@@ -301,9 +301,11 @@ def measure(wl, B: int, args, with_prompt: bool):
     p2_bytes = np.tile(2.0 * (wl.F - hots) * ranks, P)
     if path == _lib.PATH_FUSED:
         # kernel 2 gathers gate/up and W_downT rows (folded: after reading the block's P2 rows); kernel 3 adds
-        # the per-block partial sums of y (folded: all 256 of them, and assembles the mask and ids)
+        # the per-block partial sums of y (folded: all 256 of them, and assembles the mask and ids; fused: those of
+        # the max(64, ceil(n / 8)) blocks that took rows, at most n and 256)
         bytes_rows = n_prof * wl.n_mats * one_row + np.where(fold, p2_bytes, 0.0)
-        bytes_cols = (np.where(fold, 256.0, np.minimum(n_prof, 256)) * wl.D + B * wl.D) * 4.0
+        working = np.minimum(np.minimum(np.maximum(64.0, np.ceil(n_prof / 8.0)), 256.0), n_prof)
+        bytes_cols = (np.where(fold, 256.0, working) * wl.D + B * wl.D) * 4.0
     else:
         bytes_rows = n_prof * rows_mats * one_row                # per launch of kernel 2
         bytes_cols = n_prof * one_row                            # per launch of kernel 3
@@ -342,8 +344,8 @@ def measure(wl, B: int, args, with_prompt: bool):
         "kernel_us": {names[k]: round(v, 3) for k, v in mean_us.items()},
         "kernel_timing": timing,
         "prompt": prompt,
-        # every algorithmic byte the dominant kernel reads or writes per launch (for a folded layer its P2 rows
-        # too, for the fused kernel its partial sums of y), over that kernel's own launch time
+        # the dominant kernel's algorithmic bytes per launch (the active rows it gathers; for a folded layer its P2
+        # rows too; not the partial sums of y, which are this design's overhead), over its own launch time
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "traffic_detail": traffic_detail},
