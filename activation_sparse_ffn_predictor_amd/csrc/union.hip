@@ -288,11 +288,21 @@ __global__ __launch_bounds__(256) void k_act_combine(const float* __restrict__ p
   if ((int)threadIdx.x < B) bmax[(size_t)blockIdx.x * B + threadIdx.x] = __uint_as_float(smx[threadIdx.x]);
 }
 
-__global__ void k_sum_parts(const float* __restrict__ part, int KS, int n, float* __restrict__ y) {
+// Every share's load is issued before the first add (a loop over the runtime KS had each load wait for the
+// previous one: one round trip per share), then the shares are added in order.
+constexpr int SUM_PARTS_MAX = 16;
+__global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ part, int KS, int n,
+                                                   float* __restrict__ y) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const Buf bp(part, (uint32_t)KS * (uint32_t)n * 4u);
+  float v[SUM_PARTS_MAX];
+#pragma unroll
+  for (int k = 0; k < SUM_PARTS_MAX; ++k) v[k] = bp.ldf(boff(i < n && k < KS, ((uint32_t)k * (uint32_t)n + i) * 4u));
   if (i >= n) return;
   float s = 0.f;
-  for (int k = 0; k < KS; ++k) s += part[(size_t)k * n + i];
+#pragma unroll
+  for (int k = 0; k < SUM_PARTS_MAX; ++k)
+    if (k < KS) s += v[k];
   y[i] = s;
 }
 
@@ -309,6 +319,7 @@ hipError_t predict_mt(const void* P1, const void* P2, const float* c, const floa
     if (hf)                                            // the split adds the partials itself (one launch fewer)
       return sffn_launch_predict_mz(P2, c, hpart, KSH, B, F, r, tau, n_hot, mask, logits, hf, hs, st);
     const int nh = B * r;
+    if (KSH > SUM_PARTS_MAX || (size_t)KSH * nh * 4 >= ((size_t)1 << 31)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_sum_parts, dim3((nh + 255) / 256), dim3(256), 0, st, hpart, KSH, nh, hbuf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -335,6 +346,7 @@ hipError_t sffn_launch_act_combine(int act, const float* pre, int KSP, const int
 
 // y[i] = sum of the KS partials part[k * n + i], in share order
 hipError_t sffn_launch_sum_parts(const float* part, int KS, int n, float* y, hipStream_t st) {
+  if (KS < 1 || KS > SUM_PARTS_MAX || (size_t)KS * n * 4 >= ((size_t)1 << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_sum_parts, dim3((n + 255) / 256), dim3(256), 0, st, part, KS, n, y);
   return hipGetLastError();
 }
