@@ -255,34 +255,52 @@ __global__ __launch_bounds__(256) void k_act_combine(const float* __restrict__ p
   __syncthreads();
   const int BP = (B + 15) & ~15;
   const uint32_t FB = (uint32_t)F * (uint32_t)B;
-  const Buf bp(pre, (uint32_t)KSP * 2u * FB * 4u);
-  for (int q = (int)threadIdx.x; q < 64 * BP; q += 256) {
-    const int b = (q >> 3) % BP, i = i0 + (q / (8 * BP)) * 8 + (q & 7);
-    float a = 0.f;
-    if (i < n && b < B) {
-      const uint32_t e = (uint32_t)i * (uint32_t)B + (uint32_t)b;
-      float vu[KSP_MAX], vg[KSP_MAX];                  // every share's loads in flight at once
+  const Buf bp(pre, (uint32_t)KSP * 2u * FB * 4u), bid(active, (uint32_t)F * 4u);
+  const Buf bbi(bias ? (const void*)bias : (const void*)pre, bias ? (uint32_t)F * 4u : 0u);   // no bias: 0
+  // groups of 4 elements per thread: every share's loads and the row ids in one round trip, the biases in a
+  // second (an element at a time, the row id and bias loads had made two dependent round trips per element)
+  constexpr int EG = 4;
+  for (int g0 = 0; g0 < 64 * BP; g0 += 256 * EG) {   // block-uniform
+    float vu[EG][KSP_MAX], vg[EG][KSP_MAX];
+    int id[EG];
+    bool ok[EG];
+#pragma unroll
+    for (int j = 0; j < EG; ++j) {
+      const int q = g0 + j * 256 + (int)threadIdx.x;
+      const int b = (q >> 3) % BP, i = i0 + (q / (8 * BP)) * 8 + (q & 7);
+      ok[j] = q < 64 * BP && i < n && b < B;
+      const uint32_t e = ok[j] ? (uint32_t)i * (uint32_t)B + (uint32_t)b : 0u;
 #pragma unroll
       for (int k = 0; k < KSP_MAX; ++k) {
-        vu[k] = bp.ldf(boff(k < KSP, ((uint32_t)(2 * k) * FB + e) * 4u));
-        vg[k] = ACT == 1 ? bp.ldf(boff(k < KSP, ((uint32_t)(2 * k + 1) * FB + e) * 4u)) : 0.f;
+        vu[j][k] = bp.ldf(boff(ok[j] && k < KSP, ((uint32_t)(2 * k) * FB + e) * 4u));
+        vg[j][k] = ACT == 1 ? bp.ldf(boff(ok[j] && k < KSP, ((uint32_t)(2 * k + 1) * FB + e) * 4u)) : 0.f;
       }
-      float u = 0.f, g = 0.f;
-#pragma unroll
-      for (int k = 0; k < KSP_MAX; ++k) {              // in share order (shares past KSP read 0)
-        u += vu[k];
-        if (ACT == 1) g += vg[k];
-      }
-      const float bi = bias ? bias[active[i]] : 0.f;
-      if (ACT == 1) {
-        a = fmaxf(g + bi, 0.f) * u;
-      } else {
-        a = fmaxf(u + bi, 0.f);
-        if (ACT == 2) a *= a;
-      }
-      atomicMax(&smx[b], __float_as_uint(fabsf(a)));   // LDS; non-negative floats order as their bits
+      id[j] = (int)bid.ldu(boff(ok[j], (uint32_t)(ok[j] ? i : 0) * 4u));
     }
-    abuf[(size_t)i0 * BP + q] = a;
+    float bi[EG];
+#pragma unroll
+    for (int j = 0; j < EG; ++j) bi[j] = bbi.ldf(boff(ok[j], (uint32_t)id[j] * 4u));
+#pragma unroll
+    for (int j = 0; j < EG; ++j) {
+      const int q = g0 + j * 256 + (int)threadIdx.x;
+      float a = 0.f;
+      if (ok[j]) {
+        float u = 0.f, g = 0.f;
+#pragma unroll
+        for (int k = 0; k < KSP_MAX; ++k) {          // in share order (shares past KSP read 0)
+          u += vu[j][k];
+          if (ACT == 1) g += vg[j][k];
+        }
+        if (ACT == 1) {
+          a = fmaxf(g + bi[j], 0.f) * u;
+        } else {
+          a = fmaxf(u + bi[j], 0.f);
+          if (ACT == 2) a *= a;
+        }
+        atomicMax(&smx[(q >> 3) % BP], __float_as_uint(fabsf(a)));   // LDS; non-negative floats order as bits
+      }
+      if (q < 64 * BP) abuf[(size_t)i0 * BP + q] = a;
+    }
   }
   __syncthreads();
   if ((int)threadIdx.x < B) bmax[(size_t)blockIdx.x * B + threadIdx.x] = __uint_as_float(smx[threadIdx.x]);
