@@ -257,6 +257,26 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
   }
   __syncthreads();
   const int idl = ids[rt * 16 + (lane & 15)];          // this lane's A-operand row (-1: none)
+  // the epilogue's biases and token powers of two: with one k half loaded now, so that they arrive with the first
+  // chunks instead of costing a round trip after the last one (with two k halves the registers are short: in the
+  // epilogue)
+  float ebias[4], esx[NTT];
+  auto load_epi = [&]() {
+    const float* bp = GT ? bg : bu;
+    const Buf bb(bp ? (const void*)bp : (const void*)xsc, bp ? (uint32_t)F * 4u : 0u);   // no bias: 0
+    const Buf bs(xsc, (uint32_t)NTT * 64u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = ids[rt * 16 + (lane >> 4) * 4 + i];
+      ebias[i] = bb.ldf(boff(KS == 1 && id >= 0, (uint32_t)(id >= 0 ? id : 0) * 4u));
+    }
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+      const int tok = t * 16 + (lane & 15);
+      esx[t] = bs.ldf(boff(tok < B, (uint32_t)tok * 4u));
+    }
+  };
+  if constexpr (KH == 1) load_epi();
   const int jq = lane >> 4;                            // lane group: the k block of a quad this lane holds
   const int KB = (D + 31) >> 5, nblk = D >> 5;
   const int KQ = (KB + 3) >> 2;                        // quads
@@ -421,20 +441,14 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
     }
   }
   if (kh == 0) {
-    int idr[4];                                        // the rows of this lane's 4 outputs (D layout)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) idr[i] = ids[rt * 16 + (lane >> 4) * 4 + i];
-    const float* bp = GT ? bg : bu;
-    float bias[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bias[i] = (bp && idr[i] >= 0) ? bp[idr[i]] : 0.f;
+    if constexpr (KH == 2) load_epi();
     const size_t FB = (size_t)F * B;
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       amx[t] = 0.f;
       const int tok = t * 16 + (lane & 15);
       const int r0 = i0 + rt * 16 + (lane >> 4) * 4;   // this lane's 4 rows: half an octet
-      const float sx = tok < B ? xsc[tok] : 0.f;
+      const float sx = esx[t];
       float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -450,9 +464,9 @@ void k_ur(const void* __restrict__ Wg, const void* __restrict__ Sg,
           continue;
         }
         if (GT) {
-          a = fmaxf(g + bias[i], 0.f) * u;
+          a = fmaxf(g + ebias[i], 0.f) * u;
         } else {
-          a = fmaxf(u + bias[i], 0.f);
+          a = fmaxf(u + ebias[i], 0.f);
           if (ACT == 2) a *= a;
         }
         a4[i] = (tok < B && ii < n) ? a : 0.f;         // the 64-row tile is written whole: zeros past n and B
@@ -551,6 +565,18 @@ __global__ __launch_bounds__(NTR) void k_ur16(const void* __restrict__ Wg, const
   }
   __syncthreads();
   const int idl = ids[lane & 15];                      // this lane's A-operand row (-1: none)
+  // the epilogue's biases and token power of two (wave 0), loaded now so that they arrive with the first quads
+  float ebias[4], esx;
+  {
+    const float* bp = GT ? bg : bu;
+    const Buf bb(bp ? (const void*)bp : (const void*)xsc, bp ? (uint32_t)F * 4u : 0u);   // no bias: 0
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = ids[(lane >> 4) * 4 + i];
+      ebias[i] = bb.ldf(boff(w == 0 && id >= 0, (uint32_t)(id >= 0 ? id : 0) * 4u));
+    }
+    esx = Buf(xsc, 64u).ldf(boff(w == 0 && (lane & 15) < B, (uint32_t)(lane & 15) * 4u));
+  }
   const int jq = lane >> 4;                            // lane group: the k block of a quad this lane holds
   const int KB = (D + 31) >> 5, nblk = D >> 5;
   const int KQ = (KB + 3) >> 2;                        // quads
@@ -650,14 +676,12 @@ __global__ __launch_bounds__(NTR) void k_ur16(const void* __restrict__ Wg, const
   }
   const int tok = lane & 15;
   const int r0 = i0 + (lane >> 4) * 4;                 // this lane's 4 rows: half an octet
-  const float sx = tok < B ? xsc[tok] : 0.f;
-  const float* bp = GT ? bg : bu;
+  const float sx = esx;
   float a4[4], amx = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ii = r0 + i;
-    const int id = ids[(lane >> 4) * 4 + i];
-    const float bias = (bp && id >= 0) ? bp[id] : 0.f;
+    const float bias = ebias[i];
     const float u = au[i] * sx, g = ag[i] * sx;
     float a;
     if (GT) {
