@@ -141,6 +141,22 @@ def test_all_and_none_active(gpu_ready, t, expect):
         assert res["n"] == 0 and np.all(res["y"] == 0.0)
 
 
+# one token with every neuron active: the fused kernels' blocks then take several passes of 8 rows each (n > 2048
+# gives all 256 blocks 9-24 rows), and with n just above 512 the working block count rises from 64
+@pytest.mark.parametrize("name,wl", [
+    ("relu_f16_6000", small("c1", D=256, F=6000, r=16, L=1, density=0.5)),
+    ("reglu_q4_3000", small("c5", D=256, F=3000, r=8, L=1, density=0.5)),
+    ("relu_f16_520", small("c1", D=256, F=520, r=16, L=1, density=0.5)),
+])
+def test_fused_passes_all_active(gpu_ready, name, wl):
+    case = make_case(wl, 0, gpu_ready)
+    x = _x(wl, 1, 2)
+    res = run_gpu(case, torch.from_numpy(x).to(gpu_ready), t=1e-30)
+    st = check(case, x, res, t=1e-30)
+    say(f"[{name}] all active", st)
+    assert res["n"] == wl.F
+
+
 @pytest.mark.parametrize("F", [1, 63, 64, 65, 129])
 @pytest.mark.parametrize("B", [1, 3])
 def test_tiny_neuron_counts(gpu_ready, F, B):
