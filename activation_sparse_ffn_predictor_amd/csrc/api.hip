@@ -85,7 +85,9 @@ bool decode_batch(int B, int D, int F) {
 //    (ceil(F / 64) 64 x ceil(B / 16) 16 fp32); for B == 1 at least the decision bitmaps of the folded single-token
 //    layer]
 //   [B > 1: normalised x: B * D fp32]
-//   [partial y: UD_KS_MAX * B * D fp32 for B > 1, G_FUSED * D fp32 for B == 1][predictor h: B * r fp32]
+//   [partial y: UD_KS_MAX * B * D fp32 for B > 1, G_FUSED * D fp32 for B == 1]
+//   [B > 1: partial pre-activations][B > 1: token fragments and powers of two][B > 1: largest-|a| table]
+//   [predictor h: B * r fp32]
 size_t ws_a_bytes(int B, int F) {
   const size_t tiles = B > 1 ? (size_t)((F + 63) / 64) * 64 * ((B + 15) / 16) * 16 * sizeof(float) : 0;
   return align256(std::max({(size_t)F * B * sizeof(float), tiles,

@@ -63,12 +63,14 @@
  * state kept between calls): activations a [F, B] fp32 (for B == 1 at least
  * 4 KiB: sffn_decode keeps its per-block decision bitmaps there); for B > 1 the
  * normalised inputs [B, D]; partial sums of y, [256, D] fp32 for B == 1 (one
- * per block of the fused kernel) or [8, B, D] for B > 1 (row splits; the
+ * per block of the fused kernel) or [16, B, D] for B > 1 (row splits; the
  * union predictor also keeps its partial h there); for B > 1 the partial
- * pre-activations of the k-split union row kernel, [2, 2, F, B] fp32, and the
- * union row kernel's token operands (two fp16 planes of ceil(D/32) x
- * ceil(B/16) KiB, then 16 fp32 per 16 tokens); the predictor's h [B, r] fp32
- * last. One workspace may serve the predict and
+ * pre-activations of the k-split union row kernel, [KS, 2, F, B] fp32 (KS = 8,
+ * 4 or 2 shares for 7-8, 9-16 and 17-32 tokens, none otherwise), the union
+ * row kernel's token operands (room for two fp16 planes of ceil(D/32) x
+ * ceil(B/16) KiB, then 16 fp32 per 16 tokens) and its largest |a| per row
+ * tile and token; the predictor's h [B, r] fp32 last. One workspace may serve
+ * the predict and
  * forward calls of a layer in turn on one stream; calls that overlap in time
  * need separate workspaces.
  *
